@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA layer on one MI355X at 64K context, plus its roofline and the
+CPU oracle timed on a bounded sample of the same work.
+
+Prints ONE JSON line.  ``value`` is decode tokens/s at 64K context: batch 8, context 65,536,
+the ratio-128 layer (512 compressed rows, all attended, 128-token window, 64 heads over a
+512 latent, bf16); a step is one decode token for every sequence (compressor step + decode
+attention with its window-ring update).  The same line carries ``prefill``: the 2048-token
+chunk 63,488 -> 65,536 of a ratio-4 layer (overlapping compressor on both lanes, indexer
+top-512 over 15,872..16,384 rows, sparse attention), as tokens/s.
+
+Both workloads start from a prefix cache built through the library itself (compressor over
+the whole prefix in 8192-token blocks, then one attention call that fills the window ring).
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_attention_dsv4_amd as K  # noqa: E402
+import synth.csa as SC  # noqa: E402
+from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+BLOCK = 8192
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ prefix caches
+def build_prefix(layer: CsaLayer, spec: LayerSpec, seed: int, L: int):
+    """Bring every sequence of ``layer`` to L tokens: compress the whole prefix, then one
+    attention call over the last W tokens to fill the window ring."""
+    B = layer.batch
+    P = layer.params
+    for t0 in range(0, L, BLOCK):
+        S = min(BLOCK, L - t0)
+        f = ["a", "g"] + (["ai", "gi"] if spec.has_indexer else [])
+        tok = SC.batch_token_inputs(spec, seed, [t0] * B, S, device="cuda", fields=f)
+        if spec.has_rows:
+            K.dsv4_compress_prefill(spec.comp_cfg(), layer.state, tok["a"], tok["g"], [t0] * B,
+                                    P["ape"], P["norm_w"], P["inv_freq"], layer.rows)
+        if spec.has_indexer:
+            K.dsv4_compress_prefill(spec.index_comp_cfg(), layer.state_i, tok["ai"], tok["gi"],
+                                    [t0] * B, P["ape_i"], P["norm_w_i"], P["inv_freq"], layer.rows_i)
+    t0 = L - spec.window
+    tok = SC.batch_token_inputs(spec, seed, [t0] * B, spec.window, device="cuda",
+                                fields=["q", "kv", "qi", "w"])
+    n_rows = [L // spec.ratio] * B if spec.has_rows else None
+    sel = None
+    if spec.has_indexer:
+        sel = torch.empty(B, spec.window, spec.topk, dtype=torch.int32, device="cuda")
+        K.dsv4_index_topk(spec.index_cfg(), tok["qi"], tok["w"], layer.rows_i, n_rows, [t0] * B,
+                          sel, layer.ws_index)
+    out = torch.empty_like(tok["q"])
+    K.dsv4_csa_attn_prefill(spec.attn_cfg(), tok["q"], tok["kv"], layer.ring,
+                            layer.rows if spec.has_rows else None, sel, n_rows, [t0] * B,
+                            P["sinks"], out, layer.ws_attn)
+    layer.lengths = [L] * B
+    torch.cuda.synchronize()
+
+
+def kernel_time(name: str):
+    n, ms = K.dsv4_trace_read(name)
+    return n, ms
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+# ------------------------------------------------------------------ decode @ 64K
+def bench_decode(args, seed=0):
+    spec = LayerSpec(ratio=128, indexer=False, topk=0)
+    B, L = args.decode_batch, args.context
+    steps, warm = args.steps, args.warmup
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, B, L + steps + warm + 8, params, device="cuda", max_chunk=spec.window)
+    t_setup = time.time()
+    build_prefix(layer, spec, seed, L)
+    log(f"[decode] prefix of {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
+    # inputs of every step, resident before timing
+    toks = []
+    for i in range(warm + steps):
+        t = SC.batch_token_inputs(spec, seed, [L + i] * B, 1, device="cuda",
+                                  fields=["q", "kv", "a", "g"])
+        toks.append({k: v[:, 0].contiguous() for k, v in t.items()})
+    for i in range(warm):
+        layer.decode(toks[i])
+    torch.cuda.synchronize()
+    K.dsv4_trace_reset()
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        layer.decode(toks[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # kernel durations, measured in a second identical pass with the event trace on
+    K.dsv4_trace_enable(True)
+    K.dsv4_trace_reset()
+    pos = list(layer.lengths)
+    for i in range(warm, warm + steps):
+        layer.decode(toks[i])
+    torch.cuda.synchronize()
+    names = K.dsv4_trace_kernels()
+    per_kernel = {n: kernel_time(n) for n in names}
+    K.dsv4_trace_enable(False)
+    attn_name = max((n for n in per_kernel if n.startswith("attn")), key=lambda n: per_kernel[n][1])
+    n_l, ms_l = per_kernel[attn_name]
+    # algorithmic bytes of one decode attention launch: q and out (bf16) + every attended key
+    keys = spec.window + (L + warm) // spec.ratio
+    bytes_launch = B * (2 * spec.heads * spec.dim * 2 + keys * spec.dim * 2)
+    achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
+    res = {
+        "tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3,
+        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": attn_name,
+                     "bytes_per_launch": bytes_launch},
+    }
+    layer_state = (layer, toks, spec, params, pos)
+    return res, layer_state
+
+
+def cpu_baseline_decode(layer_state, sample_steps):
+    """The oracle doing the same decode work (window + all visible rows, per sequence) on
+    the host, for ``sample_steps`` steps of every sequence.  Rows and ring are the GPU
+    caches copied to the host (the oracle consumes them as inputs)."""
+    import oracle
+    layer, toks, spec, params, pos = layer_state
+    B = layer.batch
+    rows = layer.rows.float().cpu().numpy().astype(np.float64)
+    sinks = params["sinks"].cpu().numpy()
+    n = pos[0]
+    kv_hist = np.random.default_rng(0).standard_normal((spec.window, spec.dim))
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(sample_steps):
+        for b in range(B):
+            q = toks[i]["q"][b].float().cpu().numpy()[None].astype(np.float64)
+            p = n + i
+            kv = np.concatenate([kv_hist[1:], toks[i]["kv"][b].float().cpu().numpy()[None]])
+            nv = min(oracle.visible_rows(p, spec.ratio), rows.shape[1])
+            oracle.csa_attention(q, kv, rows[b, :nv], None, [p], window=spec.window,
+                                 ratio=spec.ratio, sinks=sinks, scale=spec.scale, store="bf16",
+                                 kv_offset=p - spec.window + 1)
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{sample_steps} decode steps x {B} sequences of the 64K ratio-128 layer "
+                      f"(window + {rows.shape[1]} rows per query), numpy fp32 oracle"}
+
+
+# ------------------------------------------------------------------ prefill @ 64K
+def bench_prefill(args, seed=1):
+    spec = LayerSpec(ratio=4)
+    S, L = args.chunk, args.context
+    start = L - S
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, 1, L, params, device="cuda", max_chunk=max(S, spec.window))
+    t_setup = time.time()
+    build_prefix(layer, spec, seed, start)
+    log(f"[prefill] prefix of {start} tokens built in {time.time() - t_setup:.1f}s")
+    tok = SC.batch_token_inputs(spec, seed, [start], S, device="cuda")
+    snap = {"state": layer.state.clone(), "state_i": layer.state_i.clone(), "ring": layer.ring.clone()}
+    sel = torch.empty(1, S, spec.topk, dtype=torch.int32, device="cuda")
+
+    def step():
+        layer.state.copy_(snap["state"])
+        layer.state_i.copy_(snap["state_i"])
+        layer.ring.copy_(snap["ring"])
+        layer.lengths = [start]
+        return layer.prefill(tok, sel_out=sel)
+
+    reps = max(1, args.prefill_reps)
+    for _ in range(max(1, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    K.dsv4_trace_enable(True)
+    K.dsv4_trace_reset()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    names = K.dsv4_trace_kernels()
+    per_kernel = {n: kernel_time(n) for n in names}
+    K.dsv4_trace_enable(False)
+    # algorithmic flops of the chunk: indexer q.k over every visible row, attention QK^T and PV
+    idx_pairs = sum(min((p + 1) // 4, L // 4) for p in range(start, L))
+    idx_flops = 2.0 * spec.index_heads * spec.index_dim * idx_pairs
+    keys = sum(spec.window + min(spec.topk, (p + 1) // 4) for p in range(start, L))
+    attn_flops = 4.0 * spec.heads * spec.dim * keys
+    dom = max(per_kernel, key=lambda n: per_kernel[n][1])
+    n_d, ms_d = per_kernel[dom]
+    dom_flops = idx_flops if "index" in dom else attn_flops if "attn" in dom else 0.0
+    achieved = dom_flops / (ms_d / n_d * 1e-3) / 1e12
+    total_ms = sum(v[1] for v in per_kernel.values()) / reps
+    res = {
+        "tok_s": S / wall, "ms_per_chunk": wall * 1e3,
+        "workload": f"ratio-4 layer, chunk {start}->{L} (S={S}), indexer top-{spec.topk}, "
+                    f"64 heads x 512 latent, bf16",
+        "flops_per_chunk": idx_flops + attn_flops,
+        "tflops_whole_chunk": (idx_flops + attn_flops) / (total_ms * 1e-3) / 1e12,
+        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": dom, "flops_per_launch": dom_flops},
+    }
+    return res, (layer, tok, spec, params, start, sel)
+
+
+def cpu_baseline_prefill(state, n_queries):
+    """The oracle on ``n_queries`` queries of the same chunk: indexer scores over every
+    visible row, top-k, attention over window + selected rows (rows from the GPU cache)."""
+    import oracle
+    layer, tok, spec, params, start, _ = state
+    rows = layer.rows[0].float().cpu().numpy().astype(np.float64)
+    rows_i = layer.rows_i[0].float().cpu().numpy().astype(np.float64)
+    sinks = params["sinks"].cpu().numpy()
+    S = tok["q"].shape[1]
+    idx = np.linspace(spec.window - 1, S - 1, n_queries).astype(int)   # windows inside the chunk
+    q = tok["q"][0].float().cpu().numpy().astype(np.float64)
+    kv = tok["kv"][0].float().cpu().numpy().astype(np.float64)
+    qi = tok["qi"][0].float().cpu().numpy()
+    w = tok["w"][0].cpu().numpy()
+    t0 = time.perf_counter()
+    for i in idx:
+        p = start + int(i)
+        nv = oracle.visible_rows(p, spec.ratio)
+        sc = oracle.index_scores(qi[i:i + 1], w[i:i + 1], rows_i[:nv])
+        sel = oracle.select_topk(sc, [p], ratio=spec.ratio, k=spec.topk)
+        lo = int(i) - spec.window + 1
+        oracle.csa_attention(q[i:i + 1], kv[lo:i + 1], rows, sel, [p], window=spec.window,
+                             ratio=spec.ratio, sinks=sinks, scale=spec.scale, store="bf16",
+                             kv_offset=start + lo)
+    dt = time.perf_counter() - t0
+    return {"value": n_queries / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{n_queries} of the {S} queries of the 64K prefill chunk (indexer over "
+                      f"~16K rows, top-512, attention), numpy fp32 oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--context", type=int, default=65536)
+    ap.add_argument("--decode-batch", type=int, default=8)
+    ap.add_argument("--chunk", type=int, default=2048)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--cpu-decode-steps", type=int, default=64)
+    ap.add_argument("--cpu-prefill-queries", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the CSA layer here runs on a single MI355X and has no "
+              "multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    K.lib()
+    dec, dec_state = bench_decode(args)
+    log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step']:.3f} ms/step")
+    pre = None
+    if not args.skip_prefill:
+        pre, pre_state = bench_prefill(args)
+        log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = {"decode": cpu_baseline_decode(dec_state, args.cpu_decode_steps)}
+        if pre is not None:
+            cpu["prefill"] = cpu_baseline_prefill(pre_state, args.cpu_prefill_queries)
+        cpu = dict(cpu["decode"], prefill=cpu.get("prefill"),
+                   host=platform.processor() or platform.machine())
+    line = {
+        "metric": "CSA decode tokens/s and prefill tokens/s at 64K ctx; % HBM/MFMA peak",
+        "value": dec["tok_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode, ratio-128 layer, batch {args.decode_batch}, context "
+                               f"{args.context}, 64 heads x 512 latent, window 128, all rows attended",
+                   "global_batch": args.decode_batch, "seq_len": args.context,
+                   "parallelism": "single-gpu"},
+        "roofline": dec["roofline"],
+        "kernels": dec["kernels"],
+        "prefill": pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,87 @@
+// Shared device/host helpers for the CSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+namespace dsv4 {
+
+// ------------------------------------------------------------------ storage types
+// bf16 is carried as its raw 16-bit pattern; arithmetic is always fp32.
+struct bf16 {
+    uint16_t x;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float(uint32_t(v.x) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// Round to nearest, ties to even (inputs are finite; NaN maps to a quiet NaN).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{uint16_t(0x7fc0)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16{uint16_t(u >> 16)};
+}
+// Value after a round trip through the storage type.
+template <typename T> __device__ __forceinline__ float round_to(float v) {
+    return to_f32(from_f32<T>(v));
+}
+
+// Order-preserving map of an fp32 score to a u32 key (larger score -> larger key).
+// -0.0 is folded onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------------ per-sequence host ints
+// Host-side per-sequence integers travel as kernel arguments, one launch per slice of at
+// most kSeqSlice sequences, so no device buffer is needed for them.
+constexpr int kSeqSlice = 128;
+struct SeqInts {
+    int32_t v[kSeqSlice];
+};
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+// Block-wide reductions for blockDim.x a multiple of 64, up to 1024; `red` holds 16 floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; ++i) t += red[i];
+    return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = -INFINITY;
+    for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+// ------------------------------------------------------------------ launch bookkeeping
+// Every launch goes through these so that the optional kernel trace can bracket it.
+void trace_begin(const char* name, hipStream_t s);
+void trace_end(const char* name, hipStream_t s);
+
+}  // namespace dsv4

@@ -1,0 +1,197 @@
+// Gated-pooling compressor (one lane): rows for completed windows + frontier state update.
+//
+// Pages: MTPLX PR #216 "What V4 adds" (learned gated pooling, overlapping ratio-4 windows,
+// plain ratio-128 windows, compressed lanes maintained incrementally in prefill and decode);
+// mlx-lm PR #1189 Thump604's fix list (ratio-4 lanes are 2*D wide), aidiffuser's indexer
+// path (the overlap transform folds the previous window in; the tail and previous window
+// are carried across calls; absolute positions set the APE origin), stepnoy's index-space
+// fix (tail buffered and replayed, absolute position accumulates), OmarB97 note 2 (rows
+// RoPE'd at birth at j*r); MTPLX PR #216 "Decode path" (pool in fp32, cast to the storage
+// dtype before the norm).
+//
+// Layout of the frontier state of one sequence: [lane (kv, gate)][coff][r][coff*D].  Token t
+// lives in window slot (t / r) % coff at position t % r.  With coff = 2 the state holds the
+// previous complete window and the current partial one; with coff = 1 only the current one.
+//
+// Two kernels per call:
+//   compress_rows_kernel  one workgroup per emitted row: reads every slot of the row from
+//                         the state (tokens before the call) or the new lanes, pools per
+//                         channel with an online softmax, then norm and RoPE in LDS;
+//   compress_state_kernel copies the new tokens of the last coff windows into the state.
+// The second runs after the first on the stream, because a row of this call may read a
+// state slot that the update overwrites.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dsv4 {
+
+namespace {
+
+constexpr int kCompThreads = 256;
+
+template <typename T>
+struct CompArgs {
+    int r, coff, D, rd;
+    float eps;
+    T* state;
+    const T* lane_a;
+    const T* lane_g;
+    const T* ape;
+    const T* gamma;
+    const float* inv_freq;
+    T* rows;
+    int64_t row_cap;
+    int64_t n_new;
+};
+
+// Address of token t's lane value at lane column `col`, from the state or the new lanes.
+template <typename T>
+__device__ __forceinline__ const T* token_ptr(const CompArgs<T>& a, int b, int lane, int64_t t,
+                                              int64_t lb, int col) {
+    const int W = a.coff * a.D;
+    if (t < lb) {
+        const size_t st = size_t(2) * a.coff * a.r * W;
+        const T* base = a.state + size_t(b) * st + size_t(lane) * a.coff * a.r * W;
+        return base + (size_t((t / a.r) % a.coff) * a.r + size_t(t % a.r)) * W + col;
+    }
+    const T* lanep = lane == 0 ? a.lane_a : a.lane_g;
+    return lanep + (size_t(b) * a.n_new + size_t(t - lb)) * W + col;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kCompThreads)
+compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
+    extern __shared__ float zrow[];           // [D]
+    __shared__ float red[16];
+    const int b = blockIdx.y;
+    const int64_t lb = len_before.v[b];
+    const int64_t j = lb / a.r + blockIdx.x;  // row index
+    if ((j + 1) * a.r > lb + a.n_new) return;
+    const int D = a.D, W = a.coff * a.D;
+
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        float m = -INFINITY, l = 0.f, acc = 0.f;
+        for (int half = 0; half < a.coff; ++half) {
+            // overlap: half 0 <- window j-1, half 1 <- window j; plain: half 0 <- window j
+            const int64_t win = (a.coff == 2 && half == 0) ? j - 1 : j;
+            if (win < 0) continue;
+            const int col = half * D + c;
+            for (int s = 0; s < a.r; ++s) {
+                const int64_t t = win * a.r + s;
+                const float logit = to_f32(*token_ptr(a, b, 1, t, lb, col)) +
+                                    to_f32(a.ape[size_t(s) * W + col]);
+                const float v = to_f32(*token_ptr(a, b, 0, t, lb, col));
+                if (logit > m) {
+                    const float f = expf(m - logit);   // 0 when m = -inf
+                    acc = acc * f + v;
+                    l = l * f + 1.f;
+                    m = logit;
+                } else {
+                    const float e = expf(logit - m);
+                    acc += e * v;
+                    l += e;
+                }
+            }
+        }
+        const float y = round_to<T>(acc / l);
+        zrow[c] = y;
+        ss += y * y;
+    }
+    const float tot = block_sum(ss, red);
+    const float den = sqrtf(tot / float(D) + a.eps);
+    for (int c = threadIdx.x; c < D; c += blockDim.x)
+        zrow[c] = round_to<T>(zrow[c] / den * to_f32(a.gamma[c]));
+    __syncthreads();
+    const int r0 = D - a.rd;
+    const float pos = float(j * a.r);
+    T* out = a.rows + (size_t(b) * a.row_cap + size_t(j)) * D;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        float v = zrow[c];
+        if (c >= r0) {
+            const int i = (c - r0) >> 1;
+            const float x0 = zrow[r0 + 2 * i], x1 = zrow[r0 + 2 * i + 1];
+            float sn, cs;
+            sincosf(pos * a.inv_freq[i], &sn, &cs);
+            v = ((c - r0) & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
+        }
+        out[c] = from_f32<T>(v);
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kCompThreads)
+compress_state_kernel(CompArgs<T> a, SeqInts len_before) {
+    const int b = blockIdx.y;
+    const int64_t lb = len_before.v[b];
+    const int64_t la = lb + a.n_new;
+    int64_t keep_from = (la / a.r - (a.coff - 1)) * a.r;   // first token of the kept windows
+    if (keep_from < lb) keep_from = lb;
+    const int64_t t = keep_from + blockIdx.x;
+    if (t >= la) return;
+    const int W = a.coff * a.D;
+    const size_t st = size_t(2) * a.coff * a.r * W;
+    const size_t slot = (size_t((t / a.r) % a.coff) * a.r + size_t(t % a.r)) * W;
+    const size_t src = (size_t(b) * a.n_new + size_t(t - lb)) * W;
+    T* sa = a.state + size_t(b) * st + slot;
+    T* sg = sa + size_t(a.coff) * a.r * W;
+    for (int c = threadIdx.x; c < W; c += blockDim.x) {
+        sa[c] = a.lane_a[src + c];
+        sg[c] = a.lane_g[src + c];
+    }
+}
+
+template <typename T>
+hipError_t run(const CompressJob& j, hipStream_t s) {
+    const int W = j.coff * j.D;
+    const size_t st_elems = size_t(2) * j.coff * j.r * W;
+    for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
+        const int nb = std::min(kSeqSlice, j.batch - b0);
+        SeqInts lb{};
+        int64_t max_rows = 0, max_keep = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int64_t l0 = j.len_before[b0 + i];
+            lb.v[i] = int32_t(l0);
+            const int64_t la = l0 + j.n_new;
+            max_rows = std::max(max_rows, la / j.r - l0 / j.r);
+            int64_t keep_from = std::max<int64_t>(l0, (la / j.r - (j.coff - 1)) * j.r);
+            max_keep = std::max(max_keep, la - keep_from);
+        }
+        CompArgs<T> a;
+        a.r = j.r; a.coff = j.coff; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
+        a.state = static_cast<T*>(j.state) + size_t(b0) * st_elems;
+        a.lane_a = static_cast<const T*>(j.lane_a) + size_t(b0) * j.n_new * W;
+        a.lane_g = static_cast<const T*>(j.lane_g) + size_t(b0) * j.n_new * W;
+        a.ape = static_cast<const T*>(j.ape);
+        a.gamma = static_cast<const T*>(j.gamma);
+        a.inv_freq = j.inv_freq;
+        a.rows = static_cast<T*>(j.rows) + size_t(b0) * j.row_cap * j.D;
+        a.row_cap = j.row_cap;
+        a.n_new = j.n_new;
+        if (max_rows > 0) {
+            trace_begin("compress_rows", s);
+            hipLaunchKernelGGL(compress_rows_kernel<T>, dim3(unsigned(max_rows), nb),
+                               dim3(kCompThreads), j.D * sizeof(float), s, a, lb);
+            trace_end("compress_rows", s);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (max_keep > 0) {
+            trace_begin("compress_state", s);
+            hipLaunchKernelGGL(compress_state_kernel<T>, dim3(unsigned(max_keep), nb),
+                               dim3(kCompThreads), 0, s, a, lb);
+            trace_end("compress_state", s);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressJob& j, hipStream_t s) {
+    return j.bf16 ? run<bf16>(j, s) : run<float>(j, s);
+}
+
+}  // namespace dsv4

@@ -1,0 +1,71 @@
+// Host-side launchers of the CSA kernels.  Arguments reaching these have been validated by
+// the C ABI layer (api.cpp); the launchers only split the batch and enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dsv4 {
+
+struct CompressJob {
+    int r, coff, D, rd;
+    float eps;
+    bool bf16;
+    void* state;               // [B][2][coff][r][coff*D]
+    const void* lane_a;        // [B][n_new][coff*D]
+    const void* lane_g;
+    const void* ape;           // [r][coff*D]
+    const void* gamma;         // [D]
+    const float* inv_freq;     // [rd/2]
+    void* rows;                // [B][row_cap][D]
+    int64_t row_cap;
+    int64_t n_new;
+    int batch;
+    const int64_t* len_before; // host [B]
+};
+hipError_t launch_compress(const CompressJob& j, hipStream_t s);
+
+struct IndexJob {
+    int Hi, di, k, r;
+    bool bf16;
+    const void* qi;            // [B][S][Hi][di]
+    const float* w;            // [B][S][Hi]
+    const void* rows;          // [B][row_cap][di]
+    int64_t row_cap;
+    int64_t S;
+    int64_t n_stride;          // row stride of the score workspace (>= max n_rows)
+    int batch;
+    const int64_t* n_rows;     // host [B]
+    const int64_t* pos0;       // host [B]
+    int32_t* sel;              // [B][S][k]
+    uint32_t* keys;            // workspace [B][S][n_stride]
+};
+hipError_t launch_index_topk(const IndexJob& j, hipStream_t s);
+size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max);
+
+struct AttnJob {
+    int H, D, W, r, k;
+    float scale;
+    bool bf16;
+    const void* q;             // [B][S][H][D]
+    const void* kv_new;        // [B][S][D]
+    void* ring;                // [B][W][D]
+    const void* rows;          // [B][row_cap][D] or null
+    int64_t row_cap;
+    const int32_t* sel;        // [B][S][k] or null
+    const float* sinks;        // [H]
+    void* out;                 // [B][S][H][D]
+    int64_t S;
+    int batch;
+    const int64_t* n_rows;     // host [B] or null
+    const int64_t* pos0;       // host [B]
+    void* ws;
+    size_t ws_bytes;
+};
+hipError_t launch_attention(const AttnJob& j, hipStream_t s);
+size_t attn_workspace_bytes(int H, int D, int W, int r, int k, int batch, int64_t S);
+// Largest key count (window + rows) one query may have for the attention kernels.
+int64_t attn_max_keys(int H, int D);
+
+}  // namespace dsv4

@@ -1,0 +1,155 @@
+"""One CSA layer's device state and the call order of the C ABI for prefill and decode.
+
+A ``CsaLayer`` owns, for a batch of sequences, every buffer the layer carries between calls:
+the two compressor frontiers (attention lane and indexer lane), the two compressed lanes,
+the sliding-window ring and the indexer workspace.  Per step it calls, in order (MTPLX PR
+#216 "What V4 adds": both prefill and decode maintain the lanes incrementally; mlx-lm PR
+#1189 stepnoy's index-space fix: the indexer lane is accumulated unconditionally, so its
+row count always equals the attention lane's):
+
+    compress (attention lane) -> compress (indexer lane) -> index_topk -> attention
+
+Host-side lengths are plain integers; nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (AttnCfg, CompCfg, IndexCfg, dsv4_comp_state_bytes, dsv4_compress_prefill,
+               dsv4_compress_step, dsv4_csa_attn_decode, dsv4_csa_attn_prefill,
+               dsv4_index_topk, dsv4_index_workspace_bytes, dsv4_attn_workspace_bytes)
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    """Shapes of one layer.  ratio 0 = pure sliding-window layer; overlap applies to ratio 4."""
+    ratio: int
+    heads: int = 64
+    dim: int = 512
+    rope_dim: int = 64
+    window: int = 128
+    index_heads: int = 64
+    index_dim: int = 128
+    topk: int = 512
+    indexer: bool = True          # score and select rows (else every visible row is attended)
+    overlap: bool | None = None   # default: ratio == 4
+    eps: float = 1e-6
+    dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def coff(self) -> int:
+        return 2 if self.is_overlap else 1
+
+    @property
+    def is_overlap(self) -> bool:
+        return (self.ratio == 4) if self.overlap is None else bool(self.overlap)
+
+    @property
+    def has_rows(self) -> bool:
+        return self.ratio > 0
+
+    @property
+    def has_indexer(self) -> bool:
+        return self.ratio > 0 and self.indexer
+
+    @property
+    def scale(self) -> float:
+        return self.dim ** -0.5
+
+    def comp_cfg(self) -> CompCfg:
+        return CompCfg(self.ratio, self.is_overlap, self.dim, self.rope_dim, self.eps, self.dtype)
+
+    def index_comp_cfg(self) -> CompCfg:
+        return CompCfg(self.ratio, self.is_overlap, self.index_dim, self.rope_dim, self.eps,
+                       self.dtype)
+
+    def index_cfg(self) -> IndexCfg:
+        return IndexCfg(self.index_heads, self.index_dim, self.topk, self.ratio, self.dtype)
+
+    def attn_cfg(self) -> AttnCfg:
+        return AttnCfg(self.heads, self.dim, self.window, self.ratio, self.topk, self.scale,
+                       self.dtype)
+
+
+class CsaLayer:
+    """Device state of one layer for ``batch`` sequences of up to ``max_tokens`` tokens."""
+
+    def __init__(self, spec: LayerSpec, batch: int, max_tokens: int, params: dict,
+                 device="cuda", max_chunk: int = 2048):
+        self.spec, self.batch, self.device = spec, batch, device
+        self.params = params                  # ape, norm_w, ape_i, norm_w_i, inv_freq, sinks
+        self.lengths = [0] * batch
+        dt = spec.dtype
+        self.ring = torch.zeros(batch, spec.window, spec.dim, dtype=dt, device=device)
+        self.row_cap = max_tokens // spec.ratio if spec.has_rows else 0
+        if spec.has_rows:
+            cc = spec.comp_cfg()
+            self.state = torch.empty(batch, dsv4_comp_state_bytes(cc, 1), dtype=torch.uint8,
+                                     device=device)
+            self.rows = torch.empty(batch, max(1, self.row_cap), spec.dim, dtype=dt, device=device)
+        if spec.has_indexer:
+            ic = spec.index_comp_cfg()
+            self.state_i = torch.empty(batch, dsv4_comp_state_bytes(ic, 1), dtype=torch.uint8,
+                                       device=device)
+            self.rows_i = torch.empty(batch, max(1, self.row_cap), spec.index_dim, dtype=dt,
+                                      device=device)
+            nb = dsv4_index_workspace_bytes(spec.index_cfg(), batch, max_chunk, max(1, self.row_cap))
+            self.ws_index = torch.empty(nb, dtype=torch.uint8, device=device)
+        nb = dsv4_attn_workspace_bytes(spec.attn_cfg(), batch, max_chunk)
+        self.ws_attn = torch.empty(max(1, nb), dtype=torch.uint8, device=device)
+
+    # ------------------------------------------------------------------ state views
+    def n_rows(self, extra: int = 0):
+        r = self.spec.ratio
+        return [(n + extra) // r for n in self.lengths] if r > 0 else None
+
+    # ------------------------------------------------------------------ steps
+    def prefill(self, tok: dict, sel_out=None) -> torch.Tensor:
+        """Process S new tokens of every sequence.  ``tok`` holds q [B,S,H,D], kv [B,S,D],
+        a, g [B,S,coff*D], and with an indexer ai, gi [B,S,coff*di], qi [B,S,Hi,di],
+        w [B,S,Hi].  Returns out [B,S,H,D]; writes the selection into ``sel_out`` if given."""
+        sp, P = self.spec, self.params
+        S = tok["q"].shape[1]
+        pos0 = list(self.lengths)
+        out = torch.empty_like(tok["q"])
+        sel = None
+        if sp.has_rows:
+            dsv4_compress_prefill(sp.comp_cfg(), self.state, tok["a"], tok["g"], pos0, P["ape"],
+                                  P["norm_w"], P["inv_freq"], self.rows)
+        if sp.has_indexer:
+            dsv4_compress_prefill(sp.index_comp_cfg(), self.state_i, tok["ai"], tok["gi"], pos0,
+                                  P["ape_i"], P["norm_w_i"], P["inv_freq"], self.rows_i)
+            sel = sel_out if sel_out is not None else torch.empty(
+                self.batch, S, sp.topk, dtype=torch.int32, device=self.device)
+            dsv4_index_topk(sp.index_cfg(), tok["qi"], tok["w"], self.rows_i, self.n_rows(S),
+                            pos0, sel, self.ws_index)
+        dsv4_csa_attn_prefill(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
+                              self.rows if sp.has_rows else None, sel, self.n_rows(S), pos0,
+                              P["sinks"], out, self.ws_attn)
+        self.lengths = [n + S for n in self.lengths]
+        return out
+
+    def decode(self, tok: dict, sel_out=None) -> torch.Tensor:
+        """One token per sequence; ``tok`` tensors have no S axis (q [B,H,D], kv [B,D], ...)."""
+        sp, P = self.spec, self.params
+        pos = list(self.lengths)
+        out = torch.empty_like(tok["q"])
+        sel = None
+        if sp.has_rows:
+            dsv4_compress_step(sp.comp_cfg(), self.state, tok["a"], tok["g"], pos, P["ape"],
+                               P["norm_w"], P["inv_freq"], self.rows)
+        if sp.has_indexer:
+            dsv4_compress_step(sp.index_comp_cfg(), self.state_i, tok["ai"], tok["gi"], pos,
+                               P["ape_i"], P["norm_w_i"], P["inv_freq"], self.rows_i)
+            sel = sel_out if sel_out is not None else torch.empty(
+                self.batch, 1, sp.topk, dtype=torch.int32, device=self.device)
+            dsv4_index_topk(sp.index_cfg(), tok["qi"][:, None], tok["w"][:, None], self.rows_i,
+                            self.n_rows(1), pos, sel, self.ws_index)
+            sel = sel[:, 0]
+        dsv4_csa_attn_decode(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
+                             self.rows if sp.has_rows else None, sel, self.n_rows(1), pos,
+                             P["sinks"], out, self.ws_attn)
+        self.lengths = [n + 1 for n in self.lengths]
+        return out

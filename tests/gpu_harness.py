@@ -1,0 +1,157 @@
+"""Helpers of the GPU parity tests: run the HIP path on seeded inputs, run the oracle on the
+same inputs, and compare with the tolerances the tests state.
+
+Comparison bars (from the layer's stated targets; see each function):
+  * attention outputs: max-rel per (token, head) row <= 2e-2 in bf16, <= 1e-5 in fp32,
+    where max-rel = max|gpu - ref| / max|ref| over the row's latent dims;
+  * top-k sets: exact, except rows whose oracle score lies within 1e-5 relative of the
+    k-th score (with a floor of 1e-3 * max|score| when the k-th score is ~0);
+  * compressed rows: fp32 max-rel <= 1e-5; bf16 every element within 2 ulp of the oracle's.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth.csa as SC
+from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec
+
+
+def store_of(spec: LayerSpec) -> str:
+    return "bf16" if spec.dtype == torch.bfloat16 else "f32"
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------ the HIP path
+def run_gpu(spec: LayerSpec, seed: int, batch: int, chunks, n_decode: int, device="cuda"):
+    """Prefill ``chunks`` (token counts) then ``n_decode`` decode steps, for every sequence.
+
+    Returns a dict: out [B, T, H, D] (cpu), sel [B, T, k] int32 (cpu, when indexed),
+    rows [B, T//r, D], rows_i [B, T//r, di] (cpu), and the layer."""
+    T = sum(chunks) + n_decode
+    params = SC.layer_params(spec, seed, device=device)
+    layer = CsaLayer(spec, batch, T, params, device=device, max_chunk=max(list(chunks) + [1]))
+    out = torch.empty(batch, T, spec.heads, spec.dim, dtype=spec.dtype)
+    sel = torch.full((batch, T, spec.topk), -2, dtype=torch.int32) if spec.has_indexer else None
+    t = 0
+    for S in chunks:
+        tok = SC.batch_token_inputs(spec, seed, [t] * batch, S, device=device)
+        s_buf = torch.empty(batch, S, spec.topk, dtype=torch.int32, device=device) \
+            if spec.has_indexer else None
+        o = layer.prefill(tok, sel_out=s_buf)
+        out[:, t:t + S] = o.cpu()
+        if sel is not None:
+            sel[:, t:t + S] = s_buf.cpu()
+        t += S
+    for _ in range(n_decode):
+        tok = SC.batch_token_inputs(spec, seed, [t] * batch, 1, device=device)
+        tok = {k: v[:, 0].contiguous() for k, v in tok.items()}
+        s_buf = torch.empty(batch, 1, spec.topk, dtype=torch.int32, device=device) \
+            if spec.has_indexer else None
+        o = layer.decode(tok, sel_out=s_buf)
+        out[:, t] = o.cpu()
+        if sel is not None:
+            sel[:, t] = s_buf[:, 0].cpu()
+        t += 1
+    torch.cuda.synchronize()
+    res = {"out": out, "sel": sel, "layer": layer, "T": T}
+    if spec.has_rows:
+        n = T // spec.ratio
+        res["rows"] = layer.rows[:, :n].cpu()
+        if spec.has_indexer:
+            res["rows_i"] = layer.rows_i[:, :n].cpu()
+    return res
+
+
+# ------------------------------------------------------------------ the oracle
+def oracle_inputs(spec: LayerSpec, seed: int, b: int, T: int):
+    tok = SC.token_inputs(spec, seed, b, 0, T)
+    par = SC.layer_params(spec, seed)
+    return ({k: f64(v) for k, v in tok.items()}, {k: f64(v) for k, v in par.items()})
+
+
+def oracle_rows(spec, tok, par, index_lane=False):
+    if index_lane:
+        return oracle.compressor_rows(tok["ai"], tok["gi"], par["ape_i"], par["norm_w_i"],
+                                      par["inv_freq"], ratio=spec.ratio, overlap=spec.is_overlap,
+                                      eps=spec.eps, store=store_of(spec))
+    return oracle.compressor_rows(tok["a"], tok["g"], par["ape"], par["norm_w"], par["inv_freq"],
+                                  ratio=spec.ratio, overlap=spec.is_overlap, eps=spec.eps,
+                                  store=store_of(spec))
+
+
+def oracle_scores(spec, tok, rows_i, positions):
+    P = np.asarray(positions)
+    return oracle.index_scores(tok["qi"][P], tok["w"][P], rows_i)
+
+
+def oracle_select(spec, scores, positions):
+    return oracle.select_topk(scores, positions, ratio=spec.ratio, k=spec.topk)
+
+
+def oracle_attention(spec, tok, par, rows, sel, positions):
+    return oracle.csa_attention(tok["q"][np.asarray(positions)], tok["kv"], rows, sel, positions,
+                                window=spec.window, ratio=spec.ratio, sinks=par["sinks"],
+                                scale=spec.scale, store=store_of(spec))
+
+
+# ------------------------------------------------------------------ comparisons
+def max_rel_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per row over the last axis: max|a - b| / max|b|."""
+    num = np.abs(a - b).max(axis=-1)
+    den = np.abs(b).max(axis=-1)
+    return num / np.maximum(den, 1e-30)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def assert_rows_match(gpu: np.ndarray, ref: np.ndarray, store: str, what: str):
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    if store == "f32":
+        mr = max_rel_rows(gpu, ref)
+        assert mr.max() <= 1e-5, f"{what}: fp32 max-rel {mr.max():.3g}"
+    else:
+        ulps = np.abs(gpu - ref) / bf16_ulp(ref)
+        bad = ulps > 2.0
+        assert not bad.any(), f"{what}: {bad.sum()} elements beyond 2 ulp (max {ulps.max():.1f})"
+    return float(np.abs(gpu - ref).max())
+
+
+def topk_band_ok(sel_gpu: np.ndarray, sel_ref: np.ndarray, scores: np.ndarray, positions,
+                 spec: LayerSpec):
+    """Check one batch of queries.  Returns (n_exact, n_band, n_bad, bad_queries)."""
+    n_exact = n_band = n_bad = 0
+    bad = []
+    for i, p in enumerate(positions):
+        nv = min(oracle.visible_rows(p, spec.ratio), scores.shape[1])
+        g = sel_gpu[i]
+        chosen = [int(x) for x in g if x >= 0]
+        # validity of the GPU row: ascending, unique, visible, right count, -1 padded
+        valid = (chosen == sorted(set(chosen)) and len(chosen) == min(spec.topk, nv)
+                 and all(0 <= j < nv for j in chosen)
+                 and all(int(x) == -1 for x in g[len(chosen):]))
+        if not valid:
+            n_bad += 1
+            bad.append((p, "invalid"))
+            continue
+        if np.array_equal(g, sel_ref[i]):
+            n_exact += 1
+            continue
+        s = scores[i, :nv].astype(np.float64)
+        ref = [int(x) for x in sel_ref[i] if x >= 0]
+        sk = min(s[j] for j in ref)                     # the k-th score
+        tol = 1e-5 * max(abs(sk), 1e-3 * np.abs(s).max())
+        diff = set(chosen) ^ set(ref)
+        if all(abs(s[j] - sk) <= tol for j in diff):
+            n_band += 1
+        else:
+            n_bad += 1
+            bad.append((p, sorted(diff)[:8]))
+    return n_exact, n_band, n_bad, bad

@@ -1,0 +1,219 @@
+"""Parity of the HIP path against the oracle, through the C ABI (needs a gfx950 GPU).
+
+Stage-isolated checks feed each oracle stage the GPU's own upstream outputs (rows, then the
+selection), so an independent bf16 rounding upstream cannot move a later comparison; the
+fp32 tiny layer is also checked end to end from the raw inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_dsv4_amd.layer import LayerSpec
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+TINY = LayerSpec(ratio=4, heads=4, dim=64, rope_dim=16, window=16, index_heads=2, index_dim=32,
+                 topk=8, dtype=torch.float32)
+SMALL_BF16 = LayerSpec(ratio=4, heads=8, dim=64, rope_dim=16, window=16, index_heads=4,
+                       index_dim=32, topk=16)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+
+
+def _check_layer(spec, res, b, positions, seed, end_to_end=False):
+    """Stage-isolated comparison of sequence b at the given query positions."""
+    T = res["T"]
+    tok, par = G.oracle_inputs(spec, seed, b, T)
+    store = G.store_of(spec)
+    rows = sel = None
+    report = {}
+    if spec.has_rows:
+        rows_ref = G.oracle_rows(spec, tok, par)
+        rows = G.f64(res["rows"][b])
+        report["rows_maxabs"] = G.assert_rows_match(rows, rows_ref, store, "attention-lane rows")
+        if end_to_end:
+            rows = rows_ref
+    if spec.has_indexer:
+        rows_i_ref = G.oracle_rows(spec, tok, par, index_lane=True)
+        rows_i = G.f64(res["rows_i"][b])
+        report["rows_i_maxabs"] = G.assert_rows_match(rows_i, rows_i_ref, store, "indexer-lane rows")
+        if end_to_end:
+            rows_i = rows_i_ref
+        scores = G.oracle_scores(spec, tok, rows_i, positions)
+        sel_ref = G.oracle_select(spec, scores, positions)
+        sel_gpu = res["sel"][b].numpy()[np.asarray(positions)]
+        ne, nb, nbad, bad = G.topk_band_ok(sel_gpu, sel_ref, scores, positions, spec)
+        report.update(topk_exact=ne, topk_band=nb)
+        assert nbad == 0, f"top-k mismatches outside the band: {bad[:5]}"
+        sel = sel_gpu if not end_to_end else sel_ref
+        agree = np.array([np.array_equal(sel_gpu[i], sel_ref[i]) for i in range(len(positions))])
+    else:
+        agree = np.ones(len(positions), dtype=bool)
+    ref = G.oracle_attention(spec, tok, par, rows, sel, positions)
+    gpu = G.f64(res["out"][b])[np.asarray(positions)]
+    mr = G.max_rel_rows(gpu, ref)[agree]
+    bar = 1e-5 if store == "f32" else 2e-2
+    report["attn_maxrel"] = float(mr.max()) if mr.size else 0.0
+    assert mr.size == 0 or mr.max() <= bar, f"attention max-rel {mr.max():.3g} > {bar}"
+    print(f"  seq {b}: {report}", flush=True)
+    return report
+
+
+def test_tiny_fp32_prefill_end_to_end():
+    """256-token fp32 layer (4 heads, latent 64, window 16, ratio-4 overlap, indexer 2x32,
+    top-8), one-shot prefill; every query against the oracle from the raw inputs."""
+    res = G.run_gpu(TINY, 0, 1, [256], 0)
+    _check_layer(TINY, res, 0, list(range(256)), 0, end_to_end=True)
+    _check_layer(TINY, res, 0, list(range(256)), 0)
+
+
+def test_tiny_fp32_decode_equals_prefill():
+    """Prefill 192 then 64 decode steps equals the one-shot 256-token prefill bit for bit,
+    and chunked prefills (1, 3, 7, 16, 64 ...; not aligned to r or W) equal it too."""
+    one = G.run_gpu(TINY, 0, 1, [256], 0)
+    dec = G.run_gpu(TINY, 0, 1, [192], 64)
+    chk = G.run_gpu(TINY, 0, 1, [1, 3, 7, 16, 64, 5, 33, 2, 61], 64)
+    for other in (dec, chk):
+        assert torch.equal(other["rows"], one["rows"])
+        assert torch.equal(other["rows_i"], one["rows_i"])
+        assert torch.equal(other["sel"], one["sel"])
+        assert torch.equal(other["out"], one["out"])
+    _check_layer(TINY, dec, 0, list(range(192, 256)), 0, end_to_end=True)
+
+
+def test_tiny_fp32_dense_to_sparse_crossing():
+    """The indexer engages once a query sees more than k = 8 rows (p >= 35 at ratio 4)."""
+    res = G.run_gpu(TINY, 1, 1, [30], 20)
+    sel = res["sel"][0].numpy()
+    for p in range(50):
+        nv = oracle.visible_rows(p, 4)
+        row = sel[p]
+        if nv <= 8:
+            assert list(row[:nv]) == list(range(nv)) and (row[nv:] == -1).all()
+        else:
+            assert (row >= 0).all()
+    _check_layer(TINY, res, 0, list(range(50)), 1, end_to_end=True)
+
+
+def test_small_bf16_ratio4_sparse_chunked():
+    """bf16, ratio 4 overlap, sparse regime (100 rows > k = 16), 2 sequences, chunked prefill
+    of ragged chunk sizes, then decode steps across window and compress boundaries."""
+    res = G.run_gpu(SMALL_BF16, 3, 2, [37, 100, 63], 200)
+    for b in range(2):
+        _check_layer(SMALL_BF16, res, b, list(range(0, 400, 3)) + list(range(380, 400)), 3)
+    dec = G.run_gpu(SMALL_BF16, 3, 2, [400], 0)
+    assert torch.equal(dec["rows"], res["rows"]) and torch.equal(dec["rows_i"], res["rows_i"])
+    assert torch.equal(dec["sel"], res["sel"])
+
+
+def test_ratio128_dense_bf16():
+    """Plain ratio-128 windows, no indexer (every visible row attended), across row births."""
+    spec = LayerSpec(ratio=128, heads=8, dim=64, rope_dim=16, window=16, indexer=False, topk=0)
+    res = G.run_gpu(spec, 5, 2, [100, 200], 134)
+    for b in range(2):
+        _check_layer(spec, res, b, list(range(0, 434, 5)) + list(range(380, 434)), 5)
+
+
+def test_ratio0_window_only():
+    spec = LayerSpec(ratio=0, heads=8, dim=64, rope_dim=16, window=16, indexer=False, topk=0)
+    res = G.run_gpu(spec, 6, 3, [9, 40], 30)
+    for b in range(3):
+        _check_layer(spec, res, b, list(range(79)), 6)
+
+
+def test_ratio4_overlap_off_and_odd_ratio():
+    """A non-overlapping ratio-4 lane and an odd ratio (3) with an indexer."""
+    for spec in (LayerSpec(ratio=4, overlap=False, heads=4, dim=64, rope_dim=16, window=8,
+                           index_heads=2, index_dim=32, topk=6, dtype=torch.float32),
+                 LayerSpec(ratio=3, overlap=True, heads=4, dim=64, rope_dim=16, window=8,
+                           index_heads=2, index_dim=32, topk=6, dtype=torch.float32)):
+        res = G.run_gpu(spec, 7, 1, [50, 11], 29)
+        _check_layer(spec, res, 0, list(range(90)), 7, end_to_end=True)
+
+
+def test_ragged_batch_positions():
+    """Sequences at different positions in one call: each sequence's prefix is built alone
+    (batch-1 views of the same buffers), then one batched prefill and decode continue all."""
+    import synth.csa as SC
+    from sparse_attention_dsv4_amd import layer as LY
+    spec = SMALL_BF16
+    seed, B = 9, 3
+    lens = [5, 130, 61]
+    T = max(lens) + 40 + 10
+    params = SC.layer_params(spec, seed, device="cuda")
+    big = LY.CsaLayer(spec, B, T, params, device="cuda")
+    for b, L in enumerate(lens):
+        one = LY.CsaLayer(spec, 1, T, params, device="cuda")
+        # share buffers with sequence b of the batch
+        one.state, one.rows, one.ring = big.state[b:b + 1], big.rows[b:b + 1], big.ring[b:b + 1]
+        one.state_i, one.rows_i = big.state_i[b:b + 1], big.rows_i[b:b + 1]
+        tok = SC.batch_token_inputs(spec, seed, [0], L, device="cuda")
+        tok = {k: v.clone() for k, v in tok.items()}
+        # sequence b's own stream: regenerate with b's index
+        tok = {k: SC.token_inputs(spec, seed, b, 0, L, device="cuda")[k][None].contiguous()
+               for k in tok}
+        one.prefill(tok)
+    big.lengths = list(lens)
+    tok = {k: torch.stack([SC.token_inputs(spec, seed, b, L, L + 40, device="cuda")[k]
+                           for b, L in enumerate(lens)]) for k in tok}
+    sel = torch.empty(B, 40, spec.topk, dtype=torch.int32, device="cuda")
+    out = big.prefill(tok, sel_out=sel).cpu()
+    outs = [out]
+    sels = [sel.cpu()]
+    for i in range(10):
+        t = {k: torch.stack([SC.token_inputs(spec, seed, b, L + 40 + i, L + 41 + i,
+                                             device="cuda")[k][0] for b, L in enumerate(lens)])
+             for k in tok}
+        s1 = torch.empty(B, 1, spec.topk, dtype=torch.int32, device="cuda")
+        outs.append(big.decode(t, sel_out=s1).cpu()[:, None])
+        sels.append(s1.cpu())
+    out = torch.cat(outs, 1)
+    sel = torch.cat(sels, 1)
+    for b, L in enumerate(lens):
+        Tb = L + 50
+        res = {"T": Tb, "out": torch.zeros(B, Tb, spec.heads, spec.dim),
+               "sel": torch.zeros(B, Tb, spec.topk, dtype=torch.int32),
+               "rows": big.rows[:, :Tb // 4].cpu(), "rows_i": big.rows_i[:, :Tb // 4].cpu()}
+        res["out"][b, L:] = out[b].float()
+        res["sel"][b, L:] = sel[b]
+        _check_layer(spec, res, b, list(range(L, Tb)), seed)
+
+
+def test_empty_calls_are_noops():
+    import sparse_attention_dsv4_amd as K
+    spec = SMALL_BF16
+    cfg = spec.comp_cfg()
+    rows = torch.full((1, 4, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(1, K.dsv4_comp_state_bytes(cfg, 1), dtype=torch.uint8, device="cuda")
+    lane = torch.empty(1, 0, 128, dtype=torch.bfloat16, device="cuda")
+    K.dsv4_compress_prefill(cfg, st, lane, lane, [0],
+                            torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"),
+                            torch.zeros(64, dtype=torch.bfloat16, device="cuda"),
+                            torch.zeros(8, device="cuda"), rows)
+    torch.cuda.synchronize()
+    assert (rows == 7.0).all()
+
+
+def test_fails_closed_before_launch():
+    """A capacity error leaves the buffers as they were."""
+    import sparse_attention_dsv4_amd as K
+    spec = SMALL_BF16
+    cfg = spec.comp_cfg()
+    rows = torch.full((1, 2, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(1, K.dsv4_comp_state_bytes(cfg, 1), dtype=torch.uint8, device="cuda")
+    lane = torch.ones(1, 12, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(K.Dsv4Error) as e:
+        K.dsv4_compress_prefill(cfg, st, lane, lane, [0],
+                                torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"),
+                                torch.ones(64, dtype=torch.bfloat16, device="cuda"),
+                                torch.zeros(8, device="cuda"), rows)
+    assert e.value.code == -3
+    torch.cuda.synchronize()
+    assert (rows == 3.0).all() and (st == 0).all()
