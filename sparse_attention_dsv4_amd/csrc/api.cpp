@@ -157,8 +157,8 @@ size_t dsv4_index_workspace_bytes(const dsv4_index_cfg* cfg, int32_t batch, int6
 
 size_t dsv4_attn_workspace_bytes(const dsv4_attn_cfg* cfg, int32_t batch, int64_t s) {
     if (check_attn_cfg(cfg) != DSV4_OK || batch < 0 || s < 0) return 0;
-    return dsv4::attn_workspace_bytes(cfg->heads, cfg->dim, cfg->window, cfg->ratio, cfg->topk,
-                                      batch, s);
+    return dsv4::attn_workspace_bytes(cfg->dtype == DSV4_BF16, cfg->heads, cfg->dim, cfg->window,
+                                      cfg->ratio, cfg->topk, batch, s);
 }
 
 int dsv4_compress_prefill(const dsv4_comp_cfg* cfg, void* state, const void* kv_lane,
@@ -255,7 +255,8 @@ static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_n
     if (has_rows && row_cap < 0) return fail(DSV4_EINVAL, "row_cap < 0");
     if (sel && !has_rows) return fail(DSV4_EINVAL, "sel given for a layer without rows");
     if (sel && cfg->topk < 1) return fail(DSV4_EINVAL, "sel given with topk < 1");
-    const int64_t key_cap = dsv4::attn_max_keys(cfg->heads, cfg->dim);
+    const int64_t key_cap = dsv4::attn_max_keys(cfg->dtype == DSV4_BF16, cfg->heads, cfg->dim,
+                                                cfg->topk, sel != nullptr);
     for (int b = 0; b < batch; ++b) {
         if (pos0[b] < 0) return fail(DSV4_EINVAL, "pos[%d] < 0", b);
         if (pos0[b] + s > kPosLimit) return fail(DSV4_ECAPACITY, "sequence %d passes 2^31 tokens", b);
@@ -272,8 +273,8 @@ static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_n
             return fail(DSV4_EUNSUPPORTED, "a query of sequence %d has %lld keys, above %lld", b,
                         (long long)nkeys, (long long)key_cap);
     }
-    const size_t need_ws = dsv4::attn_workspace_bytes(cfg->heads, cfg->dim, cfg->window,
-                                                      cfg->ratio, cfg->topk, batch, s);
+    const size_t need_ws = dsv4::attn_workspace_bytes(cfg->dtype == DSV4_BF16, cfg->heads, cfg->dim,
+                                                      cfg->window, cfg->ratio, cfg->topk, batch, s);
     if (need_ws > 0 && (!ws || ws_bytes < need_ws))
         return fail(DSV4_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need_ws);
     dsv4::AttnJob j;

@@ -13,8 +13,18 @@
 // visible prefix by a 4-pass, 8-bit radix select, then compacts in row order: every row
 // with key > T, plus the lowest-indexed rows with key == T until k rows are taken.  Row
 // order compaction makes the output ascending without a sort.
+//
+// mfma scoring (bf16, 64 heads x 128 dims): heads are the M dimension of
+// v_mfma_f32_32x32x16_bf16 and rows the N dimension, so a lane ends with 16 heads of one
+// row; ReLU, the folded head weights and the sum over heads happen in registers (one
+// cross-half add), and only the fp32 score key leaves the kernel.  Each wave keeps one
+// query's 64x128 block as A fragments; 128-row tiles of the lane are staged in LDS and
+// shared by the workgroup's queries (prefill: 4 queries, one per wave; decode: one query,
+// the 4 waves split the tile).  The per-(query, row) arithmetic is the same in both, so a
+// decode step and a prefill chunk give bit-identical scores.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace dsv4 {
 
@@ -74,6 +84,118 @@ index_score_kernel(ScoreArgs<T> a, SeqInts pos0, SeqInts n_rows) {
         if (lane == 0) out[j] = score_key(score);
     }
 }
+
+
+// ------------------------------------------------------------------ mfma scoring
+constexpr int IH = 64;                 // indexer heads
+constexpr int ID = 128;                // indexer dims
+constexpr int IRT = 128;               // rows per LDS tile
+constexpr int IPITCH = ID * 2 + 16;    // LDS bytes per row (padded)
+
+struct IdxMfmaArgs {
+    const bf16* qi;
+    const float* w;
+    const bf16* rows;
+    int64_t row_cap;
+    int64_t S;
+    int64_t n_stride;
+    uint32_t* keys;
+    int r;
+    float scale;
+    int rows_per_block;
+};
+
+template <int QPW>
+__global__ void __launch_bounds__(256)
+index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    __shared__ __attribute__((aligned(16))) unsigned char kt[IRT * IPITCH];
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int64_t pos0 = pos0v.v[b];
+    const int64_t s = QPW == 4 ? int64_t(blockIdx.y) * 4 + w : int64_t(blockIdx.y);
+    const bool qvalid = s < a.S;
+    int64_t s_last = QPW == 4 ? int64_t(blockIdx.y) * 4 + 3 : int64_t(blockIdx.y);
+    if (s_last > a.S - 1) s_last = a.S - 1;
+    int64_t nv_max = (pos0 + s_last + 1) / a.r;
+    if (nv_max > n_rows.v[b]) nv_max = n_rows.v[b];
+    const int64_t j_begin = int64_t(blockIdx.x) * a.rows_per_block;
+    if (j_begin >= nv_max) return;
+    const int64_t j_end = j_begin + a.rows_per_block < nv_max ? j_begin + a.rows_per_block : nv_max;
+    int64_t nv = 0;
+    if (qvalid) {
+        nv = (pos0 + s + 1) / a.r;
+        if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    }
+
+    bf16x8 qa[2][ID / 16];
+    float wsc[2][16];
+    if (qvalid) {
+        const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(s)) * IH + l32) * ID + 8 * hi;
+        const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int ks = 0; ks < ID / 16; ++ks) qa[m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wsc[m][i] = wr[32 * m + c_row(i, lane)] * a.scale;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int ks = 0; ks < ID / 16; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qa[m][ks][e] = __bf16(0.f);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wsc[m][i] = 0.f;
+        }
+    }
+    uint32_t* kout = a.keys + (size_t(b) * a.S + size_t(qvalid ? s : 0)) * a.n_stride;
+
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += IRT) {
+        // stage 128 rows: 16 lanes per 256-byte row, a wave covers 4 consecutive rows
+#pragma unroll
+        for (int i = 0; i < IRT / 16; ++i) {
+            const int row = (tid >> 4) + 16 * i;
+            const int64_t jj = j0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (jj < j_end)
+                v = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID +
+                                                    (tid & 15) * 8);
+            store16(kt + row * IPITCH + (tid & 15) * 16, v);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < (QPW == 4 ? 4 : 1); ++t) {
+            const int nt = QPW == 4 ? t : w;
+            floatx16 c0, c1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                c0[i] = 0.f;
+                c1[i] = 0.f;
+            }
+            const unsigned char* kr = kt + (32 * nt + l32) * IPITCH + 16 * hi;
+#pragma unroll
+            for (int ks = 0; ks < ID / 16; ++ks) {
+                const bf16x8 kb = load_bf16x8(kr + ks * 32);
+                c0 = mfma32x32x16(qa[0][ks], kb, c0);
+                c1 = mfma32x32x16(qa[1][ks], kb, c1);
+            }
+            float sc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc = fmaf(wsc[0][i], fmaxf(c0[i], 0.f), sc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc = fmaf(wsc[1][i], fmaxf(c1[i], 0.f), sc);
+            sc += __shfl_xor(sc, 32, 64);
+            const int64_t jj = j0 + 32 * nt + l32;
+            if (hi == 0 && jj < nv) kout[jj] = score_key(sc);
+        }
+        __syncthreads();
+    }
+}
+
+bool use_index_mfma(bool bf16_, int Hi, int di) { return bf16_ && Hi == IH && di == ID; }
 
 struct SelArgs {
     int k, r;
@@ -169,6 +291,152 @@ topk_select_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     }
 }
 
+
+// ------------------------------------------------------------------ select with keys in LDS
+// For up to kSelLdsKeys visible rows: the query's keys are staged in LDS once; an 11-bit
+// histogram over all of them locates the bucket of the k-th largest key, that bucket's keys
+// are gathered as candidates, and two more passes (11 and 10 bits) over the candidates give
+// the exact threshold.  Compaction in row order then writes the ascending selection.
+constexpr int kSelLdsKeys = 16384;
+constexpr int kSelLdsThreads = 512;
+constexpr int kSelCand = 4096;
+
+// Exclusive prefix sum over the workgroup (kSelLdsThreads threads); `tmp` holds 8 ints.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) tmp[w] = x;
+    __syncthreads();
+    int add = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kSelLdsThreads / 64; ++i) {
+        tot += tmp[i];
+        add += i < w ? tmp[i] : 0;
+    }
+    *total = tot;
+    return x - v + add;
+}
+
+// Given a histogram of `bins` bins and the count `rem` still needed from the keys it covers,
+// find the bin holding the rem-th largest key.  Writes the bin and the count still needed
+// inside it to sh[0], sh[1].
+__device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int rem, int* tmp, int* sh) {
+    const int per = bins / kSelLdsThreads;            // 4 or 2 bins per thread
+    const int t = threadIdx.x;
+    int part = 0;
+    for (int i = 0; i < per; ++i) part += int(hist[t * per + i]);
+    int total;
+    const int excl = block_excl_scan(part, tmp, &total);
+    int above = total - excl - part;                  // keys in bins above this thread's bins
+    for (int i = per - 1; i >= 0; --i) {
+        const int h = int(hist[t * per + i]);
+        if (above < rem && above + h >= rem) {
+            sh[0] = t * per + i;
+            sh[1] = rem - above;
+        }
+        above += h;
+    }
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kSelLdsThreads)
+topk_select_lds_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
+    __shared__ uint32_t keys[kSelLdsKeys];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t cand[kSelCand];
+    __shared__ int tmp[8];
+    __shared__ int sh[4];
+    const int b = blockIdx.y;
+    const int64_t s = blockIdx.x;
+    const int64_t p = int64_t(pos0.v[b]) + s;
+    int nv = int((p + 1) / a.r);
+    if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    int32_t* out = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
+    const int tid = threadIdx.x;
+    if (nv <= a.k) {
+        for (int i = tid; i < a.k; i += blockDim.x) out[i] = i < nv ? i : -1;
+        return;
+    }
+    const uint32_t* gk = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
+    for (int j = tid; j < nv; j += blockDim.x) keys[j] = gk[j];
+    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    if (tid == 0) sh[2] = 0;
+    __syncthreads();
+
+    // pass 1: bits 31..21 over every key
+    for (int j = tid; j < nv; j += blockDim.x) atomicAdd(&hist[keys[j] >> 21], 1u);
+    __syncthreads();
+    find_bucket(hist, 2048, a.k, tmp, sh);
+    const uint32_t d1 = uint32_t(sh[0]);
+    int rem = sh[1];
+    for (int j = tid; j < nv; j += blockDim.x) {
+        const uint32_t kk = keys[j];
+        if ((kk >> 21) == d1) {
+            const int pos = atomicAdd(&sh[2], 1);
+            if (pos < kSelCand) cand[pos] = kk;
+        }
+    }
+    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int ncand = sh[2];
+    const bool in_cand = ncand <= kSelCand;
+    const uint32_t* src = in_cand ? cand : keys;
+    const int nsrc = in_cand ? ncand : nv;
+
+    // pass 2: bits 20..10 of keys in bucket d1
+    for (int j = tid; j < nsrc; j += blockDim.x) {
+        const uint32_t kk = src[j];
+        if ((kk >> 21) == d1) atomicAdd(&hist[(kk >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_bucket(hist, 2048, rem, tmp, sh);
+    const uint32_t d2 = uint32_t(sh[0]);
+    rem = sh[1];
+    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    // pass 3: bits 9..0 of keys with prefix (d1, d2)
+    const uint32_t pre = (d1 << 11) | d2;
+    for (int j = tid; j < nsrc; j += blockDim.x) {
+        const uint32_t kk = src[j];
+        if ((kk >> 10) == pre) atomicAdd(&hist[kk & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bucket(hist, 1024, rem, tmp, sh);
+    const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
+    rem = sh[1];
+
+    // compaction in row order over contiguous segments
+    const int seg = (nv + blockDim.x - 1) / blockDim.x;
+    const int lo = tid * seg;
+    const int hi = lo + seg < nv ? lo + seg : nv;
+    int ngt = 0, neq = 0;
+    for (int j = lo; j < hi; ++j) {
+        const uint32_t kk = keys[j];
+        ngt += kk > thr;
+        neq += kk == thr;
+    }
+    int tg, te;
+    const int gt0 = block_excl_scan(ngt, tmp, &tg);
+    const int eq0 = block_excl_scan(neq, tmp, &te);
+    int eq_rank = eq0;
+    int o = gt0 + (eq_rank < rem ? eq_rank : rem);
+    for (int j = lo; j < hi; ++j) {
+        const uint32_t kk = keys[j];
+        if (kk > thr) {
+            out[o++] = j;
+        } else if (kk == thr) {
+            if (eq_rank < rem) out[o++] = j;
+            ++eq_rank;
+        }
+    }
+}
+
 template <typename T>
 hipError_t run(const IndexJob& j, hipStream_t st) {
     for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
@@ -182,7 +450,37 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             nv_max = std::max(nv_max, nv);
         }
         const size_t qoff = size_t(b0) * j.S;
-        if (nv_max > j.k) {
+        if (nv_max > j.k && use_index_mfma(j.bf16, j.Hi, j.di)) {
+            IdxMfmaArgs a;
+            a.qi = static_cast<const bf16*>(j.qi) + qoff * IH * ID;
+            a.w = j.w + qoff * IH;
+            a.rows = static_cast<const bf16*>(j.rows) + size_t(b0) * j.row_cap * ID;
+            a.row_cap = j.row_cap;
+            a.S = j.S;
+            a.n_stride = j.n_stride;
+            a.keys = j.keys + qoff * j.n_stride;
+            a.r = j.r;
+            a.scale = 1.0f / sqrtf(float(j.di)) / sqrtf(float(j.Hi));
+            const bool per4 = j.S >= 4;
+            const int64_t groups = per4 ? (j.S + 3) / 4 : j.S;
+            // enough row blocks to give the chip >= ~2048 workgroups
+            int64_t blocks = (2048 + groups * nb - 1) / (groups * nb);
+            const int64_t tiles = (nv_max + IRT - 1) / IRT;
+            if (blocks > tiles) blocks = tiles;
+            if (blocks < 1) blocks = 1;
+            a.rows_per_block = int(((tiles + blocks - 1) / blocks) * IRT);
+            const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
+            trace_begin("index_score_mfma", st);
+            if (per4)
+                hipLaunchKernelGGL(index_score_mfma_kernel<4>, dim3(gx, unsigned(groups), nb), dim3(256),
+                                   0, st, a, pos, nr);
+            else
+                hipLaunchKernelGGL(index_score_mfma_kernel<1>, dim3(gx, unsigned(groups), nb), dim3(256),
+                                   0, st, a, pos, nr);
+            trace_end("index_score_mfma", st);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        } else if (nv_max > j.k) {
             ScoreArgs<T> a;
             a.Hi = j.Hi; a.di = j.di; a.r = j.r;
             a.scale = 1.0f / sqrtf(float(j.di)) / sqrtf(float(j.Hi));
@@ -206,10 +504,17 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.k = j.k; sa.r = j.r; sa.S = j.S; sa.n_stride = j.n_stride;
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
-        trace_begin("topk_select", st);
-        hipLaunchKernelGGL(topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
-                           st, sa, pos, nr);
-        trace_end("topk_select", st);
+        if (nv_max <= kSelLdsKeys) {
+            trace_begin("topk_select_lds", st);
+            hipLaunchKernelGGL(topk_select_lds_kernel, dim3(unsigned(j.S), nb), dim3(kSelLdsThreads),
+                               0, st, sa, pos, nr);
+            trace_end("topk_select_lds", st);
+        } else {
+            trace_begin("topk_select", st);
+            hipLaunchKernelGGL(topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
+                               st, sa, pos, nr);
+            trace_end("topk_select", st);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

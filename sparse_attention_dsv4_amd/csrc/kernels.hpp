@@ -64,8 +64,9 @@ struct AttnJob {
     size_t ws_bytes;
 };
 hipError_t launch_attention(const AttnJob& j, hipStream_t s);
-size_t attn_workspace_bytes(int H, int D, int W, int r, int k, int batch, int64_t S);
-// Largest key count (window + rows) one query may have for the attention kernels.
-int64_t attn_max_keys(int H, int D);
+size_t attn_workspace_bytes(bool bf16, int H, int D, int W, int r, int k, int batch, int64_t S);
+// Largest key count (window + rows) one query may have for the attention kernels (0 when
+// the configuration is not supported at all).
+int64_t attn_max_keys(bool bf16, int H, int D, int k, bool has_sel);
 
 }  // namespace dsv4

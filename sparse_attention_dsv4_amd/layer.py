@@ -97,7 +97,9 @@ class CsaLayer:
                                       device=device)
             nb = dsv4_index_workspace_bytes(spec.index_cfg(), batch, max_chunk, max(1, self.row_cap))
             self.ws_index = torch.empty(nb, dtype=torch.uint8, device=device)
-        nb = dsv4_attn_workspace_bytes(spec.attn_cfg(), batch, max_chunk)
+        # the split-key partials depend on batch * S: size for every chunk length up to max_chunk
+        ac = spec.attn_cfg()
+        nb = max(dsv4_attn_workspace_bytes(ac, batch, s) for s in range(1, min(max_chunk, 1024) + 1))
         self.ws_attn = torch.empty(max(1, nb), dtype=torch.uint8, device=device)
 
     # ------------------------------------------------------------------ state views

@@ -129,8 +129,15 @@ def test_attention_validation(L):
     assert _attn(L, cfg, decode=False, s=-1) == EINVAL
     nosel = K.AttnCfg(heads=64, dim=512, window=128, ratio=4, topk=0, scale=0.04)
     assert _attn(L, nosel) == EINVAL                                  # sel with topk 0
-    # dense over far more rows than one query's key list can hold
-    assert _attn(L, cfg, sel=None, n_rows=_i64(400000), cap=400000, pos=_i64(1600000)) == EUNSUP
+    # generic (fp32) path: dense over far more rows than one query's key list can hold
+    f32 = K.AttnCfg(heads=64, dim=512, window=128, ratio=4, topk=512, scale=0.04,
+                    dtype=K.torch.float32)
+    assert _attn(L, f32, sel=None, n_rows=_i64(400000), cap=400000, pos=_i64(1600000)) == EUNSUP
+    # bf16 mfma path: decode splits the key list and needs the partials workspace
+    assert K.dsv4_attn_workspace_bytes(cfg, 1, 1) > 0
+    assert _attn(L, cfg, ws=None, ws_bytes=0) == EWS
+    assert _attn(L, cfg, ws=FAKE, ws_bytes=64) == EWS
+    assert K.dsv4_attn_workspace_bytes(cfg, 1, 2048) == 0      # one workgroup per query
     win = K.AttnCfg(heads=8, dim=64, window=16, ratio=0, topk=0, scale=0.1)
     assert _attn(L, win, sel=FAKE, rows=None, n_rows=None) == EINVAL    # sel without rows
     assert _attn(L, cfg, batch=0, q=None) == 0

@@ -217,3 +217,82 @@ def test_fails_closed_before_launch():
     assert e.value.code == -3
     torch.cuda.synchronize()
     assert (rows == 3.0).all() and (st == 0).all()
+
+
+# ---------------------------------------------------------------- V4-Flash shapes (mfma paths)
+V4_R4 = LayerSpec(ratio=4)                                      # 64 x 512, window 128, 64 x 128, top-512
+V4_R128 = LayerSpec(ratio=128, indexer=False, topk=0)
+V4_R0 = LayerSpec(ratio=0, indexer=False, topk=0)
+
+
+def test_v4_ratio4_sparse_prefill_and_decode():
+    """V4 shapes, ratio-4 overlap with the indexer: 2 sequences, ragged prefill chunks, then
+    decode steps (split-key decode attention); 601 rows by the end, so queries from p = 2051
+    on are in the sparse regime.  Rows bit-identical between decode and one-shot prefill;
+    selections too (the scoring arithmetic does not depend on the chunk)."""
+    res = G.run_gpu(V4_R4, 11, 2, [999, 1100, 205], 100)
+    pos = sorted(set(list(range(0, 2304, 37)) + list(range(2040, 2060)) + list(range(2304, 2404))))
+    for b in range(2):
+        _check_layer(V4_R4, res, b, pos, 11)
+    one = G.run_gpu(V4_R4, 11, 2, [2404], 0)
+    assert torch.equal(one["rows"], res["rows"]) and torch.equal(one["rows_i"], res["rows_i"])
+    assert torch.equal(one["sel"], res["sel"])
+
+
+def test_v4_ratio4_small_prefill_chunks_split_keys():
+    """Few queries per call: prefill attention also takes the split-key path."""
+    res = G.run_gpu(V4_R4, 12, 1, [2070, 3, 5], 2)
+    _check_layer(V4_R4, res, 0, list(range(2060, 2080)), 12)
+
+
+def test_v4_ratio128_dense():
+    res = G.run_gpu(V4_R128, 13, 3, [300, 700], 60)
+    for b in range(3):
+        _check_layer(V4_R128, res, b, list(range(0, 1000, 17)) + list(range(1000, 1060)), 13)
+
+
+def test_v4_ratio0_window():
+    res = G.run_gpu(V4_R0, 14, 2, [200], 30)
+    for b in range(2):
+        _check_layer(V4_R0, res, b, list(range(0, 230, 3)), 14)
+
+
+def test_v4_attention_with_ragged_selection():
+    """A caller-made selection with -1 entries in the middle, out-of-range and duplicate-free
+    rows: entries outside [0, visible) are skipped, the rest attended in list order."""
+    import sparse_attention_dsv4_amd as K
+    import synth.csa as SC
+    spec = V4_R4
+    seed, T = 15, 1200
+    res = G.run_gpu(spec, seed, 1, [T - 40], 0)
+    layer = res["layer"]
+    tok = SC.batch_token_inputs(spec, seed, [T - 40], 40, device="cuda")
+    nv_last = T // 4
+    rng = np.random.default_rng(0)
+    sel = np.full((1, 40, spec.topk), -1, dtype=np.int32)
+    for i in range(40):
+        p = T - 40 + i
+        nv = oracle.visible_rows(p, 4)
+        cand = rng.choice(nv, size=200, replace=False)
+        row = np.full(spec.topk, -1, dtype=np.int32)
+        slots = rng.choice(spec.topk, size=260, replace=False)
+        row[slots[:200]] = np.sort(cand)
+        row[slots[200:230]] = nv + rng.integers(0, 50, size=30)     # not yet visible
+        row[slots[230:]] = -7
+        sel[0, i] = row
+    sel_t = torch.from_numpy(sel).cuda()
+    out = torch.empty_like(tok["q"])
+    K.dsv4_csa_attn_prefill(spec.attn_cfg(), tok["q"], tok["kv"], layer.ring, layer.rows, sel_t,
+                            [nv_last], [T - 40], layer.params["sinks"], out, layer.ws_attn)
+    torch.cuda.synchronize()
+    tk, par = G.oracle_inputs(spec, seed, 0, T)
+    rows = G.f64(layer.rows[0, :nv_last])
+    pos = list(range(T - 40, T))
+    ref_sel = []
+    for i, p in enumerate(pos):
+        r = sel[0, i]
+        r = r[(r >= 0) & (r < oracle.visible_rows(p, 4))]
+        ref_sel.append(np.concatenate([r, np.full(spec.topk - len(r), -1)]))
+    ref = G.oracle_attention(spec, tk, par, rows, np.array(ref_sel), pos)
+    mr = G.max_rel_rows(G.f64(out[0]), ref)
+    assert mr.max() <= 2e-2, mr.max()
