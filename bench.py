@@ -93,7 +93,7 @@ def bench_decode(args, seed=0):
     B, L = args.decode_batch, args.context
     steps, warm = args.steps, args.warmup
     params = SC.layer_params(spec, seed, device="cuda")
-    layer = CsaLayer(spec, B, L + steps + warm + 8, params, device="cuda", max_chunk=spec.window)
+    layer = CsaLayer(spec, B, L + warm + 2 * steps + 8, params, device="cuda", max_chunk=spec.window)
     t_setup = time.time()
     build_prefix(layer, spec, seed, L)
     log(f"[decode] prefix of {L} tokens x {B} built in {time.time() - t_setup:.1f}s")

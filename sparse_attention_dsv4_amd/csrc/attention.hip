@@ -204,11 +204,30 @@ hipError_t run(const AttnJob& j, hipStream_t st) {
 constexpr int MH = 64;                    // heads
 constexpr int MD = 512;                   // latent dims
 constexpr int MKT = 64;                   // keys per tile
-constexpr int KPITCH = MD * 2 + 16;       // LDS bytes per key row (padded against bank conflicts)
+// LDS bytes per key row: 1024 + 48 makes both the Q.K^T operand reads (16 rows x 16 B) and
+// the transposed P.V operand reads (4 rows x 32 B per 16-lane group) bank-conflict free.
+constexpr int KPITCH = MD * 2 + 48;
+constexpr int KBUF = MKT * KPITCH;        // one key tile
 constexpr int PPITCH = MKT * 2 + 16;      // LDS bytes per head row of P
+constexpr int OPITCH = MD * 4 + 16;       // LDS bytes per head row of staged fp32 output
 constexpr int MAX_CODES = 1024;           // selected rows one workgroup may list
 constexpr int MAX_SPLITS = 32;
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_row + 16 l
+// (global_load_lds_dwordx4; the LDS base goes through m0 and must be wave-uniform).  Issued
+// as inline asm so the compiler does not order later LDS reads of the *other* key buffer
+// behind it; the caller waits with vmcnt(0) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds_row) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(uint32_t(size_t((const lds_u8*)lds_row)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(la), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 struct AttnMfmaArgs {
     const bf16* q;
@@ -228,6 +247,13 @@ struct AttnMfmaArgs {
     float* part_o;                        // [B][S][n_splits][H][D]  unnormalised output
 };
 
+// Barrier for LDS exchanges inside a tile: waits for this wave's LDS operations only, so
+// the next tile's direct-to-LDS loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+}
+
 // Source row of key `i` of the query's list: selected/visible rows first, then the window.
 __device__ __forceinline__ const bf16* mfma_key(const AttnMfmaArgs& a, int b, int64_t i,
                                                 int64_t nrow, const int32_t* codes, int64_t kb,
@@ -241,32 +267,142 @@ __device__ __forceinline__ const bf16* mfma_key(const AttnMfmaArgs& a, int b, in
     return a.ring + (size_t(b) * a.W + size_t(t % a.W)) * MD;
 }
 
+struct TileCtx {
+    int b, w, lane, mt, nt, l32, hi;
+    int64_t nrow, kb, t0, pos0;
+};
+
+// Enqueue the direct-to-LDS copy of keys [tb, tb + nkt) (one 1 KB row per wave instruction)
+// and zero the unused rows of a partial tile.
+__device__ __forceinline__ void load_tile(const AttnMfmaArgs& a, const TileCtx& c,
+                                          const int32_t* codes, unsigned char* buf, int64_t tb,
+                                          int nkt) {
+#pragma unroll 4
+    for (int i = 0; i < MKT / 4; ++i) {
+        const int kk = c.w + 4 * i;
+        if (kk < nkt) {
+            const bf16* src = mfma_key(a, c.b, tb + kk, c.nrow, codes, c.kb, c.t0, c.pos0);
+            dma16(src + c.lane * 8, buf + kk * KPITCH);
+        } else {
+            store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
+        }
+    }
+}
+
+// Lazy rescaling: the running reference max of a head moves only when a tile's max exceeds
+// it by more than kLazy (log2 units), so most tiles skip rescaling the output accumulators.
+// Every exponent stays <= 2^kLazy, far inside fp32 and bf16 range, and the final division
+// uses the same reference, so the result is unchanged.
+constexpr float kLazy = 8.0f;
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+    return make_uint2(uint32_t(bf16_bits(a)) | (uint32_t(bf16_bits(b)) << 16),
+                      uint32_t(bf16_bits(c)) | (uint32_t(bf16_bits(d)) << 16));
+}
+
+// One key tile.  Wave (mt, nt): S^T = K Q^T for keys 32nt.. x heads 32mt.., so lane l owns
+// head 32mt + l%32 and 16 keys; O^T += V^T P^T for dims 256nt.. x the same heads.
+__device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx& c,
+                                            const unsigned char* buf, unsigned char* ptile,
+                                            float (*xch)[2][MH], const bf16x8* qa, floatx16* o,
+                                            float& m_run, float& l_run, int nkt) {
+    const int mt = c.mt, nt = c.nt, lane = c.lane, l32 = c.l32, hi = c.hi;
+    const int head = 32 * mt + l32;
+    floatx16 st;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    const unsigned char* kr = buf + (32 * nt + l32) * KPITCH + 16 * hi;
+#pragma unroll
+    for (int ks = 0; ks < MD / 16; ++ks) st = mfma32x32x16(load_bf16x8(kr + ks * 32), qa[ks], st);
+    float sv[16];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const bool kvalid = 32 * nt + c_row(i, lane) < nkt;
+        sv[i] = kvalid ? st[i] * a.scale_log2 : -INFINITY;
+        lmax = fmaxf(lmax, sv[i]);
+    }
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));      // this key half, this head
+    if (hi == 0) xch[0][nt][head] = lmax;
+    lds_barrier();
+    const float tmax = fmaxf(lmax, xch[0][nt ^ 1][head]);
+    // the decision depends only on (m_run, tmax), equal in both waves of this head half
+    if (tmax > m_run + kLazy) {
+        const float alpha = exp2f(m_run - tmax);        // 0 on the first tile
+        m_run = tmax;
+        l_run *= alpha;
+#pragma unroll
+        for (int n8 = 0; n8 < 8; ++n8)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[n8][i] *= alpha;
+    }
+    float psum = 0.f;
+    unsigned char* prow = ptile + head * PPITCH + (32 * nt + 4 * hi) * 2;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {                    // registers 4 q4 .. 4 q4 + 3: 4 consecutive keys
+        float p4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p4[r] = exp2f(sv[4 * q4 + r] - m_run);
+            psum += p4[r];
+        }
+        *reinterpret_cast<uint2*>(prow + 16 * q4) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
+    }
+    l_run += psum + __shfl_xor(psum, 32, 64);          // this wave's key half only
+    lds_barrier();
+    // O^T += V^T P^T: A = 32 dims x 16 keys of V (two transposed reads), B = P^T fragment
+    const unsigned char* pr = ptile + head * PPITCH + 16 * hi;
+    const int j16 = lane & 15;
+    const unsigned char* vb0 = buf + (8 * hi + (j16 >> 2)) * KPITCH +
+                               (256 * nt + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
+#pragma unroll
+    for (int ks = 0; ks < MKT / 16; ++ks) {
+        const bf16x8 pb = load_bf16x8(pr + ks * 32);
+#pragma unroll
+        for (int n8 = 0; n8 < 8; ++n8) {
+            const unsigned char* vp = vb0 + 16 * ks * KPITCH + n8 * 64;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
+            bf16x8 va;
+            __builtin_memcpy(&va, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &up, 8);
+            o[n8] = mfma32x32x16(va, pb, o[n8]);
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256)
 attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
-    __shared__ __attribute__((aligned(16))) unsigned char ktile[MKT * KPITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KBUF];
     __shared__ __attribute__((aligned(16))) unsigned char ptile[MH * PPITCH];
     __shared__ float xch[2][2][MH];       // [max | sum][key half][head]
     __shared__ int32_t codes[MAX_CODES];
     __shared__ int32_t scan[256];
 
-    const int b = blockIdx.z;
+    TileCtx c;
+    c.b = blockIdx.z;
     const int64_t s = blockIdx.y;
     const int split = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int mt = w >> 1, nt = w & 1;    // head half; key half (QK) and dim half (PV)
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int64_t pos0 = pos0v.v[b];
-    const int64_t p = pos0 + s;
+    const int tid = threadIdx.x;
+    c.lane = tid & 63;
+    c.w = tid >> 6;
+    c.mt = c.w >> 1;                      // head half
+    c.nt = c.w & 1;                       // key half in Q.K^T, dim half in P.V
+    c.l32 = c.lane & 31;
+    c.hi = c.lane >> 5;
+    const int b = c.b;
+    c.pos0 = pos0v.v[b];
+    const int64_t p = c.pos0 + s;
 
     int64_t nv = 0;
     if (a.r > 0 && a.rows != nullptr) {
         nv = (p + 1) / a.r;
         if (nv > n_rows.v[b]) nv = n_rows.v[b];
     }
-    const int64_t t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
-    const int64_t nwin = p - t0 + 1;
-    const int64_t kb = int64_t(split) * a.keys_per_split;
-    int64_t nrow = nv;
+    c.t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
+    const int64_t nwin = p - c.t0 + 1;
+    c.kb = int64_t(split) * a.keys_per_split;
+    c.nrow = nv;
     if (a.sel != nullptr) {
         // compact the valid entries of the selection row, in order; keep those in this split
         const int32_t* sr = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
@@ -285,32 +421,38 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             scan[tid] += v;
             __syncthreads();
         }
-        nrow = scan[255];
+        c.nrow = scan[255];
         int64_t pos = scan[tid] - cnt;
         for (int e = e0; e < e1; ++e) {
             const int32_t j = sr[e];
             if (j >= 0 && j < nv) {
-                if (pos >= kb && pos < kb + a.keys_per_split) codes[pos - kb] = j;
+                if (pos >= c.kb && pos < c.kb + a.keys_per_split) codes[pos - c.kb] = j;
                 ++pos;
             }
         }
         __syncthreads();
     }
-    const int64_t nk = nrow + nwin;
+    const int64_t nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
-    if (kb >= nk) {                                   // nothing in this split
+    if (c.kb >= nk) {                                 // nothing in this split
         if (tid < MH) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
             a.part_ml[(pbase + tid) * 2 + 1] = 0.f;
         }
         return;
     }
-    const int64_t ke = kb + a.keys_per_split < nk ? kb + a.keys_per_split : nk;
+    const int64_t ke = c.kb + a.keys_per_split < nk ? c.kb + a.keys_per_split : nk;
+    const int ntiles = int((ke - c.kb + MKT - 1) / MKT);
+    auto tile_keys = [&](int t) -> int {
+        const int64_t left = ke - (c.kb + int64_t(t) * MKT);
+        return left < MKT ? int(left) : MKT;
+    };
 
+    load_tile(a, c, codes, kbuf[0], c.kb, tile_keys(0));
     // this wave's 32 heads of q, as MFMA A fragments over all 512 dims
     bf16x8 qa[MD / 16];
     {
-        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + 32 * mt + l32) * MD + 8 * hi;
+        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + 32 * c.mt + c.l32) * MD + 8 * c.hi;
 #pragma unroll
         for (int ks = 0; ks < MD / 16; ++ks) qa[ks] = load_bf16x8(qh + ks * 16);
     }
@@ -319,159 +461,113 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     for (int n8 = 0; n8 < 8; ++n8)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[n8][i] = 0.f;
-    float m_run[16], l_run[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;   // head 32mt + l%32; l_run over this key half
+    wait_vm();
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile(a, c, codes, kbuf[(t + 1) & 1], c.kb + int64_t(t + 1) * MKT, tile_keys(t + 1));
+        attend_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t));
+        wait_vm();                        // the next tile has landed
+        __syncthreads();                  // ... for every wave; and all are done with this one
     }
 
-    for (int64_t tb = kb; tb < ke; tb += MKT) {
-        const int nkt = ke - tb < MKT ? int(ke - tb) : MKT;
-        // stage the tile: each wave copies whole 1 KB rows (16 B per lane)
-#pragma unroll 4
-        for (int i = 0; i < MKT / 4; ++i) {
-            const int kk = w + 4 * i;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (kk < nkt) {
-                const bf16* src = mfma_key(a, b, tb + kk, nrow, codes, kb, t0, pos0);
-                v = *reinterpret_cast<const uint4*>(src + lane * 8);
-            }
-            store16(ktile + kk * KPITCH + lane * 16, v);
-        }
-        __syncthreads();
-
-        // S = Q K^T for (heads 32mt.., keys 32nt..)
-        floatx16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const unsigned char* kr = ktile + (32 * nt + l32) * KPITCH + 16 * hi;
-#pragma unroll
-        for (int ks = 0; ks < MD / 16; ++ks) sacc = mfma32x32x16(qa[ks], load_bf16x8(kr + ks * 32), sacc);
-        const bool kvalid = 32 * nt + l32 < nkt;
-        float sv[16], red[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sv[i] = kvalid ? sacc[i] * a.scale_log2 : -INFINITY;
-            red[i] = sv[i];
-        }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red[i] = fmaxf(red[i], __shfl_xor(red[i], off, 64));
-        if (l32 == 0)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xch[0][nt][32 * mt + c_row(i, lane)] = red[i];
-        __syncthreads();
-        float alpha[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float tmax = fmaxf(red[i], xch[0][nt ^ 1][32 * mt + c_row(i, lane)]);
-            const float mnew = fmaxf(m_run[i], tmax);
-            alpha[i] = exp2f(m_run[i] - mnew);
-            m_run[i] = mnew;
-            const float pv = exp2f(sv[i] - mnew);
-            red[i] = pv;
-            *reinterpret_cast<uint16_t*>(ptile + (32 * mt + c_row(i, lane)) * PPITCH +
-                                         (32 * nt + l32) * 2) = bf16_bits(pv);
-        }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red[i] += __shfl_xor(red[i], off, 64);
-        if (l32 == 0)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xch[1][nt][32 * mt + c_row(i, lane)] = red[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            l_run[i] = l_run[i] * alpha[i] + red[i] + xch[1][nt ^ 1][32 * mt + c_row(i, lane)];
-
-        // O += P V for (heads 32mt.., dims 256nt..)
-#pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[n8][i] *= alpha[i];
-        const unsigned char* pr = ptile + (32 * mt + l32) * PPITCH + 16 * hi;
-#pragma unroll
-        for (int ks = 0; ks < MKT / 16; ++ks) {
-            const bf16x8 pa = load_bf16x8(pr + ks * 32);
-            const unsigned char* vr = ktile + (16 * ks + 8 * hi) * KPITCH + (256 * nt + l32) * 2;
-#pragma unroll
-            for (int n8 = 0; n8 < 8; ++n8) {
-                bf16x8 vb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vb[e] = *reinterpret_cast<const __bf16*>(vr + e * KPITCH + n8 * 64);
-                o[n8] = mfma32x32x16(pa, vb, o[n8]);
-            }
-        }
-        __syncthreads();
-    }
-
+    // total denominator of this lane's head: both key halves
+    const int mt = c.mt, nt = c.nt, lane = c.lane, l32 = c.l32, hi = c.hi;
+    const int head = 32 * mt + l32;
+    if (hi == 0) xch[1][nt][head] = l_run;
+    __syncthreads();
+    const float l_tot = l_run + xch[1][nt ^ 1][head];
+    // stage the result in LDS (the key buffers are free now), then coalesced 16-byte stores;
+    // lane l holds head `head`, dims 256nt + 32n8 + c_row(i, l) (4 consecutive per q4)
     if (a.n_splits == 1) {
-        float f[16];
+        const float z = a.sinks[head] * kLog2e;
+        const float mf = fmaxf(m_run, z);
+        const float sc = exp2f(m_run - mf);
+        const float f = sc / (l_tot * sc + exp2f(z - mf));
+        unsigned char* stage = kbuf[0];                 // bf16 [head][dim], 1040-byte rows
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float z = a.sinks[32 * mt + c_row(i, lane)] * kLog2e;
-            const float mf = fmaxf(m_run[i], z);
-            const float sc = exp2f(m_run[i] - mf);
-            f[i] = sc / (l_run[i] * sc + exp2f(z - mf));
+        for (int n8 = 0; n8 < 8; ++n8)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<uint2*>(stage + head * (MD * 2 + 16) +
+                                          (256 * nt + 32 * n8 + 8 * q4 + 4 * hi) * 2) =
+                    pack4_bf16(o[n8][4 * q4] * f, o[n8][4 * q4 + 1] * f, o[n8][4 * q4 + 2] * f,
+                               o[n8][4 * q4 + 3] * f);
+        __syncthreads();
+        bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD;
+        for (int idx = tid; idx < MH * MD / 8; idx += 256) {
+            const int h = idx / (MD / 8), d8 = idx % (MD / 8);
+            store16(ob + size_t(h) * MD + d8 * 8,
+                    *reinterpret_cast<const uint4*>(stage + h * (MD * 2 + 16) + d8 * 16));
         }
-        bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD + 256 * nt + l32;
-#pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                ob[(32 * mt + c_row(i, lane)) * MD + 32 * n8] = from_f32<bf16>(o[n8][i] * f[i]);
     } else {
-        if (nt == 0 && l32 == 0)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const size_t h = pbase + 32 * mt + c_row(i, lane);
-                a.part_ml[h * 2 + 0] = m_run[i];
-                a.part_ml[h * 2 + 1] = l_run[i];
-            }
-        float* po = a.part_o + pbase * MD + 256 * nt + l32;
+        if (nt == 0 && hi == 0) {
+            a.part_ml[(pbase + head) * 2 + 0] = m_run;
+            a.part_ml[(pbase + head) * 2 + 1] = l_tot;
+        }
+        // fp32 [head][dim]: heads 0..31 staged in kbuf[0], 32..63 in kbuf[1] (32 x 2064 B each)
+        unsigned char* st = kbuf[mt];
 #pragma unroll
         for (int n8 = 0; n8 < 8; ++n8)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) po[(32 * mt + c_row(i, lane)) * MD + 32 * n8] = o[n8][i];
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4*>(st + l32 * OPITCH + (256 * nt + 32 * n8 + 8 * q4 + 4 * hi) * 4) =
+                    make_float4(o[n8][4 * q4], o[n8][4 * q4 + 1], o[n8][4 * q4 + 2], o[n8][4 * q4 + 3]);
+        __syncthreads();
+        float* po = a.part_o + pbase * MD;
+        for (int idx = tid; idx < MH * MD / 4; idx += 256) {
+            const int h = idx / (MD / 4), d4 = idx % (MD / 4);
+            const unsigned char* sp = kbuf[h >> 5] + (h & 31) * OPITCH + d4 * 16;
+            store16(po + size_t(h) * MD + d4 * 4, *reinterpret_cast<const uint4*>(sp));
+        }
     }
 }
 
-// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.
+// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One
+// workgroup per (query, group of 8 heads).
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnMfmaArgs a) {
-    __shared__ float wgt[MAX_SPLITS][MH];
-    const int b = blockIdx.y;
-    const int64_t s = blockIdx.x;
+    __shared__ float wgt[MAX_SPLITS][8];
+    const int b = blockIdx.z;
+    const int64_t s = blockIdx.y;
+    const int h0 = blockIdx.x * 8;
     const size_t base = (size_t(b) * a.S + size_t(s)) * a.n_splits;
     const int tid = threadIdx.x;
-    if (tid < MH) {
-        const float z = a.sinks[tid] * kLog2e;
+    if (tid < 8) {
+        const int h = h0 + tid;
+        const float z = a.sinks[h] * kLog2e;
         float M = z;
-        for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, a.part_ml[((base + sp) * MH + tid) * 2]);
+        for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, a.part_ml[((base + sp) * MH + h) * 2]);
         float den = exp2f(z - M);
         for (int sp = 0; sp < a.n_splits; ++sp) {
-            const float m = a.part_ml[((base + sp) * MH + tid) * 2];
+            const float m = a.part_ml[((base + sp) * MH + h) * 2];
             const float e = m == -INFINITY ? 0.f : exp2f(m - M);
-            den += a.part_ml[((base + sp) * MH + tid) * 2 + 1] * e;
+            den += a.part_ml[((base + sp) * MH + h) * 2 + 1] * e;
             wgt[sp][tid] = e;
         }
         const float inv = 1.f / den;
         for (int sp = 0; sp < a.n_splits; ++sp) wgt[sp][tid] *= inv;
     }
     __syncthreads();
-    bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD;
-    for (int idx = tid; idx < MH * MD; idx += blockDim.x) {
-        const int h = idx / MD;
-        float acc = 0.f;
+    // 8 heads x 512 dims = 1024 float4 lanes of work; 4 per thread
+    bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD + size_t(h0) * MD;
+    for (int idx = tid; idx < 8 * MD / 4; idx += 256) {
+        const int hh = idx / (MD / 4), d4 = idx % (MD / 4);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int sp = 0; sp < a.n_splits; ++sp) {
-            const float wv = wgt[sp][h];
-            if (wv != 0.f) acc += wv * a.part_o[(base + sp) * MH * MD + idx];
+            const float wv = wgt[sp][hh];
+            if (wv != 0.f) {
+                const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((base + sp) * MH + h0 + hh) * MD + d4 * 4);
+                acc.x += wv * v.x;
+                acc.y += wv * v.y;
+                acc.z += wv * v.z;
+                acc.w += wv * v.w;
+            }
         }
-        ob[idx] = from_f32<bf16>(acc);
+        const uint32_t lo = uint32_t(bf16_bits(acc.x)) | (uint32_t(bf16_bits(acc.y)) << 16);
+        const uint32_t up = uint32_t(bf16_bits(acc.z)) | (uint32_t(bf16_bits(acc.w)) << 16);
+        *reinterpret_cast<uint2*>(ob + size_t(hh) * MD + d4 * 4) = make_uint2(lo, up);
     }
 }
 
@@ -529,7 +625,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         if (e != hipSuccess) return e;
         if (a.n_splits > 1) {
             trace_begin("attn_combine", st);
-            hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(j.S), nb), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(attn_combine_kernel, dim3(MH / 8, unsigned(j.S), nb), dim3(256), 0, st, a);
             trace_end("attn_combine", st);
             e = hipGetLastError();
             if (e != hipSuccess) return e;

@@ -37,13 +37,15 @@ def _check_layer(spec, res, b, positions, seed, end_to_end=False):
     if spec.has_rows:
         rows_ref = G.oracle_rows(spec, tok, par)
         rows = G.f64(res["rows"][b])
-        report["rows_maxabs"] = G.assert_rows_match(rows, rows_ref, store, "attention-lane rows")
+        report["rows_maxabs"] = G.assert_rows_match(rows, rows_ref, store, "attention-lane rows",
+                                                    spec.rope_dim)
         if end_to_end:
             rows = rows_ref
     if spec.has_indexer:
         rows_i_ref = G.oracle_rows(spec, tok, par, index_lane=True)
         rows_i = G.f64(res["rows_i"][b])
-        report["rows_i_maxabs"] = G.assert_rows_match(rows_i, rows_i_ref, store, "indexer-lane rows")
+        report["rows_i_maxabs"] = G.assert_rows_match(rows_i, rows_i_ref, store, "indexer-lane rows",
+                                                      spec.rope_dim)
         if end_to_end:
             rows_i = rows_i_ref
         scores = G.oracle_scores(spec, tok, rows_i, positions)
@@ -262,11 +264,15 @@ def test_v4_attention_with_ragged_selection():
     rows: entries outside [0, visible) are skipped, the rest attended in list order."""
     import sparse_attention_dsv4_amd as K
     import synth.csa as SC
+    from sparse_attention_dsv4_amd.layer import CsaLayer
     spec = V4_R4
     seed, T = 15, 1200
-    res = G.run_gpu(spec, seed, 1, [T - 40], 0)
-    layer = res["layer"]
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, 1, T, params, device="cuda")
+    layer.prefill(SC.batch_token_inputs(spec, seed, [0], T - 40, device="cuda"))
     tok = SC.batch_token_inputs(spec, seed, [T - 40], 40, device="cuda")
+    K.dsv4_compress_prefill(spec.comp_cfg(), layer.state, tok["a"], tok["g"], [T - 40],
+                            params["ape"], params["norm_w"], params["inv_freq"], layer.rows)
     nv_last = T // 4
     rng = np.random.default_rng(0)
     sel = np.full((1, 40, spec.topk), -1, dtype=np.int32)
@@ -275,7 +281,7 @@ def test_v4_attention_with_ragged_selection():
         nv = oracle.visible_rows(p, 4)
         cand = rng.choice(nv, size=200, replace=False)
         row = np.full(spec.topk, -1, dtype=np.int32)
-        slots = rng.choice(spec.topk, size=260, replace=False)
+        slots = np.sort(rng.choice(spec.topk, size=260, replace=False))
         row[slots[:200]] = np.sort(cand)
         row[slots[200:230]] = nv + rng.integers(0, 50, size=30)     # not yet visible
         row[slots[230:]] = -7
@@ -283,7 +289,7 @@ def test_v4_attention_with_ragged_selection():
     sel_t = torch.from_numpy(sel).cuda()
     out = torch.empty_like(tok["q"])
     K.dsv4_csa_attn_prefill(spec.attn_cfg(), tok["q"], tok["kv"], layer.ring, layer.rows, sel_t,
-                            [nv_last], [T - 40], layer.params["sinks"], out, layer.ws_attn)
+                            [nv_last], [T - 40], params["sinks"], out, layer.ws_attn)
     torch.cuda.synchronize()
     tk, par = G.oracle_inputs(spec, seed, 0, T)
     rows = G.f64(layer.rows[0, :nv_last])
