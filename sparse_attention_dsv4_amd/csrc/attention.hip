@@ -434,6 +434,14 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
     const int64_t nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
+    if (a.S == 1 && split == 0) {
+        // decode: store the new latent in its ring slot here.  Slot p % W holds token p - W,
+        // which no query of this launch reads (its window is p-W+1 .. p, with p itself
+        // taken from kv_new), so the store cannot race the key loads.
+        const uint4* src = reinterpret_cast<const uint4*>(a.kv_new + size_t(b) * MD);
+        uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(a.ring) + (size_t(b) * a.W + size_t(p % a.W)) * MD);
+        if (tid < MD / 8) dst[tid] = src[tid];
+    }
     if (c.kb >= nk) {                                 // nothing in this split
         if (tid < MH) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
@@ -630,6 +638,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        if (j.S == 1) continue;          // the attention kernel stored the decode token
         AttnArgs<bf16> ra;
         ra.D = MD; ra.W = j.W; ra.S = j.S;
         ra.kv_new = a.kv_new;

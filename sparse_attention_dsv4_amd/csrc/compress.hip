@@ -19,7 +19,8 @@
 //                         channel with an online softmax, then norm and RoPE in LDS;
 //   compress_state_kernel copies the new tokens of the last coff windows into the state.
 // The second runs after the first on the stream, because a row of this call may read a
-// state slot that the update overwrites.
+// state slot that the update overwrites.  With one new token per sequence (decode) the two
+// fuse into compress_step_kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,17 +59,12 @@ __device__ __forceinline__ const T* token_ptr(const CompArgs<T>& a, int b, int l
     return lanep + (size_t(b) * a.n_new + size_t(t - lb)) * W + col;
 }
 
+// Row j of sequence b: pooled per channel with an online softmax over its slots, rounded,
+// RMS-normalised, rounded, RoPE'd on the last rd dims at position j*r, rounded.
 template <typename T>
-__global__ void __launch_bounds__(kCompThreads)
-compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
-    extern __shared__ float zrow[];           // [D]
-    __shared__ float red[16];
-    const int b = blockIdx.y;
-    const int64_t lb = len_before.v[b];
-    const int64_t j = lb / a.r + blockIdx.x;  // row index
-    if ((j + 1) * a.r > lb + a.n_new) return;
+__device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int64_t j, int64_t lb,
+                                         float* zrow, float* red) {
     const int D = a.D, W = a.coff * a.D;
-
     float ss = 0.f;
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float m = -INFINITY, l = 0.f, acc = 0.f;
@@ -121,6 +117,40 @@ compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
 
 template <typename T>
 __global__ void __launch_bounds__(kCompThreads)
+compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
+    extern __shared__ float zrow[];           // [D]
+    __shared__ float red[16];
+    const int b = blockIdx.y;
+    const int64_t lb = len_before.v[b];
+    const int64_t j = lb / a.r + blockIdx.x;  // row index
+    if ((j + 1) * a.r > lb + a.n_new) return;
+    emit_row(a, b, j, lb, zrow, red);
+}
+
+// One new token per sequence (decode): store it in the frontier and, when it completes a
+// window, emit that row -- one launch.  The row reads the state only at positions of
+// earlier tokens and takes the new token from the lane, so the store cannot race it.
+template <typename T>
+__global__ void __launch_bounds__(kCompThreads)
+compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
+    extern __shared__ float zrow[];
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    const int64_t lb = len_before.v[b];
+    const int W = a.coff * a.D;
+    const size_t st = size_t(2) * a.coff * a.r * W;
+    const size_t slot = (size_t((lb / a.r) % a.coff) * a.r + size_t(lb % a.r)) * W;
+    T* sa = a.state + size_t(b) * st + slot;
+    T* sg = sa + size_t(a.coff) * a.r * W;
+    for (int c = threadIdx.x; c < W; c += blockDim.x) {
+        sa[c] = a.lane_a[size_t(b) * W + c];
+        sg[c] = a.lane_g[size_t(b) * W + c];
+    }
+    if ((lb + 1) % a.r == 0) emit_row(a, b, lb / a.r, lb, zrow, red);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kCompThreads)
 compress_state_kernel(CompArgs<T> a, SeqInts len_before) {
     const int b = blockIdx.y;
     const int64_t lb = len_before.v[b];
@@ -148,6 +178,27 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
     for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
         const int nb = std::min(kSeqSlice, j.batch - b0);
         SeqInts lb{};
+        if (j.n_new == 1) {
+            CompArgs<T> a;
+            a.r = j.r; a.coff = j.coff; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
+            a.state = static_cast<T*>(j.state) + size_t(b0) * st_elems;
+            a.lane_a = static_cast<const T*>(j.lane_a) + size_t(b0) * W;
+            a.lane_g = static_cast<const T*>(j.lane_g) + size_t(b0) * W;
+            a.ape = static_cast<const T*>(j.ape);
+            a.gamma = static_cast<const T*>(j.gamma);
+            a.inv_freq = j.inv_freq;
+            a.rows = static_cast<T*>(j.rows) + size_t(b0) * j.row_cap * j.D;
+            a.row_cap = j.row_cap;
+            a.n_new = 1;
+            for (int i = 0; i < nb; ++i) lb.v[i] = int32_t(j.len_before[b0 + i]);
+            trace_begin("compress_step", s);
+            hipLaunchKernelGGL(compress_step_kernel<T>, dim3(nb), dim3(kCompThreads),
+                               j.D * sizeof(float), s, a, lb);
+            trace_end("compress_step", s);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            continue;
+        }
         int64_t max_rows = 0, max_keep = 0;
         for (int i = 0; i < nb; ++i) {
             const int64_t l0 = j.len_before[b0 + i];

@@ -19,9 +19,10 @@
 // row; ReLU, the folded head weights and the sum over heads happen in registers (one
 // cross-half add), and only the fp32 score key leaves the kernel.  Each wave keeps one
 // query's 64x128 block as A fragments; 128-row tiles of the lane are staged in LDS and
-// shared by the workgroup's queries (prefill: 4 queries, one per wave; decode: one query,
+// shared by the workgroup's queries (prefill: 8 queries, two per wave; decode: one query,
 // the 4 waves split the tile).  The per-(query, row) arithmetic is the same in both, so a
-// decode step and a prefill chunk give bit-identical scores.
+// decode step and a prefill chunk give bit-identical scores.  Tiles are double-buffered in
+// LDS through direct global-to-LDS loads.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -87,10 +88,23 @@ index_score_kernel(ScoreArgs<T> a, SeqInts pos0, SeqInts n_rows) {
 
 
 // ------------------------------------------------------------------ mfma scoring
+// Queries per wave in prefill scoring: one keeps 3 waves per SIMD resident (146 VGPRs),
+// which hides LDS and epilogue latency better than two (operand reuse, 1 wave per SIMD).
+#ifndef DSV4_IDX_QPW
+#define DSV4_IDX_QPW 1
+#endif
+constexpr int kIdxQpw = DSV4_IDX_QPW;
+#ifndef DSV4_IDX_WAVES
+#define DSV4_IDX_WAVES 8
+#endif
+constexpr int kIdxWaves = DSV4_IDX_WAVES;   // waves per prefill workgroup (one query each)
+
 constexpr int IH = 64;                 // indexer heads
 constexpr int ID = 128;                // indexer dims
 constexpr int IRT = 128;               // rows per LDS tile
-constexpr int IPITCH = ID * 2 + 16;    // LDS bytes per row (padded)
+constexpr int IROWB = ID * 2;          // bytes per row (unpadded: chunks are XOR-swizzled)
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 struct IdxMfmaArgs {
     const bf16* qi;
@@ -105,92 +119,144 @@ struct IdxMfmaArgs {
     int rows_per_block;
 };
 
-template <int QPW>
-__global__ void __launch_bounds__(256)
+// Direct global -> LDS copy (16 bytes per lane to lds_base + 16 lane), as inline asm so the
+// compiler does not serialise LDS reads of the other tile buffer behind it.
+__device__ __forceinline__ void idx_dma16(const void* gptr, const unsigned char* lds_base) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(uint32_t(size_t((const lds_u8*)lds_base)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(la), "v"(gptr) : "memory", "m0");
+}
+
+// Row r's 16-byte chunk c sits at chunk position c ^ (r & 15) of its 256-byte LDS row, so
+// the 32 rows an MFMA operand read touches spread over all banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 15); }
+
+// Stage rows [j0, j0 + IRT) of the lane (zeros past j_end): each wave instruction moves 4
+// rows; lane l fetches chunk swz(row, l%16) of row l/16 so that it lands at position l%16.
+template <int WAVES>
+__device__ __forceinline__ void idx_load_tile(const IdxMfmaArgs& a, int b, int64_t j0,
+                                              int64_t j_end, unsigned char* buf) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < IRT / 4 / WAVES; ++i) {          // 4 rows per wave instruction
+        const int row0 = 4 * (w + WAVES * i);
+        const int row = row0 + (lane >> 4);
+        const int64_t jj = j0 + row;
+        unsigned char* dst = buf + row0 * IROWB;
+        if (j0 + row0 + 3 < j_end) {
+            idx_dma16(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID + swz(row, lane & 15) * 8, dst);
+        } else {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (jj < j_end)
+                v = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID +
+                                                    swz(row, lane & 15) * 8);
+            store16(dst + lane * 16, v);
+        }
+    }
+}
+
+// QPW queries per wave (prefill: the workgroup covers 4 * QPW) or, for QPW == 0, one query
+// shared by the whole workgroup (decode: each wave takes one 32-row block of every tile).
+template <int QPW, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
 index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
-    __shared__ __attribute__((aligned(16))) unsigned char kt[IRT * IPITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char kt[2][IRT * IROWB];
+    constexpr bool SHARED_Q = QPW == 0;
+    constexpr int NQ = SHARED_Q ? 1 : QPW;
     const int b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const int64_t pos0 = pos0v.v[b];
-    const int64_t s = QPW == 4 ? int64_t(blockIdx.y) * 4 + w : int64_t(blockIdx.y);
-    const bool qvalid = s < a.S;
-    int64_t s_last = QPW == 4 ? int64_t(blockIdx.y) * 4 + 3 : int64_t(blockIdx.y);
+    const int64_t qbase = SHARED_Q ? int64_t(blockIdx.y) : int64_t(blockIdx.y) * WAVES * NQ + w * NQ;
+    int64_t s_last = SHARED_Q ? int64_t(blockIdx.y) : int64_t(blockIdx.y) * WAVES * NQ + WAVES * NQ - 1;
     if (s_last > a.S - 1) s_last = a.S - 1;
     int64_t nv_max = (pos0 + s_last + 1) / a.r;
     if (nv_max > n_rows.v[b]) nv_max = n_rows.v[b];
     const int64_t j_begin = int64_t(blockIdx.x) * a.rows_per_block;
     if (j_begin >= nv_max) return;
     const int64_t j_end = j_begin + a.rows_per_block < nv_max ? j_begin + a.rows_per_block : nv_max;
-    int64_t nv = 0;
-    if (qvalid) {
-        nv = (pos0 + s + 1) / a.r;
-        if (nv > n_rows.v[b]) nv = n_rows.v[b];
-    }
 
-    bf16x8 qa[2][ID / 16];
-    float wsc[2][16];
-    if (qvalid) {
-        const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(s)) * IH + l32) * ID + 8 * hi;
-        const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
+    bf16x8 qa[NQ][2][ID / 16];
+    float wsc[NQ][2][16];
+    int64_t nv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t s = qbase + q;
+        const bool qvalid = s < a.S;
+        nv[q] = 0;
+        if (qvalid) {
+            nv[q] = (pos0 + s + 1) / a.r;
+            if (nv[q] > n_rows.v[b]) nv[q] = n_rows.v[b];
+        }
+        const int64_t sq = qvalid ? s : 0;
+        const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(sq)) * IH + l32) * ID + 8 * hi;
+        const float* wr = a.w + (size_t(b) * a.S + size_t(sq)) * IH;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
-            for (int ks = 0; ks < ID / 16; ++ks) qa[m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
+            for (int ks = 0; ks < ID / 16; ++ks) qa[q][m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) wsc[m][i] = wr[32 * m + c_row(i, lane)] * a.scale;
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int ks = 0; ks < ID / 16; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qa[m][ks][e] = __bf16(0.f);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) wsc[m][i] = 0.f;
+            for (int i = 0; i < 16; ++i) wsc[q][m][i] = qvalid ? wr[32 * m + c_row(i, lane)] * a.scale : 0.f;
         }
     }
-    uint32_t* kout = a.keys + (size_t(b) * a.S + size_t(qvalid ? s : 0)) * a.n_stride;
 
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += IRT) {
-        // stage 128 rows: 16 lanes per 256-byte row, a wave covers 4 consecutive rows
+    const int ntiles = int((j_end - j_begin + IRT - 1) / IRT);
+    idx_load_tile<WAVES>(a, b, j_begin, j_end, kt[0]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int64_t j0 = j_begin + int64_t(t) * IRT;
+        if (t + 1 < ntiles) idx_load_tile<WAVES>(a, b, j0 + IRT, j_end, kt[(t + 1) & 1]);
+        const unsigned char* buf = kt[t & 1];
+        // 32-row blocks of the tile: prefill waves take all 4 (their own queries), decode waves
+        // one each.  The MFMAs of block u+1 are issued before the epilogue of block u, so the
+        // matrix pipe stays busy while the VALU reduces the previous block.
+        constexpr int NB = SHARED_Q ? 1 : 4;
+        floatx16 c[2][NQ][2];
 #pragma unroll
-        for (int i = 0; i < IRT / 16; ++i) {
-            const int row = (tid >> 4) + 16 * i;
-            const int64_t jj = j0 + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (jj < j_end)
-                v = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID +
-                                                    (tid & 15) * 8);
-            store16(kt + row * IPITCH + (tid & 15) * 16, v);
-        }
-        __syncthreads();
+        for (int u = 0; u <= NB; ++u) {
+            if (u < NB) {
+                const int nt = SHARED_Q ? w : u;
+                const int row = 32 * nt + l32;
+                const unsigned char* kr = buf + row * IROWB;
 #pragma unroll
-        for (int t = 0; t < (QPW == 4 ? 4 : 1); ++t) {
-            const int nt = QPW == 4 ? t : w;
-            floatx16 c0, c1;
+                for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                c0[i] = 0.f;
-                c1[i] = 0.f;
+                    for (int i = 0; i < 16; ++i) {
+                        c[u & 1][q][0][i] = 0.f;
+                        c[u & 1][q][1][i] = 0.f;
+                    }
+#pragma unroll
+                for (int ks = 0; ks < ID / 16; ++ks) {
+                    const bf16x8 kb = load_bf16x8(kr + swz(row, 2 * ks + hi) * 16);
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        c[u & 1][q][0] = mfma32x32x16(qa[q][0][ks], kb, c[u & 1][q][0]);
+                        c[u & 1][q][1] = mfma32x32x16(qa[q][1][ks], kb, c[u & 1][q][1]);
+                    }
+                }
             }
-            const unsigned char* kr = kt + (32 * nt + l32) * IPITCH + 16 * hi;
+            if (u > 0) {
+                const int v = u - 1;
+                const int nt = SHARED_Q ? w : v;
+                const int64_t jj = j0 + 32 * nt + l32;
 #pragma unroll
-            for (int ks = 0; ks < ID / 16; ++ks) {
-                const bf16x8 kb = load_bf16x8(kr + ks * 32);
-                c0 = mfma32x32x16(qa[0][ks], kb, c0);
-                c1 = mfma32x32x16(qa[1][ks], kb, c1);
+                for (int q = 0; q < NQ; ++q) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float x0 = c[v & 1][q][0][i], x1 = c[v & 1][q][1][i];
+                        s0 = fmaf(wsc[q][0][i], x0 > 0.f ? x0 : 0.f, s0);
+                        s1 = fmaf(wsc[q][1][i], x1 > 0.f ? x1 : 0.f, s1);
+                    }
+                    float sc = s0 + s1;
+                    sc += __shfl_xor(sc, 32, 64);
+                    if (hi == 0 && jj < nv[q])
+                        a.keys[(size_t(b) * a.S + size_t(qbase + q)) * a.n_stride + size_t(jj)] = score_key(sc);
+                }
             }
-            float sc = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc = fmaf(wsc[0][i], fmaxf(c0[i], 0.f), sc);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc = fmaf(wsc[1][i], fmaxf(c1[i], 0.f), sc);
-            sc += __shfl_xor(sc, 32, 64);
-            const int64_t jj = j0 + 32 * nt + l32;
-            if (hi == 0 && jj < nv) kout[jj] = score_key(sc);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);              // the next tile has landed
         __syncthreads();
     }
 }
@@ -461,8 +527,9 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             a.keys = j.keys + qoff * j.n_stride;
             a.r = j.r;
             a.scale = 1.0f / sqrtf(float(j.di)) / sqrtf(float(j.Hi));
-            const bool per4 = j.S >= 4;
-            const int64_t groups = per4 ? (j.S + 3) / 4 : j.S;
+            constexpr int QG = kIdxWaves * kIdxQpw;        // queries per prefill workgroup
+            const bool perq = j.S >= QG;
+            const int64_t groups = perq ? (j.S + QG - 1) / QG : j.S;
             // enough row blocks to give the chip >= ~2048 workgroups
             int64_t blocks = (2048 + groups * nb - 1) / (groups * nb);
             const int64_t tiles = (nv_max + IRT - 1) / IRT;
@@ -471,12 +538,12 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             a.rows_per_block = int(((tiles + blocks - 1) / blocks) * IRT);
             const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
             trace_begin("index_score_mfma", st);
-            if (per4)
-                hipLaunchKernelGGL(index_score_mfma_kernel<4>, dim3(gx, unsigned(groups), nb), dim3(256),
-                                   0, st, a, pos, nr);
+            if (perq)
+                hipLaunchKernelGGL((index_score_mfma_kernel<kIdxQpw, kIdxWaves>),
+                                   dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
             else
-                hipLaunchKernelGGL(index_score_mfma_kernel<1>, dim3(gx, unsigned(groups), nb), dim3(256),
-                                   0, st, a, pos, nr);
+                hipLaunchKernelGGL((index_score_mfma_kernel<0, 4>), dim3(gx, unsigned(groups), nb),
+                                   dim3(256), 0, st, a, pos, nr);
             trace_end("index_score_mfma", st);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
