@@ -273,6 +273,9 @@ def main():
     ap.add_argument("--cpu-prefill-queries", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run one workload (for per-workload profiler runs); the JSON line "
+                         "then carries that workload's numbers only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the CSA layer here runs on a single MI355X and has no "
@@ -282,12 +285,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     K.lib()
-    dec, dec_state = bench_decode(args)
-    log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step']:.3f} ms/step")
-    pre = None
-    if not args.skip_prefill:
+    dec = pre = None
+    if args.only != "prefill":
+        dec, dec_state = bench_decode(args)
+        log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step']:.3f} ms/step")
+    if not args.skip_prefill and args.only != "decode":
         pre, pre_state = bench_prefill(args)
         log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk")
+    if dec is None:                      # prefill-only profiler run
+        print(json.dumps({"workload": "prefill", "prefill": pre}), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"decode": cpu_baseline_decode(dec_state, args.cpu_decode_steps)}

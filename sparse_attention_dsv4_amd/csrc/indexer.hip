@@ -441,12 +441,18 @@ topk_select_lds_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     find_bucket(hist, 2048, a.k, tmp, sh);
     const uint32_t d1 = uint32_t(sh[0]);
     int rem = sh[1];
-    for (int j = tid; j < nv; j += blockDim.x) {
-        const uint32_t kk = keys[j];
-        if ((kk >> 21) == d1) {
-            const int pos = atomicAdd(&sh[2], 1);
-            if (pos < kSelCand) cand[pos] = kk;
-        }
+    const int lane = tid & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int j0 = tid - lane; j0 < nv; j0 += blockDim.x) {      // whole waves step together
+        const int j = j0 + lane;
+        const uint32_t kk = j < nv ? keys[j] : 0u;
+        const bool hit = j < nv && (kk >> 21) == d1;
+        const unsigned long long m = __ballot(hit);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(&sh[2], __popcll(m));
+        base = __shfl(base, 0, 64);
+        const int pos = base + __popcll(m & lt);
+        if (hit && pos < kSelCand) cand[pos] = kk;
     }
     for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
     __syncthreads();
@@ -477,29 +483,43 @@ topk_select_lds_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
     rem = sh[1];
 
-    // compaction in row order over contiguous segments
-    const int seg = (nv + blockDim.x - 1) / blockDim.x;
-    const int lo = tid * seg;
-    const int hi = lo + seg < nv ? lo + seg : nv;
+    // compaction in row order: wave w owns a contiguous chunk, read 64 keys at a time
+    // (coalesced); ballots give every lane its rank among the rows taken so far
+    const int w = tid >> 6, nw = blockDim.x >> 6;
+    const int chunk = ((nv + nw - 1) / nw + 63) & ~63;
+    const int lo = w * chunk < nv ? w * chunk : nv;
+    const int hi = lo + chunk < nv ? lo + chunk : nv;
     int ngt = 0, neq = 0;
-    for (int j = lo; j < hi; ++j) {
-        const uint32_t kk = keys[j];
-        ngt += kk > thr;
-        neq += kk == thr;
+    for (int j0 = lo; j0 < hi; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t kk = j < hi ? keys[j] : 0u;
+        ngt += __popcll(__ballot(j < hi && kk > thr));
+        neq += __popcll(__ballot(j < hi && kk == thr));
     }
-    int tg, te;
-    const int gt0 = block_excl_scan(ngt, tmp, &tg);
-    const int eq0 = block_excl_scan(neq, tmp, &te);
+    __shared__ int wtot[2][16];
+    if (lane == 0) {
+        wtot[0][w] = ngt;
+        wtot[1][w] = neq;
+    }
+    __syncthreads();
+    int gt0 = 0, eq0 = 0;
+    for (int i = 0; i < w; ++i) {
+        gt0 += wtot[0][i];
+        eq0 += wtot[1][i];
+    }
     int eq_rank = eq0;
     int o = gt0 + (eq_rank < rem ? eq_rank : rem);
-    for (int j = lo; j < hi; ++j) {
-        const uint32_t kk = keys[j];
-        if (kk > thr) {
-            out[o++] = j;
-        } else if (kk == thr) {
-            if (eq_rank < rem) out[o++] = j;
-            ++eq_rank;
-        }
+    for (int j0 = lo; j0 < hi; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t kk = j < hi ? keys[j] : 0u;
+        const bool g = j < hi && kk > thr;
+        const bool e = j < hi && kk == thr;
+        const unsigned long long be = __ballot(e);
+        const bool take = g || (e && eq_rank + __popcll(be & lt) < rem);
+        const unsigned long long bt = __ballot(take);
+        if (take) out[o + __popcll(bt & lt)] = j;
+        o += __popcll(bt);
+        eq_rank += __popcll(be);
     }
 }
 

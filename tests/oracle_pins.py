@@ -69,6 +69,20 @@ def pin_window_golden():
         assert seen == expect_seen, (d, o[0, 0, :2])
 
 
+# ------------------------------------------------------------------ storage rounding
+def pin_bf16_round_is_library_rne():
+    """bf16 rounding of fp32 values equals torch's fp32 -> bfloat16 conversion (nearest,
+    ties to even), including exact ties, subnormal-range and large values."""
+    rng = _rng(17)
+    x = np.concatenate([rng.standard_normal(5000).astype(np.float32) * 10.0,
+                        np.float32([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                                     2.0 ** -130, 3.0e38, 0.0, -0.0, 65504.0])]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+    np.testing.assert_array_equal(O.round_store(x, "bf16"), ref)
+    np.testing.assert_array_equal(O.round_store(np.float64(1.0) + 2.0 ** -30, "f32"), np.float32(1.0))
+
+
 # ------------------------------------------------------------------ compressor
 def _lanes(rng, T, r, D, overlap):
     coff = 2 if overlap else 1
