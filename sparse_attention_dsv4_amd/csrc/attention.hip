@@ -222,12 +222,23 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // (global_load_lds_dwordx4; the LDS base goes through m0 and must be wave-uniform).  Issued
 // as inline asm so the compiler does not order later LDS reads of the *other* key buffer
 // behind it; the caller waits with vmcnt(0) before the barrier that publishes the tile.
-__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds_row) {
+// The row's global base is wave-uniform (a scalar register pair) and each lane adds its own
+// byte offset, so no per-lane 64-bit address arithmetic is spent on the copy.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const unsigned char* lds_row) {
     const uint32_t la = __builtin_amdgcn_readfirstlane(uint32_t(size_t((const lds_u8*)lds_row)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(la), "v"(gptr) : "memory", "m0");
+    // readfirstlane returns int: zero-extend each half (a sign-extended low half would
+    // corrupt the upper word of an address whose bit 31 is set)
+    const uint64_t gp = reinterpret_cast<uint64_t>(sbase);
+    const uint64_t sb = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(gp)))) |
+                        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(gp >> 32)))) << 32);
+    // s_nop 4: five wait states between the last (VALU) write of the base registers or m0 and
+    // the load that reads them; the compiler does not look inside the asm for this hazard
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(la), "v"(voff), "s"(sb) : "memory", "m0");
 }
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// all but this wave's 16 most recent copies (one full tile) have landed
+__device__ __forceinline__ void wait_vm_tile() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
 struct AttnMfmaArgs {
     const bf16* q;
@@ -250,43 +261,93 @@ struct AttnMfmaArgs {
 // Barrier for LDS exchanges inside a tile: waits for this wave's LDS operations only, so
 // the next tile's direct-to-LDS loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
-    __builtin_amdgcn_s_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Source row of key `i` of the query's list: selected/visible rows first, then the window.
-__device__ __forceinline__ const bf16* mfma_key(const AttnMfmaArgs& a, int b, int64_t i,
-                                                int64_t nrow, const int32_t* codes, int64_t kb,
-                                                int64_t t0, int64_t pos0) {
-    if (i < nrow) {
-        const int64_t j = a.sel ? codes[i - kb] : i;
-        return a.rows + (size_t(b) * a.row_cap + size_t(j)) * MD;
-    }
-    const int64_t t = t0 + (i - nrow);
-    if (t >= pos0) return a.kv_new + (size_t(b) * a.S + size_t(t - pos0)) * MD;
-    return a.ring + (size_t(b) * a.W + size_t(t % a.W)) * MD;
-}
-
+// Where the keys of one query come from.  Key i of the query's list: the compressed rows
+// first (i < nrow; the i-th valid selected row, or row i when every visible row is attended),
+// then the window tokens t0 + (i - nrow) .. p, read from kv_new for tokens of this call and
+// from ring slot t % W for earlier ones.  All key and token indices fit in 32 bits (the entry
+// points cap positions below 2^31 and keys per query at 2^30).
 struct TileCtx {
     int b, w, lane, mt, nt, l32, hi;
-    int64_t nrow, kb, t0, pos0;
+    int nrow, kb;             // keys before the window; first key of this workgroup's split
+    int t0, pos0;             // first window token; first token of this call
+    uint32_t slot0, W;        // ring slot of t0; ring length
+    bool sel;
+    const bf16* rows;         // this sequence's compressed rows
+    const bf16* ring;         // this sequence's window ring
+    const bf16* kv_new;       // this sequence's tokens of this call
 };
 
+__device__ __forceinline__ void key_ctx(TileCtx& c, const AttnMfmaArgs& a, int b, int t0, int pos0) {
+    c.t0 = t0;
+    c.pos0 = pos0;
+    c.W = uint32_t(a.W);
+    c.slot0 = uint32_t(t0) % c.W;
+    c.sel = a.sel != nullptr;
+    c.rows = a.rows ? a.rows + size_t(b) * size_t(a.row_cap) * MD : nullptr;
+    c.ring = a.ring + size_t(b) * size_t(a.W) * MD;
+    c.kv_new = a.kv_new + size_t(b) * size_t(a.S) * MD;
+}
+
+__device__ __forceinline__ const bf16* key_src(const TileCtx& c, const int32_t* codes, int i) {
+    if (i < c.nrow) return c.rows + size_t(c.sel ? codes[i - c.kb] : i) * MD;
+    const int u = i - c.nrow;
+    const int t = c.t0 + u;
+    if (t >= c.pos0) return c.kv_new + size_t(t - c.pos0) * MD;
+    uint32_t slot = c.slot0 + uint32_t(u);          // < 2W: one wrap at most
+    if (slot >= c.W) slot -= c.W;
+    return c.ring + size_t(slot) * MD;
+}
+
 // Enqueue the direct-to-LDS copy of keys [tb, tb + nkt) (one 1 KB row per wave instruction)
-// and zero the unused rows of a partial tile.
-__device__ __forceinline__ void load_tile(const AttnMfmaArgs& a, const TileCtx& c,
-                                          const int32_t* codes, unsigned char* buf, int64_t tb,
-                                          int nkt) {
-#pragma unroll 4
+// and zero the unused rows of a partial tile.  Wave w copies rows w, w + 4, ..: lane l < 16
+// finds the source of row w + 4 l once, and the copies read it back as a scalar.
+__device__ __forceinline__ void load_tile(const TileCtx& c, const int32_t* codes, unsigned char* buf,
+                                          int tb, int nkt) {
+    const int kk_l = c.w + 4 * (c.lane & 15);
+    const bf16* mine = kk_l < nkt ? key_src(c, codes, tb + kk_l) : c.ring;
+    const uint64_t mp = reinterpret_cast<uint64_t>(mine);
+    const uint32_t plo = uint32_t(mp), phi = uint32_t(mp >> 32);
+#pragma unroll
     for (int i = 0; i < MKT / 4; ++i) {
         const int kk = c.w + 4 * i;
         if (kk < nkt) {
-            const bf16* src = mfma_key(a, c.b, tb + kk, c.nrow, codes, c.kb, c.t0, c.pos0);
-            dma16(src + c.lane * 8, buf + kk * KPITCH);
+            const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(plo), i))) |
+                                (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), i))) << 32);
+            dma16(reinterpret_cast<const void*>(sp), uint32_t(c.lane) * 16, buf + kk * KPITCH);
         } else {
             store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
         }
     }
+}
+
+// Compact the valid entries (0 <= j < nv) of one selection row, keeping their order: the
+// entry of rank n goes to codes[n - kb] when kb <= n < kb + kps.  Returns the count of valid
+// entries.  Ranks come from wave ballots; wsum holds 2 x 4 per-wave counts.
+__device__ __forceinline__ int compact_selection(const int32_t* sr, int k, int nv, int kb, int kps,
+                                                 int32_t* codes, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int base = 0;
+    for (int r0 = 0; r0 < k; r0 += 256) {
+        const int e = r0 + tid;
+        const int32_t j = e < k ? sr[e] : -1;
+        const bool ok = j >= 0 && j < nv;
+        const uint64_t m = __ballot(ok);
+        int* ws = wsum + ((r0 >> 8) & 1) * 4;
+        if (lane == 0) ws[w] = __popcll(m);
+        __syncthreads();
+        int off = base;
+        for (int v = 0; v < w; ++v) off += ws[v];
+        if (ok) {
+            const int rank = off + __popcll(m & ((uint64_t(1) << lane) - 1));
+            if (rank >= kb && rank < kb + kps) codes[rank - kb] = j;
+        }
+        base += (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    }
+    __syncthreads();
+    return base;
 }
 
 // Lazy rescaling: the running reference max of a head moves only when a tile's max exceeds
@@ -377,7 +438,7 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __shared__ __attribute__((aligned(16))) unsigned char ptile[MH * PPITCH];
     __shared__ float xch[2][2][MH];       // [max | sum][key half][head]
     __shared__ int32_t codes[MAX_CODES];
-    __shared__ int32_t scan[256];
+    __shared__ int wsum[8];
 
     TileCtx c;
     c.b = blockIdx.z;
@@ -385,63 +446,30 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int split = blockIdx.x;
     const int tid = threadIdx.x;
     c.lane = tid & 63;
-    c.w = tid >> 6;
+    c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     c.mt = c.w >> 1;                      // head half
     c.nt = c.w & 1;                       // key half in Q.K^T, dim half in P.V
     c.l32 = c.lane & 31;
     c.hi = c.lane >> 5;
     const int b = c.b;
-    c.pos0 = pos0v.v[b];
-    const int64_t p = c.pos0 + s;
+    const int pos0 = pos0v.v[b];
+    const int p = pos0 + int(s);
 
-    int64_t nv = 0;
+    int nv = 0;
     if (a.r > 0 && a.rows != nullptr) {
         nv = (p + 1) / a.r;
         if (nv > n_rows.v[b]) nv = n_rows.v[b];
     }
-    c.t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
-    const int64_t nwin = p - c.t0 + 1;
-    c.kb = int64_t(split) * a.keys_per_split;
+    const int t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
+    const int nwin = p - t0 + 1;
+    key_ctx(c, a, b, t0, pos0);
+    c.kb = split * a.keys_per_split;
     c.nrow = nv;
-    if (a.sel != nullptr) {
-        // compact the valid entries of the selection row, in order; keep those in this split
-        const int32_t* sr = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
-        const int per = (a.k + 255) / 256;
-        const int e0 = tid * per, e1 = e0 + per < a.k ? e0 + per : a.k;
-        int cnt = 0;
-        for (int e = e0; e < e1; ++e) {
-            const int32_t j = sr[e];
-            cnt += (j >= 0 && j < nv);
-        }
-        scan[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {      // inclusive scan (Hillis-Steele)
-            const int v = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += v;
-            __syncthreads();
-        }
-        c.nrow = scan[255];
-        int64_t pos = scan[tid] - cnt;
-        for (int e = e0; e < e1; ++e) {
-            const int32_t j = sr[e];
-            if (j >= 0 && j < nv) {
-                if (pos >= c.kb && pos < c.kb + a.keys_per_split) codes[pos - c.kb] = j;
-                ++pos;
-            }
-        }
-        __syncthreads();
-    }
-    const int64_t nk = c.nrow + nwin;
+    if (a.sel != nullptr)
+        c.nrow = compact_selection(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, nv, c.kb,
+                                   a.keys_per_split, codes, wsum);
+    const int nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
-    if (a.S == 1 && split == 0) {
-        // decode: store the new latent in its ring slot here.  Slot p % W holds token p - W,
-        // which no query of this launch reads (its window is p-W+1 .. p, with p itself
-        // taken from kv_new), so the store cannot race the key loads.
-        const uint4* src = reinterpret_cast<const uint4*>(a.kv_new + size_t(b) * MD);
-        uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(a.ring) + (size_t(b) * a.W + size_t(p % a.W)) * MD);
-        if (tid < MD / 8) dst[tid] = src[tid];
-    }
     if (c.kb >= nk) {                                 // nothing in this split
         if (tid < MH) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
@@ -449,14 +477,14 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         }
         return;
     }
-    const int64_t ke = c.kb + a.keys_per_split < nk ? c.kb + a.keys_per_split : nk;
-    const int ntiles = int((ke - c.kb + MKT - 1) / MKT);
+    const int ke = c.kb + a.keys_per_split < nk ? c.kb + a.keys_per_split : nk;
+    const int ntiles = (ke - c.kb + MKT - 1) / MKT;
     auto tile_keys = [&](int t) -> int {
-        const int64_t left = ke - (c.kb + int64_t(t) * MKT);
-        return left < MKT ? int(left) : MKT;
+        const int left = ke - (c.kb + t * MKT);
+        return left < MKT ? left : MKT;
     };
 
-    load_tile(a, c, codes, kbuf[0], c.kb, tile_keys(0));
+    load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
     // this wave's 32 heads of q, as MFMA A fragments over all 512 dims
     bf16x8 qa[MD / 16];
     {
@@ -474,7 +502,7 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(a, c, codes, kbuf[(t + 1) & 1], c.kb + int64_t(t + 1) * MKT, tile_keys(t + 1));
+        if (t + 1 < ntiles) load_tile(c, codes, kbuf[(t + 1) & 1], c.kb + (t + 1) * MKT, tile_keys(t + 1));
         attend_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t));
         wait_vm();                        // the next tile has landed
         __syncthreads();                  // ... for every wave; and all are done with this one
@@ -532,57 +560,246 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 }
 
-// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One
-// workgroup per (query, group of 8 heads).
+
+// ------------------------------------------------------------------ decode path
+// One query per sequence: workgroups per (sequence, 16-head group, key split), so the
+// partials a split writes are 16 heads x 512 fp32 and enough workgroups run at once.
+// v_mfma_f32_16x16x32_bf16: each wave scores 16 keys of every 64-key tile for the group's
+// 16 heads (S^T = K Q^T, lane l owns head l%16) and accumulates 128 dims of O^T = V^T P^T.
+constexpr int DHG = 16;                   // heads per decode workgroup
+constexpr int QPITCH = MD * 2 + 16;       // LDS row of a staged q (offset rows: no bank conflicts)
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(AttnMfmaArgs a) {
-    __shared__ float wgt[MAX_SPLITS][8];
-    const int b = blockIdx.z;
-    const int64_t s = blockIdx.y;
-    const int h0 = blockIdx.x * 8;
-    const size_t base = (size_t(b) * a.S + size_t(s)) * a.n_splits;
+attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KBUF];
+    __shared__ __attribute__((aligned(16))) unsigned char ptile[DHG * PPITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char qs[DHG * QPITCH];
+    __shared__ float xch[2][4][DHG];      // [max | sum][wave][head]
+    __shared__ int32_t codes[MAX_CODES];
+    __shared__ int wsum[8];
+
+    TileCtx c;
+    c.b = blockIdx.z;
+    const int hg = blockIdx.y;            // heads 16 hg .. 16 hg + 15
+    const int split = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < 8) {
-        const int h = h0 + tid;
-        const float z = a.sinks[h] * kLog2e;
-        float M = z;
-        for (int sp = 0; sp < a.n_splits; ++sp) M = fmaxf(M, a.part_ml[((base + sp) * MH + h) * 2]);
-        float den = exp2f(z - M);
-        for (int sp = 0; sp < a.n_splits; ++sp) {
-            const float m = a.part_ml[((base + sp) * MH + h) * 2];
-            const float e = m == -INFINITY ? 0.f : exp2f(m - M);
-            den += a.part_ml[((base + sp) * MH + h) * 2 + 1] * e;
-            wgt[sp][tid] = e;
-        }
-        const float inv = 1.f / den;
-        for (int sp = 0; sp < a.n_splits; ++sp) wgt[sp][tid] *= inv;
+    c.lane = tid & 63;
+    c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+    c.mt = 0; c.nt = 0; c.l32 = c.lane & 31; c.hi = c.lane >> 5;
+    const int b = c.b, w = c.w, lane = c.lane;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int p = pos0v.v[b];             // one query: pos0 == p
+
+    int nv = 0;
+    if (a.r > 0 && a.rows != nullptr) {
+        nv = (p + 1) / a.r;
+        if (nv > n_rows.v[b]) nv = n_rows.v[b];
     }
-    __syncthreads();
-    // 8 heads x 512 dims = 1024 float4 lanes of work; 4 per thread
-    bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD + size_t(h0) * MD;
-    for (int idx = tid; idx < 8 * MD / 4; idx += 256) {
-        const int hh = idx / (MD / 4), d4 = idx % (MD / 4);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < a.n_splits; ++sp) {
-            const float wv = wgt[sp][hh];
-            if (wv != 0.f) {
-                const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((base + sp) * MH + h0 + hh) * MD + d4 * 4);
-                acc.x += wv * v.x;
-                acc.y += wv * v.y;
-                acc.z += wv * v.z;
-                acc.w += wv * v.w;
+    const int t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
+    const int nwin = p - t0 + 1;
+    key_ctx(c, a, b, t0, p);
+    c.kb = split * a.keys_per_split;
+    c.nrow = nv;
+    if (a.sel != nullptr)
+        c.nrow = compact_selection(a.sel + size_t(b) * a.k, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
+    const int nk = c.nrow + nwin;
+    const size_t pbase = (size_t(b) * a.n_splits + split) * MH + DHG * hg;
+    if (split == 0 && hg == 0) {
+        // store the new latent in its ring slot.  Slot p % W holds token p - W, which this
+        // query does not read (its window is p-W+1 .. p, with p itself taken from kv_new),
+        // so the store cannot race the key loads of the other workgroups.
+        const uint4* src = reinterpret_cast<const uint4*>(c.kv_new);
+        uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(c.ring) + size_t(uint32_t(p) % c.W) * MD);
+        if (tid < MD / 8) dst[tid] = src[tid];
+    }
+    if (c.kb >= nk) {
+        if (tid < DHG) {
+            a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
+            a.part_ml[(pbase + tid) * 2 + 1] = 0.f;
+        }
+        return;
+    }
+    const int ke = c.kb + a.keys_per_split < nk ? c.kb + a.keys_per_split : nk;
+    const int ntiles = (ke - c.kb + MKT - 1) / MKT;
+    auto tile_keys = [&](int t) -> int {
+        const int left = ke - (c.kb + t * MKT);
+        return left < MKT ? left : MKT;
+    };
+    // copies in flight: the group's q rows, tile 0, tile 1
+    {
+        const bf16* qg = a.q + (size_t(b) * MH + DHG * hg) * MD;
+#pragma unroll
+        for (int i = 0; i < DHG / 4; ++i)
+            dma16(qg + size_t(w + 4 * i) * MD, uint32_t(lane) * 16, qs + (w + 4 * i) * QPITCH);
+    }
+    load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
+    if (ntiles > 1) load_tile(c, codes, kbuf[1], c.kb + MKT, tile_keys(1));
+    floatx4 o[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[m][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;     // head 16 hg + l%16; l_run over this wave's keys
+    // tile t has landed once only tile t+1's copies may be pending (a partial tile t+1
+    // issues fewer than 16 per wave: then wait for everything)
+    auto wait_tile = [&](int t) {
+        if (t + 1 < ntiles && tile_keys(t + 1) == MKT) wait_vm_tile(); else wait_vm();
+        lds_barrier();
+    };
+    wait_tile(0);
+    bf16x8 qb[MD / 32];                       // Q^T: lane l holds head 16 hg + l%16, dims 32 ks + 8 g
+#pragma unroll
+    for (int ks = 0; ks < MD / 32; ++ks) qb[ks] = load_bf16x8(qs + l16 * QPITCH + ks * 64 + 16 * g);
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t > 0) wait_tile(t);
+        const int nkt = tile_keys(t);
+        const unsigned char* buf = kbuf[t & 1];
+        // S^T for keys 16 w .. 16 w + 15
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+        const unsigned char* kr = buf + (16 * w + l16) * KPITCH + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < MD / 32; ++ks) st = mfma16x16x32(load_bf16x8(kr + ks * 64), qb[ks], st);
+        float sv[4];
+        float lmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sv[i] = 16 * w + 4 * g + i < nkt ? st[i] * a.scale_log2 : -INFINITY;
+            lmax = fmaxf(lmax, sv[i]);
+        }
+        lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+        lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+        if (g == 0) xch[0][w][l16] = lmax;
+        lds_barrier();
+        const float tmax = fmaxf(fmaxf(xch[0][0][l16], xch[0][1][l16]), fmaxf(xch[0][2][l16], xch[0][3][l16]));
+        if (tmax > m_run + kLazy) {
+            const float alpha = exp2f(m_run - tmax);
+            m_run = tmax;
+            l_run *= alpha;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[m][i] *= alpha;
+        }
+        float p4[4], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p4[i] = exp2f(sv[i] - m_run);
+            psum += p4[i];
+        }
+        *reinterpret_cast<uint2*>(ptile + l16 * PPITCH + (16 * w + 4 * g) * 2) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
+        psum += __shfl_xor(psum, 16, 64);
+        l_run += psum + __shfl_xor(psum, 32, 64);
+        lds_barrier();
+        // O^T for dims 128 w .. 128 w + 127: 8 tiles of 16 dims x 2 k-steps of 32 keys
+        const unsigned char* pr = ptile + l16 * PPITCH + 16 * g;
+        const unsigned char* vb0 = buf + (8 * g + (l16 >> 2)) * KPITCH + (128 * w + 4 * (l16 & 3)) * 2;
+#pragma unroll
+        for (int ks = 0; ks < MKT / 32; ++ks) {
+            const bf16x8 pb = load_bf16x8(pr + ks * 64);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const unsigned char* vp = vb0 + 32 * ks * KPITCH + m * 32;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+                const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
+                bf16x8 va;
+                __builtin_memcpy(&va, &lo, 8);
+                __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &up, 8);
+                o[m] = mfma16x16x32(va, pb, o[m]);
             }
         }
-        const uint32_t lo = uint32_t(bf16_bits(acc.x)) | (uint32_t(bf16_bits(acc.y)) << 16);
-        const uint32_t up = uint32_t(bf16_bits(acc.z)) | (uint32_t(bf16_bits(acc.w)) << 16);
-        *reinterpret_cast<uint2*>(ob + size_t(hh) * MD + d4 * 4) = make_uint2(lo, up);
+        if (t + 2 < ntiles) {
+            lds_barrier();                    // every wave is done with this buffer
+            load_tile(c, codes, kbuf[t & 1], c.kb + (t + 2) * MKT, tile_keys(t + 2));
+        }
     }
+
+    // denominator of head 16 hg + l%16 over all four waves' keys
+    if (g == 0) xch[1][w][l16] = l_run;
+    __syncthreads();
+    const float l_tot = (xch[1][0][l16] + xch[1][1][l16]) + (xch[1][2][l16] + xch[1][3][l16]);
+    const int head = DHG * hg + l16;
+    // lane l holds dims 128 w + 16 m + 4 g + i of head `head`
+    if (a.n_splits == 1) {
+        const float z = a.sinks[head] * kLog2e;
+        const float mf = fmaxf(m_run, z);
+        const float sc = exp2f(m_run - mf);
+        const float f = sc / (l_tot * sc + exp2f(z - mf));
+        bf16* ob = a.out + (size_t(b) * MH + head) * MD + 128 * w + 4 * g;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            *reinterpret_cast<uint2*>(ob + 16 * m) = pack4_bf16(o[m][0] * f, o[m][1] * f, o[m][2] * f, o[m][3] * f);
+    } else {
+        if (w == 0 && g == 0) {
+            a.part_ml[(pbase + l16) * 2 + 0] = m_run;
+            a.part_ml[(pbase + l16) * 2 + 1] = l_tot;
+        }
+        float* po = a.part_o + (pbase + l16) * MD + 128 * w + 4 * g;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) *reinterpret_cast<float4*>(po + 16 * m) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+    }
+}
+
+// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One
+// workgroup of 128 threads per (query, head); thread t owns latent dims 4t .. 4t + 3 and
+// issues its split loads independently of each other.
+__global__ void __launch_bounds__(128)
+attn_combine_kernel(AttnMfmaArgs a) {
+    __shared__ float wgt[MAX_SPLITS];
+    const int b = blockIdx.z;
+    const int64_t s = blockIdx.y;
+    const int h = blockIdx.x;
+    const size_t base = (size_t(b) * a.S + size_t(s)) * a.n_splits;
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const bool on = tid < a.n_splits;
+        const float m = on ? a.part_ml[((base + tid) * MH + h) * 2] : -INFINITY;
+        const float l = on ? a.part_ml[((base + tid) * MH + h) * 2 + 1] : 0.f;
+        const float z = a.sinks[h] * kLog2e;
+        const float M = wave_max(fmaxf(m, z));
+        const float e = m == -INFINITY ? 0.f : exp2f(m - M);
+        const float den = wave_sum(l * e) + exp2f(z - M);
+        if (on) wgt[tid] = e / den;
+    }
+    __syncthreads();
+    const float* po = a.part_o + (base * MH + h) * MD + tid * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int sp = 0; sp < a.n_splits; ++sp) {
+        // an empty split wrote no output: its weight is 0 and its stale values are skipped
+        const float wv = wgt[sp];
+        const float4 v = *reinterpret_cast<const float4*>(po + size_t(sp) * MH * MD);
+        acc.x += wv != 0.f ? wv * v.x : 0.f;
+        acc.y += wv != 0.f ? wv * v.y : 0.f;
+        acc.z += wv != 0.f ? wv * v.z : 0.f;
+        acc.w += wv != 0.f ? wv * v.w : 0.f;
+    }
+    bf16* ob = a.out + ((size_t(b) * a.S + size_t(s)) * MH + h) * MD + tid * 4;
+    *reinterpret_cast<uint2*>(ob) = pack4_bf16(acc.x, acc.y, acc.z, acc.w);
 }
 
 // Splits per query: enough workgroups to cover the chip when there are few queries.
 int mfma_splits(int64_t queries, int64_t nk_max, int* keys_per_split) {
     const int64_t tiles = (nk_max + MKT - 1) / MKT;
     int64_t want = queries >= 512 ? 1 : (512 + queries - 1) / queries;
+    if (want > MAX_SPLITS) want = MAX_SPLITS;
+    if (want > tiles) want = tiles;
+    if (want < 1) want = 1;
+    const int64_t tiles_per = (tiles + want - 1) / want;
+    *keys_per_split = int(tiles_per * MKT);
+    return int((tiles + tiles_per - 1) / tiles_per);
+}
+
+// Decode key splits: about 128 workgroups over (sequence, head group, split), each split a
+// whole number of 64-key tiles.
+int decode_splits(int batch, int64_t nk_max, int* keys_per_split) {
+    const int64_t tiles = (nk_max + MKT - 1) / MKT;
+    int64_t want = (128 + 4 * batch - 1) / (4 * batch);
     if (want > MAX_SPLITS) want = MAX_SPLITS;
     if (want > tiles) want = tiles;
     if (want < 1) want = 1;
@@ -621,19 +838,31 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         a.W = j.W;
         a.r = j.r;
         a.scale_log2 = j.scale * kLog2e;
-        a.n_splits = mfma_splits(int64_t(nb) * j.S, nrow_max + j.W, &a.keys_per_split);
+        const bool decode = j.S == 1;
+        if (decode)
+            a.n_splits = decode_splits(nb, nrow_max + j.W, &a.keys_per_split);
+        else
+            a.n_splits = mfma_splits(int64_t(nb) * j.S, nrow_max + j.W, &a.keys_per_split);
         float* ws = static_cast<float*>(j.ws);
         a.part_ml = ws;
         a.part_o = ws + size_t(nb) * j.S * a.n_splits * MH * 2;
-        trace_begin("attn_mfma", st);
-        hipLaunchKernelGGL(attn_mfma_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(256),
-                           0, st, a, pos, nr);
-        trace_end("attn_mfma", st);
-        hipError_t e = hipGetLastError();
+        hipError_t e;
+        if (decode) {
+            trace_begin("attn_decode", st);
+            hipLaunchKernelGGL(attn_decode_kernel, dim3(unsigned(a.n_splits), MH / DHG, nb), dim3(256),
+                               0, st, a, pos, nr);
+            trace_end("attn_decode", st);
+        } else {
+            trace_begin("attn_mfma", st);
+            hipLaunchKernelGGL(attn_mfma_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(256),
+                               0, st, a, pos, nr);
+            trace_end("attn_mfma", st);
+        }
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.n_splits > 1) {
             trace_begin("attn_combine", st);
-            hipLaunchKernelGGL(attn_combine_kernel, dim3(MH / 8, unsigned(j.S), nb), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(attn_combine_kernel, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
             trace_end("attn_combine", st);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -656,7 +885,8 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
 }  // namespace
 
 int64_t attn_max_keys(bool bf16_, int H, int D, int k, bool has_sel) {
-    if (use_mfma(bf16_, H, D)) return has_sel && k > MAX_CODES ? 0 : (int64_t(1) << 31) - 1;
+    // the MFMA kernels index keys in 32 bits
+    if (use_mfma(bf16_, H, D)) return has_sel && k > MAX_CODES ? 0 : int64_t(1) << 30;
     return int64_t((kAttnLdsMax - size_t(D) * 4) / 8);
 }
 
