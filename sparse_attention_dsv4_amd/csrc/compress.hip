@@ -29,6 +29,7 @@ namespace dsv4 {
 namespace {
 
 constexpr int kCompThreads = 256;
+constexpr int kStepThreads = 512;     // decode step: one latent channel per thread at D = 512
 
 template <typename T>
 struct CompArgs {
@@ -45,52 +46,60 @@ struct CompArgs {
     int64_t n_new;
 };
 
-// Address of token t's lane value at lane column `col`, from the state or the new lanes.
-template <typename T>
-__device__ __forceinline__ const T* token_ptr(const CompArgs<T>& a, int b, int lane, int64_t t,
-                                              int64_t lb, int col) {
-    const int W = a.coff * a.D;
-    if (t < lb) {
-        const size_t st = size_t(2) * a.coff * a.r * W;
-        const T* base = a.state + size_t(b) * st + size_t(lane) * a.coff * a.r * W;
-        return base + (size_t((t / a.r) % a.coff) * a.r + size_t(t % a.r)) * W + col;
-    }
-    const T* lanep = lane == 0 ? a.lane_a : a.lane_g;
-    return lanep + (size_t(b) * a.n_new + size_t(t - lb)) * W + col;
+// One slot of the per-channel online softmax.  Branch-free form of the usual update: when
+// the logit does not raise the running max, f = exp(0) = 1 and e = exp(logit - m); when it
+// does, f = exp(m - logit) and e = exp(0) = 1 -- the same values as the branching update.
+__device__ __forceinline__ void pool_slot(float logit, float v, float& m, float& l, float& acc) {
+    const float mn = fmaxf(m, logit);
+    const float f = expf(m - mn);             // 0 when m = -inf
+    const float e = expf(logit - mn);
+    acc = acc * f + e * v;
+    l = l * f + e;
+    m = mn;
 }
 
 // Row j of sequence b: pooled per channel with an online softmax over its slots, rounded,
-// RMS-normalised, rounded, RoPE'd on the last rd dims at position j*r, rounded.
+// RMS-normalised, rounded, RoPE'd on the last rd dims at position j*r, rounded.  Slot s of
+// window w is token w*r + s: tokens before the call (t < lb) sit in state window (w % coff)
+// at position s, later ones in the new lanes at t - lb.  All positions fit in 32 bits.
 template <typename T>
-__device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int64_t j, int64_t lb,
+__device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int lb,
                                          float* zrow, float* red) {
-    const int D = a.D, W = a.coff * a.D;
+    const int D = a.D, W = a.coff * a.D, r = a.r;
+    const size_t st = size_t(2) * a.coff * r * W;
+    const T* sa0 = a.state + size_t(b) * st;                 // kv lane of this sequence
+    const T* sg0 = sa0 + size_t(a.coff) * r * W;             // gate lane
     float ss = 0.f;
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float m = -INFINITY, l = 0.f, acc = 0.f;
         for (int half = 0; half < a.coff; ++half) {
             // overlap: half 0 <- window j-1, half 1 <- window j; plain: half 0 <- window j
-            const int64_t win = (a.coff == 2 && half == 0) ? j - 1 : j;
+            const int win = (a.coff == 2 && half == 0) ? j - 1 : j;
             if (win < 0) continue;
             const int col = half * D + c;
-            for (int s = 0; s < a.r; ++s) {
-                const int64_t t = win * a.r + s;
-                const float logit = to_f32(*token_ptr(a, b, 1, t, lb, col)) +
-                                    to_f32(a.ape[size_t(s) * W + col]);
-                const float v = to_f32(*token_ptr(a, b, 0, t, lb, col));
-                if (logit > m) {
-                    const float f = expf(m - logit);   // 0 when m = -inf
-                    acc = acc * f + v;
-                    l = l * f + 1.f;
-                    m = logit;
-                } else {
-                    const float e = expf(logit - m);
-                    acc += e * v;
-                    l += e;
+            const int t0 = win * r;
+            int n_state = lb - t0;                             // slots taken from the state
+            n_state = n_state < 0 ? 0 : (n_state > r ? r : n_state);
+            const size_t wo = size_t(win % a.coff) * r * W + col;
+            const T* sa = sa0 + wo;
+            const T* sg = sg0 + wo;
+            const T* ap = a.ape + col;
+#pragma unroll 8
+            for (int s = 0; s < n_state; ++s)
+                pool_slot(to_f32(sg[size_t(s) * W]) + to_f32(ap[size_t(s) * W]),
+                          to_f32(sa[size_t(s) * W]), m, l, acc);
+            if (n_state < r) {                                 // first new token: t0 + n_state
+                const size_t first = size_t(b) * a.n_new + size_t(t0 + n_state - lb);
+                const T* la = a.lane_a + first * W + col;
+                const T* lg = a.lane_g + first * W + col;
+#pragma unroll 8
+                for (int s = n_state; s < r; ++s) {
+                    const size_t o = size_t(s - n_state) * W;
+                    pool_slot(to_f32(lg[o]) + to_f32(ap[size_t(s) * W]), to_f32(la[o]), m, l, acc);
                 }
             }
         }
-        const float y = round_to<T>(acc / l);
+    const float y = round_to<T>(acc / l);
         zrow[c] = y;
         ss += y * y;
     }
@@ -100,7 +109,7 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int64_t j,
         zrow[c] = round_to<T>(zrow[c] / den * to_f32(a.gamma[c]));
     __syncthreads();
     const int r0 = D - a.rd;
-    const float pos = float(j * a.r);
+    const float pos = float(int64_t(j) * a.r);
     T* out = a.rows + (size_t(b) * a.row_cap + size_t(j)) * D;
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float v = zrow[c];
@@ -121,9 +130,9 @@ compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
     extern __shared__ float zrow[];           // [D]
     __shared__ float red[16];
     const int b = blockIdx.y;
-    const int64_t lb = len_before.v[b];
-    const int64_t j = lb / a.r + blockIdx.x;  // row index
-    if ((j + 1) * a.r > lb + a.n_new) return;
+    const int lb = len_before.v[b];
+    const int j = lb / a.r + int(blockIdx.x);  // row index
+    if (int64_t(j + 1) * a.r > lb + a.n_new) return;
     emit_row(a, b, j, lb, zrow, red);
 }
 
@@ -131,7 +140,7 @@ compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
 // window, emit that row -- one launch.  The row reads the state only at positions of
 // earlier tokens and takes the new token from the lane, so the store cannot race it.
 template <typename T>
-__global__ void __launch_bounds__(kCompThreads)
+__global__ void __launch_bounds__(kStepThreads)
 compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
     extern __shared__ float zrow[];
     __shared__ float red[16];
@@ -146,7 +155,7 @@ compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
         sa[c] = a.lane_a[size_t(b) * W + c];
         sg[c] = a.lane_g[size_t(b) * W + c];
     }
-    if ((lb + 1) % a.r == 0) emit_row(a, b, lb / a.r, lb, zrow, red);
+    if ((lb + 1) % a.r == 0) emit_row(a, b, int(lb / a.r), int(lb), zrow, red);
 }
 
 template <typename T>
@@ -192,7 +201,7 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
             a.n_new = 1;
             for (int i = 0; i < nb; ++i) lb.v[i] = int32_t(j.len_before[b0 + i]);
             trace_begin("compress_step", s);
-            hipLaunchKernelGGL(compress_step_kernel<T>, dim3(nb), dim3(kCompThreads),
+            hipLaunchKernelGGL(compress_step_kernel<T>, dim3(nb), dim3(kStepThreads),
                                j.D * sizeof(float), s, a, lb);
             trace_end("compress_step", s);
             hipError_t e = hipGetLastError();
