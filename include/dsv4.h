@@ -149,6 +149,7 @@ int dsv4_compress_step(const dsv4_comp_cfg* cfg, void* state, const void* kv_lan
  *             are at most k of them, else the k visible rows with the largest scores, ties
  *             to the lower row index; ascending, then -1 padding.  -0.0 ties +0.0.
  *   ws        workspace of at least dsv4_index_workspace_bytes(cfg, batch, s, max n_rows)
+ *             bytes, 16-byte aligned (EINVAL otherwise); no initialisation needed
  * Errors: EINVAL, ECAPACITY (n_rows > row_cap), EWORKSPACE, EUNSUPPORTED (H_i or d_i out
  * of range), EHIP. */
 int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,

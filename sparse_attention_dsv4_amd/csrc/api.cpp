@@ -226,11 +226,13 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
     const size_t need_ws = dsv4::index_workspace_bytes(cfg->heads, cfg->dim, cfg->topk, batch, s, n_max);
     if (!ws || ws_bytes < need_ws)
         return fail(DSV4_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need_ws);
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(DSV4_EINVAL, "workspace must be 16-byte aligned");
     dsv4::IndexJob j;
     j.Hi = cfg->heads; j.di = cfg->dim; j.k = cfg->topk; j.r = cfg->ratio;
     j.bf16 = cfg->dtype == DSV4_BF16;
     j.qi = qi; j.w = w; j.rows = idx_rows; j.row_cap = row_cap; j.S = s;
-    j.n_stride = n_max < 1 ? 1 : n_max;
+    j.n_stride = dsv4::index_key_stride(n_max);
     j.batch = batch; j.n_rows = n_rows; j.pos0 = pos0; j.sel = sel;
     j.keys = static_cast<uint32_t*>(ws);
     return hip_status(dsv4::launch_index_topk(j, static_cast<hipStream_t>(stream)), "index_topk");

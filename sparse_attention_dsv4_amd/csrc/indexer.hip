@@ -358,16 +358,12 @@ topk_select_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
 }
 
 
-// ------------------------------------------------------------------ select with keys in LDS
-// For up to kSelLdsKeys visible rows: the query's keys are staged in LDS once; an 11-bit
-// histogram over all of them locates the bucket of the k-th largest key, that bucket's keys
-// are gathered as candidates, and two more passes (11 and 10 bits) over the candidates give
-// the exact threshold.  Compaction in row order then writes the ascending selection.
-constexpr int kSelLdsKeys = 16384;
-constexpr int kSelLdsThreads = 512;
-constexpr int kSelCand = 4096;
+// ------------------------------------------------------------------ exact top-k select
+// Radix select of the k-th largest key of the query's visible prefix, then compaction in
+// row order (helpers first: block-wide scan and bucket search over a histogram).
+constexpr int kSelRegThreads = 512;
 
-// Exclusive prefix sum over the workgroup (kSelLdsThreads threads); `tmp` holds 8 ints.
+// Exclusive prefix sum over the workgroup (kSelRegThreads threads); `tmp` holds 8 ints.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
@@ -381,7 +377,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     __syncthreads();
     int add = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kSelLdsThreads / 64; ++i) {
+    for (int i = 0; i < kSelRegThreads / 64; ++i) {
         tot += tmp[i];
         add += i < w ? tmp[i] : 0;
     }
@@ -393,7 +389,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 // find the bin holding the rem-th largest key.  Writes the bin and the count still needed
 // inside it to sh[0], sh[1].
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int rem, int* tmp, int* sh) {
-    const int per = bins / kSelLdsThreads;            // 4 or 2 bins per thread
+    const int per = bins / kSelRegThreads;            // 4 or 2 bins per thread
     const int t = threadIdx.x;
     int part = 0;
     for (int i = 0; i < per; ++i) part += int(hist[t * per + i]);
@@ -411,115 +407,139 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int 
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kSelLdsThreads)
-topk_select_lds_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
-    __shared__ uint32_t keys[kSelLdsKeys];
+// ------------------------------------------------------------------ select with keys in registers
+// For up to 512 * KPT visible rows.  Wave w owns the contiguous key range [w C, (w+1) C),
+// C = 64 KPT; within it lane l holds groups of 4 consecutive keys at w C + 256 i + 4 l, read
+// with one 16-byte load each (a wave instruction reads 1 KB contiguous).  The three radix
+// passes (11, 11, 10 bits) histogram the keys straight from registers; the compaction walks
+// each wave's groups in row order, with lane prefix sums giving every taken row its slot.
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+template <int KPT>
+__global__ void __launch_bounds__(kSelRegThreads)
+topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
+    constexpr int G = KPT / 4;                         // groups of 4 keys per lane
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t cand[kSelCand];
     __shared__ int tmp[8];
     __shared__ int sh[4];
+    __shared__ int wtot[2][kSelRegThreads / 64];
     const int b = blockIdx.y;
-    const int64_t s = blockIdx.x;
-    const int64_t p = int64_t(pos0.v[b]) + s;
-    int nv = int((p + 1) / a.r);
+    const int s = blockIdx.x;
+    const int p = pos0.v[b] + s;
+    int nv = (p + 1) / a.r;
     if (nv > n_rows.v[b]) nv = n_rows.v[b];
     int32_t* out = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (nv <= a.k) {
         for (int i = tid; i < a.k; i += blockDim.x) out[i] = i < nv ? i : -1;
         return;
     }
+    // keys (0 for rows past nv; they are never counted)
     const uint32_t* gk = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
-    for (int j = tid; j < nv; j += blockDim.x) keys[j] = gk[j];
-    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
-    if (tid == 0) sh[2] = 0;
+    const int wbase = w * 64 * KPT + 4 * lane;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int j = wbase + 256 * i;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (j < nv) v = *reinterpret_cast<const uint4*>(gk + j);   // in the row: stride % 4 == 0
+        key[4 * i + 0] = v.x;
+        key[4 * i + 1] = j + 1 < nv ? v.y : 0u;
+        key[4 * i + 2] = j + 2 < nv ? v.z : 0u;
+        key[4 * i + 3] = j + 3 < nv ? v.w : 0u;
+    }
+    auto valid = [&](int e) { return wbase + 256 * (e >> 2) + (e & 3) < nv; };
+    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
     __syncthreads();
-
-    // pass 1: bits 31..21 over every key
-    for (int j = tid; j < nv; j += blockDim.x) atomicAdd(&hist[keys[j] >> 21], 1u);
+    // pass 1: bits 31..21
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (valid(e)) atomicAdd(&hist[key[e] >> 21], 1u);
     __syncthreads();
     find_bucket(hist, 2048, a.k, tmp, sh);
     const uint32_t d1 = uint32_t(sh[0]);
     int rem = sh[1];
-    const int lane = tid & 63;
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    for (int j0 = tid - lane; j0 < nv; j0 += blockDim.x) {      // whole waves step together
-        const int j = j0 + lane;
-        const uint32_t kk = j < nv ? keys[j] : 0u;
-        const bool hit = j < nv && (kk >> 21) == d1;
-        const unsigned long long m = __ballot(hit);
-        int base = 0;
-        if (lane == 0 && m) base = atomicAdd(&sh[2], __popcll(m));
-        base = __shfl(base, 0, 64);
-        const int pos = base + __popcll(m & lt);
-        if (hit && pos < kSelCand) cand[pos] = kk;
-    }
-    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
     __syncthreads();
-    const int ncand = sh[2];
-    const bool in_cand = ncand <= kSelCand;
-    const uint32_t* src = in_cand ? cand : keys;
-    const int nsrc = in_cand ? ncand : nv;
-
-    // pass 2: bits 20..10 of keys in bucket d1
-    for (int j = tid; j < nsrc; j += blockDim.x) {
-        const uint32_t kk = src[j];
-        if ((kk >> 21) == d1) atomicAdd(&hist[(kk >> 10) & 2047u], 1u);
-    }
+    // pass 2: bits 20..10 of the keys in bucket d1
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (valid(e) && (key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
     __syncthreads();
     find_bucket(hist, 2048, rem, tmp, sh);
-    const uint32_t d2 = uint32_t(sh[0]);
+    const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
     rem = sh[1];
-    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
     __syncthreads();
-    // pass 3: bits 9..0 of keys with prefix (d1, d2)
-    const uint32_t pre = (d1 << 11) | d2;
-    for (int j = tid; j < nsrc; j += blockDim.x) {
-        const uint32_t kk = src[j];
-        if ((kk >> 10) == pre) atomicAdd(&hist[kk & 1023u], 1u);
-    }
+    // pass 3: bits 9..0 of the keys with prefix (d1, d2)
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (valid(e) && (key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
     __syncthreads();
     find_bucket(hist, 1024, rem, tmp, sh);
     const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
-    rem = sh[1];
+    rem = sh[1];                                       // rows with key == thr still to take
 
-    // compaction in row order: wave w owns a contiguous chunk, read 64 keys at a time
-    // (coalesced); ballots give every lane its rank among the rows taken so far
-    const int w = tid >> 6, nw = blockDim.x >> 6;
-    const int chunk = ((nv + nw - 1) / nw + 63) & ~63;
-    const int lo = w * chunk < nv ? w * chunk : nv;
-    const int hi = lo + chunk < nv ? lo + chunk : nv;
+    // compaction in row order: wave totals first, then each wave walks its groups
     int ngt = 0, neq = 0;
-    for (int j0 = lo; j0 < hi; j0 += 64) {
-        const int j = j0 + lane;
-        const uint32_t kk = j < hi ? keys[j] : 0u;
-        ngt += __popcll(__ballot(j < hi && kk > thr));
-        neq += __popcll(__ballot(j < hi && kk == thr));
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        ngt += valid(e) && key[e] > thr;
+        neq += valid(e) && key[e] == thr;
     }
-    __shared__ int wtot[2][16];
+    ngt = wave_sum_int(ngt);
+    neq = wave_sum_int(neq);
     if (lane == 0) {
         wtot[0][w] = ngt;
         wtot[1][w] = neq;
     }
     __syncthreads();
-    int gt0 = 0, eq0 = 0;
-    for (int i = 0; i < w; ++i) {
-        gt0 += wtot[0][i];
-        eq0 += wtot[1][i];
+    int o = 0, eqb = 0;                                // rows taken / ties seen before this wave
+    for (int v = 0; v < w; ++v) {
+        eqb += wtot[1][v];
+        o += wtot[0][v];
     }
-    int eq_rank = eq0;
-    int o = gt0 + (eq_rank < rem ? eq_rank : rem);
-    for (int j0 = lo; j0 < hi; j0 += 64) {
-        const int j = j0 + lane;
-        const uint32_t kk = j < hi ? keys[j] : 0u;
-        const bool g = j < hi && kk > thr;
-        const bool e = j < hi && kk == thr;
-        const unsigned long long be = __ballot(e);
-        const bool take = g || (e && eq_rank + __popcll(be & lt) < rem);
-        const unsigned long long bt = __ballot(take);
-        if (take) out[o + __popcll(bt & lt)] = j;
-        o += __popcll(bt);
-        eq_rank += __popcll(be);
+    o += eqb < rem ? eqb : rem;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        int ge = 0;
+#pragma unroll
+        for (int e = 4 * i; e < 4 * i + 4; ++e) ge += valid(e) && key[e] == thr;
+        const int ge_incl = wave_incl_scan(ge);
+        int eq_rank = eqb + ge_incl - ge;               // ties before this lane's first key
+        int mask = 0;
+#pragma unroll
+        for (int e = 4 * i; e < 4 * i + 4; ++e) {
+            const bool v = valid(e);
+            const bool gt = v && key[e] > thr;
+            const bool eq = v && key[e] == thr;
+            const bool take = gt || (eq && eq_rank < rem);
+            eq_rank += eq;
+            mask |= int(take) << (e - 4 * i);
+        }
+        const int nt = __popc(mask);
+        const int nt_incl = wave_incl_scan(nt);
+        int slot = o + nt_incl - nt;
+        const int j0 = wbase + 256 * i;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (mask & (1 << e)) out[slot++] = j0 + e;
+        o += __shfl(nt_incl, 63, 64);
+        eqb += __shfl(ge_incl, 63, 64);
     }
 }
 
@@ -591,11 +611,16 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.k = j.k; sa.r = j.r; sa.S = j.S; sa.n_stride = j.n_stride;
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
-        if (nv_max <= kSelLdsKeys) {
-            trace_begin("topk_select_lds", st);
-            hipLaunchKernelGGL(topk_select_lds_kernel, dim3(unsigned(j.S), nb), dim3(kSelLdsThreads),
-                               0, st, sa, pos, nr);
-            trace_end("topk_select_lds", st);
+        if (nv_max <= int64_t(kSelRegThreads) * 32) {
+            trace_begin("topk_select_reg", st);
+            hipLaunchKernelGGL(topk_select_reg_kernel<32>, dim3(unsigned(j.S), nb),
+                               dim3(kSelRegThreads), 0, st, sa, pos, nr);
+            trace_end("topk_select_reg", st);
+        } else if (nv_max <= int64_t(kSelRegThreads) * 64) {
+            trace_begin("topk_select_reg", st);
+            hipLaunchKernelGGL(topk_select_reg_kernel<64>, dim3(unsigned(j.S), nb),
+                               dim3(kSelRegThreads), 0, st, sa, pos, nr);
+            trace_end("topk_select_reg", st);
         } else {
             trace_begin("topk_select", st);
             hipLaunchKernelGGL(topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
@@ -610,9 +635,11 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
 
 }  // namespace
 
+int64_t index_key_stride(int64_t n_max) { return ((n_max < 1 ? 1 : n_max) + 3) & ~int64_t(3); }
+
 size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max) {
     (void)Hi; (void)di; (void)k;
-    return size_t(batch) * size_t(S) * size_t(n_max < 1 ? 1 : n_max) * sizeof(uint32_t);
+    return size_t(batch) * size_t(S) * size_t(index_key_stride(n_max)) * sizeof(uint32_t);
 }
 
 hipError_t launch_index_topk(const IndexJob& j, hipStream_t s) {

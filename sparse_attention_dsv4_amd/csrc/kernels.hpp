@@ -43,6 +43,8 @@ struct IndexJob {
 };
 hipError_t launch_index_topk(const IndexJob& j, hipStream_t s);
 size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max);
+// Row stride (in keys) of the score-key workspace: a multiple of 4, so rows are 16-byte aligned.
+int64_t index_key_stride(int64_t n_max);
 
 struct AttnJob {
     int H, D, W, r, k;

@@ -95,6 +95,10 @@ def test_index_validation(L):
     assert _index(L, cfg, pos0=_i64(-1)) == EINVAL
     assert _index(L, cfg, ws_bytes=16) == EWS
     assert _index(L, cfg, ws=None) == EWS
+    assert _index(L, cfg, ws=ctypes.c_void_p(FAKE.value + 4)) == EINVAL    # key rows need 16 B
+    assert "aligned" in L.dsv4_last_error().decode()
+    # key rows are padded to a multiple of 4 keys
+    assert K.dsv4_index_workspace_bytes(cfg, 2, 3, 601) == 2 * 3 * 604 * 4
     assert _index(L, cfg, sel=None) == EINVAL
     assert _index(L, cfg, s=70000) == EUNSUP
     assert _index(L, cfg, s=0, qi=None) == 0

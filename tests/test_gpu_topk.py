@@ -1,0 +1,87 @@
+"""Indexer top-k through the C ABI at row counts that reach every selection kernel, and
+with massive exact ties (needs a gfx950 GPU).
+
+The indexer rows are drawn directly (the index call takes them as input), so the oracle only
+scores and selects: fp32 scores, the k largest, ties to the lower row, ascending output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_dsv4_amd as K
+from tests import gpu_harness as G
+from sparse_attention_dsv4_amd.layer import LayerSpec
+
+pytestmark = pytest.mark.gpu
+
+SPEC = LayerSpec(ratio=4)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+
+
+def _run(rows_i, qi, w, positions, n_rows):
+    """rows_i [B, cap, di] bf16, qi [B, S, Hi, di] bf16, w [B, S, Hi] fp32 (GPU tensors)."""
+    B, S = qi.shape[0], qi.shape[1]
+    cfg = SPEC.index_cfg()
+    sel = torch.full((B, S, SPEC.topk), -2, dtype=torch.int32, device="cuda")
+    nb = K.dsv4_index_workspace_bytes(cfg, B, S, max(n_rows))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    K.dsv4_index_topk(cfg, qi, w, rows_i, n_rows, [p[0] for p in positions], sel, ws)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()
+
+
+def _check(rows_i, qi, w, positions, sel, exact):
+    for b in range(qi.shape[0]):
+        P = positions[b]
+        rows = G.f64(rows_i[b])
+        scores = oracle.index_scores(G.f64(qi[b]), G.f64(w[b]), rows)
+        ref = oracle.select_topk(scores, P, ratio=SPEC.ratio, k=SPEC.topk)
+        if exact:
+            assert np.array_equal(sel[b], ref), f"sequence {b}: selection differs"
+        else:
+            ne, nb, nbad, bad = G.topk_band_ok(sel[b], ref, scores, P, SPEC)
+            print(f"  seq {b}: exact {ne}, in band {nb}")
+            assert nbad == 0, bad[:4]
+
+
+@pytest.mark.parametrize("n_vis", [16384, 20001, 32768, 33001])
+def test_topk_large_lanes(n_vis):
+    B, S = 2, 3
+    cap = n_vis + 8
+    g = 11 + n_vis
+    rows_i = synth.normal((B, cap, SPEC.index_dim), seed=g, stream="rows_i", dtype=torch.bfloat16,
+                          device="cuda")
+    qi = synth.normal((B, S, SPEC.index_heads, SPEC.index_dim), seed=g, stream="qi",
+                      dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, SPEC.index_heads), seed=g, stream="w", device="cuda")
+    # consecutive queries; the last one of sequence 0 sees exactly n_vis rows
+    positions = [[4 * n_vis - S - b + i for i in range(S)] for b in range(B)]
+    n_rows = [min(cap, (positions[b][-1] + 1) // 4) for b in range(B)]
+    sel = _run(rows_i, qi, w, positions, n_rows)
+    _check(rows_i, qi, w, positions, sel, exact=False)
+
+
+def test_topk_exact_ties_take_lower_rows():
+    """Rows repeat with period 7, so the scores take 7 values and the k-th score sits inside
+    a block of ~1/7 of the rows: the selection must take the lowest rows of that block."""
+    B, S, n_vis = 2, 2, 12000
+    cap = n_vis
+    base = synth.normal((7, SPEC.index_dim), seed=3, stream="base", dtype=torch.bfloat16,
+                        device="cuda")
+    idx = torch.arange(cap, device="cuda") % 7
+    rows_i = base[idx][None].repeat(B, 1, 1).contiguous()
+    qi = synth.normal((B, S, SPEC.index_heads, SPEC.index_dim), seed=4, stream="qi",
+                      dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, SPEC.index_heads), seed=4, stream="w", device="cuda")
+    positions = [[4 * n_vis - S + i for i in range(S)] for _ in range(B)]
+    n_rows = [cap] * B
+    sel = _run(rows_i, qi, w, positions, n_rows)
+    _check(rows_i, qi, w, positions, sel, exact=True)
