@@ -99,6 +99,10 @@ constexpr int kIdxQpw = DSV4_IDX_QPW;
 #endif
 constexpr int kIdxWaves = DSV4_IDX_WAVES;   // waves per prefill workgroup (one query each)
 
+#ifndef DSV4_IDX_STAGES
+#define DSV4_IDX_STAGES 4
+#endif
+constexpr int kIdxStages = DSV4_IDX_STAGES;   // LDS tile buffers of the scoring pipeline
 constexpr int IH = 64;                 // indexer heads
 constexpr int ID = 128;                // indexer dims
 constexpr int IRT = 128;               // rows per LDS tile
@@ -127,6 +131,17 @@ __device__ __forceinline__ void idx_dma16(const void* gptr, const unsigned char*
                  :: "s"(la), "v"(gptr) : "memory", "m0");
 }
 
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for LDS data only (copies to other buffers stay in flight).
+__device__ __forceinline__ void idx_lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Row r's 16-byte chunk c sits at chunk position c ^ (r & 15) of its 256-byte LDS row, so
 // the 32 rows an MFMA operand read touches spread over all banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 15); }
@@ -146,10 +161,13 @@ __device__ __forceinline__ void idx_load_tile(const IdxMfmaArgs& a, int b, int64
         if (j0 + row0 + 3 < j_end) {
             idx_dma16(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID + swz(row, lane & 15) * 8, dst);
         } else {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (jj < j_end)
-                v = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(jj)) * ID +
-                                                    swz(row, lane & 15) * 8);
+            // the rows past j_end are zero; the load is still issued (from the last row), so
+            // every wave issues exactly IRT / 4 / WAVES loads per tile and the pipeline's
+            // counted waits stay exact
+            const int64_t js = jj < j_end ? jj : j_end - 1;
+            uint4 v = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(js)) * ID +
+                                                      swz(row, lane & 15) * 8);
+            if (jj >= j_end) v = make_uint4(0, 0, 0, 0);
             store16(dst + lane * 16, v);
         }
     }
@@ -157,10 +175,10 @@ __device__ __forceinline__ void idx_load_tile(const IdxMfmaArgs& a, int b, int64
 
 // QPW queries per wave (prefill: the workgroup covers 4 * QPW) or, for QPW == 0, one query
 // shared by the whole workgroup (decode: each wave takes one 32-row block of every tile).
-template <int QPW, int WAVES>
+template <int QPW, int WAVES, int NSTAGE>
 __global__ void __launch_bounds__(64 * WAVES)
 index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
-    __shared__ __attribute__((aligned(16))) unsigned char kt[2][IRT * IROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char kt[NSTAGE][IRT * IROWB];
     constexpr bool SHARED_Q = QPW == 0;
     constexpr int NQ = SHARED_Q ? 1 : QPW;
     const int b = blockIdx.z;
@@ -200,14 +218,25 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         }
     }
 
+    // NSTAGE-buffer ring: tile t + NSTAGE - 1 is requested when tile t starts, so each copy
+    // has NSTAGE - 1 tiles of compute to land.  Every wave issues exactly OPS loads per tile;
+    // tile t has landed once at most the loads of the tiles after it are pending (stores in
+    // between can only make the counted wait stricter).
+    constexpr int OPS = IRT / 4 / WAVES;
     const int ntiles = int((j_end - j_begin + IRT - 1) / IRT);
-    idx_load_tile<WAVES>(a, b, j_begin, j_end, kt[0]);
-    __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NSTAGE - 1; ++t)
+        if (t < ntiles) idx_load_tile<WAVES>(a, b, j_begin + int64_t(t) * IRT, j_end, kt[t]);
     for (int t = 0; t < ntiles; ++t) {
         const int64_t j0 = j_begin + int64_t(t) * IRT;
-        if (t + 1 < ntiles) idx_load_tile<WAVES>(a, b, j0 + IRT, j_end, kt[(t + 1) & 1]);
-        const unsigned char* buf = kt[t & 1];
+        const int later = ntiles - 1 - t < NSTAGE - 2 ? ntiles - 1 - t : NSTAGE - 2;
+        if (later >= 2) wait_vm_loads<2 * OPS>();
+        else if (later == 1) wait_vm_loads<OPS>();
+        else wait_vm_loads<0>();
+        idx_lds_barrier();                             // tile t visible; tile t-1 fully read
+        if (t + NSTAGE - 1 < ntiles)
+            idx_load_tile<WAVES>(a, b, j0 + int64_t(NSTAGE - 1) * IRT, j_end, kt[(t + NSTAGE - 1) % NSTAGE]);
+        const unsigned char* buf = kt[t % NSTAGE];
         // 32-row blocks of the tile: prefill waves take all 4 (their own queries), decode waves
         // one each.  The MFMAs of block u+1 are issued before the epilogue of block u, so the
         // matrix pipe stays busy while the VALU reduces the previous block.
@@ -256,8 +285,6 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);              // the next tile has landed
-        __syncthreads();
     }
 }
 
@@ -579,10 +606,10 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
             trace_begin("index_score_mfma", st);
             if (perq)
-                hipLaunchKernelGGL((index_score_mfma_kernel<kIdxQpw, kIdxWaves>),
+                hipLaunchKernelGGL((index_score_mfma_kernel<kIdxQpw, kIdxWaves, kIdxStages>),
                                    dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
             else
-                hipLaunchKernelGGL((index_score_mfma_kernel<0, 4>), dim3(gx, unsigned(groups), nb),
+                hipLaunchKernelGGL((index_score_mfma_kernel<0, 4, kIdxStages>), dim3(gx, unsigned(groups), nb),
                                    dim3(256), 0, st, a, pos, nr);
             trace_end("index_score_mfma", st);
             hipError_t e = hipGetLastError();
