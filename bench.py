@@ -18,11 +18,16 @@ Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
+from collections import defaultdict
 
 import numpy as np
 import torch
@@ -165,7 +170,8 @@ def bench_decode(args, seed=0):
                   "mode": "one library call per lane per step from Python"},
         "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": attn_name,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile(TRAFFIC_DECODE, attn_name), "kernel": attn_name,
                      "bytes_per_launch": bytes_launch},
     }
     layer_state = (layer, toks, spec, params, pos)
@@ -257,7 +263,8 @@ def bench_prefill(args, seed=1):
         "tflops_whole_chunk": (idx_flops + attn_flops) / (total_ms * 1e-3) / 1e12,
         "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                     "traffic": traffic_from_profile(TRAFFIC_PREFILL, dom),
                      "kernel": dom, "flops_per_launch": dom_flops},
     }
     return res, (layer, tok, spec, params, start, sel)
@@ -293,7 +300,157 @@ def cpu_baseline_prefill(state, n_queries):
                       f"~16K rows, top-512, attention), numpy fp32 oracle"}
 
 
+# ------------------------------------------------------------------ profiles
+# The summaries under profiles/ are written from rocprofv3 output by the modes below (no GPU
+# needed), so each one names commands that run committed files only.  A traffic summary
+# records a digest of its kernel's sources; the JSON line reports its traffic only while the
+# sources still match (a changed kernel reports null until it is measured again).
+CSRC = os.path.join(ROOT, "sparse_attention_dsv4_amd", "csrc")
+KERNEL_SOURCES = {"attn": "attention.hip", "ring": "attention.hip", "index": "indexer.hip",
+                  "topk": "indexer.hip", "compress": "compress.hip"}
+COPY_CALIB_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
+TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_mfma_ctx65536_chunk2048_ratio4.txt")
+
+
+def kernel_source_digest(kernel: str) -> str:
+    src = next(v for k, v in KERNEL_SOURCES.items() if kernel.startswith(k))
+    h = hashlib.sha256()
+    for f in (src, "common.hpp", "mfma.hpp", "kernels.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """A device-to-device copy of COPY_CALIB_BYTES, three times: the reference dispatch that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    a = torch.randn(COPY_CALIB_BYTES // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_CALIB_BYTES} bytes x 3", flush=True)
+
+
+def _short_kernel(name: str):
+    if "copyBuffer" in name:
+        return "copy"
+    m = re.search(r"(\w+)_kernel", name)
+    return m.group(1) if m and "dsv4" in name else None
+
+
+def _csv_rows(directory: str, pattern: str):
+    for f in sorted(glob.glob(os.path.join(directory, "**", pattern), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _grid(r: dict) -> str:
+    g = [r[k] for k in ("Grid_Size", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z") if k in r]
+    return "x".join(g) if g else "?"
+
+
+def _pmc(directory: str, counter: str):
+    """{(kernel, grid): {dispatch: value}} of one rocprofv3 --pmc pass."""
+    out = defaultdict(lambda: defaultdict(float))
+    for r in _csv_rows(directory, "*counter_collection.csv"):
+        k = _short_kernel(r["Kernel_Name"])
+        if k is None or r["Counter_Name"] != counter:
+            continue
+        out[(k, _grid(r))][r.get("Dispatch_Id", r.get("Correlation_Id"))] += float(r["Counter_Value"])
+    return out
+
+
+def _main_group(groups: dict, kernel: str):
+    """The (grid, values) of `kernel` with the most dispatches (the timed launches)."""
+    cand = [(len(v), g, list(v.values())) for (k, g), v in groups.items() if k == kernel]
+    if not cand:
+        raise SystemExit(f"no dispatches of {kernel}")
+    n, g, vals = max(cand)
+    return g, vals
+
+
+def write_traffic_profile(a):
+    cf = _main_group(_pmc(a.calib_fetch, "FETCH_SIZE"), "copy")[1]
+    cw = _main_group(_pmc(a.calib_write, "WRITE_SIZE"), "copy")[1]
+    ff = COPY_CALIB_BYTES / (np.mean(cf) * 1024.0)
+    wf = COPY_CALIB_BYTES / (np.mean(cw) * 1024.0)
+    g, fv = _main_group(_pmc(a.fetch, "FETCH_SIZE"), a.kernel)
+    gw, wv = _main_group(_pmc(a.write, "WRITE_SIZE"), a.kernel)
+    traffic = np.mean(fv) * 1024.0 * ff + np.mean(wv) * 1024.0 * wf
+    with open(a.out, "w") as f:
+        f.write(f"# HBM traffic of {a.kernel}: {a.title}\n")
+        f.write("# commands (run on the MI355X box from the repository root; each --pmc pass its own run):\n")
+        for c in a.command:
+            f.write(f"#   {c}\n")
+        f.write("# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, summed over the counter's instances;\n"
+                "# each is scaled by the ratio of known bytes to the counter's reading on the copy.\n")
+        f.write(f"kernel: {a.kernel}\n")
+        f.write(f"source_digest: {kernel_source_digest(a.kernel)}\n")
+        f.write(f"grid: {g}\n")
+        f.write(f"dispatches: {len(fv)} fetch, {len(wv)} write\n")
+        f.write(f"fetch_kib_per_dispatch: {np.mean(fv):.1f}\n")
+        f.write(f"write_kib_per_dispatch: {np.mean(wv):.1f}\n")
+        f.write(f"copy_calibration: {COPY_CALIB_BYTES} bytes read and written; FETCH_SIZE {np.mean(cf):.1f} KiB, "
+                f"WRITE_SIZE {np.mean(cw):.1f} KiB -> scale {ff:.4f} (fetch), {wf:.4f} (write)\n")
+        f.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
+    print(open(a.out).read())
+
+
+def traffic_from_profile(path: str, kernel: str):
+    """Bytes per launch from a committed traffic summary, or None when it is absent or was
+    measured on other sources of the kernel."""
+    try:
+        kv = dict(l.split(": ", 1) for l in open(path).read().splitlines() if not l.startswith("#") and ": " in l)
+    except OSError:
+        return None
+    if kv.get("kernel") != kernel or kv.get("source_digest") != kernel_source_digest(kernel):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def write_kernel_profile(a):
+    groups = defaultdict(list)
+    for r in _csv_rows(a.trace_dir, "*kernel_trace.csv"):
+        k = _short_kernel(r["Kernel_Name"])
+        if k is None or k == "copy":
+            continue
+        groups[(k, _grid(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    with open(a.out, "w") as f:
+        f.write(f"# rocprofv3 kernel summary: {a.title}\n")
+        f.write("# commands (run on the MI355X box from the repository root):\n")
+        for c in a.command:
+            f.write(f"#   {c}\n")
+        f.write("# per (kernel, grid) from kernel_trace.csv of that run; library kernels only (the input\n"
+                "# generation and copies of the setup are omitted).  The grid with the most launches is the\n"
+                "# timed one; others come from building the prefix cache once per run.\n#\n")
+        f.write(f"# {'kernel':<20s} {'grid':<22s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_us':>12s}\n")
+        for (k, g), v in sorted(groups.items(), key=lambda x: -sum(x[1])):
+            f.write(f"  {k:<20s} {g:<22s} {len(v):6d} {np.mean(v):10.2f} {min(v):10.2f} {max(v):10.2f} {sum(v):12.1f}\n")
+    print(open(a.out).read())
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] in ("--write-traffic-profile", "--write-kernel-profile"):
+        mode = sys.argv[1]
+        pp = argparse.ArgumentParser(prog=f"bench.py {mode}")
+        pp.add_argument("--out", required=True)
+        pp.add_argument("--title", required=True)
+        pp.add_argument("--command", action="append", default=[])
+        pp.add_argument("--kernel")
+        pp.add_argument("--fetch")
+        pp.add_argument("--write")
+        pp.add_argument("--calib-fetch")
+        pp.add_argument("--calib-write")
+        pp.add_argument("--trace-dir")
+        a = pp.parse_args(sys.argv[2:])
+        (write_traffic_profile if mode == "--write-traffic-profile" else write_kernel_profile)(a)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
+        copy_calibration()
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)

@@ -192,8 +192,9 @@ int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* k
                           const float* sinks, void* out, int32_t batch, int64_t s, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* Kernel timing for measurement.  While enabled, every kernel the library launches is
- * bracketed by HIP events recorded on its launch stream.  dsv4_trace_read() waits for the
+/* Kernel timing for measurement.  While enabled, every kernel the library launches carries
+ * a start/stop HIP event pair attached to its own dispatch (hipExtLaunchKernelGGL), so each
+ * record is that kernel's execution time on its launch stream.  dsv4_trace_read() waits for the
  * recorded events and returns, for the kernels whose name contains `name_substr` (all when
  * NULL or ""), the launch count and the summed GPU duration in milliseconds.  Tracing
  * creates HIP events (it is the one facility that allocates); leave it off in production. */

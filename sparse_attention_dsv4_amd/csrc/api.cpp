@@ -112,27 +112,22 @@ hipEvent_t take_event() {
 
 namespace dsv4 {
 
-void trace_begin(const char* name, hipStream_t s) {
-    if (!g_trace_on.load(std::memory_order_relaxed)) return;
+bool trace_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_trace_on.load(std::memory_order_relaxed)) return false;
     std::lock_guard<std::mutex> lk(g_trace_mu);
-    TraceRec r{name, take_event(), nullptr};
-    if (r.start) hipEventRecord(r.start, s);
-    g_recs.push_back(r);
-}
-
-void trace_end(const char* name, hipStream_t s) {
-    if (!g_trace_on.load(std::memory_order_relaxed)) return;
-    std::lock_guard<std::mutex> lk(g_trace_mu);
-    for (auto it = g_recs.rbegin(); it != g_recs.rend(); ++it) {
-        if (it->stop == nullptr && std::strcmp(it->name, name) == 0) {
-            it->stop = take_event();
-            if (it->stop) hipEventRecord(it->stop, s);
-            break;
-        }
+    TraceRec r{name, take_event(), take_event()};
+    if (!r.start || !r.stop) {                 // no events: launch untraced, keep the pool
+        if (r.start) g_event_pool.push_back(r.start);
+        if (r.stop) g_event_pool.push_back(r.stop);
+        return false;
     }
+    g_recs.push_back(r);
     bool known = false;
     for (auto& n : g_trace_names) known |= (n == name);
     if (!known) g_trace_names.emplace_back(name);
+    *start = r.start;
+    *stop = r.stop;
+    return true;
 }
 
 }  // namespace dsv4

@@ -182,17 +182,13 @@ hipError_t run(const AttnJob& j, hipStream_t st) {
         a.S = j.S;
         a.nk_cap = int(nrow_max + j.W);
         const size_t lds = size_t(j.D) * 4 + size_t(a.nk_cap) * 8;
-        trace_begin("attn_generic", st);
-        hipLaunchKernelGGL(attn_generic_kernel<T>, dim3(unsigned(j.S), unsigned(j.H), nb),
+        DSV4_LAUNCH("attn_generic", attn_generic_kernel<T>, dim3(unsigned(j.S), unsigned(j.H), nb),
                            dim3(kAttnThreads), lds, st, a, pos, nr);
-        trace_end("attn_generic", st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t nupd = std::min<int64_t>(j.S, j.W);
-        trace_begin("ring_update", st);
-        hipLaunchKernelGGL(ring_update_kernel<T>, dim3(unsigned(nupd), nb), dim3(kAttnThreads), 0,
+        DSV4_LAUNCH("ring_update", ring_update_kernel<T>, dim3(unsigned(nupd), nb), dim3(kAttnThreads), 0,
                            st, a, pos);
-        trace_end("ring_update", st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -848,22 +844,16 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         a.part_o = ws + size_t(nb) * j.S * a.n_splits * MH * 2;
         hipError_t e;
         if (decode) {
-            trace_begin("attn_decode", st);
-            hipLaunchKernelGGL(attn_decode_kernel, dim3(unsigned(a.n_splits), MH / DHG, nb), dim3(256),
+            DSV4_LAUNCH("attn_decode", attn_decode_kernel, dim3(unsigned(a.n_splits), MH / DHG, nb), dim3(256),
                                0, st, a, pos, nr);
-            trace_end("attn_decode", st);
         } else {
-            trace_begin("attn_mfma", st);
-            hipLaunchKernelGGL(attn_mfma_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(256),
+            DSV4_LAUNCH("attn_mfma", attn_mfma_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(256),
                                0, st, a, pos, nr);
-            trace_end("attn_mfma", st);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.n_splits > 1) {
-            trace_begin("attn_combine", st);
-            hipLaunchKernelGGL(attn_combine_kernel, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
-            trace_end("attn_combine", st);
+            DSV4_LAUNCH("attn_combine", attn_combine_kernel, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -873,9 +863,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         ra.kv_new = a.kv_new;
         ra.ring = static_cast<bf16*>(j.ring) + size_t(b0) * j.W * MD;
         const int64_t nupd = std::min<int64_t>(j.S, j.W);
-        trace_begin("ring_update", st);
-        hipLaunchKernelGGL(ring_update_kernel<bf16>, dim3(unsigned(nupd), nb), dim3(256), 0, st, ra, pos);
-        trace_end("ring_update", st);
+        DSV4_LAUNCH("ring_update", ring_update_kernel<bf16>, dim3(unsigned(nupd), nb), dim3(256), 0, st, ra, pos);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

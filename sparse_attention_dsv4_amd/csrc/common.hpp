@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 #include <string>
@@ -80,8 +81,19 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // ------------------------------------------------------------------ launch bookkeeping
-// Every launch goes through these so that the optional kernel trace can bracket it.
-void trace_begin(const char* name, hipStream_t s);
-void trace_end(const char* name, hipStream_t s);
+// Kernel trace: while it is on, trace_events hands out a start/stop event pair for the next
+// launch of `name` and returns true.  DSV4_LAUNCH attaches the pair to the dispatch itself
+// (hipExtLaunchKernelGGL), so the recorded time is the kernel's own duration, without the
+// queue gaps that events recorded around the launch would add.
+bool trace_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+#define DSV4_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                              \
+    do {                                                                                         \
+        hipEvent_t ev0_, ev1_;                                                                   \
+        if (::dsv4::trace_events(name, &ev0_, &ev1_))                                           \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev0_, ev1_, 0, __VA_ARGS__); \
+        else                                                                                     \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                 \
+    } while (0)
 
 }  // namespace dsv4

@@ -200,10 +200,8 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
             a.row_cap = j.row_cap;
             a.n_new = 1;
             for (int i = 0; i < nb; ++i) lb.v[i] = int32_t(j.len_before[b0 + i]);
-            trace_begin("compress_step", s);
-            hipLaunchKernelGGL(compress_step_kernel<T>, dim3(nb), dim3(kStepThreads),
+            DSV4_LAUNCH("compress_step", compress_step_kernel<T>, dim3(nb), dim3(kStepThreads),
                                j.D * sizeof(float), s, a, lb);
-            trace_end("compress_step", s);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             continue;
@@ -229,18 +227,14 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
         a.row_cap = j.row_cap;
         a.n_new = j.n_new;
         if (max_rows > 0) {
-            trace_begin("compress_rows", s);
-            hipLaunchKernelGGL(compress_rows_kernel<T>, dim3(unsigned(max_rows), nb),
+            DSV4_LAUNCH("compress_rows", compress_rows_kernel<T>, dim3(unsigned(max_rows), nb),
                                dim3(kCompThreads), j.D * sizeof(float), s, a, lb);
-            trace_end("compress_rows", s);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         if (max_keep > 0) {
-            trace_begin("compress_state", s);
-            hipLaunchKernelGGL(compress_state_kernel<T>, dim3(unsigned(max_keep), nb),
+            DSV4_LAUNCH("compress_state", compress_state_kernel<T>, dim3(unsigned(max_keep), nb),
                                dim3(kCompThreads), 0, s, a, lb);
-            trace_end("compress_state", s);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -604,14 +604,12 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             if (blocks < 1) blocks = 1;
             a.rows_per_block = int(((tiles + blocks - 1) / blocks) * IRT);
             const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
-            trace_begin("index_score_mfma", st);
             if (perq)
-                hipLaunchKernelGGL((index_score_mfma_kernel<kIdxQpw, kIdxWaves, kIdxStages>),
-                                   dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
+                DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<kIdxQpw, kIdxWaves, kIdxStages>),
+                            dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
             else
-                hipLaunchKernelGGL((index_score_mfma_kernel<0, 4, kIdxStages>), dim3(gx, unsigned(groups), nb),
-                                   dim3(256), 0, st, a, pos, nr);
-            trace_end("index_score_mfma", st);
+                DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<0, 4, kIdxStages>),
+                            dim3(gx, unsigned(groups), nb), dim3(256), 0, st, a, pos, nr);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         } else if (nv_max > j.k) {
@@ -627,10 +625,8 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             a.keys = j.keys + qoff * j.n_stride;
             const unsigned gx = unsigned((nv_max + kScoreRows - 1) / kScoreRows);
             const size_t lds = size_t(j.Hi) * j.di * sizeof(float) + j.Hi * sizeof(float);
-            trace_begin("index_score", st);
-            hipLaunchKernelGGL(index_score_kernel<T>, dim3(gx, unsigned(j.S), nb),
+            DSV4_LAUNCH("index_score", index_score_kernel<T>, dim3(gx, unsigned(j.S), nb),
                                dim3(kScoreThreads), lds, st, a, pos, nr);
-            trace_end("index_score", st);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -639,20 +635,14 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
         if (nv_max <= int64_t(kSelRegThreads) * 32) {
-            trace_begin("topk_select_reg", st);
-            hipLaunchKernelGGL(topk_select_reg_kernel<32>, dim3(unsigned(j.S), nb),
+            DSV4_LAUNCH("topk_select_reg", topk_select_reg_kernel<32>, dim3(unsigned(j.S), nb),
                                dim3(kSelRegThreads), 0, st, sa, pos, nr);
-            trace_end("topk_select_reg", st);
         } else if (nv_max <= int64_t(kSelRegThreads) * 64) {
-            trace_begin("topk_select_reg", st);
-            hipLaunchKernelGGL(topk_select_reg_kernel<64>, dim3(unsigned(j.S), nb),
+            DSV4_LAUNCH("topk_select_reg", topk_select_reg_kernel<64>, dim3(unsigned(j.S), nb),
                                dim3(kSelRegThreads), 0, st, sa, pos, nr);
-            trace_end("topk_select_reg", st);
         } else {
-            trace_begin("topk_select", st);
-            hipLaunchKernelGGL(topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
+            DSV4_LAUNCH("topk_select", topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
                                st, sa, pos, nr);
-            trace_end("topk_select", st);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
