@@ -297,17 +297,21 @@ __device__ __forceinline__ const bf16* key_src(const TileCtx& c, const int32_t* 
     return c.ring + size_t(slot) * MD;
 }
 
-// Enqueue the direct-to-LDS copy of keys [tb, tb + nkt) (one 1 KB row per wave instruction)
-// and zero the unused rows of a partial tile.  Wave w copies rows w, w + 4, ..: lane l < 16
-// finds the source of row w + 4 l once, and the copies read it back as a scalar.
-__device__ __forceinline__ void load_tile(const TileCtx& c, const int32_t* codes, unsigned char* buf,
-                                          int tb, int nkt) {
+// Copy of keys [tb, tb + nkt) into an LDS tile (one 1 KB row per wave instruction), in two
+// steps so the copies can be spread between other work: tile_rows finds, in lane l < 16 of
+// wave w, the source of row w + 4 l; tile_copy<I0, I1> issues rows w + 4 i for i in [I0, I1)
+// (reading each source back as a scalar) and zero-fills the rows past nkt.
+__device__ __forceinline__ uint64_t tile_rows(const TileCtx& c, const int32_t* codes, int tb, int nkt) {
     const int kk_l = c.w + 4 * (c.lane & 15);
     const bf16* mine = kk_l < nkt ? key_src(c, codes, tb + kk_l) : c.ring;
-    const uint64_t mp = reinterpret_cast<uint64_t>(mine);
-    const uint32_t plo = uint32_t(mp), phi = uint32_t(mp >> 32);
+    return reinterpret_cast<uint64_t>(mine);
+}
+
+template <int I0, int I1>
+__device__ __forceinline__ void tile_copy(const TileCtx& c, uint64_t src, unsigned char* buf, int nkt) {
+    const uint32_t plo = uint32_t(src), phi = uint32_t(src >> 32);
 #pragma unroll
-    for (int i = 0; i < MKT / 4; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const int kk = c.w + 4 * i;
         if (kk < nkt) {
             const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(plo), i))) |
@@ -319,21 +323,47 @@ __device__ __forceinline__ void load_tile(const TileCtx& c, const int32_t* codes
     }
 }
 
+__device__ __forceinline__ void load_tile(const TileCtx& c, const int32_t* codes, unsigned char* buf,
+                                          int tb, int nkt) {
+    tile_copy<0, MKT / 4>(c, tile_rows(c, codes, tb, nkt), buf, nkt);
+}
+
+// The next tile's copy, handed to attend_tile so it can issue it in parts between MFMA groups
+// (a wave issuing all 16 copies at once stalls on the CU's load pipe and computes nothing).
+struct NextTile {
+    bool on;
+    uint64_t src;
+    unsigned char* buf;
+    int nkt;
+};
+
+// The selection row as this thread's entries e = 256 r + tid (-1 past k; k <= MAX_CODES).
+constexpr int SEL_PER_THREAD = MAX_CODES / 256;
+__device__ __forceinline__ void load_selection(const int32_t* sr, int k, int32_t (&selv)[SEL_PER_THREAD]) {
+#pragma unroll
+    for (int r = 0; r < SEL_PER_THREAD; ++r) {
+        const int e = 256 * r + int(threadIdx.x);
+        selv[r] = e < k ? sr[e] : -1;
+    }
+}
+
 // Compact the valid entries (0 <= j < nv) of one selection row, keeping their order: the
 // entry of rank n goes to codes[n - kb] when kb <= n < kb + kps.  Returns the count of valid
-// entries.  Ranks come from wave ballots; wsum holds 2 x 4 per-wave counts.
-__device__ __forceinline__ int compact_selection(const int32_t* sr, int k, int nv, int kb, int kps,
-                                                 int32_t* codes, int* wsum) {
+// entries.  Ranks come from wave ballots; wsum holds 2 x 4 per-wave counts.  The barriers
+// wait for LDS only, so global loads issued before (q fragments) stay in flight.
+__device__ __forceinline__ int compact_selection(const int32_t (&selv)[SEL_PER_THREAD], int k, int nv,
+                                                 int kb, int kps, int32_t* codes, int* wsum) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int base = 0;
-    for (int r0 = 0; r0 < k; r0 += 256) {
-        const int e = r0 + tid;
-        const int32_t j = e < k ? sr[e] : -1;
+#pragma unroll
+    for (int r = 0; r < SEL_PER_THREAD; ++r) {
+        if (256 * r >= k) break;
+        const int32_t j = selv[r];
         const bool ok = j >= 0 && j < nv;
         const uint64_t m = __ballot(ok);
-        int* ws = wsum + ((r0 >> 8) & 1) * 4;
+        int* ws = wsum + (r & 1) * 4;
         if (lane == 0) ws[w] = __popcll(m);
-        __syncthreads();
+        lds_barrier();
         int off = base;
         for (int v = 0; v < w; ++v) off += ws[v];
         if (ok) {
@@ -342,7 +372,7 @@ __device__ __forceinline__ int compact_selection(const int32_t* sr, int k, int n
         }
         base += (ws[0] + ws[1]) + (ws[2] + ws[3]);
     }
-    __syncthreads();
+    lds_barrier();
     return base;
 }
 
@@ -351,6 +381,8 @@ __device__ __forceinline__ int compact_selection(const int32_t* sr, int k, int n
 // Every exponent stays <= 2^kLazy, far inside fp32 and bf16 range, and the final division
 // uses the same reference, so the result is unchanged.
 constexpr float kLazy = 8.0f;
+constexpr int SXBYTES = 4 * 64 * 16 * 4;  // S^T partials: 4 waves x 64 lanes x 16 fp32
+
 
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
     return make_uint2(uint32_t(bf16_bits(a)) | (uint32_t(bf16_bits(b)) << 16),
@@ -362,15 +394,49 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx& c,
                                             const unsigned char* buf, unsigned char* ptile,
                                             float (*xch)[2][MH], const bf16x8* qa, floatx16* o,
-                                            float& m_run, float& l_run, int nkt) {
+                                            float& m_run, float& l_run, int nkt, const NextTile& nx) {
     const int mt = c.mt, nt = c.nt, lane = c.lane, l32 = c.l32, hi = c.hi;
     const int head = 32 * mt + l32;
-    floatx16 st;
+    // S^T partials over this wave's 256 dims (dim half nt) for both 32-key halves; the key
+    // half nt^1 goes to the partner wave (same heads, other dims) through LDS, so each wave
+    // ends with the full S^T of key half nt.  sx aliases the P tile (free until P is written).
+    floatx16 sp[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = 0.f;
-    const unsigned char* kr = buf + (32 * nt + l32) * KPITCH + 16 * hi;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int ks = 0; ks < MD / 16; ++ks) st = mfma32x32x16(load_bf16x8(kr + ks * 32), qa[ks], st);
+        for (int i = 0; i < 16; ++i) sp[u][i] = 0.f;
+    if (nx.on) tile_copy<0, 4>(c, nx.src, nx.buf, nx.nkt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const unsigned char* kr = buf + (32 * kb + l32) * KPITCH + 512 * nt + 16 * hi;
+#pragma unroll
+        for (int ks = 0; ks < MD / 32; ++ks) sp[kb] = mfma32x32x16(load_bf16x8(kr + ks * 32), qa[ks], sp[kb]);
+        if (nx.on) {
+            if (kb == 0) tile_copy<4, 8>(c, nx.src, nx.buf, nx.nkt);
+            else tile_copy<8, 12>(c, nx.src, nx.buf, nx.nkt);
+        }
+    }
+    float* sx = reinterpret_cast<float*>(ptile);
+    {
+        const floatx16& give = nt ? sp[0] : sp[1];
+        float* dst = sx + ((2 * mt + (nt ^ 1)) * 64 + lane) * 16;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4*>(dst + 4 * q4) = make_float4(give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]);
+    }
+    lds_barrier();
+    floatx16 st = nt ? sp[1] : sp[0];
+    {
+        const float* src = sx + ((2 * mt + nt) * 64 + lane) * 16;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = *reinterpret_cast<const float4*>(src + 4 * q4);
+            st[4 * q4] += v.x;
+            st[4 * q4 + 1] += v.y;
+            st[4 * q4 + 2] += v.z;
+            st[4 * q4 + 3] += v.w;
+        }
+    }
     float sv[16];
     float lmax = -INFINITY;
 #pragma unroll
@@ -414,6 +480,7 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
                                (256 * nt + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
 #pragma unroll
     for (int ks = 0; ks < MKT / 16; ++ks) {
+        if (ks == 2 && nx.on) tile_copy<12, 16>(c, nx.src, nx.buf, nx.nkt);
         const bf16x8 pb = load_bf16x8(pr + ks * 32);
 #pragma unroll
         for (int n8 = 0; n8 < 8; ++n8) {
@@ -431,7 +498,8 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
 __global__ void __launch_bounds__(256)
 attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char ptile[MH * PPITCH];
+    // P tile; before P is written it holds the S^T partials exchanged between the dim halves
+    __shared__ __attribute__((aligned(16))) unsigned char ptile[SXBYTES > MH * PPITCH ? SXBYTES : MH * PPITCH];
     __shared__ float xch[2][2][MH];       // [max | sum][key half][head]
     __shared__ int32_t codes[MAX_CODES];
     __shared__ int wsum[8];
@@ -444,7 +512,7 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     c.lane = tid & 63;
     c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     c.mt = c.w >> 1;                      // head half
-    c.nt = c.w & 1;                       // key half in Q.K^T, dim half in P.V
+    c.nt = c.w & 1;                       // dim half in Q.K^T and P.V; key half of the softmax
     c.l32 = c.lane & 31;
     c.hi = c.lane >> 5;
     const int b = c.b;
@@ -461,9 +529,18 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     key_ctx(c, a, b, t0, pos0);
     c.kb = split * a.keys_per_split;
     c.nrow = nv;
+    // issue order: selection entries, then this wave's 32 heads of q (MFMA A fragments over
+    // all 512 dims), so the compaction waits for the former only and the q loads overlap it
+    int32_t selv[SEL_PER_THREAD];
+    if (a.sel != nullptr) load_selection(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, selv);
+    bf16x8 qa[MD / 32];                   // heads 32 mt .. +31, dims 256 nt .. +255
+    {
+        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + 32 * c.mt + c.l32) * MD + 256 * c.nt + 8 * c.hi;
+#pragma unroll
+        for (int ks = 0; ks < MD / 32; ++ks) qa[ks] = load_bf16x8(qh + ks * 16);
+    }
     if (a.sel != nullptr)
-        c.nrow = compact_selection(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, nv, c.kb,
-                                   a.keys_per_split, codes, wsum);
+        c.nrow = compact_selection(selv, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
     const int nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
     if (c.kb >= nk) {                                 // nothing in this split
@@ -481,13 +558,6 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     };
 
     load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
-    // this wave's 32 heads of q, as MFMA A fragments over all 512 dims
-    bf16x8 qa[MD / 16];
-    {
-        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + 32 * c.mt + c.l32) * MD + 8 * c.hi;
-#pragma unroll
-        for (int ks = 0; ks < MD / 16; ++ks) qa[ks] = load_bf16x8(qh + ks * 16);
-    }
     floatx16 o[8];
 #pragma unroll
     for (int n8 = 0; n8 < 8; ++n8)
@@ -498,8 +568,12 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(c, codes, kbuf[(t + 1) & 1], c.kb + (t + 1) * MKT, tile_keys(t + 1));
-        attend_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t));
+        NextTile nx;
+        nx.on = t + 1 < ntiles;
+        nx.nkt = nx.on ? tile_keys(t + 1) : 0;
+        nx.src = nx.on ? tile_rows(c, codes, c.kb + (t + 1) * MKT, nx.nkt) : 0;
+        nx.buf = kbuf[(t + 1) & 1];
+        attend_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t), nx);
         wait_vm();                        // the next tile has landed
         __syncthreads();                  // ... for every wave; and all are done with this one
     }
@@ -601,8 +675,11 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     key_ctx(c, a, b, t0, p);
     c.kb = split * a.keys_per_split;
     c.nrow = nv;
-    if (a.sel != nullptr)
-        c.nrow = compact_selection(a.sel + size_t(b) * a.k, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
+    if (a.sel != nullptr) {
+        int32_t selv[SEL_PER_THREAD];
+        load_selection(a.sel + size_t(b) * a.k, a.k, selv);
+        c.nrow = compact_selection(selv, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
+    }
     const int nk = c.nrow + nwin;
     const size_t pbase = (size_t(b) * a.n_splits + split) * MH + DHG * hg;
     if (split == 0 && hg == 0) {

@@ -90,6 +90,13 @@ def test_tiny_fp32_decode_equals_prefill():
     _check_layer(TINY, dec, 0, list(range(192, 256)), 0, end_to_end=True)
 
 
+def test_tiny_fp32_config_prefill_256_then_64_decode():
+    """The tiny fp32 configuration as stated: prefill of 256 tokens, then 64 decode steps;
+    every position against the oracle from the raw inputs."""
+    res = G.run_gpu(TINY, 0, 1, [256], 64)
+    _check_layer(TINY, res, 0, list(range(320)), 0, end_to_end=True)
+
+
 def test_tiny_fp32_dense_to_sparse_crossing():
     """The indexer engages once a query sees more than k = 8 rows (p >= 35 at ratio 4)."""
     res = G.run_gpu(TINY, 1, 1, [30], 20)
