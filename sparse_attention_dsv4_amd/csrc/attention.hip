@@ -17,9 +17,10 @@
 // 64 heads sharing every 64-key tile staged in LDS.  Q*K^T and P*V run on
 // v_mfma_f32_32x32x16_bf16; the softmax is online in base 2 with fp32 running max and sum;
 // P is rounded to bf16 before P*V (the pages' reference kernel does the same, MTPLX PR #216
-// "Decode path").  A query whose key list is split over several workgroups (decode) writes
-// fp32 partials (max, sum, unnormalised output) that attn_combine_kernel merges with the
-// sink; a query handled by one workgroup (prefill) normalises and writes its output.
+// "Decode path").  A query whose key list is split over several workgroups writes partials
+// (fp32 max and sum; the unnormalised output in bf16 for decode, fp32 for prefill) that
+// attn_combine_kernel merges with the sink; a query handled by one workgroup normalises and
+// writes its output.
 //
 // The ring update runs after the attention kernel on the stream: writing token t evicts
 // token t - W, which an earlier query of the same call may still need.
@@ -233,8 +234,6 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const un
                  :: "s"(la), "v"(voff), "s"(sb) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// all but this wave's 16 most recent copies (one full tile) have landed
-__device__ __forceinline__ void wait_vm_tile() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
 struct AttnMfmaArgs {
     const bf16* q;
@@ -385,9 +384,12 @@ constexpr int SXBYTES = 4 * 64 * 16 * 4;  // S^T partials: 4 waves x 64 lanes x 
 
 
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-    return make_uint2(uint32_t(bf16_bits(a)) | (uint32_t(bf16_bits(b)) << 16),
-                      uint32_t(bf16_bits(c)) | (uint32_t(bf16_bits(d)) << 16));
+    return make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
 }
+
+// 2^x on v_exp_f32 alone: the softmax arguments are <= kLazy and results below 2^-126 only
+// lose weights that are far below bf16 resolution of the sum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One key tile.  Wave (mt, nt): S^T = K Q^T for keys 32nt.. x heads 32mt.., so lane l owns
 // head 32mt + l%32 and 16 keys; O^T += V^T P^T for dims 256nt.. x the same heads.
@@ -409,8 +411,23 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const unsigned char* kr = buf + (32 * kb + l32) * KPITCH + 512 * nt + 16 * hi;
+        // K operands in blocks of 4 k-steps, the next block issued before this one's MFMAs;
+        // the scheduling barriers keep each read from being paired with (and waited on right
+        // before) its MFMA
+        bf16x8 kx[2][4];
 #pragma unroll
-        for (int ks = 0; ks < MD / 32; ++ks) sp[kb] = mfma32x32x16(load_bf16x8(kr + ks * 32), qa[ks], sp[kb]);
+        for (int i = 0; i < 4; ++i) kx[0][i] = load_bf16x8(kr + i * 32);
+#pragma unroll
+        for (int blk = 0; blk < MD / 128; ++blk) {
+            if (blk + 1 < MD / 128) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kx[(blk + 1) & 1][i] = load_bf16x8(kr + (4 * (blk + 1) + i) * 32);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp[kb] = mfma32x32x16(kx[blk & 1][i], qa[4 * blk + i], sp[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (nx.on) {
             if (kb == 0) tile_copy<4, 8>(c, nx.src, nx.buf, nx.nkt);
             else tile_copy<8, 12>(c, nx.src, nx.buf, nx.nkt);
@@ -466,7 +483,7 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
         float p4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p4[r] = exp2f(sv[4 * q4 + r] - m_run);
+            p4[r] = fast_exp2(sv[4 * q4 + r] - m_run);
             psum += p4[r];
         }
         *reinterpret_cast<uint2*>(prow + 16 * q4) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
@@ -633,10 +650,18 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
 
 // ------------------------------------------------------------------ decode path
 // One query per sequence: workgroups per (sequence, 16-head group, key split), so the
-// partials a split writes are 16 heads x 512 fp32 and enough workgroups run at once.
-// v_mfma_f32_16x16x32_bf16: each wave scores 16 keys of every 64-key tile for the group's
-// 16 heads (S^T = K Q^T, lane l owns head l%16) and accumulates 128 dims of O^T = V^T P^T.
+// partials a split writes are 16 heads x 512 fp32 and enough workgroups run at once.  A
+// split's keys (up to DKC of them; longer splits run in chunks) sit in LDS together, so the
+// softmax of a chunk is taken once, after all of its scores are known:
+//   * wave w copies and scores the 16-key subtiles u = w, w + 4 (S^T = K Q^T on
+//     v_mfma_f32_16x16x32_bf16, lane l owns head l%16), waiting only for its own copies;
+//   * the scores meet in LDS (one barrier), every wave takes the same max, exponentials and
+//     bf16 P of the whole chunk;
+//   * wave w accumulates dims 128 w .. 128 w + 127 of O^T = V^T P^T over every key, so no
+//     partial output is merged inside the workgroup.
 constexpr int DHG = 16;                   // heads per decode workgroup
+constexpr int DKC = 128;                  // keys of one decode chunk (8 subtiles of 16)
+constexpr int SXP = DKC + 4;              // floats per head row of the exchanged scores
 constexpr int QPITCH = MD * 2 + 16;       // LDS row of a staged q (offset rows: no bank conflicts)
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -644,13 +669,93 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+}
+
+// Softmax and P*V of one decode chunk of NKS 32-key steps.  Lane (l%16, g) takes keys
+// 32 ks + 8 g + e of head l%16 from the exchanged scores, the layout of the P^T operand, so
+// every wave computes the same max, exponentials and bf16 P; wave w then accumulates dims
+// 128 w .. 128 w + 127 of O^T = V^T P^T (8 tiles of 16 dims per k-step).
+template <int NKS>
+__device__ __forceinline__ void decode_chunk_pv(const float* sx, const unsigned char* kbuf, int l16, int g, int w,
+                                                int nkt, bool first, float& m_run, float& l_run,
+                                                floatx4 (&o)[8]) {
+    float sv[NKS][8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const float* sr = sx + l16 * SXP + 32 * ks + 8 * g;
+        const float4 x0 = *reinterpret_cast<const float4*>(sr);
+        const float4 x1 = *reinterpret_cast<const float4*>(sr + 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sv[ks][e] = 32 * ks + 8 * g + e < nkt ? xs[e] : -INFINITY;
+            cmax = fmaxf(cmax, sv[ks][e]);
+        }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    if (first) {
+        m_run = cmax;                         // o and l_run are still zero
+    } else if (cmax > m_run + kLazy) {
+        const float alpha = fast_exp2(m_run - cmax);
+        m_run = cmax;
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[m][i] *= alpha;
+    }
+    bf16x8 pb[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pe[e] = fast_exp2(sv[ks][e] - m_run);
+            l_run += pe[e];
+        }
+        const uint4 pk = make_uint4(pack2_bf16(pe[0], pe[1]), pack2_bf16(pe[2], pe[3]),
+                                    pack2_bf16(pe[4], pe[5]), pack2_bf16(pe[6], pe[7]));
+        __builtin_memcpy(&pb[ks], &pk, 16);
+    }
+    // V^T operands of one k-step go out as a block; the next block is issued before this
+    // step's MFMAs, and the scheduling barriers keep the compiler from pairing every read
+    // with its MFMA (which would expose the full LDS latency per MFMA)
+    const unsigned char* vb0 = kbuf + (8 * g + (l16 >> 2)) * KPITCH + (128 * w + 4 * (l16 & 3)) * 2;
+    bf16x8 va[2][8];
+    auto load_v = [&](int ks, bf16x8 (&dst)[8]) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const unsigned char* vp = vb0 + 32 * ks * KPITCH + m * 32;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
+            __builtin_memcpy(&dst[m], &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&dst[m]) + 8, &up, 8);
+        }
+    };
+    load_v(0, va[0]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) load_v(ks + 1, va[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] = mfma16x16x32(va[ks & 1][m], pb[ks], o[m]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 __global__ void __launch_bounds__(256)
 attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
-    __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KBUF];
-    __shared__ __attribute__((aligned(16))) unsigned char ptile[DHG * PPITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char kbuf[DKC * KPITCH];
     __shared__ __attribute__((aligned(16))) unsigned char qs[DHG * QPITCH];
-    __shared__ float xch[2][4][DHG];      // [max | sum][wave][head]
-    __shared__ int32_t codes[MAX_CODES];
+    __shared__ __attribute__((aligned(16))) float sx[DHG * SXP];   // scaled scores [head][key]
+    __shared__ int32_t codes[DKC];
     __shared__ int wsum[8];
 
     TileCtx c;
@@ -673,12 +778,14 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int t0 = p - a.W + 1 > 0 ? p - a.W + 1 : 0;
     const int nwin = p - t0 + 1;
     key_ctx(c, a, b, t0, p);
-    c.kb = split * a.keys_per_split;
+    const int kb0 = split * a.keys_per_split;
+    c.kb = kb0;
     c.nrow = nv;
+    int32_t selv[SEL_PER_THREAD];
     if (a.sel != nullptr) {
-        int32_t selv[SEL_PER_THREAD];
         load_selection(a.sel + size_t(b) * a.k, a.k, selv);
-        c.nrow = compact_selection(selv, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
+        c.nrow = compact_selection(selv, a.k, nv, kb0, a.keys_per_split < DKC ? a.keys_per_split : DKC,
+                                   codes, wsum);
     }
     const int nk = c.nrow + nwin;
     const size_t pbase = (size_t(b) * a.n_splits + split) * MH + DHG * hg;
@@ -690,114 +797,109 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(c.ring) + size_t(uint32_t(p) % c.W) * MD);
         if (tid < MD / 8) dst[tid] = src[tid];
     }
-    if (c.kb >= nk) {
+    if (kb0 >= nk) {
         if (tid < DHG) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
             a.part_ml[(pbase + tid) * 2 + 1] = 0.f;
         }
         return;
     }
-    const int ke = c.kb + a.keys_per_split < nk ? c.kb + a.keys_per_split : nk;
-    const int ntiles = (ke - c.kb + MKT - 1) / MKT;
-    auto tile_keys = [&](int t) -> int {
-        const int left = ke - (c.kb + t * MKT);
-        return left < MKT ? left : MKT;
-    };
-    // copies in flight: the group's q rows, tile 0, tile 1
-    {
-        const bf16* qg = a.q + (size_t(b) * MH + DHG * hg) * MD;
-#pragma unroll
-        for (int i = 0; i < DHG / 4; ++i)
-            dma16(qg + size_t(w + 4 * i) * MD, uint32_t(lane) * 16, qs + (w + 4 * i) * QPITCH);
-    }
-    load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
-    if (ntiles > 1) load_tile(c, codes, kbuf[1], c.kb + MKT, tile_keys(1));
-    floatx4 o[8];
+    const int ke = kb0 + a.keys_per_split < nk ? kb0 + a.keys_per_split : nk;
+
+    floatx4 o[8];                             // lane l: dims 128 w + 16 m + 4 g + i of head l%16
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[m][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;     // head 16 hg + l%16; l_run over this wave's keys
-    // tile t has landed once only tile t+1's copies may be pending (a partial tile t+1
-    // issues fewer than 16 per wave: then wait for everything)
-    auto wait_tile = [&](int t) {
-        if (t + 1 < ntiles && tile_keys(t + 1) == MKT) wait_vm_tile(); else wait_vm();
-        lds_barrier();
-    };
-    wait_tile(0);
-    bf16x8 qb[MD / 32];                       // Q^T: lane l holds head 16 hg + l%16, dims 32 ks + 8 g
-#pragma unroll
-    for (int ks = 0; ks < MD / 32; ++ks) qb[ks] = load_bf16x8(qs + l16 * QPITCH + ks * 64 + 16 * g);
+    float m_run = -INFINITY, l_run = 0.f;     // l_run: this lane's keys 8 g + e of every k-step
 
-    for (int t = 0; t < ntiles; ++t) {
-        if (t > 0) wait_tile(t);
-        const int nkt = tile_keys(t);
-        const unsigned char* buf = kbuf[t & 1];
-        // S^T for keys 16 w .. 16 w + 15
-        floatx4 st = {0.f, 0.f, 0.f, 0.f};
-        const unsigned char* kr = buf + (16 * w + l16) * KPITCH + 16 * g;
-#pragma unroll
-        for (int ks = 0; ks < MD / 32; ++ks) st = mfma16x16x32(load_bf16x8(kr + ks * 64), qb[ks], st);
-        float sv[4];
-        float lmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sv[i] = 16 * w + 4 * g + i < nkt ? st[i] * a.scale_log2 : -INFINITY;
-            lmax = fmaxf(lmax, sv[i]);
+    for (int cb = kb0; cb < ke; cb += DKC) {
+        const bool first = cb == kb0;
+        if (!first) {
+            __syncthreads();                  // every wave is done with the previous chunk
+            if (a.sel != nullptr) compact_selection(selv, a.k, nv, cb, DKC, codes, wsum);
+            c.kb = cb;
         }
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-        if (g == 0) xch[0][w][l16] = lmax;
-        lds_barrier();
-        const float tmax = fmaxf(fmaxf(xch[0][0][l16], xch[0][1][l16]), fmaxf(xch[0][2][l16], xch[0][3][l16]));
-        if (tmax > m_run + kLazy) {
-            const float alpha = exp2f(m_run - tmax);
-            m_run = tmax;
-            l_run *= alpha;
+        const int nkt = ke - cb < DKC ? ke - cb : DKC;
+        const int nsub = (nkt + 15) >> 4;     // 16-key subtiles to score
+        const int nks = (nkt + 31) >> 5;      // 32-key steps of P*V
+        const int own = (nsub > w) + (nsub > w + 4);
+        if (first) {
+            const bf16* qg = a.q + (size_t(b) * MH + DHG * hg) * MD;
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[m][i] *= alpha;
+            for (int i = 0; i < DHG / 4; ++i)
+                dma16(qg + size_t(w + 4 * i) * MD, uint32_t(lane) * 16, qs + (w + 4 * i) * QPITCH);
         }
-        float p4[4], psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p4[i] = exp2f(sv[i] - m_run);
-            psum += p4[i];
+        // rows of subtiles w and w + 4: lane 16 v + j finds the source of row 16 (w + 4 v) + j;
+        // rows past the chunk's keys copy its last key (finite values; their scores are masked)
+        uint64_t src = 0;
+        {
+            const int v = lane >> 4, row = 16 * (w + 4 * v) + (lane & 15);
+            if (lane < 32 && w + 4 * v < nsub) src = reinterpret_cast<uint64_t>(key_src(c, codes, cb + (row < nkt ? row : nkt - 1)));
         }
-        *reinterpret_cast<uint2*>(ptile + l16 * PPITCH + (16 * w + 4 * g) * 2) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
-        psum += __shfl_xor(psum, 16, 64);
-        l_run += psum + __shfl_xor(psum, 32, 64);
-        lds_barrier();
-        // O^T for dims 128 w .. 128 w + 127: 8 tiles of 16 dims x 2 k-steps of 32 keys
-        const unsigned char* pr = ptile + l16 * PPITCH + 16 * g;
-        const unsigned char* vb0 = buf + (8 * g + (l16 >> 2)) * KPITCH + (128 * w + 4 * (l16 & 3)) * 2;
+        const uint32_t plo = uint32_t(src), phi = uint32_t(src >> 32);
 #pragma unroll
-        for (int ks = 0; ks < MKT / 32; ++ks) {
-            const bf16x8 pb = load_bf16x8(pr + ks * 64);
+        for (int v = 0; v < 2; ++v) {
+            if (w + 4 * v >= nsub) break;
+            unsigned char* dst = kbuf + 16 * (w + 4 * v) * KPITCH;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const unsigned char* vp = vb0 + 32 * ks * KPITCH + m * 32;
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
-                const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
-                bf16x8 va;
-                __builtin_memcpy(&va, &lo, 8);
-                __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &up, 8);
-                o[m] = mfma16x16x32(va, pb, o[m]);
+            for (int j = 0; j < 16; ++j) {
+                const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(plo), 16 * v + j))) |
+                                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), 16 * v + j))) << 32);
+                dma16(reinterpret_cast<const void*>(sp), uint32_t(lane) * 16, dst + j * KPITCH);
             }
         }
-        if (t + 2 < ntiles) {
-            lds_barrier();                    // every wave is done with this buffer
-            load_tile(c, codes, kbuf[t & 1], c.kb + (t + 2) * MKT, tile_keys(t + 2));
+        // an odd subtile count leaves the second half of the last P*V step: zero rows
+        if (2 * nks > nsub && (nsub & 3) == w) {
+#pragma unroll 4
+            for (int j = 0; j < 16; ++j) store16(kbuf + (16 * nsub + j) * KPITCH + lane * 16, make_uint4(0, 0, 0, 0));
+        }
+        if (first) {
+            // this wave's q rows precede its 16 * own key copies
+            if (own == 2) wait_vm_n<32>(); else if (own == 1) wait_vm_n<16>(); else wait_vm_n<0>();
+            lds_barrier();                    // every wave's q rows have landed
+        }
+        bf16x8 qb[MD / 32];                   // Q^T: lane l holds head 16 hg + l%16, dims 32 ks + 8 g
+#pragma unroll
+        for (int ks = 0; ks < MD / 32; ++ks) qb[ks] = load_bf16x8(qs + l16 * QPITCH + ks * 64 + 16 * g);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int u = w + 4 * v;
+            if (u >= nsub) break;
+            if (v == 0 && own == 2) wait_vm_n<16>(); else wait_vm_n<0>();
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            const unsigned char* kr = kbuf + (16 * u + l16) * KPITCH + 16 * g;
+            // all K operands of the subtile go out before the first MFMA
+            bf16x8 ka[MD / 32];
+#pragma unroll
+            for (int ks = 0; ks < MD / 32; ++ks) ka[ks] = load_bf16x8(kr + ks * 64);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < MD / 32; ks += 2) {
+                s0 = mfma16x16x32(ka[ks], qb[ks], s0);
+                s1 = mfma16x16x32(ka[ks + 1], qb[ks + 1], s1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // lane (l%16, g) holds keys 16 u + 4 g + i of head l%16
+            *reinterpret_cast<float4*>(sx + l16 * SXP + 16 * u + 4 * g) =
+                make_float4((s0[0] + s1[0]) * a.scale_log2, (s0[1] + s1[1]) * a.scale_log2,
+                            (s0[2] + s1[2]) * a.scale_log2, (s0[3] + s1[3]) * a.scale_log2);
+        }
+        wait_vm_n<0>();
+        lds_barrier();                        // every key row, zero row and score is in LDS
+
+        switch (nks) {
+            case 1: decode_chunk_pv<1>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
+            case 2: decode_chunk_pv<2>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
+            case 3: decode_chunk_pv<3>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
+            default: decode_chunk_pv<4>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
         }
     }
 
-    // denominator of head 16 hg + l%16 over all four waves' keys
-    if (g == 0) xch[1][w][l16] = l_run;
-    __syncthreads();
-    const float l_tot = (xch[1][0][l16] + xch[1][1][l16]) + (xch[1][2][l16] + xch[1][3][l16]);
+    // denominator of head 16 hg + l%16: sum over the four lane groups
+    l_run += __shfl_xor(l_run, 16, 64);
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const int head = DHG * hg + l16;
-    // lane l holds dims 128 w + 16 m + 4 g + i of head `head`
     if (a.n_splits == 1) {
         const float z = a.sinks[head] * kLog2e;
         const float mf = fmaxf(m_run, z);
@@ -812,15 +914,24 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             a.part_ml[(pbase + l16) * 2 + 0] = m_run;
             a.part_ml[(pbase + l16) * 2 + 1] = l_tot;
         }
-        float* po = a.part_o + (pbase + l16) * MD + 128 * w + 4 * g;
+        // bf16 partial output (the kernel's run time is dominated by writing these back)
+        bf16* po = reinterpret_cast<bf16*>(a.part_o) + (pbase + l16) * MD + 128 * w + 4 * g;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) *reinterpret_cast<float4*>(po + 16 * m) = make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+        for (int m = 0; m < 8; ++m) *reinterpret_cast<uint2*>(po + 16 * m) = pack4_bf16(o[m][0], o[m][1], o[m][2], o[m][3]);
     }
+}
+
+__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_f32(const bf16* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
 // Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One
 // workgroup of 128 threads per (query, head); thread t owns latent dims 4t .. 4t + 3 and
 // issues its split loads independently of each other.
+template <typename P>
 __global__ void __launch_bounds__(128)
 attn_combine_kernel(AttnMfmaArgs a) {
     __shared__ float wgt[MAX_SPLITS];
@@ -840,13 +951,13 @@ attn_combine_kernel(AttnMfmaArgs a) {
         if (on) wgt[tid] = e / den;
     }
     __syncthreads();
-    const float* po = a.part_o + (base * MH + h) * MD + tid * 4;
+    const P* po = reinterpret_cast<const P*>(a.part_o) + (base * MH + h) * MD + tid * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
     for (int sp = 0; sp < a.n_splits; ++sp) {
         // an empty split wrote no output: its weight is 0 and its stale values are skipped
         const float wv = wgt[sp];
-        const float4 v = *reinterpret_cast<const float4*>(po + size_t(sp) * MH * MD);
+        const float4 v = load4_f32(po + size_t(sp) * MH * MD);
         acc.x += wv != 0.f ? wv * v.x : 0.f;
         acc.y += wv != 0.f ? wv * v.y : 0.f;
         acc.z += wv != 0.f ? wv * v.z : 0.f;
@@ -868,17 +979,18 @@ int mfma_splits(int64_t queries, int64_t nk_max, int* keys_per_split) {
     return int((tiles + tiles_per - 1) / tiles_per);
 }
 
-// Decode key splits: about 128 workgroups over (sequence, head group, split), each split a
-// whole number of 64-key tiles.
+// Decode key splits: about kDecodeWgs workgroups over (sequence, head group, split), each
+// split a whole number of 16-key subtiles.
+constexpr int kDecodeWgs = 256;
 int decode_splits(int batch, int64_t nk_max, int* keys_per_split) {
-    const int64_t tiles = (nk_max + MKT - 1) / MKT;
-    int64_t want = (128 + 4 * batch - 1) / (4 * batch);
+    const int64_t units = (nk_max + 15) / 16;
+    int64_t want = (kDecodeWgs + 4 * batch - 1) / (4 * batch);
     if (want > MAX_SPLITS) want = MAX_SPLITS;
-    if (want > tiles) want = tiles;
+    if (want > units) want = units;
     if (want < 1) want = 1;
-    const int64_t tiles_per = (tiles + want - 1) / want;
-    *keys_per_split = int(tiles_per * MKT);
-    return int((tiles + tiles_per - 1) / tiles_per);
+    const int64_t per = (units + want - 1) / want;
+    *keys_per_split = int(per * 16);
+    return int((units + per - 1) / per);
 }
 
 bool use_mfma(bool bf16_, int H, int D) { return bf16_ && H == MH && D == MD; }
@@ -930,7 +1042,11 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.n_splits > 1) {
-            DSV4_LAUNCH("attn_combine", attn_combine_kernel, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
+            // decode partial outputs are bf16, prefill ones fp32
+            if (decode)
+                DSV4_LAUNCH("attn_combine", attn_combine_kernel<bf16>, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
+            else
+                DSV4_LAUNCH("attn_combine", attn_combine_kernel<float>, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

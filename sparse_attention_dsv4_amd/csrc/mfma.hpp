@@ -13,6 +13,8 @@
 namespace dsv4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const floatx16& c) {
@@ -30,6 +32,15 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
 }
 
 __device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in the low half.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    const floatx2 v = {a, b};
+    const bf16x2 r = __builtin_convertvector(v, bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
+}
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) {
     uint32_t u = __float_as_uint(v);

@@ -242,3 +242,25 @@ def test_config_stack_262k_batch4(ratio):
     samples = [(i, b) for i in (0, 3, 127, 255) for b in range(B)]
     worst, ne = _check_decode_queries(spec, seed, layer, outs, sels, L, samples)
     print(f"  262K ratio-{ratio} decode: worst max-rel {worst:.3g}; top-k exact {ne} of {len(samples)}")
+
+
+@pytest.mark.parametrize("case", ["dense_ratio4_b8", "selected_b16"])
+def test_decode_splits_longer_than_one_lds_chunk(case):
+    """Decode splits that hold more keys than one LDS chunk (128 keys), so the attention
+    workgroup runs several chunks with the running max carried between them: a dense ratio-4
+    lane at batch 8 (1500 rows + window: 208-key splits, chunks 128 + 80), and the indexer's
+    top-512 at batch 16 (640 keys: 160-key splits, the selection compacted again for the
+    second chunk)."""
+    if case == "dense_ratio4_b8":
+        spec = LayerSpec(ratio=4, indexer=False, topk=0)
+        seed, B, L, steps = 31, 8, 6000, 2
+    else:
+        spec = LayerSpec(ratio=4)
+        seed, B, L, steps = 32, 16, 4096, 2
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, B, L + steps + 8, params, device="cuda", max_chunk=spec.window)
+    bench.build_prefix(layer, spec, seed, L)
+    outs, sels = _decode_steps(layer, spec, seed, B, L, steps)
+    samples = [(i, b) for i in range(steps) for b in range(B)]
+    worst, ne = _check_decode_queries(spec, seed, layer, outs, sels, L, samples)
+    print(f"  {case}: worst max-rel {worst:.3g}; top-k exact {ne} of {len(samples)}")
