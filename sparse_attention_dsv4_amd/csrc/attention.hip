@@ -259,14 +259,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Where the keys of one query come from.  Key i of the query's list: the compressed rows
-// first (i < nrow; the i-th valid selected row, or row i when every visible row is attended),
-// then the window tokens t0 + (i - nrow) .. p, read from kv_new for tokens of this call and
-// from ring slot t % W for earlier ones.  All key and token indices fit in 32 bits (the entry
-// points cap positions below 2^31 and keys per query at 2^30).
+// Where the keys of one query come from.  Key i of the query's list: the window tokens
+// first, t0 + i for i < nwin, read from kv_new for tokens of this call and from ring slot
+// t % W for earlier ones; then the compressed rows (rank i - nwin: the rank-th valid selected
+// row, or row rank when every visible row is attended).  The window goes first because its
+// sources are known before the selection is compacted.  All key and token indices fit in 32
+// bits (the entry points cap positions below 2^31 and keys per query at 2^30).
 struct TileCtx {
     int b, w, lane, mt, nt, l32, hi;
-    int nrow, kb;             // keys before the window; first key of this workgroup's split
+    int nrow, kb;             // attended rows; first key of this workgroup's split (or chunk)
+    int nwin, kbs;            // window tokens; selection rank held in codes[0]
     int t0, pos0;             // first window token; first token of this call
     uint32_t slot0, W;        // ring slot of t0; ring length
     bool sel;
@@ -287,13 +289,15 @@ __device__ __forceinline__ void key_ctx(TileCtx& c, const AttnMfmaArgs& a, int b
 }
 
 __device__ __forceinline__ const bf16* key_src(const TileCtx& c, const int32_t* codes, int i) {
-    if (i < c.nrow) return c.rows + size_t(c.sel ? codes[i - c.kb] : i) * MD;
-    const int u = i - c.nrow;
-    const int t = c.t0 + u;
-    if (t >= c.pos0) return c.kv_new + size_t(t - c.pos0) * MD;
-    uint32_t slot = c.slot0 + uint32_t(u);          // < 2W: one wrap at most
-    if (slot >= c.W) slot -= c.W;
-    return c.ring + size_t(slot) * MD;
+    if (i < c.nwin) {
+        const int t = c.t0 + i;
+        if (t >= c.pos0) return c.kv_new + size_t(t - c.pos0) * MD;
+        uint32_t slot = c.slot0 + uint32_t(i);      // < 2W: one wrap at most
+        if (slot >= c.W) slot -= c.W;
+        return c.ring + size_t(slot) * MD;
+    }
+    const int j = i - c.nwin;
+    return c.rows + size_t(c.sel ? codes[j - c.kbs] : j) * MD;
 }
 
 // Copy of keys [tb, tb + nkt) into an LDS tile (one 1 KB row per wave instruction), in two
@@ -319,6 +323,18 @@ __device__ __forceinline__ void tile_copy(const TileCtx& c, uint64_t src, unsign
         } else {
             store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
         }
+    }
+}
+
+// One row of tile_copy: row w + 4 i (i wave-uniform).
+__device__ __forceinline__ void tile_copy1(const TileCtx& c, uint64_t src, unsigned char* buf, int nkt, int i) {
+    const int kk = c.w + 4 * i;
+    if (kk < nkt) {
+        const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src)), i))) |
+                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src >> 32)), i))) << 32);
+        dma16(reinterpret_cast<const void*>(sp), uint32_t(c.lane) * 16, buf + kk * KPITCH);
+    } else {
+        store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
     }
 }
 
@@ -407,7 +423,8 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sp[u][i] = 0.f;
-    if (nx.on) tile_copy<0, 4>(c, nx.src, nx.buf, nx.nkt);
+    // the next tile's 16 row copies of this wave go out one per 4 MFMAs (8 in Q*K^T, 8 in
+    // P*V), so the CU's copy queue never holds a burst that stalls the issuing wave
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const unsigned char* kr = buf + (32 * kb + l32) * KPITCH + 512 * nt + 16 * hi;
@@ -426,11 +443,8 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sp[kb] = mfma32x32x16(kx[blk & 1][i], qa[4 * blk + i], sp[kb]);
+            if (nx.on) tile_copy1(c, nx.src, nx.buf, nx.nkt, 4 * kb + blk);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        if (nx.on) {
-            if (kb == 0) tile_copy<4, 8>(c, nx.src, nx.buf, nx.nkt);
-            else tile_copy<8, 12>(c, nx.src, nx.buf, nx.nkt);
         }
     }
     float* sx = reinterpret_cast<float*>(ptile);
@@ -497,7 +511,6 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
                                (256 * nt + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
 #pragma unroll
     for (int ks = 0; ks < MKT / 16; ++ks) {
-        if (ks == 2 && nx.on) tile_copy<12, 16>(c, nx.src, nx.buf, nx.nkt);
         const bf16x8 pb = load_bf16x8(pr + ks * 32);
 #pragma unroll
         for (int n8 = 0; n8 < 8; ++n8) {
@@ -508,6 +521,7 @@ __device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx
             __builtin_memcpy(&va, &lo, 8);
             __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &up, 8);
             o[n8] = mfma32x32x16(va, pb, o[n8]);
+            if ((n8 & 3) == 3 && nx.on) tile_copy1(c, nx.src, nx.buf, nx.nkt, 8 + 2 * ks + (n8 >> 2));
         }
     }
 }
@@ -545,9 +559,14 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int nwin = p - t0 + 1;
     key_ctx(c, a, b, t0, pos0);
     c.kb = split * a.keys_per_split;
+    c.nwin = nwin;
+    c.kbs = c.kb > nwin ? c.kb - nwin : 0;
     c.nrow = nv;
-    // issue order: selection entries, then this wave's 32 heads of q (MFMA A fragments over
-    // all 512 dims), so the compaction waits for the former only and the q loads overlap it
+    // issue order: tile 0 when it holds window tokens only (its sources need no selection),
+    // the selection entries, then this wave's 32 heads of q (MFMA A fragments over all 512
+    // dims), so the compaction waits for the selection only and the rest overlaps it
+    const bool tile0_early = c.kb + MKT <= nwin;
+    if (tile0_early) load_tile(c, codes, kbuf[0], c.kb, MKT);
     int32_t selv[SEL_PER_THREAD];
     if (a.sel != nullptr) load_selection(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, selv);
     bf16x8 qa[MD / 32];                   // heads 32 mt .. +31, dims 256 nt .. +255
@@ -557,10 +576,10 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         for (int ks = 0; ks < MD / 32; ++ks) qa[ks] = load_bf16x8(qh + ks * 16);
     }
     if (a.sel != nullptr)
-        c.nrow = compact_selection(selv, a.k, nv, c.kb, a.keys_per_split, codes, wsum);
+        c.nrow = compact_selection(selv, a.k, nv, c.kbs, a.keys_per_split, codes, wsum);
     const int nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
-    if (c.kb >= nk) {                                 // nothing in this split
+    if (c.kb >= nk) {                                 // nothing in this split (no tile issued)
         if (tid < MH) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
             a.part_ml[(pbase + tid) * 2 + 1] = 0.f;
@@ -574,7 +593,7 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         return left < MKT ? left : MKT;
     };
 
-    load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
+    if (!tile0_early) load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
     floatx16 o[8];
 #pragma unroll
     for (int n8 = 0; n8 < 8; ++n8)
@@ -780,11 +799,13 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     key_ctx(c, a, b, t0, p);
     const int kb0 = split * a.keys_per_split;
     c.kb = kb0;
+    c.nwin = nwin;
+    c.kbs = kb0 > nwin ? kb0 - nwin : 0;
     c.nrow = nv;
     int32_t selv[SEL_PER_THREAD];
     if (a.sel != nullptr) {
         load_selection(a.sel + size_t(b) * a.k, a.k, selv);
-        c.nrow = compact_selection(selv, a.k, nv, kb0, a.keys_per_split < DKC ? a.keys_per_split : DKC,
+        c.nrow = compact_selection(selv, a.k, nv, c.kbs, a.keys_per_split < DKC ? a.keys_per_split : DKC,
                                    codes, wsum);
     }
     const int nk = c.nrow + nwin;
@@ -817,8 +838,9 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         const bool first = cb == kb0;
         if (!first) {
             __syncthreads();                  // every wave is done with the previous chunk
-            if (a.sel != nullptr) compact_selection(selv, a.k, nv, cb, DKC, codes, wsum);
             c.kb = cb;
+            c.kbs = cb > nwin ? cb - nwin : 0;
+            if (a.sel != nullptr) compact_selection(selv, a.k, nv, c.kbs, DKC, codes, wsum);
         }
         const int nkt = ke - cb < DKC ? ke - cb : DKC;
         const int nsub = (nkt + 15) >> 4;     // 16-key subtiles to score
@@ -921,50 +943,62 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 }
 
-__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load4_f32(const bf16* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+// 8 consecutive partial-output values as fp32
+__device__ __forceinline__ void load8_f32(const float* p, float (&v)[8]) {
+    const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+__device__ __forceinline__ void load8_f32(const bf16* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w4[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+    }
 }
 
-// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One
-// workgroup of 128 threads per (query, head); thread t owns latent dims 4t .. 4t + 3 and
-// issues its split loads independently of each other.
+// Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One wave
+// per (query, head): lane l holds split l's (max, sum) and latent dims 8l .. 8l + 7.  The
+// partial-output loads of the first 8 splits go out before the weights are formed, the
+// weights reach every lane by readlane, and nothing passes through LDS.
 template <typename P>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(64)
 attn_combine_kernel(AttnMfmaArgs a) {
-    __shared__ float wgt[MAX_SPLITS];
     const int b = blockIdx.z;
     const int64_t s = blockIdx.y;
     const int h = blockIdx.x;
-    const size_t base = (size_t(b) * a.S + size_t(s)) * a.n_splits;
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-        const bool on = tid < a.n_splits;
-        const float m = on ? a.part_ml[((base + tid) * MH + h) * 2] : -INFINITY;
-        const float l = on ? a.part_ml[((base + tid) * MH + h) * 2 + 1] : 0.f;
-        const float z = a.sinks[h] * kLog2e;
-        const float M = wave_max(fmaxf(m, z));
-        const float e = m == -INFINITY ? 0.f : exp2f(m - M);
-        const float den = wave_sum(l * e) + exp2f(z - M);
-        if (on) wgt[tid] = e / den;
+    const int lane = threadIdx.x;
+    const int n = a.n_splits;
+    const size_t base = (size_t(b) * a.S + size_t(s)) * n;
+    const bool on = lane < n;
+    const float m = on ? a.part_ml[((base + lane) * MH + h) * 2] : -INFINITY;
+    const float l = on ? a.part_ml[((base + lane) * MH + h) * 2 + 1] : 0.f;
+    const P* po = reinterpret_cast<const P*>(a.part_o) + (base * MH + h) * MD + 8 * lane;
+    float wl = 0.f;                           // weight of split `lane`
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g0 = 0; g0 < n; g0 += 8) {
+        float v[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load8_f32(po + size_t(g0 + i < n ? g0 + i : n - 1) * MH * MD, v[i]);
+        if (g0 == 0) {
+            const float z = a.sinks[h] * kLog2e;
+            const float M = wave_max(fmaxf(m, z));
+            const float e = m == -INFINITY ? 0.f : exp2f(m - M);
+            const float den = wave_sum(l * e) + exp2f(z - M);
+            wl = e / den;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // an empty split (weight 0) wrote no output: its stale values are skipped
+            const float wv = g0 + i < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), g0 + i)) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += wv != 0.f ? wv * v[i][e] : 0.f;
+        }
     }
-    __syncthreads();
-    const P* po = reinterpret_cast<const P*>(a.part_o) + (base * MH + h) * MD + tid * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int sp = 0; sp < a.n_splits; ++sp) {
-        // an empty split wrote no output: its weight is 0 and its stale values are skipped
-        const float wv = wgt[sp];
-        const float4 v = load4_f32(po + size_t(sp) * MH * MD);
-        acc.x += wv != 0.f ? wv * v.x : 0.f;
-        acc.y += wv != 0.f ? wv * v.y : 0.f;
-        acc.z += wv != 0.f ? wv * v.z : 0.f;
-        acc.w += wv != 0.f ? wv * v.w : 0.f;
-    }
-    bf16* ob = a.out + ((size_t(b) * a.S + size_t(s)) * MH + h) * MD + tid * 4;
-    *reinterpret_cast<uint2*>(ob) = pack4_bf16(acc.x, acc.y, acc.z, acc.w);
+    bf16* ob = a.out + ((size_t(b) * a.S + size_t(s)) * MH + h) * MD + 8 * lane;
+    *reinterpret_cast<uint4*>(ob) = make_uint4(pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]),
+                                               pack2_bf16(acc[4], acc[5]), pack2_bf16(acc[6], acc[7]));
 }
 
 // Splits per query: enough workgroups to cover the chip when there are few queries.
@@ -1044,9 +1078,9 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         if (a.n_splits > 1) {
             // decode partial outputs are bf16, prefill ones fp32
             if (decode)
-                DSV4_LAUNCH("attn_combine", attn_combine_kernel<bf16>, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
+                DSV4_LAUNCH("attn_combine", attn_combine_kernel<bf16>, dim3(MH, unsigned(j.S), nb), dim3(64), 0, st, a);
             else
-                DSV4_LAUNCH("attn_combine", attn_combine_kernel<float>, dim3(MH, unsigned(j.S), nb), dim3(128), 0, st, a);
+                DSV4_LAUNCH("attn_combine", attn_combine_kernel<float>, dim3(MH, unsigned(j.S), nb), dim3(64), 0, st, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
