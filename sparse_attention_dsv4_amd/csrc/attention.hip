@@ -13,14 +13,15 @@
 // into LDS (one wave per key), phase 2 takes the max (with the sink) and the exponentials,
 // phase 3 forms the weighted sum of the key rows with threads over the latent dims.
 //
-// mfma kernel (bf16, 64 heads, 512 latent): one workgroup per (query, key split) with all
-// 64 heads sharing every 64-key tile staged in LDS.  Q*K^T and P*V run on
-// v_mfma_f32_32x32x16_bf16; the softmax is online in base 2 with fp32 running max and sum;
-// P is rounded to bf16 before P*V (the pages' reference kernel does the same, MTPLX PR #216
-// "Decode path").  A query whose key list is split over several workgroups writes partials
-// (fp32 max and sum; the unnormalised output in bf16 for decode, fp32 for prefill) that
-// attn_combine_kernel merges with the sink; a query handled by one workgroup normalises and
-// writes its output.
+// mfma kernels (bf16, 64 heads, 512 latent), all on v_mfma_f32_16x16x32_bf16 with the key
+// rows copied straight from memory into LDS tiles: prefill runs one workgroup of 8 waves per
+// (query, key split) over 64-key tiles; decode runs one workgroup per (sequence, group of 16
+// heads, key split) holding the whole split in LDS.  The softmax is in base 2 with fp32 max
+// and sum; P is rounded to bf16 before P*V (the pages' reference kernel does the same, MTPLX
+// PR #216 "Decode path").  A query whose key list is split over several workgroups writes
+// partials (fp32 max and sum; the unnormalised output in bf16 for decode, fp32 for prefill)
+// that attn_combine_kernel merges with the sink; a query handled by one workgroup normalises
+// and writes its output.
 //
 // The ring update runs after the attention kernel on the stream: writing token t evicts
 // token t - W, which an earlier query of the same call may still need.
@@ -303,51 +304,8 @@ __device__ __forceinline__ const bf16* key_src(const TileCtx& c, const int32_t* 
     return c.rows + size_t(c.sel ? codes[j - c.kbs] : j) * MD;
 }
 
-// Copy of keys [tb, tb + nkt) into an LDS tile (one 1 KB row per wave instruction), in two
-// steps so the copies can be spread between other work: tile_rows finds, in lane l < 16 of
-// wave w, the source of row w + 4 l; tile_copy<I0, I1> issues rows w + 4 i for i in [I0, I1)
-// (reading each source back as a scalar) and zero-fills the rows past nkt.
-__device__ __forceinline__ uint64_t tile_rows(const TileCtx& c, const int32_t* codes, int tb, int nkt) {
-    const int kk_l = c.w + 4 * (c.lane & 15);
-    const bf16* mine = kk_l < nkt ? key_src(c, codes, tb + kk_l) : c.ring;
-    return reinterpret_cast<uint64_t>(mine);
-}
-
-template <int I0, int I1>
-__device__ __forceinline__ void tile_copy(const TileCtx& c, uint64_t src, unsigned char* buf, int nkt) {
-    const uint32_t plo = uint32_t(src), phi = uint32_t(src >> 32);
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        const int kk = c.w + 4 * i;
-        if (kk < nkt) {
-            const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(plo), i))) |
-                                (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), i))) << 32);
-            dma16(reinterpret_cast<const void*>(sp), uint32_t(c.lane) * 16, buf + kk * KPITCH);
-        } else {
-            store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
-        }
-    }
-}
-
-// One row of tile_copy: row w + 4 i (i wave-uniform).
-__device__ __forceinline__ void tile_copy1(const TileCtx& c, uint64_t src, unsigned char* buf, int nkt, int i) {
-    const int kk = c.w + 4 * i;
-    if (kk < nkt) {
-        const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src)), i))) |
-                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src >> 32)), i))) << 32);
-        dma16(reinterpret_cast<const void*>(sp), uint32_t(c.lane) * 16, buf + kk * KPITCH);
-    } else {
-        store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
-    }
-}
-
-__device__ __forceinline__ void load_tile(const TileCtx& c, const int32_t* codes, unsigned char* buf,
-                                          int tb, int nkt) {
-    tile_copy<0, MKT / 4>(c, tile_rows(c, codes, tb, nkt), buf, nkt);
-}
-
-// The next tile's copy, handed to attend_tile so it can issue it in parts between MFMA groups
-// (a wave issuing all 16 copies at once stalls on the CU's load pipe and computes nothing).
+// The next tile's copy, handed to prefill_tile so it can issue it in parts between MFMA groups
+// (a wave issuing all of its copies at once stalls on the CU's load pipe and computes nothing).
 struct NextTile {
     bool on;
     uint64_t src;
@@ -355,31 +313,35 @@ struct NextTile {
     int nkt;
 };
 
-// The selection row as this thread's entries e = 256 r + tid (-1 past k; k <= MAX_CODES).
+// The selection row as this thread's entries e = NT r + tid (-1 past k; k <= MAX_CODES), for
+// a workgroup of NT threads.
 constexpr int SEL_PER_THREAD = MAX_CODES / 256;
-__device__ __forceinline__ void load_selection(const int32_t* sr, int k, int32_t (&selv)[SEL_PER_THREAD]) {
+template <int NT = 256>
+__device__ __forceinline__ void load_selection(const int32_t* sr, int k, int32_t (&selv)[MAX_CODES / NT]) {
 #pragma unroll
-    for (int r = 0; r < SEL_PER_THREAD; ++r) {
-        const int e = 256 * r + int(threadIdx.x);
+    for (int r = 0; r < MAX_CODES / NT; ++r) {
+        const int e = NT * r + int(threadIdx.x);
         selv[r] = e < k ? sr[e] : -1;
     }
 }
 
 // Compact the valid entries (0 <= j < nv) of one selection row, keeping their order: the
 // entry of rank n goes to codes[n - kb] when kb <= n < kb + kps.  Returns the count of valid
-// entries.  Ranks come from wave ballots; wsum holds 2 x 4 per-wave counts.  The barriers
-// wait for LDS only, so global loads issued before (q fragments) stay in flight.
-__device__ __forceinline__ int compact_selection(const int32_t (&selv)[SEL_PER_THREAD], int k, int nv,
+// entries.  Ranks come from wave ballots; wsum holds 2 x (NT / 64) per-wave counts.  The
+// barriers wait for LDS only, so global loads issued before (q fragments) stay in flight.
+template <int NT = 256>
+__device__ __forceinline__ int compact_selection(const int32_t (&selv)[MAX_CODES / NT], int k, int nv,
                                                  int kb, int kps, int32_t* codes, int* wsum) {
+    constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int base = 0;
 #pragma unroll
-    for (int r = 0; r < SEL_PER_THREAD; ++r) {
-        if (256 * r >= k) break;
+    for (int r = 0; r < MAX_CODES / NT; ++r) {
+        if (NT * r >= k) break;
         const int32_t j = selv[r];
         const bool ok = j >= 0 && j < nv;
         const uint64_t m = __ballot(ok);
-        int* ws = wsum + (r & 1) * 4;
+        int* ws = wsum + (r & 1) * NW;
         if (lane == 0) ws[w] = __popcll(m);
         lds_barrier();
         int off = base;
@@ -388,7 +350,8 @@ __device__ __forceinline__ int compact_selection(const int32_t (&selv)[SEL_PER_T
             const int rank = off + __popcll(m & ((uint64_t(1) << lane) - 1));
             if (rank >= kb && rank < kb + kps) codes[rank - kb] = j;
         }
-        base += (ws[0] + ws[1]) + (ws[2] + ws[3]);
+#pragma unroll
+        for (int v = 0; v < NW; ++v) base += ws[v];
     }
     lds_barrier();
     return base;
@@ -399,7 +362,7 @@ __device__ __forceinline__ int compact_selection(const int32_t (&selv)[SEL_PER_T
 // Every exponent stays <= 2^kLazy, far inside fp32 and bf16 range, and the final division
 // uses the same reference, so the result is unchanged.
 constexpr float kLazy = 8.0f;
-constexpr int SXBYTES = 4 * 64 * 16 * 4;  // S^T partials: 4 waves x 64 lanes x 16 fp32
+constexpr int SXBYTES = 8 * 2 * 64 * 4 * 4;   // S^T partials: 8 (head group, dim half) x 2 subtiles x 64 lanes x 4 fp32
 
 
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
@@ -410,133 +373,179 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 // lose weights that are far below bf16 resolution of the sum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One key tile.  Wave (mt, nt): S^T = K Q^T for keys 32nt.. x heads 32mt.., so lane l owns
-// head 32mt + l%32 and 16 keys; O^T += V^T P^T for dims 256nt.. x the same heads.
-__device__ __forceinline__ void attend_tile(const AttnMfmaArgs& a, const TileCtx& c,
-                                            const unsigned char* buf, unsigned char* ptile,
-                                            float (*xch)[2][MH], const bf16x8* qa, floatx16* o,
-                                            float& m_run, float& l_run, int nkt, const NextTile& nx) {
-    const int mt = c.mt, nt = c.nt, lane = c.lane, l32 = c.l32, hi = c.hi;
-    const int head = 32 * mt + l32;
-    // S^T partials over this wave's 256 dims (dim half nt) for both 32-key halves; the key
-    // half nt^1 goes to the partner wave (same heads, other dims) through LDS, so each wave
-    // ends with the full S^T of key half nt.  sx aliases the P tile (free until P is written).
-    floatx16 sp[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sp[u][i] = 0.f;
-    // the next tile's 16 row copies of this wave go out one per 4 MFMAs (8 in Q*K^T, 8 in
-    // P*V), so the CU's copy queue never holds a burst that stalls the issuing wave
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const unsigned char* kr = buf + (32 * kb + l32) * KPITCH + 512 * nt + 16 * hi;
-        // K operands in blocks of 4 k-steps, the next block issued before this one's MFMAs;
-        // the scheduling barriers keep each read from being paired with (and waited on right
-        // before) its MFMA
-        bf16x8 kx[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kx[0][i] = load_bf16x8(kr + i * 32);
-#pragma unroll
-        for (int blk = 0; blk < MD / 128; ++blk) {
-            if (blk + 1 < MD / 128) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) kx[(blk + 1) & 1][i] = load_bf16x8(kr + (4 * (blk + 1) + i) * 32);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sp[kb] = mfma32x32x16(kx[blk & 1][i], qa[4 * blk + i], sp[kb]);
-            if (nx.on) tile_copy1(c, nx.src, nx.buf, nx.nkt, 4 * kb + blk);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    float* sx = reinterpret_cast<float*>(ptile);
-    {
-        const floatx16& give = nt ? sp[0] : sp[1];
-        float* dst = sx + ((2 * mt + (nt ^ 1)) * 64 + lane) * 16;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<float4*>(dst + 4 * q4) = make_float4(give[4 * q4], give[4 * q4 + 1], give[4 * q4 + 2], give[4 * q4 + 3]);
-    }
-    lds_barrier();
-    floatx16 st = nt ? sp[1] : sp[0];
-    {
-        const float* src = sx + ((2 * mt + nt) * 64 + lane) * 16;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = *reinterpret_cast<const float4*>(src + 4 * q4);
-            st[4 * q4] += v.x;
-            st[4 * q4 + 1] += v.y;
-            st[4 * q4 + 2] += v.z;
-            st[4 * q4 + 3] += v.w;
-        }
-    }
-    float sv[16];
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const bool kvalid = 32 * nt + c_row(i, lane) < nkt;
-        sv[i] = kvalid ? st[i] * a.scale_log2 : -INFINITY;
-        lmax = fmaxf(lmax, sv[i]);
-    }
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));      // this key half, this head
-    if (hi == 0) xch[0][nt][head] = lmax;
-    lds_barrier();
-    const float tmax = fmaxf(lmax, xch[0][nt ^ 1][head]);
-    // the decision depends only on (m_run, tmax), equal in both waves of this head half
-    if (tmax > m_run + kLazy) {
-        const float alpha = exp2f(m_run - tmax);        // 0 on the first tile
-        m_run = tmax;
-        l_run *= alpha;
-#pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[n8][i] *= alpha;
-    }
-    float psum = 0.f;
-    unsigned char* prow = ptile + head * PPITCH + (32 * nt + 4 * hi) * 2;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {                    // registers 4 q4 .. 4 q4 + 3: 4 consecutive keys
-        float p4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p4[r] = fast_exp2(sv[4 * q4 + r] - m_run);
-            psum += p4[r];
-        }
-        *reinterpret_cast<uint2*>(prow + 16 * q4) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
-    }
-    l_run += psum + __shfl_xor(psum, 32, 64);          // this wave's key half only
-    lds_barrier();
-    // O^T += V^T P^T: A = 32 dims x 16 keys of V (two transposed reads), B = P^T fragment
-    const unsigned char* pr = ptile + head * PPITCH + 16 * hi;
-    const int j16 = lane & 15;
-    const unsigned char* vb0 = buf + (8 * hi + (j16 >> 2)) * KPITCH +
-                               (256 * nt + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2;
-#pragma unroll
-    for (int ks = 0; ks < MKT / 16; ++ks) {
-        const bf16x8 pb = load_bf16x8(pr + ks * 32);
-#pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8) {
-            const unsigned char* vp = vb0 + 16 * ks * KPITCH + n8 * 64;
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
-            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
-            bf16x8 va;
-            __builtin_memcpy(&va, &lo, 8);
-            __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &up, 8);
-            o[n8] = mfma32x32x16(va, pb, o[n8]);
-            if ((n8 & 3) == 3 && nx.on) tile_copy1(c, nx.src, nx.buf, nx.nkt, 8 + 2 * ks + (n8 >> 2));
-        }
+constexpr int DHG = 16;                   // heads per 16x16x32 head group
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8 (l/16) + 0..7], B lane l holds
+// B[8 (l/16) + 0..7][l%16], C lane l register i holds C[4 (l/16) + i][l%16].
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ prefill path
+// One workgroup of 8 waves per (query, key split).  Wave w holds heads 16 (w >> 1) .. +15
+// and latent dims 256 (w & 1) .. +255, so its accumulators (16 heads x 256 dims fp32) and q
+// fragments fit in 256 registers and two waves share each SIMD: while one waits on a copy,
+// an LDS read or a barrier, the other issues MFMAs.  Per 64-key tile, on
+// v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T over the wave's 256 dims for the 4 subtiles of 16 keys; the two dim halves
+//   of a head group swap, through LDS, the partials of the key half each does not keep;
+//   online softmax over the kept key half, the halves' maxima meet in LDS, P (bf16) to LDS;
+//   O^T += V^T P^T for the wave's 256 dims over all 64 keys.
+constexpr int PWAVES = 8;
+constexpr int PTHREADS = 64 * PWAVES;
+
+// Sources of a tile's rows for 8 waves: lane l < 8 of wave w finds the source of row w + 8 l.
+__device__ __forceinline__ uint64_t prow_srcs(const TileCtx& c, const int32_t* codes, int tb, int nkt) {
+    const int kk = c.w + PWAVES * (c.lane & 7);
+    const bf16* src = kk < nkt ? key_src(c, codes, tb + kk) : c.ring;
+    return reinterpret_cast<uint64_t>(src);
+}
+
+// Row w + 8 i of a tile (i wave-uniform): one 1 KB copy, or zeros past nkt.
+__device__ __forceinline__ void prow_copy(const TileCtx& c, uint64_t src, unsigned char* buf, int nkt, int i) {
+    const int kk = c.w + PWAVES * i;
+    if (kk < nkt) {
+        const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src)), i))) |
+                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src >> 32)), i))) << 32);
+        dma16(reinterpret_cast<const void*>(sp), uint32_t(c.lane) * 16, buf + kk * KPITCH);
+    } else {
+        store16(buf + kk * KPITCH + c.lane * 16, make_uint4(0, 0, 0, 0));
     }
 }
 
-__global__ void __launch_bounds__(256)
-attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+__device__ __forceinline__ void prefill_load_tile(const TileCtx& c, const int32_t* codes, unsigned char* buf,
+                                                  int tb, int nkt) {
+    const uint64_t src = prow_srcs(c, codes, tb, nkt);
+#pragma unroll
+    for (int i = 0; i < MKT / PWAVES; ++i) prow_copy(c, src, buf, nkt, i);
+}
+
+// One key tile of the 8-wave prefill workgroup (see above).  nx: the next tile, whose 8 row
+// copies of this wave go out between this tile's MFMA groups.
+__device__ __forceinline__ void prefill_tile(const AttnMfmaArgs& a, const TileCtx& c, const unsigned char* buf,
+                                             unsigned char* ptile, float (*xch)[2][MH], const bf16x8 (&qa)[8],
+                                             floatx4 (&o)[16], float& m_run, float& l_run, int nkt,
+                                             const NextTile& nx) {
+    const int lane = c.lane, l16 = lane & 15, g = lane >> 4;
+    const int hq = c.w >> 1, nt = c.w & 1;
+    const int head = DHG * hq + l16;
+    // S^T partials over dims 256 nt .. +255: subtile u = keys 16 u .. 16 u + 15; the K operands
+    // of subtile u+1 go out before the MFMAs of subtile u
+    floatx4 sp[4];
+    const unsigned char* kr0 = buf + l16 * KPITCH + 512 * nt + 16 * g;
+    bf16x8 ka[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[0][ks] = load_bf16x8(kr0 + ks * 64);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) ka[(u + 1) & 1][ks] = load_bf16x8(kr0 + 16 * (u + 1) * KPITCH + ks * 64);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sp[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) sp[u] = mfma16x16x32(ka[u & 1][ks], qa[ks], sp[u]);
+        if (nx.on) prow_copy(c, nx.src, nx.buf, nx.nkt, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // keep key half nt (subtiles 2 nt, 2 nt + 1); the partner wave (other dims) gets the other
+    // half.  Exchange region (head group, receiving dim half): [subtile][lane][4] fp32
+    // (selects rather than indexing sp by nt: a register array indexed at run time would go
+    // to scratch memory)
+    const floatx4 keep0 = nt ? sp[2] : sp[0], keep1 = nt ? sp[3] : sp[1];
+    const floatx4 give0 = nt ? sp[0] : sp[2], give1 = nt ? sp[1] : sp[3];
+    float* sx = reinterpret_cast<float*>(ptile);
+    {
+        float* give = sx + (hq * 2 + (nt ^ 1)) * 512;
+        *reinterpret_cast<floatx4*>(give + lane * 4) = give0;
+        *reinterpret_cast<floatx4*>(give + (64 + lane) * 4) = give1;
+    }
+    lds_barrier();
+    float sv[2][4];
+    float lmax = -INFINITY;
+    {
+        const float* take = sx + (hq * 2 + nt) * 512;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const floatx4 pv = *reinterpret_cast<const floatx4*>(take + (v * 64 + lane) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool kvalid = 32 * nt + 16 * v + 4 * g + i < nkt;
+                sv[v][i] = kvalid ? ((v ? keep1[i] : keep0[i]) + pv[i]) * a.scale_log2 : -INFINITY;
+                lmax = fmaxf(lmax, sv[v][i]);
+            }
+        }
+    }
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));       // this key half, this head
+    if (g == 0) xch[0][nt][head] = lmax;
+    lds_barrier();
+    const float tmax = fmaxf(lmax, xch[0][nt ^ 1][head]);
+    // the decision depends only on (m_run, tmax), equal in both waves of this head group
+    if (tmax > m_run + kLazy) {
+        const float alpha = fast_exp2(m_run - tmax);    // 0 on the first tile
+        m_run = tmax;
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[m][i] *= alpha;
+    }
+    float psum = 0.f;
+    unsigned char* prow = ptile + head * PPITCH + (32 * nt + 4 * g) * 2;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        float p4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p4[i] = fast_exp2(sv[v][i] - m_run);
+            psum += p4[i];
+        }
+        *reinterpret_cast<uint2*>(prow + 32 * v) = pack4_bf16(p4[0], p4[1], p4[2], p4[3]);
+    }
+    l_run += psum;                                      // this lane's keys only
+    lds_barrier();
+    // O^T for dims 256 nt .. +255 (16 tiles of 16 dims) over 2 k-steps of 32 keys; the V^T
+    // operands of each group of 8 tiles go out before the previous group's MFMAs
+    const unsigned char* pr = ptile + head * PPITCH + 16 * g;
+    const bf16x8 pb0 = load_bf16x8(pr), pb1 = load_bf16x8(pr + 64);
+    const unsigned char* vb0 = buf + (8 * g + (l16 >> 2)) * KPITCH + (256 * nt + 4 * (l16 & 3)) * 2;
+    bf16x8 va[2][8];
+    auto load_v = [&](int grp, bf16x8 (&dst)[8]) {     // grp = 2 ks + (tile half)
+        const int ks = grp >> 1, m0 = 8 * (grp & 1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const unsigned char* vp = vb0 + 32 * ks * KPITCH + (m0 + m) * 32;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 4 * KPITCH));
+            __builtin_memcpy(&dst[m], &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&dst[m]) + 8, &up, 8);
+        }
+    };
+    load_v(0, va[0]);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+        if (grp + 1 < 4) load_v(grp + 1, va[(grp + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8& pb = (grp >> 1) ? pb1 : pb0;
+        const int m0 = 8 * (grp & 1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m0 + m] = mfma16x16x32(va[grp & 1][m], pb, o[m0 + m]);
+        if (nx.on) prow_copy(c, nx.src, nx.buf, nx.nkt, 4 + grp);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ void __launch_bounds__(PTHREADS)
+attn_prefill_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KBUF];
-    // P tile; before P is written it holds the S^T partials exchanged between the dim halves
+    // S^T partials exchanged between the dim halves, then P [head][key] bf16
     __shared__ __attribute__((aligned(16))) unsigned char ptile[SXBYTES > MH * PPITCH ? SXBYTES : MH * PPITCH];
     __shared__ float xch[2][2][MH];       // [max | sum][key half][head]
     __shared__ int32_t codes[MAX_CODES];
-    __shared__ int wsum[8];
+    __shared__ int wsum[2 * PWAVES];
 
     TileCtx c;
     c.b = blockIdx.z;
@@ -545,11 +554,13 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int tid = threadIdx.x;
     c.lane = tid & 63;
     c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-    c.mt = c.w >> 1;                      // head half
-    c.nt = c.w & 1;                       // dim half in Q.K^T and P.V; key half of the softmax
+    c.mt = c.w >> 1;
+    c.nt = c.w & 1;
     c.l32 = c.lane & 31;
     c.hi = c.lane >> 5;
-    const int b = c.b;
+    const int b = c.b, lane = c.lane, l16 = lane & 15, g = lane >> 4;
+    const int hq = c.w >> 1, nt = c.w & 1;
+    const int head = DHG * hq + l16;
     const int pos0 = pos0v.v[b];
     const int p = pos0 + int(s);
 
@@ -566,20 +577,20 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     c.kbs = c.kb > nwin ? c.kb - nwin : 0;
     c.nrow = nv;
     // issue order: tile 0 when it holds window tokens only (its sources need no selection),
-    // the selection entries, then this wave's 32 heads of q (MFMA A fragments over all 512
-    // dims), so the compaction waits for the selection only and the rest overlaps it
+    // the selection entries, then this wave's q fragments (16 heads x 256 dims), so the
+    // compaction waits for the selection only and the rest overlaps it
     const bool tile0_early = c.kb + MKT <= nwin;
-    if (tile0_early) load_tile(c, codes, kbuf[0], c.kb, MKT);
-    int32_t selv[SEL_PER_THREAD];
-    if (a.sel != nullptr) load_selection(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, selv);
-    bf16x8 qa[MD / 32];                   // heads 32 mt .. +31, dims 256 nt .. +255
+    if (tile0_early) prefill_load_tile(c, codes, kbuf[0], c.kb, MKT);
+    int32_t selv[MAX_CODES / PTHREADS];
+    if (a.sel != nullptr) load_selection<PTHREADS>(a.sel + (size_t(b) * a.S + size_t(s)) * a.k, a.k, selv);
+    bf16x8 qa[8];                         // Q^T: lane l holds head 16 hq + l%16, dims 256 nt + 32 ks + 8 (l/16)
     {
-        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + 32 * c.mt + c.l32) * MD + 256 * c.nt + 8 * c.hi;
+        const bf16* qh = a.q + ((size_t(b) * a.S + size_t(s)) * MH + head) * MD + 256 * nt + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < MD / 32; ++ks) qa[ks] = load_bf16x8(qh + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) qa[ks] = load_bf16x8(qh + 32 * ks);
     }
     if (a.sel != nullptr)
-        c.nrow = compact_selection(selv, a.k, nv, c.kbs, a.keys_per_split, codes, wsum);
+        c.nrow = compact_selection<PTHREADS>(selv, a.k, nv, c.kbs, a.keys_per_split, codes, wsum);
     const int nk = c.nrow + nwin;
     const size_t pbase = ((size_t(b) * a.S + size_t(s)) * a.n_splits + split) * MH;
     if (c.kb >= nk) {                                 // nothing in this split (no tile issued)
@@ -595,14 +606,13 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         const int left = ke - (c.kb + t * MKT);
         return left < MKT ? left : MKT;
     };
-
-    if (!tile0_early) load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
-    floatx16 o[8];
+    if (!tile0_early) prefill_load_tile(c, codes, kbuf[0], c.kb, tile_keys(0));
+    floatx4 o[16];                        // lane l: dims 256 nt + 16 m + 4 (l/16) + i of its head
 #pragma unroll
-    for (int n8 = 0; n8 < 8; ++n8)
+    for (int m = 0; m < 16; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[n8][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;   // head 32mt + l%32; l_run over this key half
+        for (int i = 0; i < 4; ++i) o[m][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
     wait_vm();
     __syncthreads();
 
@@ -610,21 +620,20 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         NextTile nx;
         nx.on = t + 1 < ntiles;
         nx.nkt = nx.on ? tile_keys(t + 1) : 0;
-        nx.src = nx.on ? tile_rows(c, codes, c.kb + (t + 1) * MKT, nx.nkt) : 0;
+        nx.src = nx.on ? prow_srcs(c, codes, c.kb + (t + 1) * MKT, nx.nkt) : 0;
         nx.buf = kbuf[(t + 1) & 1];
-        attend_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t), nx);
+        prefill_tile(a, c, kbuf[t & 1], ptile, xch, qa, o, m_run, l_run, tile_keys(t), nx);
         wait_vm();                        // the next tile has landed
         __syncthreads();                  // ... for every wave; and all are done with this one
     }
 
-    // total denominator of this lane's head: both key halves
-    const int mt = c.mt, nt = c.nt, lane = c.lane, l32 = c.l32, hi = c.hi;
-    const int head = 32 * mt + l32;
-    if (hi == 0) xch[1][nt][head] = l_run;
+    // denominator of this lane's head: its lane group's keys, then both key halves
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (g == 0) xch[1][nt][head] = l_run;
     __syncthreads();
-    const float l_tot = l_run + xch[1][nt ^ 1][head];
-    // stage the result in LDS (the key buffers are free now), then coalesced 16-byte stores;
-    // lane l holds head `head`, dims 256nt + 32n8 + c_row(i, l) (4 consecutive per q4)
+    const float l_tot = xch[1][0][head] + xch[1][1][head];
+    // stage the result in LDS (the key buffers are free now), then coalesced 16-byte stores
     if (a.n_splits == 1) {
         const float z = a.sinks[head] * kLog2e;
         const float mf = fmaxf(m_run, z);
@@ -632,36 +641,30 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         const float f = sc / (l_tot * sc + exp2f(z - mf));
         unsigned char* stage = kbuf[0];                 // bf16 [head][dim], 1040-byte rows
 #pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<uint2*>(stage + head * (MD * 2 + 16) +
-                                          (256 * nt + 32 * n8 + 8 * q4 + 4 * hi) * 2) =
-                    pack4_bf16(o[n8][4 * q4] * f, o[n8][4 * q4 + 1] * f, o[n8][4 * q4 + 2] * f,
-                               o[n8][4 * q4 + 3] * f);
+        for (int m = 0; m < 16; ++m)
+            *reinterpret_cast<uint2*>(stage + head * (MD * 2 + 16) + (256 * nt + 16 * m + 4 * g) * 2) =
+                pack4_bf16(o[m][0] * f, o[m][1] * f, o[m][2] * f, o[m][3] * f);
         __syncthreads();
         bf16* ob = a.out + (size_t(b) * a.S + size_t(s)) * MH * MD;
-        for (int idx = tid; idx < MH * MD / 8; idx += 256) {
+        for (int idx = tid; idx < MH * MD / 8; idx += PTHREADS) {
             const int h = idx / (MD / 8), d8 = idx % (MD / 8);
             store16(ob + size_t(h) * MD + d8 * 8,
                     *reinterpret_cast<const uint4*>(stage + h * (MD * 2 + 16) + d8 * 16));
         }
     } else {
-        if (nt == 0 && hi == 0) {
+        if (nt == 0 && g == 0) {
             a.part_ml[(pbase + head) * 2 + 0] = m_run;
             a.part_ml[(pbase + head) * 2 + 1] = l_tot;
         }
         // fp32 [head][dim]: heads 0..31 staged in kbuf[0], 32..63 in kbuf[1] (32 x 2064 B each)
-        unsigned char* st = kbuf[mt];
+        unsigned char* st = kbuf[head >> 5] + (head & 31) * OPITCH;
 #pragma unroll
-        for (int n8 = 0; n8 < 8; ++n8)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<float4*>(st + l32 * OPITCH + (256 * nt + 32 * n8 + 8 * q4 + 4 * hi) * 4) =
-                    make_float4(o[n8][4 * q4], o[n8][4 * q4 + 1], o[n8][4 * q4 + 2], o[n8][4 * q4 + 3]);
+        for (int m = 0; m < 16; ++m)
+            *reinterpret_cast<float4*>(st + (256 * nt + 16 * m + 4 * g) * 4) =
+                make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
         __syncthreads();
         float* po = a.part_o + pbase * MD;
-        for (int idx = tid; idx < MH * MD / 4; idx += 256) {
+        for (int idx = tid; idx < MH * MD / 4; idx += PTHREADS) {
             const int h = idx / (MD / 4), d4 = idx % (MD / 4);
             const unsigned char* sp = kbuf[h >> 5] + (h & 31) * OPITCH + d4 * 16;
             store16(po + size_t(h) * MD + d4 * 4, *reinterpret_cast<const uint4*>(sp));
@@ -681,15 +684,9 @@ attn_mfma_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
 //     bf16 P of the whole chunk;
 //   * wave w accumulates dims 128 w .. 128 w + 127 of O^T = V^T P^T over every key, so no
 //     partial output is merged inside the workgroup.
-constexpr int DHG = 16;                   // heads per decode workgroup
 constexpr int DKC = 128;                  // keys of one decode chunk (8 subtiles of 16)
 constexpr int SXP = DKC + 4;              // floats per head row of the exchanged scores
 constexpr int QPITCH = MD * 2 + 16;       // LDS row of a staged q (offset rows: no bank conflicts)
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
@@ -1073,7 +1070,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
             DSV4_LAUNCH("attn_decode", attn_decode_kernel, dim3(unsigned(a.n_splits), MH / DHG, nb), dim3(256),
                                0, st, a, pos, nr);
         } else {
-            DSV4_LAUNCH("attn_mfma", attn_mfma_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(256),
+            DSV4_LAUNCH("attn_prefill", attn_prefill_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(PTHREADS),
                                0, st, a, pos, nr);
         }
         e = hipGetLastError();

@@ -24,7 +24,7 @@ def _hipcc():
 
 
 @pytest.mark.parametrize("src,kernel", [
-    ("attention.hip", "attn_mfma_kernel"),
+    ("attention.hip", "attn_prefill_kernel"),
     ("attention.hip", "attn_decode_kernel"),
     ("indexer.hip", "index_score_mfma_kernel"),
 ])
@@ -51,7 +51,7 @@ def test_m0_only_feeds_lds_dma(tmp_path, src, kernel):
         assert any(l.startswith("global_load_lds_dwordx4") for l in follow), (code[i], follow)
 
 
-@pytest.mark.parametrize("kernel", ["attn_mfma_kernel", "attn_decode_kernel"])
+@pytest.mark.parametrize("kernel", ["attn_prefill_kernel", "attn_decode_kernel"])
 def test_dma_base_is_not_sign_extended(tmp_path, kernel):
     """The key-row copies rebuild a 64-bit scalar base from two 32-bit lane reads.  A signed
     widening of the low half (s_bfe_i64 ... 0x200000) would set the upper word of any address
