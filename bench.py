@@ -178,6 +178,94 @@ def bench_decode(args, seed=0):
     return res, layer_state
 
 
+def bench_stack(args, seed=23):
+    """Decode of the [0, 4, 128] stack at 262,144 tokens, batch 4: a window-only layer, a
+    ratio-4 layer (65,536 rows, indexer top-512) and a ratio-128 layer (2048 rows, top-512).
+    A step is one decode token of every sequence through all three layers; the K steps are
+    replayed as a HIP graph like the headline decode.  The roofline is the ratio-4 layer's
+    indexer scan (HBM-bound: every visible indexer row is read once per step)."""
+    B, L = 4, 262144
+    steps, warm = min(args.steps, 64), args.warmup
+    specs = [LayerSpec(ratio=0, indexer=False, topk=0), LayerSpec(ratio=4), LayerSpec(ratio=128)]
+    layers, toks = [], []
+    t_setup = time.time()
+    for i, spec in enumerate(specs):
+        params = SC.layer_params(spec, seed + spec.ratio, device="cuda")
+        layer = CsaLayer(spec, B, L + warm + 3 * steps + 8, params, device="cuda", max_chunk=spec.window)
+        build_prefix(layer, spec, seed + spec.ratio, L)
+        layers.append(layer)
+        tl = []
+        for j in range(warm + steps):
+            t = SC.batch_token_inputs(spec, seed + spec.ratio, [L + j] * B, 1, device="cuda")
+            tl.append({k: v[:, 0].contiguous() for k, v in t.items()})
+        toks.append(tl)
+    log(f"[stack] three layers at {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
+
+    def step(j, trace_layer=None):
+        for i, layer in enumerate(layers):
+            if trace_layer is not None:
+                K.dsv4_trace_enable(i == trace_layer)
+            layer.decode(toks[i][j])
+        if trace_layer is not None:
+            K.dsv4_trace_enable(False)
+
+    for j in range(warm):
+        step(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(warm, warm + steps):
+        step(j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # kernel durations of the ratio-4 layer, in a second identical pass with the trace on
+    K.dsv4_trace_reset()
+    for j in range(warm, warm + steps):
+        step(j, trace_layer=1)
+    torch.cuda.synchronize()
+    per_kernel = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+    # graph replay of the K steps (state restored outside the timed region)
+    names = ("ring", "state", "rows", "state_i", "rows_i")
+    snap = [{n: getattr(l, n).clone() for n in names if hasattr(l, n)} for l in layers]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(warm, warm + steps):
+            step(j)
+
+    def restore():
+        for l, sn in zip(layers, snap):
+            for n, v in sn.items():
+                getattr(l, n).copy_(v)
+        torch.cuda.synchronize()
+
+    restore()
+    graph.replay()
+    torch.cuda.synchronize()
+    restore()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    g_wall = time.perf_counter() - t0
+    spec4 = specs[1]
+    nv = (L + warm) // spec4.ratio
+    n_l, ms_l = per_kernel["index_score_mfma"]
+    # algorithmic bytes of one scan: every visible indexer row, the queries and head weights
+    bytes_launch = B * (nv * spec4.index_dim * 2 + spec4.index_heads * (spec4.index_dim * 2 + 4))
+    achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
+    return {
+        "workload": f"decode, [0, 4, 128] stack (window-only, ratio-4 with top-512 over ~{nv} rows, "
+                    f"ratio-128 with top-512 over ~{L // 128} rows), batch {B}, context {L}",
+        "tok_s": B * steps / g_wall, "ms_per_step": g_wall / steps * 1e3,
+        "mode": "hip-graph replay of the K captured steps (three layers per step)",
+        "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3},
+        "kernels_ratio4_layer": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
+                                 for n, v in per_kernel.items()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "index_score_mfma",
+                     "bytes_per_launch": bytes_launch},
+    }
+
+
+
 def cpu_baseline_decode(layer_state, sample_steps):
     """The oracle doing the same decode work (window + all visible rows, per sequence) on
     the host, for ``sample_steps`` steps of every sequence.  Rows and ring are the GPU
@@ -463,6 +551,8 @@ def main():
     ap.add_argument("--cpu-prefill-queries", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-stack", action="store_true",
+                    help="leave out the 262,144-token [0, 4, 128] stack decode sub-line")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run one workload (for per-workload profiler runs); the JSON line "
                          "then carries that workload's numbers only")
@@ -483,6 +573,11 @@ def main():
     if not args.skip_prefill and args.only != "decode":
         pre, pre_state = bench_prefill(args)
         log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk")
+    stack = None
+    if not args.skip_stack and args.only is None:
+        stack = bench_stack(args)
+        log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step; index scan "
+            f"{stack['roofline']['achieved']:.0f} GB/s ({stack['roofline']['frac'] * 100:.1f}% of HBM)")
     if dec is None:                      # prefill-only profiler run
         print(json.dumps({"workload": "prefill", "prefill": pre}), flush=True)
         return
@@ -515,6 +610,7 @@ def main():
         "eager": dec["eager"],
         "kernels": dec["kernels"],
         "prefill": pre,
+        "decode_262k_stack": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

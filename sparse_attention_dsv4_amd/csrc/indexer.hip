@@ -99,8 +99,8 @@ index_score_kernel(ScoreArgs<T> a, SeqInts pos0, SeqInts n_rows) {
 
 
 // ------------------------------------------------------------------ mfma scoring
-// Queries per wave in prefill scoring: one keeps 3 waves per SIMD resident (146 VGPRs),
-// which hides LDS and epilogue latency better than two (operand reuse, 1 wave per SIMD).
+// Queries per wave in prefill scoring: one (226 VGPRs, two waves per SIMD) hides LDS and
+// epilogue latency better than two (more operand reuse, but one wave per SIMD).
 #ifndef DSV4_IDX_QPW
 #define DSV4_IDX_QPW 1
 #endif
@@ -109,6 +109,10 @@ constexpr int kIdxQpw = DSV4_IDX_QPW;
 #define DSV4_IDX_WAVES 8
 #endif
 constexpr int kIdxWaves = DSV4_IDX_WAVES;   // waves per prefill workgroup (one query each)
+#ifndef DSV4_IDX_DEC_WGS
+#define DSV4_IDX_DEC_WGS 256
+#endif
+constexpr int64_t kIdxDecodeWgs = DSV4_IDX_DEC_WGS;   // decode scoring workgroups (all queries)
 
 #ifndef DSV4_IDX_STAGES
 #define DSV4_IDX_STAGES 4
@@ -462,9 +466,10 @@ topk_select_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
 // ------------------------------------------------------------------ exact top-k select
 // Radix select of the k-th largest key of the query's visible prefix, then compaction in
 // row order (helpers first: block-wide scan and bucket search over a histogram).
-constexpr int kSelRegThreads = 512;
+constexpr int64_t kSelRegMaxRows = 1024 * 68;   // largest lane the register select holds
 
-// Exclusive prefix sum over the workgroup (kSelRegThreads threads); `tmp` holds 8 ints.
+// Exclusive prefix sum over a workgroup of NT threads; `tmp` holds NT / 64 ints.
+template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
@@ -478,7 +483,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     __syncthreads();
     int add = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kSelRegThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         tot += tmp[i];
         add += i < w ? tmp[i] : 0;
     }
@@ -488,14 +493,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 
 // Given a histogram of `bins` bins and the count `rem` still needed from the keys it covers,
 // find the bin holding the rem-th largest key.  Writes the bin and the count still needed
-// inside it to sh[0], sh[1].
+// inside it to sh[0], sh[1].  NT threads, bins a multiple of NT.
+template <int NT>
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int rem, int* tmp, int* sh) {
-    const int per = bins / kSelRegThreads;            // 4 or 2 bins per thread
+    const int per = bins / NT;                        // 1 to 4 bins per thread
     const int t = threadIdx.x;
     int part = 0;
     for (int i = 0; i < per; ++i) part += int(hist[t * per + i]);
     int total;
-    const int excl = block_excl_scan(part, tmp, &total);
+    const int excl = block_excl_scan<NT>(part, tmp, &total);
     int above = total - excl - part;                  // keys in bins above this thread's bins
     for (int i = per - 1; i >= 0; --i) {
         const int h = int(hist[t * per + i]);
@@ -509,7 +515,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int 
 }
 
 // ------------------------------------------------------------------ select with keys in registers
-// For up to 512 * KPT visible rows.  Wave w owns the contiguous key range [w C, (w+1) C),
+// For up to NT * KPT visible rows (NT threads).  Wave w owns the contiguous key range [w C, (w+1) C),
 // C = 64 KPT; within it lane l holds groups of 4 consecutive keys at w C + 256 i + 4 l, read
 // with one 16-byte load each (a wave instruction reads 1 KB contiguous).  The three radix
 // passes (11, 11, 10 bits) histogram the keys straight from registers; the compaction walks
@@ -530,14 +536,14 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-template <int KPT>
-__global__ void __launch_bounds__(kSelRegThreads)
+template <int KPT, int NT>
+__global__ void __launch_bounds__(NT)
 topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     constexpr int G = KPT / 4;                         // groups of 4 keys per lane
     __shared__ uint32_t hist[2048];
-    __shared__ int tmp[8];
+    __shared__ int tmp[NT / 64];
     __shared__ int sh[4];
-    __shared__ int wtot[2][kSelRegThreads / 64];
+    __shared__ int wtot[2][NT / 64];
     const int b = blockIdx.y;
     const int s = blockIdx.x;
     const int p = pos0.v[b] + s;
@@ -563,35 +569,37 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
         key[4 * i + 2] = j + 2 < nv ? v.z : 0u;
         key[4 * i + 3] = j + 3 < nv ? v.w : 0u;
     }
-    auto valid = [&](int e) { return wbase + 256 * (e >> 2) + (e & 3) < nv; };
-    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
+    // a row past nv holds key 0, which no score maps to (score_key gives 0 only to the NaN
+    // with every bit set), so validity is a compare with 0 rather than a position test
+    auto valid = [&](int e) { return key[e] != 0u; };
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 1: bits 31..21
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
         if (valid(e)) atomicAdd(&hist[key[e] >> 21], 1u);
     __syncthreads();
-    find_bucket(hist, 2048, a.k, tmp, sh);
+    find_bucket<NT>(hist, 2048, a.k, tmp, sh);
     const uint32_t d1 = uint32_t(sh[0]);
     int rem = sh[1];
-    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 2: bits 20..10 of the keys in bucket d1
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
         if (valid(e) && (key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
     __syncthreads();
-    find_bucket(hist, 2048, rem, tmp, sh);
+    find_bucket<NT>(hist, 2048, rem, tmp, sh);
     const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
     rem = sh[1];
-    for (int i = tid; i < 2048; i += kSelRegThreads) hist[i] = 0;
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 3: bits 9..0 of the keys with prefix (d1, d2)
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
         if (valid(e) && (key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
     __syncthreads();
-    find_bucket(hist, 1024, rem, tmp, sh);
+    find_bucket<NT>(hist, 1024, rem, tmp, sh);
     const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
     rem = sh[1];                                       // rows with key == thr still to take
 
@@ -671,8 +679,11 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             constexpr int QG = kIdxWaves * kIdxQpw;        // queries per prefill workgroup
             const bool perq = j.S >= QG;
             const int64_t groups = perq ? (j.S + QG - 1) / QG : j.S;
-            // enough row blocks to give the chip >= ~2048 workgroups
-            int64_t blocks = (2048 + groups * nb - 1) / (groups * nb);
+            // enough row blocks to give the chip >= ~2048 workgroups in prefill; in decode (one
+            // query per group) fewer, longer blocks, so each streams several tiles through
+            // the copy ring and loads its query once
+            const int64_t want_wgs = perq ? 2048 : kIdxDecodeWgs;
+            int64_t blocks = (want_wgs + groups * nb - 1) / (groups * nb);
             const int64_t tiles = (nv_max + IRT - 1) / IRT;
             if (blocks > tiles) blocks = tiles;
             if (blocks < 1) blocks = 1;
@@ -708,12 +719,17 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.k = j.k; sa.r = j.r; sa.S = j.S; sa.n_stride = j.n_stride;
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
-        if (nv_max <= int64_t(kSelRegThreads) * 32) {
-            DSV4_LAUNCH("topk_select_reg", topk_select_reg_kernel<32>, dim3(unsigned(j.S), nb),
-                               dim3(kSelRegThreads), 0, st, sa, pos, nr);
-        } else if (nv_max <= int64_t(kSelRegThreads) * 64) {
-            DSV4_LAUNCH("topk_select_reg", topk_select_reg_kernel<64>, dim3(unsigned(j.S), nb),
-                               dim3(kSelRegThreads), 0, st, sa, pos, nr);
+        // keys in registers: 512 threads x 32 or 64 keys, 1024 threads x 68 keys (69,632 rows,
+        // which covers a 262,144-token ratio-4 lane plus its decode steps); beyond, in memory
+        if (nv_max <= 512 * 32) {
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<32, 512>), dim3(unsigned(j.S), nb),
+                               dim3(512), 0, st, sa, pos, nr);
+        } else if (nv_max <= 512 * 64) {
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<64, 512>), dim3(unsigned(j.S), nb),
+                               dim3(512), 0, st, sa, pos, nr);
+        } else if (nv_max <= kSelRegMaxRows) {
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<68, 1024>), dim3(unsigned(j.S), nb),
+                               dim3(1024), 0, st, sa, pos, nr);
         } else {
             DSV4_LAUNCH("topk_select", topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
                                st, sa, pos, nr);

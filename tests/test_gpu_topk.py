@@ -1,5 +1,6 @@
-"""Indexer top-k through the C ABI at row counts that reach every selection kernel, and
-with massive exact ties (needs a gfx950 GPU).
+"""Indexer top-k through the C ABI at row counts that reach every selection kernel (keys in
+registers up to 16,384 / 32,768 / 69,632 rows, in memory beyond), and with massive exact ties
+(needs a gfx950 GPU).
 
 The indexer rows are drawn directly (the index call takes them as input), so the oracle only
 scores and selects: fp32 scores, the k largest, ties to the lower row, ascending output.
@@ -52,7 +53,7 @@ def _check(rows_i, qi, w, positions, sel, exact):
             assert nbad == 0, bad[:4]
 
 
-@pytest.mark.parametrize("n_vis", [16384, 20001, 32768, 33001])
+@pytest.mark.parametrize("n_vis", [16384, 20001, 32768, 33001, 65600, 69632, 69633])
 def test_topk_large_lanes(n_vis):
     B, S = 2, 3
     cap = n_vis + 8
