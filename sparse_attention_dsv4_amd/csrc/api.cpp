@@ -228,6 +228,7 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
     j.bf16 = cfg->dtype == DSV4_BF16;
     j.qi = qi; j.w = w; j.rows = idx_rows; j.row_cap = row_cap; j.S = s;
     j.n_stride = dsv4::index_key_stride(n_max);
+    j.n_max = n_max;
     j.batch = batch; j.n_rows = n_rows; j.pos0 = pos0; j.sel = sel;
     j.keys = static_cast<uint32_t*>(ws);
     return hip_status(dsv4::launch_index_topk(j, static_cast<hipStream_t>(stream)), "index_topk");

@@ -374,6 +374,9 @@ struct SelArgs {
     int64_t n_stride;
     const uint32_t* keys;
     int32_t* sel;
+    int32_t* cand;             // split selection: [B][S][n_chunks][k] candidate rows
+    uint32_t* cand_key;        // and their keys (0 for a -1 candidate)
+    int chunk, n_chunks;       // rows per chunk, chunks per query
 };
 
 // One workgroup selects for one query.
@@ -519,24 +522,22 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int 
 // C = 64 KPT; within it lane l holds groups of 4 consecutive keys at w C + 256 i + 4 l, read
 // with one 16-byte load each (a wave instruction reads 1 KB contiguous).  The three radix
 // passes (11, 11, 10 bits) histogram the keys straight from registers; the compaction walks
-// each wave's groups in row order, with lane prefix sums giving every taken row its slot.
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+// each wave's groups in row order, with lane-mask bit counts giving every taken row its slot.
+// Number of set bits of a wave mask in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
+// Split selection, for few queries over many rows: stage 1 (SEL_CHUNK) selects the k best of
+// each chunk of a.chunk rows into a candidate list, stage 2 (SEL_MERGE) the k best of those
+// candidates.  The order (key descending, then row ascending) is total, so a row among a
+// query's k best is among the k best of its chunk, and the candidate lists, chunk after chunk
+// and ascending within one, are in row order: the lower position wins a tie, and the rows
+// come out ascending.  Stage 1 stores each candidate's key beside its row; a candidate -1 (a
+// chunk with k rows or fewer) has key 0.
+enum SelMode { SEL_DIRECT = 0, SEL_CHUNK = 1, SEL_MERGE = 2 };
 
-template <int KPT, int NT>
+template <int KPT, int NT, int MODE>
 __global__ void __launch_bounds__(NT)
 topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     constexpr int G = KPT / 4;                         // groups of 4 keys per lane
@@ -549,35 +550,71 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     const int p = pos0.v[b] + s;
     int nv = (p + 1) / a.r;
     if (nv > n_rows.v[b]) nv = n_rows.v[b];
-    int32_t* out = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
+    const size_t q = size_t(b) * a.S + size_t(s);
+    const uint32_t* gk = a.keys + q * a.n_stride;
+    const size_t cbase = q * size_t(a.n_chunks) * a.k;   // this query's candidates
+    const int32_t* cq = a.cand + cbase;
+    int32_t* out = a.sel + q * a.k;
+    uint32_t* okey = nullptr;                          // stage 1: keys of the candidates
+    int base = 0;                                      // row of key 0 (stage 1)
+    int n = nv;                                        // keys selected among
+    if (MODE == SEL_CHUNK) {
+        base = int(blockIdx.z) * a.chunk;
+        n = nv - base < a.chunk ? nv - base : a.chunk;
+        n = n > 0 ? n : 0;
+        gk += base;
+        out = a.cand + cbase + blockIdx.z * size_t(a.k);
+        okey = a.cand_key + cbase + blockIdx.z * size_t(a.k);
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (nv <= a.k) {
-        for (int i = tid; i < a.k; i += blockDim.x) out[i] = i < nv ? i : -1;
+    if (n <= a.k) {
+        for (int i = tid; i < a.k; i += blockDim.x) {
+            out[i] = i < n ? base + i : -1;
+            if (MODE == SEL_CHUNK) okey[i] = i < n ? gk[i] : 0u;
+        }
         return;
     }
-    // keys (0 for rows past nv; they are never counted)
-    const uint32_t* gk = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
+    if (MODE == SEL_MERGE) n = a.n_chunks * a.k;       // candidate positions
+    // keys (0 past n)
     const int wbase = w * 64 * KPT + 4 * lane;
     uint32_t key[KPT];
+    int32_t crow[KPT];                                 // stage 2: the candidates' rows
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int j = wbase + 256 * i;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (j < nv) v = *reinterpret_cast<const uint4*>(gk + j);   // in the row: stride % 4 == 0
-        key[4 * i + 0] = v.x;
-        key[4 * i + 1] = j + 1 < nv ? v.y : 0u;
-        key[4 * i + 2] = j + 2 < nv ? v.z : 0u;
-        key[4 * i + 3] = j + 3 < nv ? v.w : 0u;
+        if (MODE == SEL_MERGE) {
+            const uint32_t* ck = a.cand_key + cbase;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                key[4 * i + e] = j + e < n ? ck[j + e] : 0u;
+                crow[4 * i + e] = j + e < n ? cq[j + e] : -1;
+            }
+        } else {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (j < n) v = *reinterpret_cast<const uint4*>(gk + j);   // stride, chunk % 4 == 0
+            key[4 * i + 0] = v.x;
+            key[4 * i + 1] = j + 1 < n ? v.y : 0u;
+            key[4 * i + 2] = j + 2 < n ? v.z : 0u;
+            key[4 * i + 3] = j + 3 < n ? v.w : 0u;
+        }
     }
-    // a row past nv holds key 0, which no score maps to (score_key gives 0 only to the NaN
-    // with every bit set), so validity is a compare with 0 rather than a position test
-    auto valid = [&](int e) { return key[e] != 0u; };
+    // A row past n holds key 0, below the key of every score (score_key gives 0 only to the
+    // NaN with every bit set).  The passes skip a wave's groups of 4 x 64 rows that lie wholly
+    // past n and count the other zeros as keys of value 0: as at least k valid keys lie above
+    // 0, the k-th largest key is a valid row's, every bin count above it is that of the valid
+    // rows alone, and the compaction takes only keys >= thr > 0.  No per-key validity test is
+    // then needed.
+    const int ngv = __builtin_amdgcn_readfirstlane(
+        max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a row below n
     for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 1: bits 31..21
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        if (valid(e)) atomicAdd(&hist[key[e] >> 21], 1u);
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e) atomicAdd(&hist[key[e] >> 21], 1u);
+        }
     __syncthreads();
     find_bucket<NT>(hist, 2048, a.k, tmp, sh);
     const uint32_t d1 = uint32_t(sh[0]);
@@ -586,8 +623,12 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     __syncthreads();
     // pass 2: bits 20..10 of the keys in bucket d1
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        if (valid(e) && (key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e)
+                if ((key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
+        }
     __syncthreads();
     find_bucket<NT>(hist, 2048, rem, tmp, sh);
     const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
@@ -596,22 +637,26 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     __syncthreads();
     // pass 3: bits 9..0 of the keys with prefix (d1, d2)
 #pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        if (valid(e) && (key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e)
+                if ((key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
+        }
     __syncthreads();
     find_bucket<NT>(hist, 1024, rem, tmp, sh);
     const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
     rem = sh[1];                                       // rows with key == thr still to take
 
-    // compaction in row order: wave totals first, then each wave walks its groups
+    // Compaction in row order.  Lane masks (the compare results themselves) give every count: wave totals
+    // first, then each wave walks its groups of 4 x 64 rows, where row 4 l + j of a group is
+    // key j of lane l, so the rows before it are those of lower lanes and its own lower j.
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        ngt += valid(e) && key[e] > thr;
-        neq += valid(e) && key[e] == thr;
+        ngt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
+        neq += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] == thr)));
     }
-    ngt = wave_sum_int(ngt);
-    neq = wave_sum_int(neq);
     if (lane == 0) {
         wtot[0][w] = ngt;
         wtot[1][w] = neq;
@@ -625,35 +670,67 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     o += eqb < rem ? eqb : rem;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        int ge = 0;
+        uint64_t em[4], any = 0;
 #pragma unroll
-        for (int e = 4 * i; e < 4 * i + 4; ++e) ge += valid(e) && key[e] == thr;
-        const int ge_incl = wave_incl_scan(ge);
-        int eq_rank = eqb + ge_incl - ge;               // ties before this lane's first key
-        int mask = 0;
-#pragma unroll
-        for (int e = 4 * i; e < 4 * i + 4; ++e) {
-            const bool v = valid(e);
-            const bool gt = v && key[e] > thr;
-            const bool eq = v && key[e] == thr;
-            const bool take = gt || (eq && eq_rank < rem);
-            eq_rank += eq;
-            mask |= int(take) << (e - 4 * i);
+        for (int j = 0; j < 4; ++j) {
+            em[j] = __builtin_amdgcn_ballot_w64(key[4 * i + j] == thr);
+            any |= em[j] | __builtin_amdgcn_ballot_w64(key[4 * i + j] > thr);
         }
-        const int nt = __popc(mask);
-        const int nt_incl = wave_incl_scan(nt);
-        int slot = o + nt_incl - nt;
+        if (any == 0) continue;                        // nothing taken in this group
+        int eq_rank = eqb;                             // ties before this lane's first key
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eq_rank += lanes_below(em[j]);
+        bool take[4];
+        int slot = o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool eq = key[4 * i + j] == thr;
+            take[j] = key[4 * i + j] > thr || (eq && eq_rank < rem);
+            eq_rank += eq;
+            const uint64_t tm = __builtin_amdgcn_ballot_w64(take[j]);
+            slot += lanes_below(tm);
+            o += int(__popcll(tm));
+            eqb += int(__popcll(em[j]));
+        }
         const int j0 = wbase + 256 * i;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (mask & (1 << e)) out[slot++] = j0 + e;
-        o += __shfl(nt_incl, 63, 64);
-        eqb += __shfl(ge_incl, 63, 64);
+        for (int j = 0; j < 4; ++j)
+            if (take[j]) {
+                if (MODE == SEL_CHUNK) okey[slot] = key[4 * i + j];
+                out[slot++] = MODE == SEL_MERGE ? crow[4 * i + j] : base + j0 + j;
+            }
     }
+}
+
+#ifndef DSV4_TOPK_CHUNK
+#define DSV4_TOPK_CHUNK 8192
+#endif
+constexpr int kSelChunk = DSV4_TOPK_CHUNK;           // rows per chunk of a split selection
+static_assert(kSelChunk % 2048 == 0 && kSelChunk <= 512 * 64, "chunk: 512 threads x 4k keys");
+#ifndef DSV4_TOPK_MERGE_THREADS
+#define DSV4_TOPK_MERGE_THREADS 512
+#endif
+constexpr int kMergeThreads = DSV4_TOPK_MERGE_THREADS;   // workgroup of the merge stage
+
+// Chunks per query of a split selection, 0 for one workgroup per query.  The split pays where
+// a call has too few queries to fill the chip (at most 64) and many rows each (above 16,384),
+// and its merge stage holds all n_chunks x k candidates in registers (64 per thread).
+int64_t topk_chunks(int64_t queries, int64_t n_max, int k) {
+    if (queries > 64 || n_max <= 16384) return 0;
+    const int64_t c = (n_max + kSelChunk - 1) / kSelChunk;
+    return c * k <= kMergeThreads * 64 ? c : 0;
+}
+
+// Bytes of the score-key part of the workspace (the candidate lists follow, 256-aligned).
+size_t index_keys_bytes(int batch, int64_t S, int64_t n_stride) {
+    return (size_t(batch) * size_t(S) * size_t(n_stride) * sizeof(uint32_t) + 255) & ~size_t(255);
 }
 
 template <typename T>
 hipError_t run(const IndexJob& j, hipStream_t st) {
+    const int64_t n_chunks = topk_chunks(int64_t(j.batch) * j.S, j.n_max, j.k);
+    int32_t* cand = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(j.keys) +
+                                               index_keys_bytes(j.batch, j.S, j.n_stride));
     for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
         const int nb = std::min(kSeqSlice, j.batch - b0);
         SeqInts pos{}, nr{};
@@ -719,20 +796,46 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.k = j.k; sa.r = j.r; sa.S = j.S; sa.n_stride = j.n_stride;
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
-        // keys in registers: 512 threads x 32 or 64 keys, 1024 threads x 68 keys (69,632 rows,
-        // which covers a 262,144-token ratio-4 lane plus its decode steps); beyond, in memory
-        if (nv_max <= 512 * 32) {
-            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<32, 512>), dim3(unsigned(j.S), nb),
-                               dim3(512), 0, st, sa, pos, nr);
+        sa.chunk = kSelChunk;
+        sa.n_chunks = int(n_chunks);
+        sa.cand = cand + qoff * size_t(n_chunks) * j.k;
+        sa.cand_key = reinterpret_cast<uint32_t*>(cand + size_t(j.batch) * j.S * n_chunks * j.k) +
+                      qoff * size_t(n_chunks) * j.k;
+        if (n_chunks > 0) {
+            // stage 1 over (query, chunk), stage 2 over the n_chunks x k candidates
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<kSelChunk / 512, 512, SEL_CHUNK>),
+                        dim3(unsigned(j.S), nb, unsigned(n_chunks)), dim3(512), 0, st, sa, pos, nr);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t nc = n_chunks * j.k;
+            constexpr int MT = kMergeThreads;
+            if (nc <= MT * 8)
+                DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<8, MT, SEL_MERGE>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+            else if (nc <= MT * 16)
+                DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<16, MT, SEL_MERGE>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+            else if (nc <= MT * 32)
+                DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<32, MT, SEL_MERGE>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+            else
+                DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<64, MT, SEL_MERGE>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+        } else if (nv_max <= 512 * 32) {
+            // keys in registers: 512 threads x 32 or 64 keys, 1024 threads x 68 keys (69,632
+            // rows, which covers a 262,144-token ratio-4 lane plus its decode steps); beyond,
+            // in memory
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<32, 512, SEL_DIRECT>),
+                        dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
         } else if (nv_max <= 512 * 64) {
-            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<64, 512>), dim3(unsigned(j.S), nb),
-                               dim3(512), 0, st, sa, pos, nr);
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<64, 512, SEL_DIRECT>),
+                        dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
         } else if (nv_max <= kSelRegMaxRows) {
-            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<68, 1024>), dim3(unsigned(j.S), nb),
-                               dim3(1024), 0, st, sa, pos, nr);
+            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<68, 1024, SEL_DIRECT>),
+                        dim3(unsigned(j.S), nb), dim3(1024), 0, st, sa, pos, nr);
         } else {
             DSV4_LAUNCH("topk_select", topk_select_kernel, dim3(unsigned(j.S), nb), dim3(kSelThreads), 0,
-                               st, sa, pos, nr);
+                        st, sa, pos, nr);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -745,8 +848,10 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
 int64_t index_key_stride(int64_t n_max) { return ((n_max < 1 ? 1 : n_max) + 3) & ~int64_t(3); }
 
 size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max) {
-    (void)Hi; (void)di; (void)k;
-    return size_t(batch) * size_t(S) * size_t(index_key_stride(n_max)) * sizeof(uint32_t);
+    (void)Hi; (void)di;
+    const int64_t c = topk_chunks(int64_t(batch) * S, n_max, k);
+    return index_keys_bytes(batch, S, index_key_stride(n_max)) +
+           2 * size_t(batch) * size_t(S) * size_t(c) * size_t(k) * sizeof(int32_t);
 }
 
 hipError_t launch_index_topk(const IndexJob& j, hipStream_t s) {

@@ -35,11 +35,12 @@ struct IndexJob {
     int64_t row_cap;
     int64_t S;
     int64_t n_stride;          // row stride of the score workspace (>= max n_rows)
+    int64_t n_max;             // max n_rows, as given to index_workspace_bytes
     int batch;
     const int64_t* n_rows;     // host [B]
     const int64_t* pos0;       // host [B]
     int32_t* sel;              // [B][S][k]
-    uint32_t* keys;            // workspace [B][S][n_stride]
+    uint32_t* keys;            // workspace: keys [B][S][n_stride], then candidate lists
 };
 hipError_t launch_index_topk(const IndexJob& j, hipStream_t s);
 size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max);

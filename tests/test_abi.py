@@ -97,8 +97,13 @@ def test_index_validation(L):
     assert _index(L, cfg, ws=None) == EWS
     assert _index(L, cfg, ws=ctypes.c_void_p(FAKE.value + 4)) == EINVAL    # key rows need 16 B
     assert "aligned" in L.dsv4_last_error().decode()
-    # key rows are padded to a multiple of 4 keys
-    assert K.dsv4_index_workspace_bytes(cfg, 2, 3, 601) == 2 * 3 * 604 * 4
+    # key rows are padded to a multiple of 4 keys, the key block to 256 bytes
+    assert K.dsv4_index_workspace_bytes(cfg, 2, 3, 601) == 2 * 3 * 604 * 4 + 96
+    # few queries over many rows add k candidate rows and keys per 8192-row chunk (split
+    # selection)
+    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 65536) == 4 * 65536 * 4 + 2 * 4 * 8 * 512 * 4
+    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 16384) == 4 * 16384 * 4
+    assert K.dsv4_index_workspace_bytes(cfg, 65, 1, 65536) == 65 * 65536 * 4
     assert _index(L, cfg, sel=None) == EINVAL
     assert _index(L, cfg, s=70000) == EUNSUP
     assert _index(L, cfg, s=0, qi=None) == 0

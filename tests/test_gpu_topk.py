@@ -53,9 +53,13 @@ def _check(rows_i, qi, w, positions, sel, exact):
             assert nbad == 0, bad[:4]
 
 
-@pytest.mark.parametrize("n_vis", [16384, 20001, 32768, 33001, 65600, 69632, 69633])
-def test_topk_large_lanes(n_vis):
-    B, S = 2, 3
+@pytest.mark.parametrize("queries", ["few", "many"])
+@pytest.mark.parametrize("n_vis", [16384, 16684, 20001, 32768, 33001, 65600, 69632, 69633])
+def test_topk_large_lanes(n_vis, queries):
+    """Few queries (6) over more than 16,384 rows take the split selection (k best per
+    8192-row chunk, then of the candidates; 16,684 leaves a last chunk of k rows or fewer);
+    many (65 in one sequence) take one workgroup per query."""
+    B, S = (2, 3) if queries == "few" else (1, 65)
     cap = n_vis + 8
     g = 11 + n_vis
     rows_i = synth.normal((B, cap, SPEC.index_dim), seed=g, stream="rows_i", dtype=torch.bfloat16,
@@ -70,10 +74,13 @@ def test_topk_large_lanes(n_vis):
     _check(rows_i, qi, w, positions, sel, exact=False)
 
 
-def test_topk_exact_ties_take_lower_rows():
+@pytest.mark.parametrize("n_vis,S", [(12000, 2), (30000, 2), (80000, 2), (30000, 40),
+                                     (60000, 40), (80000, 40)])
+def test_topk_exact_ties_take_lower_rows(n_vis, S):
     """Rows repeat with period 7, so the scores take 7 values and the k-th score sits inside
-    a block of ~1/7 of the rows: the selection must take the lowest rows of that block."""
-    B, S, n_vis = 2, 2, 12000
+    a block of ~1/7 of the rows: the selection must take the lowest rows of that block.  The
+    row counts and query counts (4 or 80 per call) reach each selection kernel, split or not."""
+    B = 2
     cap = n_vis
     base = synth.normal((7, SPEC.index_dim), seed=3, stream="base", dtype=torch.bfloat16,
                         device="cuda")
