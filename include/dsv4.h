@@ -178,6 +178,34 @@ int dsv4_csa_attn_decode(const dsv4_attn_cfg* cfg, const void* q, const void* kv
                          const float* sinks, void* out, int32_t batch, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* A compressor lane's decode step folded into dsv4_csa_attn_decode_store. */
+typedef struct {
+    const dsv4_comp_cfg* cfg;  /* the lane's compressor (ratio and dtype as the attention's)  */
+    void* state;               /* [batch] frontier states, as dsv4_compress_step              */
+    const void* kv_lane;       /* [batch, coff*D] kv lane of token pos[b]                     */
+    const void* gate_lane;     /* [batch, coff*D] gate lane of the same token                 */
+} dsv4_frontier_store;
+
+/* Decode attention (as dsv4_csa_attn_decode) together with the compressor steps of the same
+ * token for n_stores lanes (0..2: the attention lane and the indexer lane), for a step at
+ * which no sequence completes a compressed row: (pos[b] + 1) % ratio != 0 for every b.  Such
+ * a step only stores the token's lanes in the frontier state (dsv4_compress_step writes no
+ * row then), which nothing in the attention reads, so the stores ride in the attention
+ * launch instead of one launch per lane.  The result is bit for bit that of
+ * dsv4_compress_step for each lane (len_before = pos) followed by dsv4_csa_attn_decode.
+ * Pages: MTPLX PR #216 "What V4 adds" (the compressor frontier carried across decode steps;
+ * a row is emitted only when its window completes).
+ * Errors: as dsv4_csa_attn_decode; EINVAL also for n_stores outside 0..2, a NULL store
+ * pointer, a store whose cfg is invalid or whose ratio or dtype differs from cfg's, or a
+ * sequence that completes a row at pos[b] (call dsv4_compress_step, then
+ * dsv4_csa_attn_decode).  Nothing is launched on an error. */
+int dsv4_csa_attn_decode_store(const dsv4_attn_cfg* cfg, const void* q, const void* kv_new,
+                               void* win_ring, const void* rows, int64_t row_cap,
+                               const int32_t* sel, const int64_t* n_rows, const int64_t* pos,
+                               const float* sinks, void* out, int32_t batch, void* ws,
+                               size_t ws_bytes, const dsv4_frontier_store* stores,
+                               int32_t n_stores, void* stream);
+
 /* Prefill attention for s queries per sequence at positions pos0[b] .. pos0[b]+s-1.
  *   q       [batch, s, H, D];  kv_new [batch, s, D] latents of those tokens
  *   win_ring as in decode, holding the W tokens before pos0[b]; after the call it holds

@@ -18,8 +18,8 @@ __all__ = [
     "Dsv4Error", "CompCfg", "IndexCfg", "AttnCfg", "lib", "lib_path",
     "dsv4_version", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
-    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_prefill",
-    "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
+    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
+    "dsv4_csa_attn_prefill", "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -30,8 +30,9 @@ lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4.so"
 EXPORTED_SYMBOLS = (
     "dsv4_version", "dsv4_last_error", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
-    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_prefill", "dsv4_trace_enable",
-    "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernel_name",
+    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
+    "dsv4_csa_attn_prefill", "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read",
+    "dsv4_trace_kernel_name",
 )
 
 
@@ -55,6 +56,11 @@ class _AttnCfg(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("ratio", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32)]
+
+
+class _FrontierStore(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(_CompCfg)), ("state", ctypes.c_void_p),
+                ("kv_lane", ctypes.c_void_p), ("gate_lane", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -133,6 +139,9 @@ def lib():
         L.dsv4_csa_attn_decode.argtypes = [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, ctypes.c_int64,
                                            _P, _I64P, _I64P, _P, _P, ctypes.c_int32, _P,
                                            ctypes.c_size_t, _P]
+        L.dsv4_csa_attn_decode_store.argtypes = [
+            ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, ctypes.c_int64, _P, _I64P, _I64P, _P, _P,
+            ctypes.c_int32, _P, ctypes.c_size_t, ctypes.POINTER(_FrontierStore), ctypes.c_int32, _P]
         L.dsv4_csa_attn_prefill.argtypes = [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, ctypes.c_int64,
                                             _P, _I64P, _I64P, _P, _P, ctypes.c_int32, ctypes.c_int64,
                                             _P, ctypes.c_size_t, _P]
@@ -287,6 +296,36 @@ def dsv4_csa_attn_decode(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_rows, p
         _ptr(sel), _host_i64(n_rows, B, "n_rows") if cfg.ratio > 0 else None,
         _host_i64(pos, B, "pos"), _ptr(sinks), _ptr(out), B, _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsv4_csa_attn_decode_store(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_rows, pos, sinks,
+                               out, stores, ws=None, stream=None):
+    """dsv4_csa_attn_decode, plus the compressor steps of the same token for the lanes in
+    ``stores``: a list of up to two (CompCfg, state, kv_lane [B, coff*D], gate_lane) -- for a
+    step at which no sequence completes a compressed row ((pos + 1) % ratio != 0)."""
+    B = q.shape[0]
+    _need(q, (B, cfg.heads, cfg.dim), cfg.dtype, "q")
+    _need(kv_new, (B, cfg.dim), cfg.dtype, "kv_new")
+    _need(win_ring, (B, cfg.window, cfg.dim), cfg.dtype, "win_ring")
+    _need(sinks, (cfg.heads,), torch.float32, "sinks")
+    _need(out, (B, cfg.heads, cfg.dim), cfg.dtype, "out")
+    _attn_common_checks(cfg, rows, sel, n_rows, B, (B, cfg.topk))
+    ccfgs = []
+    arr = (_FrontierStore * max(1, len(stores)))()
+    for i, (ccfg, state, kv_lane, gate_lane) in enumerate(stores):
+        W = ccfg.coff * ccfg.dim
+        _need(kv_lane, (B, W), ccfg.dtype, "kv_lane")
+        _need(gate_lane, (B, W), ccfg.dtype, "gate_lane")
+        _need(state, (B, dsv4_comp_state_bytes(ccfg, 1)), torch.uint8, "state")
+        ccfgs.append(ccfg.c())
+        arr[i] = _FrontierStore(ctypes.pointer(ccfgs[-1]), _ptr(state), _ptr(kv_lane), _ptr(gate_lane))
+    c = cfg.c()
+    _check(lib().dsv4_csa_attn_decode_store(
+        ctypes.byref(c), _ptr(q), _ptr(kv_new), _ptr(win_ring),
+        _ptr(rows) if cfg.ratio > 0 else None, rows.shape[1] if cfg.ratio > 0 else 0,
+        _ptr(sel), _host_i64(n_rows, B, "n_rows") if cfg.ratio > 0 else None,
+        _host_i64(pos, B, "pos"), _ptr(sinks), _ptr(out), B, _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), arr, len(stores), _stream(stream)))
 
 
 def dsv4_csa_attn_prefill(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_rows, pos0, sinks,

@@ -238,7 +238,8 @@ static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_n
                        void* win_ring, const void* rows, int64_t row_cap, const int32_t* sel,
                        const int64_t* n_rows, const int64_t* pos0, const float* sinks,
                        void* out, int32_t batch, int64_t s, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, const dsv4_frontier_store* stores = nullptr,
+                       int32_t n_stores = 0) {
     int st = check_attn_cfg(cfg);
     if (st) return st;
     if (batch < 0) return fail(DSV4_EINVAL, "batch %d < 0", batch);
@@ -275,12 +276,35 @@ static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_n
                                                       cfg->window, cfg->ratio, cfg->topk, batch, s);
     if (need_ws > 0 && (!ws || ws_bytes < need_ws))
         return fail(DSV4_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need_ws);
+    if (n_stores < 0 || n_stores > 2) return fail(DSV4_EINVAL, "n_stores %d outside 0..2", n_stores);
+    if (n_stores > 0 && !stores) return fail(DSV4_EINVAL, "stores is NULL");
+    dsv4::FrontierJob fronts[2];
+    for (int f = 0; f < n_stores; ++f) {
+        const dsv4_frontier_store& fs = stores[f];
+        if (!fs.cfg) return fail(DSV4_EINVAL, "stores[%d].cfg is NULL", f);
+        st = check_comp_cfg(fs.cfg);
+        if (st) return st;
+        if (fs.cfg->ratio != cfg->ratio || fs.cfg->dtype != cfg->dtype)
+            return fail(DSV4_EINVAL, "stores[%d]: ratio or dtype differs from the attention's", f);
+        if (!fs.state || !fs.kv_lane || !fs.gate_lane)
+            return fail(DSV4_EINVAL, "stores[%d]: NULL buffer pointer", f);
+        for (int b = 0; b < batch; ++b)
+            if ((pos0[b] + 1) % cfg->ratio == 0)
+                return fail(DSV4_EINVAL, "sequence %d completes row %lld at this step: call "
+                            "dsv4_compress_step, then dsv4_csa_attn_decode", b,
+                            (long long)((pos0[b] + 1) / cfg->ratio - 1));
+        const int coff = fs.cfg->overlap ? 2 : 1;
+        fronts[f].state = fs.state; fronts[f].lane_a = fs.kv_lane; fronts[f].lane_g = fs.gate_lane;
+        fronts[f].r = fs.cfg->ratio; fronts[f].coff = coff; fronts[f].W = coff * fs.cfg->dim;
+    }
     dsv4::AttnJob j;
     j.H = cfg->heads; j.D = cfg->dim; j.W = cfg->window; j.r = cfg->ratio; j.k = cfg->topk;
     j.scale = cfg->scale; j.bf16 = cfg->dtype == DSV4_BF16;
     j.q = q; j.kv_new = kv_new; j.ring = win_ring; j.rows = has_rows ? rows : nullptr;
     j.row_cap = row_cap; j.sel = sel; j.sinks = sinks; j.out = out; j.S = s; j.batch = batch;
     j.n_rows = has_rows ? n_rows : nullptr; j.pos0 = pos0; j.ws = ws; j.ws_bytes = ws_bytes;
+    j.n_fronts = n_stores;
+    for (int f = 0; f < n_stores; ++f) j.fronts[f] = fronts[f];
     return hip_status(dsv4::launch_attention(j, static_cast<hipStream_t>(stream)), "attention");
 }
 
@@ -291,6 +315,18 @@ int dsv4_csa_attn_decode(const dsv4_attn_cfg* cfg, const void* q, const void* kv
                          size_t ws_bytes, void* stream) {
     return attn_common(cfg, q, kv_new, win_ring, rows, row_cap, sel, n_rows, pos, sinks, out,
                        batch, 1, ws, ws_bytes, stream);
+}
+
+int dsv4_csa_attn_decode_store(const dsv4_attn_cfg* cfg, const void* q, const void* kv_new,
+                               void* win_ring, const void* rows, int64_t row_cap,
+                               const int32_t* sel, const int64_t* n_rows, const int64_t* pos,
+                               const float* sinks, void* out, int32_t batch, void* ws,
+                               size_t ws_bytes, const dsv4_frontier_store* stores,
+                               int32_t n_stores, void* stream) {
+    if (cfg && cfg->ratio <= 0 && n_stores > 0)
+        return fail(DSV4_EINVAL, "frontier stores given for a layer without a compressed lane");
+    return attn_common(cfg, q, kv_new, win_ring, rows, row_cap, sel, n_rows, pos, sinks, out,
+                       batch, 1, ws, ws_bytes, stream, stores, n_stores);
 }
 
 int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* kv_new,

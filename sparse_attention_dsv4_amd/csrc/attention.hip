@@ -255,6 +255,14 @@ struct AttnMfmaArgs {
     int keys_per_split, n_splits;
     float* part_ml;                       // [B][S][n_splits][H][2]  running max, sum
     float* part_o;                        // [B][S][n_splits][H][D]  unnormalised output
+    // decode: compressor frontier stores of this token (lanes of a step completing no row)
+    struct Front {
+        bf16* state;                      // [B][2][coff][r][W]
+        const bf16* a;                    // [B][W] kv lane, then gate lane
+        const bf16* g;
+        int r, coff, W;
+    } fr[2];
+    int n_fr;
 };
 
 // Barrier for LDS exchanges inside a tile: waits for this wave's LDS operations only, so
@@ -818,6 +826,19 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(c.ring) + size_t(uint32_t(p) % c.W) * MD);
         if (tid < MD / 8) dst[tid] = src[tid];
     }
+    if (split == 0 && hg >= 1 && hg <= a.n_fr) {
+        // the compressor step of this token for lane hg - 1, at a step that completes no row:
+        // its kv and gate lanes go to the token's frontier slot (nothing here reads the state)
+        const AttnMfmaArgs::Front f = hg == 1 ? a.fr[0] : a.fr[1];
+        bf16* sa = f.state + size_t(b) * (size_t(2) * f.coff * f.r * f.W) + frontier_slot(p, f.r, f.coff, f.W);
+        bf16* sg = sa + size_t(f.coff) * f.r * f.W;
+        const bf16* la = f.a + size_t(b) * f.W;
+        const bf16* lg = f.g + size_t(b) * f.W;
+        for (int c = tid; c < f.W; c += 256) {
+            sa[c] = la[c];
+            sg[c] = lg[c];
+        }
+    }
     if (kb0 >= nk) {
         if (tid < DHG) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
@@ -1062,6 +1083,16 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
             a.n_splits = decode_splits(nb, nrow_max + j.W, &a.keys_per_split);
         else
             a.n_splits = mfma_splits(int64_t(nb) * j.S, nrow_max + j.W, &a.keys_per_split);
+        a.n_fr = decode ? j.n_fronts : 0;
+        for (int f = 0; f < a.n_fr; ++f) {
+            const FrontierJob& fj = j.fronts[f];
+            a.fr[f].state = static_cast<bf16*>(fj.state) + size_t(b0) * 2 * fj.coff * fj.r * fj.W;
+            a.fr[f].a = static_cast<const bf16*>(fj.lane_a) + size_t(b0) * fj.W;
+            a.fr[f].g = static_cast<const bf16*>(fj.lane_g) + size_t(b0) * fj.W;
+            a.fr[f].r = fj.r;
+            a.fr[f].coff = fj.coff;
+            a.fr[f].W = fj.W;
+        }
         float* ws = static_cast<float*>(j.ws);
         a.part_ml = ws;
         a.part_o = ws + size_t(nb) * j.S * a.n_splits * MH * 2;
@@ -1121,6 +1152,11 @@ size_t attn_workspace_bytes(bool bf16_, int H, int D, int W, int r, int k, int b
 }
 
 hipError_t launch_attention(const AttnJob& j, hipStream_t s) {
+    if (use_mfma(j.bf16, j.H, j.D) && j.S == 1) return run_mfma(j, s);   // stores folded in
+    for (int f = 0; f < j.n_fronts; ++f) {
+        const hipError_t e = launch_frontier_store(j.fronts[f], j.bf16, j.batch, j.pos0, s);
+        if (e != hipSuccess) return e;
+    }
     if (use_mfma(j.bf16, j.H, j.D)) return run_mfma(j, s);
     return j.bf16 ? run<bf16>(j, s) : run<float>(j, s);
 }

@@ -148,8 +148,7 @@ compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
     const int64_t lb = len_before.v[b];
     const int W = a.coff * a.D;
     const size_t st = size_t(2) * a.coff * a.r * W;
-    const size_t slot = (size_t((lb / a.r) % a.coff) * a.r + size_t(lb % a.r)) * W;
-    T* sa = a.state + size_t(b) * st + slot;
+    T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.coff, W);
     T* sg = sa + size_t(a.coff) * a.r * W;
     for (int c = threadIdx.x; c < W; c += blockDim.x) {
         sa[c] = a.lane_a[size_t(b) * W + c];
@@ -170,13 +169,28 @@ compress_state_kernel(CompArgs<T> a, SeqInts len_before) {
     if (t >= la) return;
     const int W = a.coff * a.D;
     const size_t st = size_t(2) * a.coff * a.r * W;
-    const size_t slot = (size_t((t / a.r) % a.coff) * a.r + size_t(t % a.r)) * W;
     const size_t src = (size_t(b) * a.n_new + size_t(t - lb)) * W;
-    T* sa = a.state + size_t(b) * st + slot;
+    T* sa = a.state + size_t(b) * st + frontier_slot(t, a.r, a.coff, W);
     T* sg = sa + size_t(a.coff) * a.r * W;
     for (int c = threadIdx.x; c < W; c += blockDim.x) {
         sa[c] = a.lane_a[src + c];
         sg[c] = a.lane_g[src + c];
+    }
+}
+
+// The frontier store of a decode step alone (no row completes): one workgroup per sequence.
+template <typename T>
+__global__ void __launch_bounds__(kCompThreads)
+frontier_store_kernel(FrontierJob f, SeqInts pos) {
+    const int b = blockIdx.x;
+    const size_t st = size_t(2) * f.coff * f.r * f.W;
+    T* sa = static_cast<T*>(f.state) + size_t(b) * st + frontier_slot(pos.v[b], f.r, f.coff, f.W);
+    T* sg = sa + size_t(f.coff) * f.r * f.W;
+    const T* la = static_cast<const T*>(f.lane_a) + size_t(b) * f.W;
+    const T* lg = static_cast<const T*>(f.lane_g) + size_t(b) * f.W;
+    for (int c = threadIdx.x; c < f.W; c += blockDim.x) {
+        sa[c] = la[c];
+        sg[c] = lg[c];
     }
 }
 
@@ -246,6 +260,28 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
 
 hipError_t launch_compress(const CompressJob& j, hipStream_t s) {
     return j.bf16 ? run<bf16>(j, s) : run<float>(j, s);
+}
+
+hipError_t launch_frontier_store(const FrontierJob& f, bool bf16_, int batch, const int64_t* pos,
+                                 hipStream_t s) {
+    const size_t es = bf16_ ? sizeof(bf16) : sizeof(float);
+    const size_t st = size_t(2) * f.coff * f.r * f.W;
+    for (int b0 = 0; b0 < batch; b0 += kSeqSlice) {
+        const int nb = std::min(kSeqSlice, batch - b0);
+        SeqInts p{};
+        for (int i = 0; i < nb; ++i) p.v[i] = int32_t(pos[b0 + i]);
+        FrontierJob g = f;
+        g.state = static_cast<char*>(f.state) + size_t(b0) * st * es;
+        g.lane_a = static_cast<const char*>(f.lane_a) + size_t(b0) * f.W * es;
+        g.lane_g = static_cast<const char*>(f.lane_g) + size_t(b0) * f.W * es;
+        if (bf16_)
+            DSV4_LAUNCH("frontier_store", frontier_store_kernel<bf16>, dim3(nb), dim3(kCompThreads), 0, s, g, p);
+        else
+            DSV4_LAUNCH("frontier_store", frontier_store_kernel<float>, dim3(nb), dim3(kCompThreads), 0, s, g, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace dsv4

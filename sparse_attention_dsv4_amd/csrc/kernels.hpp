@@ -8,6 +8,23 @@
 
 namespace dsv4 {
 
+// Frontier state of one compressor lane for one sequence: [lane (kv, gate)][coff][r][coff*D]
+// elements.  Token t sits in window slot (t / r) % coff at position t % r; this is the
+// element offset of its kv-lane entry (the gate lane's is coff * r * coff*D further).
+__host__ __device__ inline size_t frontier_slot(int64_t t, int r, int coff, int W) {
+    return (size_t((t / r) % coff) * size_t(r) + size_t(t % r)) * size_t(W);
+}
+
+// One lane's frontier store of a decode step (the token's kv and gate lanes into its slot).
+struct FrontierJob {
+    void* state;               // [B][2][coff][r][coff*D]
+    const void* lane_a;        // [B][coff*D]
+    const void* lane_g;
+    int r, coff, W;            // W = coff*D
+};
+hipError_t launch_frontier_store(const FrontierJob& f, bool bf16, int batch, const int64_t* pos,
+                                 hipStream_t s);
+
 struct CompressJob {
     int r, coff, D, rd;
     float eps;
@@ -65,6 +82,8 @@ struct AttnJob {
     const int64_t* pos0;       // host [B]
     void* ws;
     size_t ws_bytes;
+    int n_fronts = 0;          // decode only: frontier stores folded into the launch
+    FrontierJob fronts[2];
 };
 hipError_t launch_attention(const AttnJob& j, hipStream_t s);
 size_t attn_workspace_bytes(bool bf16, int H, int D, int W, int r, int k, int batch, int64_t S);

@@ -9,7 +9,11 @@ row count always equals the attention lane's):
 
     compress (attention lane) -> compress (indexer lane) -> index_topk -> attention
 
-Host-side lengths are plain integers; nothing here computes any part of the layer.
+A decode step at which no sequence completes a compressed row only stores the token's
+lanes in the compressor frontiers, which neither the selection nor the attention reads: it
+goes as index_topk -> attention with the two frontier stores folded into the attention
+launch (``dsv4_csa_attn_decode_store``).  Host-side lengths are plain integers; nothing here
+computes any part of the layer.
 """
 from __future__ import annotations
 
@@ -18,8 +22,9 @@ from dataclasses import dataclass
 import torch
 
 from . import (AttnCfg, CompCfg, IndexCfg, dsv4_comp_state_bytes, dsv4_compress_prefill,
-               dsv4_compress_step, dsv4_csa_attn_decode, dsv4_csa_attn_prefill,
-               dsv4_index_topk, dsv4_index_workspace_bytes, dsv4_attn_workspace_bytes)
+               dsv4_compress_step, dsv4_csa_attn_decode, dsv4_csa_attn_decode_store,
+               dsv4_csa_attn_prefill, dsv4_index_topk, dsv4_index_workspace_bytes,
+               dsv4_attn_workspace_bytes)
 
 
 @dataclass(frozen=True)
@@ -77,8 +82,9 @@ class CsaLayer:
     """Device state of one layer for ``batch`` sequences of up to ``max_tokens`` tokens."""
 
     def __init__(self, spec: LayerSpec, batch: int, max_tokens: int, params: dict,
-                 device="cuda", max_chunk: int = 2048):
+                 device="cuda", max_chunk: int = 2048, fold_stores: bool = True):
         self.spec, self.batch, self.device = spec, batch, device
+        self.fold_stores = fold_stores        # decode: frontier stores ride in the attention
         self.params = params                  # ape, norm_w, ape_i, norm_w_i, inv_freq, sinks
         self.lengths = [0] * batch
         dt = spec.dtype
@@ -139,19 +145,33 @@ class CsaLayer:
         pos = list(self.lengths)
         out = torch.empty_like(tok["q"])
         sel = None
+        fold = (self.fold_stores and sp.has_rows and
+                all((p + 1) % sp.ratio != 0 for p in pos))   # no row completes at this step
+        stores = []
         if sp.has_rows:
-            dsv4_compress_step(sp.comp_cfg(), self.state, tok["a"], tok["g"], pos, P["ape"],
-                               P["norm_w"], P["inv_freq"], self.rows)
+            if fold:
+                stores.append((sp.comp_cfg(), self.state, tok["a"], tok["g"]))
+            else:
+                dsv4_compress_step(sp.comp_cfg(), self.state, tok["a"], tok["g"], pos, P["ape"],
+                                   P["norm_w"], P["inv_freq"], self.rows)
         if sp.has_indexer:
-            dsv4_compress_step(sp.index_comp_cfg(), self.state_i, tok["ai"], tok["gi"], pos,
-                               P["ape_i"], P["norm_w_i"], P["inv_freq"], self.rows_i)
+            if fold:
+                stores.append((sp.index_comp_cfg(), self.state_i, tok["ai"], tok["gi"]))
+            else:
+                dsv4_compress_step(sp.index_comp_cfg(), self.state_i, tok["ai"], tok["gi"], pos,
+                                   P["ape_i"], P["norm_w_i"], P["inv_freq"], self.rows_i)
             sel = sel_out if sel_out is not None else torch.empty(
                 self.batch, 1, sp.topk, dtype=torch.int32, device=self.device)
             dsv4_index_topk(sp.index_cfg(), tok["qi"][:, None], tok["w"][:, None], self.rows_i,
                             self.n_rows(1), pos, sel, self.ws_index)
             sel = sel[:, 0]
-        dsv4_csa_attn_decode(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
-                             self.rows if sp.has_rows else None, sel, self.n_rows(1), pos,
-                             P["sinks"], out, self.ws_attn)
+        if fold:
+            dsv4_csa_attn_decode_store(sp.attn_cfg(), tok["q"], tok["kv"], self.ring, self.rows,
+                                       sel, self.n_rows(1), pos, P["sinks"], out, stores,
+                                       self.ws_attn)
+        else:
+            dsv4_csa_attn_decode(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
+                                 self.rows if sp.has_rows else None, sel, self.n_rows(1), pos,
+                                 P["sinks"], out, self.ws_attn)
         self.lengths = [n + 1 for n in self.lengths]
         return out

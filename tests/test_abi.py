@@ -152,6 +152,48 @@ def test_attention_validation(L):
     assert _attn(L, cfg, batch=0, q=None) == 0
 
 
+def _store(L, cfg, stores, n=None, **kw):
+    """dsv4_csa_attn_decode_store with a valid decode call (ws big enough to pass the size
+    check) apart from the frontier stores; every case below fails validation."""
+    a = dict(q=FAKE, kv=FAKE, ring=FAKE, rows=FAKE, cap=1000, sel=FAKE, n_rows=_i64(600),
+             pos=_i64(2000), sinks=FAKE, out=FAKE, batch=1, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    c = cfg.c()
+    keep = [s_cfg.c() for s_cfg, *_ in stores]
+    arr = (K._FrontierStore * max(1, len(stores)))()
+    for i, (s_cfg, st, kv, g) in enumerate(stores):
+        arr[i] = K._FrontierStore(ctypes.pointer(keep[i]), st, kv, g)
+    return L.dsv4_csa_attn_decode_store(ctypes.byref(c), a["q"], a["kv"], a["ring"], a["rows"],
+                                        a["cap"], a["sel"], a["n_rows"], a["pos"], a["sinks"],
+                                        a["out"], a["batch"], a["ws"], a["ws_bytes"],
+                                        arr if stores or n is None else None,
+                                        len(stores) if n is None else n, None)
+
+
+def test_decode_store_validation(L):
+    cfg = K.AttnCfg(heads=64, dim=512, window=128, ratio=4, topk=512, scale=0.04)
+    lane = K.CompCfg(ratio=4, overlap=True, dim=512, rope_dim=64)
+    good = (lane, FAKE, FAKE, FAKE)
+    # position 2000: token 2000 does not complete a window ((2000 + 1) % 4 != 0), but the
+    # FAKE buffers never reach a launch because each case breaks one rule
+    assert _store(L, cfg, [good], pos=_i64(2003)) == EINVAL          # completes row 500
+    assert "dsv4_compress_step" in L.dsv4_last_error().decode()
+    assert _store(L, cfg, [good, good, good]) == EINVAL              # more than two lanes
+    assert _store(L, cfg, [], n=1) == EINVAL                         # stores NULL
+    assert _store(L, cfg, [(K.CompCfg(ratio=128, overlap=False, dim=512, rope_dim=64),
+                            FAKE, FAKE, FAKE)]) == EINVAL            # other ratio
+    assert _store(L, cfg, [(K.CompCfg(ratio=4, overlap=True, dim=512, rope_dim=64,
+                                      dtype=K.torch.float32), FAKE, FAKE, FAKE)]) == EINVAL
+    assert _store(L, cfg, [(lane, None, FAKE, FAKE)]) == EINVAL       # NULL state
+    assert _store(L, cfg, [(K.CompCfg(ratio=4, overlap=True, dim=0, rope_dim=0),
+                            FAKE, FAKE, FAKE)]) == EINVAL            # bad lane cfg
+    win = K.AttnCfg(heads=8, dim=64, window=16, ratio=0, topk=0, scale=0.1)
+    assert _store(L, win, [good], rows=None, n_rows=None, sel=None) == EINVAL
+    # the attention's own checks come first
+    assert _store(L, cfg, [good], q=None) == EINVAL
+    assert _store(L, cfg, [good], batch=0, q=None) == 0
+
+
 def test_trace_calls(L):
     K.dsv4_trace_reset()
     assert K.dsv4_trace_read("") == (0, 0.0)
