@@ -260,7 +260,8 @@ def bench_stack(args, seed=23):
         "kernels_ratio4_layer": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
                                  for n, v in per_kernel.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "index_score_mfma",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(TRAFFIC_STACK, "index_score_mfma"),
+                     "kernel": "index_score_mfma",
                      "bytes_per_launch": bytes_launch},
     }
 
@@ -400,6 +401,7 @@ COPY_CALIB_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
 TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_mfma_ctx65536_chunk2048_ratio4.txt")
+TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_mfma_decode_ctx262144_b4_stack.txt")
 
 
 def kernel_source_digest(kernel: str) -> str:
@@ -422,11 +424,15 @@ def copy_calibration():
     print(f"copied {COPY_CALIB_BYTES} bytes x 3", flush=True)
 
 
-def _short_kernel(name: str):
+def _short_kernel(name: str, with_args: bool = False):
+    """Library kernel name without the namespace and the _kernel suffix (with its template
+    arguments when asked: one kernel template serves several selection stages)."""
     if "copyBuffer" in name:
         return "copy"
-    m = re.search(r"(\w+)_kernel", name)
-    return m.group(1) if m and "dsv4" in name else None
+    m = re.search(r"(\w+)_kernel(<[^>(]*>)?", name)
+    if not m or "dsv4" not in name:
+        return None
+    return m.group(1) + (m.group(2).replace(" ", "") if with_args and m.group(2) else "")
 
 
 def _csv_rows(directory: str, pattern: str):
@@ -451,12 +457,20 @@ def _pmc(directory: str, counter: str):
     return out
 
 
-def _main_group(groups: dict, kernel: str):
-    """The (grid, values) of `kernel` with the most dispatches (the timed launches)."""
+def _main_group(groups: dict, kernel: str, largest_grid: bool = False):
+    """The (grid, values) of `kernel` with the most dispatches (the timed launches), or, where
+    several layers launch the kernel equally often, the largest grid among those launched at
+    least 8 times (the timed steps, not the one-off prefix build)."""
     cand = [(len(v), g, list(v.values())) for (k, g), v in groups.items() if k == kernel]
+    if largest_grid:
+        cand = [c for c in cand if c[0] >= 8]
     if not cand:
         raise SystemExit(f"no dispatches of {kernel}")
-    n, g, vals = max(cand)
+    if largest_grid:
+        size = lambda g: int(np.prod([int(x) for x in g.split("x")])) if g != "?" else 0
+        n, g, vals = max(cand, key=lambda c: size(c[1]))
+    else:
+        n, g, vals = max(cand)
     return g, vals
 
 
@@ -465,8 +479,8 @@ def write_traffic_profile(a):
     cw = _main_group(_pmc(a.calib_write, "WRITE_SIZE"), "copy")[1]
     ff = COPY_CALIB_BYTES / (np.mean(cf) * 1024.0)
     wf = COPY_CALIB_BYTES / (np.mean(cw) * 1024.0)
-    g, fv = _main_group(_pmc(a.fetch, "FETCH_SIZE"), a.kernel)
-    gw, wv = _main_group(_pmc(a.write, "WRITE_SIZE"), a.kernel)
+    g, fv = _main_group(_pmc(a.fetch, "FETCH_SIZE"), a.kernel, a.largest_grid)
+    gw, wv = _main_group(_pmc(a.write, "WRITE_SIZE"), a.kernel, a.largest_grid)
     traffic = np.mean(fv) * 1024.0 * ff + np.mean(wv) * 1024.0 * wf
     with open(a.out, "w") as f:
         f.write(f"# HBM traffic of {a.kernel}: {a.title}\n")
@@ -502,7 +516,7 @@ def traffic_from_profile(path: str, kernel: str):
 def write_kernel_profile(a):
     groups = defaultdict(list)
     for r in _csv_rows(a.trace_dir, "*kernel_trace.csv"):
-        k = _short_kernel(r["Kernel_Name"])
+        k = _short_kernel(r["Kernel_Name"], with_args=True)
         if k is None or k == "copy":
             continue
         groups[(k, _grid(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -514,9 +528,9 @@ def write_kernel_profile(a):
         f.write("# per (kernel, grid) from kernel_trace.csv of that run; library kernels only (the input\n"
                 "# generation and copies of the setup are omitted).  The grid with the most launches is the\n"
                 "# timed one; others come from building the prefix cache once per run.\n#\n")
-        f.write(f"# {'kernel':<20s} {'grid':<22s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_us':>12s}\n")
+        f.write(f"# {'kernel':<32s} {'grid':<22s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_us':>12s}\n")
         for (k, g), v in sorted(groups.items(), key=lambda x: -sum(x[1])):
-            f.write(f"  {k:<20s} {g:<22s} {len(v):6d} {np.mean(v):10.2f} {min(v):10.2f} {max(v):10.2f} {sum(v):12.1f}\n")
+            f.write(f"  {k:<32s} {g:<22s} {len(v):6d} {np.mean(v):10.2f} {min(v):10.2f} {max(v):10.2f} {sum(v):12.1f}\n")
     print(open(a.out).read())
 
 
@@ -533,6 +547,8 @@ def main():
         pp.add_argument("--calib-fetch")
         pp.add_argument("--calib-write")
         pp.add_argument("--trace-dir")
+        pp.add_argument("--largest-grid", action="store_true",
+                        help="take the kernel's dispatches of the largest grid launched 8+ times")
         a = pp.parse_args(sys.argv[2:])
         (write_traffic_profile if mode == "--write-traffic-profile" else write_kernel_profile)(a)
         return
@@ -553,7 +569,7 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-stack", action="store_true",
                     help="leave out the 262,144-token [0, 4, 128] stack decode sub-line")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "stack"], default=None,
                     help="run one workload (for per-workload profiler runs); the JSON line "
                          "then carries that workload's numbers only")
     args = ap.parse_args()
@@ -565,6 +581,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     K.lib()
+    if args.only == "stack":             # stack-only profiler run
+        stack = bench_stack(args)
+        log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step")
+        print(json.dumps({"workload": "stack", "decode_262k_stack": stack}), flush=True)
+        return
     dec = pre = None
     if args.only != "prefill":
         dec, dec_state = bench_decode(args)
