@@ -11,6 +11,7 @@ Sources ("the pages"):
                review thread (Thump604's fix list; OmarB97's RoPE/visibility notes;
                aidiffuser's mask diagnosis; stepnoy's patch; aidiffuser's indexer path;
                stepnoy's index-space fix).
+  [V41-MLX]    "deepseek-v41-mlx" (section "Why this exists": the landmines kept from V4).
 
 Readings where the pages leave a step open are marked READING and listed in the design doc.
 Every parity claim of the HIP path is against these functions.
@@ -22,6 +23,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "round_store", "rope_rows", "rms_norm", "compressor_rows",
     "rows_completed", "visible_rows", "index_scores", "select_topk", "csa_attention",
+    "rope_heads", "grouped_out_proj",
 ]
 
 
@@ -298,3 +300,50 @@ def csa_attention(q, kv, rows, sel, positions, *, window: int, ratio: int, sinks
         o = np.matmul(e, X) / denom[:, None]
         out[i] = round_store(o, store)
     return out
+
+
+# --------------------------------------------------------------------------------------
+# The layer's neighbours on either side of the attention: RoPE of the per-head inputs, and
+# the output path (inverse rotation of the attention output, grouped output projection)
+# --------------------------------------------------------------------------------------
+def rope_heads(x, positions, inv_freq, *, inverse: bool = False, work=np.float32) -> np.ndarray:
+    """RoPE of every head of every token at the token's position (q, kv, qi), or its inverse
+    (the attention output).
+
+    [MLXLM-1189] OmarB97's note 2 and stepnoy's patch: the rotary dims are the last ``rd`` of
+    each head, turned in interleaved pairs by position * inv_freq (as ``rope_rows``);
+    Thump604's fix list: "inverse output rotation for the post-attention rope dims";
+    [V41-MLX] "Why this exists": the rope inverse on the attention output.  The inverse turns
+    each pair back by the same angle: rotating at -position, since the fp32 angle
+    fp32(-p) * inv_freq is exactly the negated fp32(p) * inv_freq.
+
+    x: [N, H, D]; positions: [N].  Returns float64 (not rounded).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, h, d = x.shape
+    pos = np.repeat(np.asarray(positions, dtype=np.float64), h)
+    if inverse:
+        pos = -pos
+    return rope_rows(x.reshape(n * h, d), pos, inv_freq, work).reshape(n, h, d)
+
+
+def grouped_out_proj(o, wo_a) -> np.ndarray:
+    """Grouped (block-diagonal) output projection of the attention output.
+
+    [MTPLX-216] opening ("What V4 adds"): grouped output-LoRA on the attention output
+    projection, 8 groups of rank 1024; "Decode path: reference-faithful bf16 activation
+    storage", item 2: wo_a is [8192, 4096] (8 x 1024 outputs, 4096 inputs per group);
+    [V41-MLX] "Why this exists": wo_a is block-diagonal.  READING: group g takes heads
+    g*H/G .. (g+1)*H/G - 1 (their H/G * D values, head-major) and produces outputs
+    g*R .. (g+1)*R - 1.
+
+    o: [N, H, D] (the attention output after the inverse rotation); wo_a: [G, R, H/G * D].
+    Returns [N, G * R] float64 (not rounded).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    w = np.asarray(wo_a, dtype=np.float64)
+    n, h, d = o.shape
+    g, r, k = w.shape
+    assert h % g == 0 and k == (h // g) * d
+    xo = o.reshape(n, g, k)
+    return np.einsum("ngk,grk->ngr", xo, w).reshape(n, g * r)

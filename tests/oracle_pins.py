@@ -464,5 +464,52 @@ def pin_attention_bruteforce_layer():
             np.testing.assert_allclose(out[p, h], num / den, rtol=2e-6, atol=2e-7)
 
 
+# ------------------------------------------------------------------ output path
+def pin_rope_heads_inverse_and_heads():
+    """Every head of a token turns by the token's angle; the inverse undoes the forward;
+    a one-hot pair turns back clockwise by exactly that angle."""
+    rng = _rng(21)
+    N, H, D, rd = 5, 3, 10, 6
+    inv = _inv_freq(rd, theta=50.0)
+    x = rng.standard_normal((N, H, D))
+    pos = np.array([0, 3, 9, 40, 1000], dtype=np.float64)
+    f = O.rope_heads(x, pos, inv, work=F64)
+    for h in range(H):                                   # heads are independent rows
+        np.testing.assert_array_equal(f[:, h], O.rope_rows(x[:, h], pos, inv, F64))
+    np.testing.assert_allclose(O.rope_heads(f, pos, inv, inverse=True, work=F64), x,
+                               rtol=1e-9, atol=1e-9)
+    np.testing.assert_array_equal(f[0], x[0])            # position 0
+    e = np.zeros((1, 1, D))
+    e[0, 0, D - rd + 2] = 1.0                            # pair 1, first component
+    th = float(np.float32(7.0) * inv[1])
+    b = O.rope_heads(e, [7.0], inv, inverse=True, work=F64)[0, 0, D - rd + 2:D - rd + 4]
+    np.testing.assert_allclose(b, [np.cos(th), -np.sin(th)], atol=1e-12)
+
+
+def pin_grouped_proj_is_block_diagonal():
+    """The grouped projection equals one dense matmul with the block-diagonal weight written
+    out (zeros off the blocks); one group is a plain matmul; a one-hot input picks one
+    weight column of its own group only."""
+    rng = _rng(22)
+    N, H, D, G, R = 4, 6, 5, 3, 7
+    o = rng.standard_normal((N, H, D))
+    w = rng.standard_normal((G, R, H // G * D))
+    y = O.grouped_out_proj(o, w)
+    dense = np.zeros((G * R, H * D))
+    for g in range(G):
+        dense[g * R:(g + 1) * R, g * (H // G) * D:(g + 1) * (H // G) * D] = w[g]
+    np.testing.assert_allclose(y, o.reshape(N, H * D) @ dense.T, rtol=1e-12, atol=1e-12)
+    w1 = rng.standard_normal((1, R, H * D))
+    np.testing.assert_allclose(O.grouped_out_proj(o, w1), np.matmul(o.reshape(N, H * D), w1[0].T),
+                               rtol=1e-12, atol=1e-12)
+    e = np.zeros((1, H, D))
+    h, d = 3, 2                                          # head 3 is in group 1 (2 heads per group)
+    e[0, h, d] = 1.0
+    ye = O.grouped_out_proj(e, w)[0]
+    np.testing.assert_array_equal(ye[:R], 0.0)
+    np.testing.assert_array_equal(ye[2 * R:], 0.0)
+    np.testing.assert_array_equal(ye[R:2 * R], w[1][:, (h - 2) * D + d])
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items())
             if name.startswith("pin_") and callable(fn)}

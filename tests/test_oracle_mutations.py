@@ -116,6 +116,22 @@ def _sigmoid_weights(qi, w, K, work=np.float32):
     return _orig["index_scores"](qi, 1.0 / (1.0 + np.exp(-np.asarray(w))), K, work)
 
 
+def _inverse_turns_forward(x, positions, inv_freq, *, inverse=False, work=np.float32):
+    return _orig["rope_heads"](x, positions, inv_freq, inverse=False, work=work)
+
+
+def _groups_interleaved(o, wo_a):              # head h to group h mod G
+    o = np.asarray(o, dtype=np.float64)
+    n, h, d = o.shape
+    g = np.shape(wo_a)[0]
+    perm = np.concatenate([np.arange(j, h, g) for j in range(g)])
+    return _orig["grouped_out_proj"](o[:, perm], wo_a)
+
+
+def _groups_reversed(o, wo_a):                 # group g takes the weight of group G-1-g
+    return _orig["grouped_out_proj"](o, np.asarray(wo_a)[::-1])
+
+
 MUTATIONS = {
     "visibility (j+1)r <= p": ("visible_rows", _visibility_off_by_one),
     "window one token longer": ("csa_attention", _window_one_longer),
@@ -133,6 +149,9 @@ MUTATIONS = {
     "indexer averages heads": ("index_scores", _mean_over_heads),
     "indexer without ReLU": ("index_scores", _no_relu),
     "indexer sigmoid on weights": ("index_scores", _sigmoid_weights),
+    "inverse rotation turns forward": ("rope_heads", _inverse_turns_forward),
+    "output groups interleaved": ("grouped_out_proj", _groups_interleaved),
+    "output groups reversed": ("grouped_out_proj", _groups_reversed),
 }
 
 
