@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 import sparse_attention_dsv4_amd as K  # noqa: E402
 import synth.csa as SC  # noqa: E402
-from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec  # noqa: E402
+from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec, output_path  # noqa: E402
+import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
@@ -389,6 +390,61 @@ def cpu_baseline_prefill(state, n_queries):
                       f"~16K rows, top-512, attention), numpy fp32 oracle"}
 
 
+def bench_output_path(args, seed=41):
+    """The attention output's way out of a layer at the layer's shapes: inverse RoPE of the
+    rotary dims of 64 heads x 512 (in place), then the grouped block-diagonal projection
+    (wo_a: 8 groups x 1024 outputs x 4096 inputs).  Decode: one token of each of 8
+    sequences (the projection streams wo_a's 64 MiB once: HBM-bound); prefill: one 2048-token
+    chunk (MFMA-bound: 2 * 2048 * 8 * 1024 * 4096 flop).  Kernel times from the trace over
+    ``reps`` calls; the weights are synthetic (N(0, 1/4096))."""
+    spec = LayerSpec(ratio=4)
+    G, R = 8, 1024
+    Kd = spec.heads // G * spec.dim
+    inv = SC.inv_freq(spec.rope_dim).cuda()
+    wo_a = synth.normal((G, R, Kd), seed=seed, stream="wo_a", scale=Kd ** -0.5,
+                        dtype=torch.bfloat16, device="cuda")
+    out = {}
+    for name, B, S, pos in (("decode_b8", 8, 1, args.context), ("prefill_2048", 1, args.chunk,
+                                                                 args.context - args.chunk)):
+        o = synth.normal((B, S, spec.heads, spec.dim), seed=seed, stream="attn_out",
+                         dtype=torch.bfloat16, device="cuda")
+        y = torch.empty(B, S, G, R, dtype=torch.bfloat16, device="cuda")
+        reps = 20
+        for _ in range(3):
+            output_path(spec, o, [pos] * B, inv, wo_a, y)
+        torch.cuda.synchronize()
+        K.dsv4_trace_reset()
+        K.dsv4_trace_enable(True)
+        for _ in range(reps):
+            output_path(spec, o, [pos] * B, inv, wo_a, y)
+        torch.cuda.synchronize()
+        K.dsv4_trace_enable(False)
+        times = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+        T = B * S
+        gname = next(n for n in times if n.startswith("gproj") and times[n][0])
+        n_g, ms_g = times[gname]
+        us_g = ms_g / n_g * 1e3
+        n_r, ms_r = times["rope"]
+        entry = {"tokens": T, "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
+                                         for n, v in times.items() if v[0]}}
+        if S == 1:
+            byts = G * R * Kd * 2 + T * G * Kd * 2 + T * G * R * 2
+            ach = byts / (us_g * 1e-6) / 1e9
+            entry["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": gname,
+                                 "bytes_per_launch": byts}
+        else:
+            fl = 2.0 * T * G * R * Kd
+            ach = fl / (us_g * 1e-6) / 1e12
+            entry["roofline"] = {"bound": "mfma", "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": ach / BF16_MFMA_PEAK_TFLOPS,
+                                 "traffic": None, "kernel": gname, "flops_per_launch": fl}
+        entry["us_per_call"] = us_g + ms_r / n_r * 1e3
+        out[name] = entry
+        del o, y
+    return out
+
+
 # ------------------------------------------------------------------ profiles
 # The summaries under profiles/ are written from rocprofv3 output by the modes below (no GPU
 # needed), so each one names commands that run committed files only.  A traffic summary
@@ -594,6 +650,12 @@ def main():
     if not args.skip_prefill and args.only != "decode":
         pre, pre_state = bench_prefill(args)
         log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk")
+    outp = None
+    if args.only is None:
+        outp = bench_output_path(args)
+        log(f"[output path] decode b8 {outp['decode_b8']['us_per_call']:.1f} us "
+            f"({outp['decode_b8']['roofline']['frac'] * 100:.0f}% of HBM in the projection); prefill 2048 "
+            f"{outp['prefill_2048']['us_per_call']:.1f} us ({outp['prefill_2048']['roofline']['frac'] * 100:.0f}% of MFMA)")
     stack = None
     if not args.skip_stack and args.only is None:
         stack = bench_stack(args)
@@ -632,6 +694,7 @@ def main():
         "kernels": dec["kernels"],
         "prefill": pre,
         "decode_262k_stack": stack,
+        "output_path": outp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -220,6 +220,49 @@ int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* k
                           const float* sinks, void* out, int32_t batch, int64_t s, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* The layer's neighbours on either side of the attention (survey's next rows).
+ * Pages: mlx-lm PR #1189 (OmarB97's note 2 and stepnoy's patch: the rotary dims are the last
+ * rd of each head, interleaved pairs turned by position * inv_freq; Thump604's fix list:
+ * inverse output rotation of the post-attention rope dims); MTPLX PR #216 opening ("What V4
+ * adds": grouped output-LoRA, 8 groups of rank 1024) and "Decode path: reference-faithful
+ * bf16 activation storage" item 2 (wo_a [8192, 4096]); deepseek-v41-mlx "Why this exists"
+ * (the rope inverse on the attention output; wo_a block-diagonal). */
+typedef struct {
+    int32_t heads;     /* H, 1..65535                                                      */
+    int32_t dim;       /* D: head width, 1..4096                                           */
+    int32_t rope_dim;  /* rd, even, 0..D: the last rd dims of each head turn               */
+    int32_t inverse;   /* 0: turn by +angle (q, kv, qi before attention); 1: turn back by
+                          the same angle (the attention output)                            */
+    int32_t dtype;     /* dsv4_dtype                                                       */
+} dsv4_rope_cfg;
+
+/* RoPE in place on x [batch, s, H, D]: token t of sequence b (position pos0[b] + t) has the
+ * pairs (x[D-rd+2i], x[D-rd+2i+1]) of every head turned by theta_i = fp32(position) *
+ * inv_freq[i] (fp32 product), result (x0 cos - x1 sin, x0 sin + x1 cos) in fp32 (with -theta
+ * when inverse), rounded to the storage dtype; other dims untouched.  inv_freq [rd/2] fp32.
+ * Errors: EINVAL (NULL pointer, bad cfg, negative batch/s/position), ECAPACITY (a position
+ * >= 2^31 - 1), EUNSUPPORTED (s > 65535), EHIP. */
+int dsv4_rope(const dsv4_rope_cfg* cfg, void* x, const int64_t* pos0, int32_t batch, int64_t s,
+              const float* inv_freq, void* stream);
+
+typedef struct {
+    int32_t groups;    /* G >= 1                                                           */
+    int32_t in_dim;    /* K: inputs per group (H/G heads x D of the attention output)      */
+    int32_t out_dim;   /* R: outputs per group (the rank)                                  */
+    int32_t dtype;     /* dsv4_dtype of x, w and y                                         */
+} dsv4_gproj_cfg;
+
+/* Grouped (block-diagonal) projection: y[t, g, r] = sum_k w[g, r, k] * x[t, g, k], fp32
+ * accumulation, rounded once to the storage dtype.
+ *   x [tokens, G, K]  (the attention output [tokens, H, D] after the inverse rotation is
+ *                      this with K = H/G * D: group g holds heads g*H/G .. (g+1)*H/G - 1)
+ *   w [G, R, K]       (wo_a [G*R, K] read as G blocks of R rows)
+ *   y [tokens, G, R]
+ * Errors: EINVAL (NULL pointer, bad cfg, tokens < 0), EUNSUPPORTED (tokens x G x R above
+ * 2^39), EHIP. */
+int dsv4_grouped_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w, void* y,
+                      int64_t tokens, void* stream);
+
 /* Kernel timing for measurement.  While enabled, every kernel the library launches carries
  * a start/stop HIP event pair attached to its own dispatch (hipExtLaunchKernelGGL), so each
  * record is that kernel's execution time on its launch stream.  dsv4_trace_read() waits for the

@@ -18,5 +18,7 @@ from .csa import (  # noqa: F401
     visible_rows,
     index_scores,
     select_topk,
+    rope_heads,
+    grouped_out_proj,
     csa_attention,
 )

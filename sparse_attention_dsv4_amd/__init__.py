@@ -19,7 +19,8 @@ __all__ = [
     "dsv4_version", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
     "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
-    "dsv4_csa_attn_prefill", "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
+    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "RopeCfg", "GprojCfg",
+    "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -31,8 +32,8 @@ EXPORTED_SYMBOLS = (
     "dsv4_version", "dsv4_last_error", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
     "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
-    "dsv4_csa_attn_prefill", "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read",
-    "dsv4_trace_kernel_name",
+    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "dsv4_trace_enable",
+    "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernel_name",
 )
 
 
@@ -55,6 +56,16 @@ class _IndexCfg(ctypes.Structure):
 class _AttnCfg(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("ratio", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class _RopeCfg(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("inverse", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _GprojCfg(ctypes.Structure):
+    _fields_ = [("groups", ctypes.c_int32), ("in_dim", ctypes.c_int32), ("out_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
 
 
@@ -91,6 +102,29 @@ class IndexCfg:
 
     def c(self):
         return _IndexCfg(self.heads, self.dim, self.topk, self.ratio, _DTYPES[self.dtype])
+
+
+@dataclass(frozen=True)
+class RopeCfg:
+    heads: int
+    dim: int
+    rope_dim: int
+    inverse: bool = False
+    dtype: torch.dtype = torch.bfloat16
+
+    def c(self):
+        return _RopeCfg(self.heads, self.dim, self.rope_dim, int(self.inverse), _DTYPES[self.dtype])
+
+
+@dataclass(frozen=True)
+class GprojCfg:
+    groups: int
+    in_dim: int
+    out_dim: int
+    dtype: torch.dtype = torch.bfloat16
+
+    def c(self):
+        return _GprojCfg(self.groups, self.in_dim, self.out_dim, _DTYPES[self.dtype])
 
 
 @dataclass(frozen=True)
@@ -145,6 +179,9 @@ def lib():
         L.dsv4_csa_attn_prefill.argtypes = [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, ctypes.c_int64,
                                             _P, _I64P, _I64P, _P, _P, ctypes.c_int32, ctypes.c_int64,
                                             _P, ctypes.c_size_t, _P]
+        L.dsv4_rope.argtypes = [ctypes.POINTER(_RopeCfg), _P, _I64P, ctypes.c_int32, ctypes.c_int64,
+                                _P, _P]
+        L.dsv4_grouped_proj.argtypes = [ctypes.POINTER(_GprojCfg), _P, _P, _P, ctypes.c_int64, _P]
         L.dsv4_trace_enable.argtypes = [ctypes.c_int32]
         L.dsv4_trace_read.argtypes = [ctypes.c_char_p, _I64P, ctypes.POINTER(ctypes.c_double)]
         _lib = L
@@ -373,3 +410,28 @@ def dsv4_trace_kernels():
             return out
         out.append(n.decode())
         i += 1
+
+
+def dsv4_rope(cfg: RopeCfg, x, pos0, inv_freq, stream=None):
+    """RoPE in place on x [B, S, H, D] (token t of sequence b at position pos0[b] + t), or its
+    inverse when cfg.inverse; inv_freq [rd/2] fp32."""
+    if x is None or x.dim() != 4:
+        raise ValueError("x must be [B, S, H, D]")
+    B, S = x.shape[0], x.shape[1]
+    _need(x, (B, S, cfg.heads, cfg.dim), cfg.dtype, "x")
+    _need(inv_freq, (cfg.rope_dim // 2,), torch.float32, "inv_freq")
+    c = cfg.c()
+    _check(lib().dsv4_rope(ctypes.byref(c), _ptr(x), _host_i64(pos0, B, "pos0"), B, S,
+                           _ptr(inv_freq), _stream(stream)))
+
+
+def dsv4_grouped_proj(cfg: GprojCfg, x, w, y, stream=None):
+    """y [T, G, R] = per group g: x [T, G, K][:, g] @ w [G, R, K][g].T (fp32 accumulation)."""
+    if x is None or x.dim() != 3:
+        raise ValueError("x must be [T, G, K]")
+    T = x.shape[0]
+    _need(x, (T, cfg.groups, cfg.in_dim), cfg.dtype, "x")
+    _need(w, (cfg.groups, cfg.out_dim, cfg.in_dim), cfg.dtype, "w")
+    _need(y, (T, cfg.groups, cfg.out_dim), cfg.dtype, "y")
+    c = cfg.c()
+    _check(lib().dsv4_grouped_proj(ctypes.byref(c), _ptr(x), _ptr(w), _ptr(y), T, _stream(stream)))

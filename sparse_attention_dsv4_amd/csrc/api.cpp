@@ -18,6 +18,7 @@
 #include "../../include/dsv4.h"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "proj.hpp"
 
 namespace {
 
@@ -336,6 +337,49 @@ int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* k
                           size_t ws_bytes, void* stream) {
     return attn_common(cfg, q, kv_new, win_ring, rows, row_cap, sel, n_rows, pos0, sinks, out,
                        batch, s, ws, ws_bytes, stream);
+}
+
+int dsv4_rope(const dsv4_rope_cfg* cfg, void* x, const int64_t* pos0, int32_t batch, int64_t s,
+              const float* inv_freq, void* stream) {
+    if (!cfg) return fail(DSV4_EINVAL, "cfg is NULL");
+    if (cfg->heads < 1 || cfg->heads > 65535) return fail(DSV4_EINVAL, "heads %d outside 1..65535", cfg->heads);
+    if (cfg->dim < 1 || cfg->dim > 4096) return fail(DSV4_EINVAL, "dim %d outside 1..4096", cfg->dim);
+    if (cfg->rope_dim < 0 || cfg->rope_dim > cfg->dim || (cfg->rope_dim & 1))
+        return fail(DSV4_EINVAL, "rope_dim %d must be even and within 0..dim", cfg->rope_dim);
+    if (cfg->inverse != 0 && cfg->inverse != 1) return fail(DSV4_EINVAL, "inverse must be 0 or 1");
+    if (!dtype_ok(cfg->dtype)) return fail(DSV4_EINVAL, "unknown dtype %d", cfg->dtype);
+    if (batch < 0) return fail(DSV4_EINVAL, "batch %d < 0", batch);
+    if (s < 0) return fail(DSV4_EINVAL, "s < 0");
+    if (s > 65535) return fail(DSV4_EUNSUPPORTED, "s %lld above 65535 tokens per call", (long long)s);
+    if (batch == 0 || s == 0 || cfg->rope_dim == 0) return ok();
+    if (!x || !pos0 || !inv_freq) return fail(DSV4_EINVAL, "NULL buffer pointer");
+    for (int b = 0; b < batch; ++b) {
+        if (pos0[b] < 0) return fail(DSV4_EINVAL, "pos0[%d] < 0", b);
+        if (pos0[b] + s > kPosLimit) return fail(DSV4_ECAPACITY, "sequence %d passes 2^31 tokens", b);
+    }
+    dsv4::RopeJob j;
+    j.H = cfg->heads; j.D = cfg->dim; j.rd = cfg->rope_dim; j.inverse = cfg->inverse != 0;
+    j.bf16 = cfg->dtype == DSV4_BF16; j.x = x; j.inv_freq = inv_freq; j.S = s; j.batch = batch;
+    j.pos0 = pos0;
+    return hip_status(dsv4::launch_rope(j, static_cast<hipStream_t>(stream)), "rope");
+}
+
+int dsv4_grouped_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w, void* y,
+                      int64_t tokens, void* stream) {
+    if (!cfg) return fail(DSV4_EINVAL, "cfg is NULL");
+    if (cfg->groups < 1) return fail(DSV4_EINVAL, "groups %d < 1", cfg->groups);
+    if (cfg->in_dim < 1 || cfg->in_dim > 65536) return fail(DSV4_EINVAL, "in_dim %d outside 1..65536", cfg->in_dim);
+    if (cfg->out_dim < 1 || cfg->out_dim > 65536) return fail(DSV4_EINVAL, "out_dim %d outside 1..65536", cfg->out_dim);
+    if (!dtype_ok(cfg->dtype)) return fail(DSV4_EINVAL, "unknown dtype %d", cfg->dtype);
+    if (tokens < 0) return fail(DSV4_EINVAL, "tokens < 0");
+    if (tokens == 0) return ok();
+    if (!x || !w || !y) return fail(DSV4_EINVAL, "NULL buffer pointer");
+    if (tokens * cfg->groups * int64_t(cfg->out_dim) > (int64_t(1) << 39) || tokens > (int64_t(1) << 31))
+        return fail(DSV4_EUNSUPPORTED, "tokens x groups x out_dim too large");
+    dsv4::GprojJob j;
+    j.G = cfg->groups; j.K = cfg->in_dim; j.R = cfg->out_dim; j.bf16 = cfg->dtype == DSV4_BF16;
+    j.x = x; j.w = w; j.y = y; j.T = tokens;
+    return hip_status(dsv4::launch_grouped_proj(j, static_cast<hipStream_t>(stream)), "grouped_proj");
 }
 
 int dsv4_trace_enable(int32_t on) {

@@ -1,0 +1,348 @@
+// The layer's neighbours on either side of the attention (gfx950, wave64):
+//   rope_kernel          RoPE of the last rd dims of every head of every token (q, kv, qi),
+//                        or its inverse (the attention output): interleaved pairs turned by
+//                        position * inv_freq, angle and rotation in fp32, rounded to storage;
+//   gproj_small_kernel   grouped (block-diagonal) output projection for up to 32 tokens
+//                        (decode): weight streaming, HBM-bound -- each 32-row block of a
+//                        group's weight is read once, straight into registers, by 8 waves
+//                        that split K and meet in LDS;
+//   gproj_tile_kernel    the same for more tokens (prefill): MFMA-bound 256-token x
+//                        256-row tiles (8 waves), both operands staged in LDS by direct
+//                        global-to-LDS copies, k blocks of 64 double-buffered;
+//   gproj_generic_kernel any shape or fp32: one thread per output.
+// Every product accumulates in fp32 (v_mfma_f32_32x32x16_bf16 on the bf16 paths); outputs
+// are rounded once to the storage type.
+#include "common.hpp"
+#include "mfma.hpp"
+#include "proj.hpp"
+
+namespace dsv4 {
+
+namespace {
+
+// ------------------------------------------------------------------ RoPE
+constexpr int kRopeHeadsPerThread = 8;   // one angle serves 8 heads of the token
+
+template <typename T>
+struct RopeArgs {
+    int H, D, rd;
+    bool inverse;
+    T* x;
+    const float* inv_freq;
+    int64_t S;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) rope_kernel(RopeArgs<T> a, SeqInts pos0) {
+    const int P = a.rd / 2;
+    const int HC = (a.H + kRopeHeadsPerThread - 1) / kRopeHeadsPerThread;
+    const int item = int(blockIdx.x) * 256 + int(threadIdx.x);      // (head chunk, pair)
+    if (item >= HC * P) return;
+    const int hc = item / P, i = item % P;
+    const int64_t s = blockIdx.y;
+    const int b = blockIdx.z;
+    // fp32 angle of the fp32 position, as the compressor's rows
+    const float p = float(int64_t(pos0.v[b]) + s);
+    float sn, cs;
+    sincosf(p * a.inv_freq[i], &sn, &cs);
+    if (a.inverse) sn = -sn;
+    T* base = a.x + (size_t(b) * a.S + size_t(s)) * a.H * a.D + (a.D - a.rd) + 2 * i;
+    const int h1 = (hc + 1) * kRopeHeadsPerThread < a.H ? (hc + 1) * kRopeHeadsPerThread : a.H;
+    for (int h = hc * kRopeHeadsPerThread; h < h1; ++h) {
+        T* px = base + size_t(h) * a.D;
+        const float x0 = to_f32(px[0]), x1 = to_f32(px[1]);
+        px[0] = from_f32<T>(x0 * cs - x1 * sn);
+        px[1] = from_f32<T>(x0 * sn + x1 * cs);
+    }
+}
+
+// ------------------------------------------------------------------ grouped projection
+struct GprojArgs {
+    int G, K, R;
+    const bf16* x;             // [T][G][K]
+    const bf16* w;             // [G][R][K]
+    bf16* y;                   // [T][G][R]
+    int64_t T;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+// MFMA k-slot order: in a 64-wide k block, lane (m, hh) of MFMA j holds k = 32 hh + 8 j + e,
+// so the 4 MFMAs of a block take a lane's 64 contiguous bytes of its row (A and B alike).
+#ifndef DSV4_GPROJ_SMALL_WAVES
+#define DSV4_GPROJ_SMALL_WAVES 8
+#endif
+constexpr int kSmallWaves = DSV4_GPROJ_SMALL_WAVES;
+constexpr int kSmallMaxT = 32;
+
+// Up to 32 tokens: workgroup (32-row block, group); wave w of the W waves multiplies k in
+// [w K/W, (w+1) K/W) (KBW blocks of 64), the W partial 32 x 32 tiles meet in LDS.
+template <int KBW>
+__global__ void __launch_bounds__(64 * kSmallWaves) gproj_small_kernel(GprojArgs a) {
+    __shared__ float part[kSmallWaves][32 * 33];
+    const int rb = blockIdx.x, g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int m = lane & 31, hh = lane >> 5;
+    const int k0 = w * 64 * KBW + 32 * hh;
+    const bf16* wrow = a.w + (size_t(g) * a.R + size_t(rb) * 32 + m) * a.K + k0;
+    const bool tv = m < a.T;
+    const bf16* xrow = a.x + (size_t(tv ? m : 0) * a.G + g) * a.K + k0;
+    uint4 wv[KBW][4];
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wv[kb][c] = *reinterpret_cast<const uint4*>(wrow + kb * 64 + 8 * c);
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KBW; ++kb) {
+        uint4 xv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            xv[c] = tv ? *reinterpret_cast<const uint4*>(xrow + kb * 64 + 8 * c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma32x32x16(as_bf16x8(wv[kb][j]), as_bf16x8(xv[j]), acc);
+    }
+    // C[row][token]: register i of lane l is row c_row(i, l), token l % 32
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[w][c_row(i, lane) * 33 + m] = acc[i];
+    __syncthreads();
+    for (int o = tid; o < 32 * 32; o += 64 * kSmallWaves) {
+        const int t = o >> 5, row = o & 31;
+        if (t >= a.T) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < kSmallWaves; ++v) s += part[v][row * 33 + t];
+        a.y[(size_t(t) * a.G + g) * a.R + size_t(rb) * 32 + row] = from_f32<bf16>(s);
+    }
+}
+
+// More tokens: workgroup tile 64 WT tokens x 256 rows of one group, 2 WT waves of 64 x 128
+// (2 x 4 MFMA blocks; C[token][row]), k in blocks of BK through an NST-stage LDS ring.  A
+// stage holds 128 token rows and 256 weight rows of 2 BK bytes; the 16-byte chunk c of row r
+// sits at chunk c ^ ((r / (16 / CPR)) % CPR) (CPR chunks per row), so the 16 rows of one
+// MFMA operand read phase hit 16 different 16-byte bank groups.  Token rows past T load row
+// T - 1 (finite values whose outputs are not stored).
+#ifndef DSV4_GPROJ_BK
+#define DSV4_GPROJ_BK 64
+#endif
+#ifndef DSV4_GPROJ_STAGES
+#define DSV4_GPROJ_STAGES 2
+#endif
+#ifndef DSV4_GPROJ_WT
+#define DSV4_GPROJ_WT 4
+#endif
+constexpr int kTileWt = DSV4_GPROJ_WT;                   // waves along the tokens (64 each)
+constexpr int kTileWaves = 2 * kTileWt;                  // and two along the rows (128 each)
+constexpr int kTileT = 64 * kTileWt, kTileR = 256;
+constexpr int kTileK = DSV4_GPROJ_BK, kTileStages = DSV4_GPROJ_STAGES;
+constexpr int kRowB = kTileK * 2;                        // bytes per staged row
+constexpr int kCpr = kRowB / 16;                         // 16-byte chunks per row
+constexpr int kRowsPerOp = 1024 / kRowB;                 // rows per 1 KB copy
+constexpr int kStageB = (kTileT + kTileR) * kRowB;
+constexpr int kTileOps = (kTileT + kTileR) / kRowsPerOp / kTileWaves;   // copies per wave per stage
+static_assert(kCpr == 4 || kCpr == 8, "k block of 32 or 64");
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds_base) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(uint32_t(size_t((const lds_u8*)lds_base)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(la), "v"(gptr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ ((row / (16 / kCpr)) % kCpr); }
+
+// Copy k block kb of the tile into stage buffer buf: 1 KB copies of kRowsPerOp rows; wave w
+// takes copies w, w + 2 WT, ... (the token rows first, then the weight rows).
+__device__ __forceinline__ void tile_load(const GprojArgs& a, int g, int64_t t0, int r0, int kb,
+                                          unsigned char* buf) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kTileOps; ++i) {
+        const int op = w + kTileWaves * i;
+        const int row = kRowsPerOp * op + lane / kCpr;   // row of the stage
+        const int c = tswz(row, lane % kCpr);            // logical chunk landing at lane % kCpr
+        const bf16* src;
+        if (row < kTileT) {
+            int64_t t = t0 + row;
+            t = t < a.T ? t : a.T - 1;
+            src = a.x + (size_t(t) * a.G + g) * a.K + size_t(kb) * kTileK + 8 * c;
+        } else {
+            const int r = r0 + row - kTileT;
+            src = a.w + (size_t(g) * a.R + r) * a.K + size_t(kb) * kTileK + 8 * c;
+        }
+        dma16(src, buf + op * 1024);
+    }
+}
+
+__global__ void __launch_bounds__(64 * kTileWaves) gproj_tile_kernel(GprojArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char st[kTileStages][kStageB];
+    const int g = blockIdx.z;
+    const int64_t t0 = int64_t(blockIdx.x) * kTileT;
+    const int r0 = int(blockIdx.y) * kTileR;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = lane & 31, hh = lane >> 5;
+    const int wt = w % kTileWt, wr = w / kTileWt;        // wave tile: tokens 64 wt, rows 128 wr
+    const int nk = a.K / kTileK;
+    floatx16 acc[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kTileStages - 1; ++s)
+        if (s < nk) tile_load(a, g, t0, r0, s, st[s]);
+    for (int kb = 0; kb < nk; ++kb) {
+        // stage kb has landed once at most the copies of the stages issued after it are
+        // pending: min(NST - 2, blocks left after kb) stages
+        const int later = nk - 1 - kb < kTileStages - 2 ? nk - 1 - kb : kTileStages - 2;
+        if (later >= 2) wait_vm<2 * kTileOps>();
+        else if (later == 1) wait_vm<kTileOps>();
+        else wait_vm<0>();
+        lds_barrier();                                   // stage kb visible; kb-1 fully read
+        if (kb + kTileStages - 1 < nk)
+            tile_load(a, g, t0, r0, kb + kTileStages - 1, st[(kb + kTileStages - 1) % kTileStages]);
+        const unsigned char* buf = st[kb % kTileStages];
+#pragma unroll
+        for (int j = 0; j < kTileK / 16; ++j) {          // MFMA k steps of this block
+            const int lc = 2 * j + hh;                   // logical chunk of this lane
+            bf16x8 xa[2], wb[4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = 64 * wt + 32 * u + m;
+                xa[u] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = kTileT + 128 * wr + 32 * v + m;
+                wb[v] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = mfma32x32x16(xa[u], wb[v], acc[u][v]);
+        }
+    }
+    // C[token][row]: register i of lane l is token c_row(i, l), row l % 32
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t t = t0 + 64 * wt + 32 * u + c_row(i, lane);
+            if (t >= a.T) continue;
+            bf16* yr = a.y + (size_t(t) * a.G + g) * a.R + r0 + 128 * wr + m;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
+        }
+}
+
+template <typename T>
+struct GenericArgs {
+    int G, K, R;
+    const T* x;
+    const T* w;
+    T* y;
+    int64_t T_;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) gproj_generic_kernel(GenericArgs<T> a) {
+    const int64_t o = int64_t(blockIdx.x) * 256 + threadIdx.x;    // (t, g, r), r fastest
+    const int64_t n = a.T_ * a.G * a.R;
+    if (o >= n) return;
+    const int r = int(o % a.R);
+    const int g = int((o / a.R) % a.G);
+    const int64_t t = o / (int64_t(a.R) * a.G);
+    const T* xr = a.x + (size_t(t) * a.G + g) * a.K;
+    const T* wr = a.w + (size_t(g) * a.R + r) * a.K;
+    float s = 0.f;
+    for (int k = 0; k < a.K; ++k) s = fmaf(to_f32(xr[k]), to_f32(wr[k]), s);
+    a.y[o] = from_f32<T>(s);
+}
+
+template <typename T>
+hipError_t rope_run(const RopeJob& j, hipStream_t st) {
+    const int HC = (j.H + kRopeHeadsPerThread - 1) / kRopeHeadsPerThread;
+    const unsigned gx = unsigned((HC * (j.rd / 2) + 255) / 256);
+    for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
+        const int nb = std::min(kSeqSlice, j.batch - b0);
+        SeqInts pos{};
+        for (int i = 0; i < nb; ++i) pos.v[i] = int32_t(j.pos0[b0 + i]);
+        RopeArgs<T> a;
+        a.H = j.H; a.D = j.D; a.rd = j.rd; a.inverse = j.inverse;
+        a.x = static_cast<T*>(j.x) + size_t(b0) * j.S * j.H * j.D;
+        a.inv_freq = j.inv_freq;
+        a.S = j.S;
+        DSV4_LAUNCH("rope", rope_kernel<T>, dim3(gx, unsigned(j.S), nb), dim3(256), 0, st, a, pos);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_rope(const RopeJob& j, hipStream_t s) {
+    if (j.rd == 0) return hipSuccess;
+    return j.bf16 ? rope_run<bf16>(j, s) : rope_run<float>(j, s);
+}
+
+hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
+    constexpr int kSmallK = 64 * kSmallWaves;          // k per KBW step of the workgroup
+    if (j.bf16 && j.T <= kSmallMaxT && j.K % kSmallK == 0 && j.K <= 8 * kSmallK && j.R % 32 == 0) {
+        GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
+                    static_cast<bf16*>(j.y), j.T};
+        const dim3 grid(unsigned(j.R / 32), unsigned(j.G));
+        const dim3 block(64 * kSmallWaves);
+        switch (j.K / kSmallK) {
+            case 1: DSV4_LAUNCH("gproj_small", gproj_small_kernel<1>, grid, block, 0, s, a); break;
+            case 2: DSV4_LAUNCH("gproj_small", gproj_small_kernel<2>, grid, block, 0, s, a); break;
+            case 3: DSV4_LAUNCH("gproj_small", gproj_small_kernel<3>, grid, block, 0, s, a); break;
+            case 4: DSV4_LAUNCH("gproj_small", gproj_small_kernel<4>, grid, block, 0, s, a); break;
+            case 5: DSV4_LAUNCH("gproj_small", gproj_small_kernel<5>, grid, block, 0, s, a); break;
+            case 6: DSV4_LAUNCH("gproj_small", gproj_small_kernel<6>, grid, block, 0, s, a); break;
+            case 7: DSV4_LAUNCH("gproj_small", gproj_small_kernel<7>, grid, block, 0, s, a); break;
+            default: DSV4_LAUNCH("gproj_small", gproj_small_kernel<8>, grid, block, 0, s, a); break;
+        }
+        return hipGetLastError();
+    }
+    if (j.bf16 && j.K % kTileK == 0 && j.R % kTileR == 0) {
+        GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
+                    static_cast<bf16*>(j.y), j.T};
+        const dim3 grid(unsigned((j.T + kTileT - 1) / kTileT), unsigned(j.R / kTileR), unsigned(j.G));
+        DSV4_LAUNCH("gproj_tile", gproj_tile_kernel, grid, dim3(64 * kTileWaves), 0, s, a);
+        return hipGetLastError();
+    }
+    const int64_t n = j.T * j.G * j.R;
+    const unsigned blocks = unsigned((n + 255) / 256);
+    if (j.bf16) {
+        GenericArgs<bf16> a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
+                            static_cast<bf16*>(j.y), j.T};
+        DSV4_LAUNCH("gproj_generic", gproj_generic_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        GenericArgs<float> a{j.G, j.K, j.R, static_cast<const float*>(j.x), static_cast<const float*>(j.w),
+                             static_cast<float*>(j.y), j.T};
+        DSV4_LAUNCH("gproj_generic", gproj_generic_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsv4

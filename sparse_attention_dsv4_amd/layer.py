@@ -21,10 +21,10 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (AttnCfg, CompCfg, IndexCfg, dsv4_comp_state_bytes, dsv4_compress_prefill,
-               dsv4_compress_step, dsv4_csa_attn_decode, dsv4_csa_attn_decode_store,
-               dsv4_csa_attn_prefill, dsv4_index_topk, dsv4_index_workspace_bytes,
-               dsv4_attn_workspace_bytes)
+from . import (AttnCfg, CompCfg, GprojCfg, IndexCfg, RopeCfg, dsv4_comp_state_bytes,
+               dsv4_compress_prefill, dsv4_compress_step, dsv4_csa_attn_decode,
+               dsv4_csa_attn_decode_store, dsv4_csa_attn_prefill, dsv4_grouped_proj,
+               dsv4_index_topk, dsv4_index_workspace_bytes, dsv4_attn_workspace_bytes, dsv4_rope)
 
 
 @dataclass(frozen=True)
@@ -175,3 +175,18 @@ class CsaLayer:
                                  P["sinks"], out, self.ws_attn)
         self.lengths = [n + 1 for n in self.lengths]
         return out
+
+
+def output_path(spec: LayerSpec, o: torch.Tensor, pos0, inv_freq: torch.Tensor,
+                wo_a: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """The attention output's way out of the layer: the rotary dims of every head turned back
+    (inverse RoPE at the token's position, in place on ``o``), then the grouped block-diagonal
+    projection by ``wo_a`` [G, R, H/G * D].  o: [B, S, H, D] (decode: S = 1); returns
+    y [B, S, G, R].  Two library calls: dsv4_rope (inverse) and dsv4_grouped_proj."""
+    B, S = o.shape[0], o.shape[1]
+    G, R, Kd = wo_a.shape
+    dsv4_rope(RopeCfg(spec.heads, spec.dim, spec.rope_dim, True, spec.dtype), o, pos0, inv_freq)
+    if y is None:
+        y = torch.empty(B, S, G, R, dtype=spec.dtype, device=o.device)
+    dsv4_grouped_proj(GprojCfg(G, Kd, R, spec.dtype), o.view(B * S, G, Kd), wo_a, y.view(B * S, G, R))
+    return y

@@ -194,6 +194,34 @@ def test_decode_store_validation(L):
     assert _store(L, cfg, [good], batch=0, q=None) == 0
 
 
+def test_rope_and_projection_validation(L):
+    def rope(cfg, x=FAKE, pos=_i64(10, 20), batch=2, s=4, inv=FAKE):
+        c = cfg.c()
+        return L.dsv4_rope(ctypes.byref(c), x, pos, batch, s, inv, None)
+    ok_cfg = K.RopeCfg(heads=64, dim=512, rope_dim=64, inverse=True)
+    assert rope(K.RopeCfg(heads=0, dim=512, rope_dim=64)) == EINVAL
+    assert rope(K.RopeCfg(heads=64, dim=512, rope_dim=63)) == EINVAL      # odd
+    assert rope(K.RopeCfg(heads=64, dim=64, rope_dim=80)) == EINVAL       # above dim
+    assert rope(ok_cfg, x=None) == EINVAL
+    assert rope(ok_cfg, inv=None) == EINVAL
+    assert rope(ok_cfg, pos=_i64(10, -1)) == EINVAL
+    assert rope(ok_cfg, pos=_i64(10, (1 << 31) - 3)) == ECAP
+    assert rope(ok_cfg, s=70000) == EUNSUP
+    assert rope(ok_cfg, batch=0, x=None) == 0
+    assert rope(K.RopeCfg(heads=64, dim=512, rope_dim=0), x=None) == 0    # nothing turns
+
+    def proj(cfg, x=FAKE, w=FAKE, y=FAKE, t=8):
+        c = cfg.c()
+        return L.dsv4_grouped_proj(ctypes.byref(c), x, w, y, t, None)
+    g = K.GprojCfg(groups=8, in_dim=4096, out_dim=1024)
+    assert proj(K.GprojCfg(groups=0, in_dim=4096, out_dim=1024)) == EINVAL
+    assert proj(K.GprojCfg(groups=8, in_dim=0, out_dim=1024)) == EINVAL
+    assert proj(g, w=None) == EINVAL
+    assert proj(g, t=-1) == EINVAL
+    assert proj(g, t=1 << 32) == EUNSUP
+    assert proj(g, t=0, x=None) == 0
+
+
 def test_trace_calls(L):
     K.dsv4_trace_reset()
     assert K.dsv4_trace_read("") == (0, 0.0)

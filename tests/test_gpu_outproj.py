@@ -1,0 +1,127 @@
+"""The layer's neighbours through the C ABI against the oracle (needs a gfx950 GPU):
+RoPE of per-head vectors and its inverse (dsv4_rope), and the grouped block-diagonal output
+projection (dsv4_grouped_proj) on all three of its kernels (up to 32 tokens: weight
+streaming; more: LDS-tiled MFMA; fp32 or other shapes: one thread per output).
+
+Bars: RoPE as the compressed rows (bf16 within 2 ulp of the pair's norm, fp32 max-rel
+1e-5 per head); projection max-rel per (token, group) row 4e-3 in bf16 (two ulps of the
+output rounding; the fp32 accumulation of up to 4096 products adds ~1e-6) and 1e-5 in fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_dsv4_amd as K
+from sparse_attention_dsv4_amd.layer import LayerSpec, output_path
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+
+
+def _inv_freq(rd, theta=160000.0):
+    return torch.tensor([theta ** (-2.0 * i / rd) for i in range(rd // 2)], dtype=torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("inverse", [False, True], ids=["forward", "inverse"])
+@pytest.mark.parametrize("H,D,rd", [(64, 512, 64), (1, 512, 64), (64, 128, 64), (3, 20, 6)],
+                         ids=["q", "kv", "qi", "odd"])
+def test_rope_matches_oracle(H, D, rd, inverse, dtype):
+    B, S = 2, 37
+    pos0 = [0, (1 << 20) + 13]                          # near zero and far along
+    x = synth.normal((B, S, H, D), seed=H + D + rd, stream="rope_x", dtype=dtype, device="cuda")
+    inv = _inv_freq(rd)
+    y = x.clone()
+    K.dsv4_rope(K.RopeCfg(H, D, rd, inverse, dtype), y, pos0, inv.cuda())
+    torch.cuda.synchronize()
+    for b in range(B):
+        pos = np.arange(S) + pos0[b]
+        ref = oracle.rope_heads(G.f64(x[b]), pos, inv.numpy(), inverse=inverse)
+        G.assert_rows_match(G.f64(y[b]), ref, "bf16" if dtype == torch.bfloat16 else "f32",
+                            f"rope seq {b}", rd)
+    # the inverse undoes the forward (up to the storage rounding of the two passes)
+    z = y.clone()
+    K.dsv4_rope(K.RopeCfg(H, D, rd, not inverse, dtype), z, pos0, inv.cuda())
+    torch.cuda.synchronize()
+    tol = 2 ** -6 if dtype == torch.bfloat16 else 1e-5
+    assert G.max_rel_rows(G.f64(z), G.f64(x)).max() <= tol
+
+
+def _proj_case(T, Gr, Kd, R, dtype, seed, sample=None):
+    x = synth.normal((T, Gr, Kd), seed=seed, stream="proj_x", dtype=dtype, device="cuda")
+    w = synth.normal((Gr, R, Kd), seed=seed, stream="proj_w", scale=Kd ** -0.5, dtype=dtype,
+                     device="cuda")
+    y = torch.full((T, Gr, R), float("nan"), dtype=dtype, device="cuda")
+    K.dsv4_grouped_proj(K.GprojCfg(Gr, Kd, R, dtype), x, w, y)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if sample is None else np.unique(np.concatenate(
+        [[0, T - 1], np.random.default_rng(seed).integers(0, T, sample)]))
+    idx = torch.as_tensor(rows, device=x.device)
+    xs = G.f64(x[idx]).reshape(len(rows), Gr, Kd)
+    # the oracle takes [tokens, H, D]: here H = G heads of width K
+    ref = oracle.grouped_out_proj(xs, G.f64(w)).reshape(len(rows), Gr, R)
+    got = G.f64(y[idx])
+    assert np.isfinite(got).all(), "outputs left unwritten"
+    mr = G.max_rel_rows(got, ref)
+    bar = 4e-3 if dtype == torch.bfloat16 else 1e-5
+    assert mr.max() <= bar, f"max-rel {mr.max():.3g} (T={T}, G={Gr}, K={Kd}, R={R})"
+    return mr.max()
+
+
+@pytest.mark.parametrize("T", [1, 8, 31, 32])
+def test_grouped_proj_streaming(T):
+    """Decode shapes (wo_a: 8 groups x 1024 x 4096): the weight-streaming kernel."""
+    _proj_case(T, 8, 4096, 1024, torch.bfloat16, seed=100 + T)
+
+
+@pytest.mark.parametrize("T", [33, 200, 2048])
+def test_grouped_proj_tiled(T):
+    """Prefill shapes: 128 x 256 tiles; 33 and 200 leave ragged token tiles."""
+    _proj_case(T, 8, 4096, 1024, torch.bfloat16, seed=200 + T, sample=None if T < 2048 else 96)
+
+
+def test_grouped_proj_other_k():
+    """Smaller K on both MFMA kernels (K = 512 and 1536)."""
+    _proj_case(5, 2, 512, 64, torch.bfloat16, seed=7)
+    _proj_case(300, 3, 1536, 256, torch.bfloat16, seed=8)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_grouped_proj_generic(dtype):
+    """Shapes the MFMA kernels do not take (and fp32): one thread per output."""
+    _proj_case(9, 3, 40, 24, dtype, seed=9)
+    _proj_case(70, 2, 96, 48, dtype, seed=10)
+
+
+@pytest.mark.parametrize("S", [1, 40], ids=["decode", "prefill"])
+def test_output_path_matches_oracle(S):
+    """Attention output -> inverse RoPE (rounded to bf16, as the stored activation) -> grouped
+    projection, end to end through the layer's output path at the layer's shapes."""
+    spec = LayerSpec(ratio=4)
+    B, Gr, R = 3, 8, 1024
+    Kd = spec.heads // Gr * spec.dim
+    pos0 = [7, 4096 + 3, 65536 + 100]
+    o = synth.normal((B, S, spec.heads, spec.dim), seed=31 + S, stream="attn_out",
+                     dtype=torch.bfloat16, device="cuda")
+    wo_a = synth.normal((Gr, R, Kd), seed=31, stream="wo_a", scale=Kd ** -0.5,
+                        dtype=torch.bfloat16, device="cuda")
+    inv = _inv_freq(spec.rope_dim)
+    o_in = G.f64(o)
+    y = output_path(spec, o, pos0, inv.cuda(), wo_a)
+    torch.cuda.synchronize()
+    w64 = G.f64(wo_a)
+    for b in range(B):
+        pos = np.arange(S) + pos0[b]
+        turned = oracle.bf16_round(oracle.rope_heads(o_in[b], pos, inv.numpy(), inverse=True))
+        ref = oracle.grouped_out_proj(turned, w64).reshape(S, Gr, R)
+        mr = G.max_rel_rows(G.f64(y[b]), ref)
+        assert mr.max() <= 4e-3, f"sequence {b}: max-rel {mr.max():.3g}"
