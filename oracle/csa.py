@@ -346,4 +346,4 @@ def grouped_out_proj(o, wo_a) -> np.ndarray:
     g, r, k = w.shape
     assert h % g == 0 and k == (h // g) * d
     xo = o.reshape(n, g, k)
-    return np.einsum("ngk,grk->ngr", xo, w).reshape(n, g * r)
+    return np.stack([xo[:, j] @ w[j].T for j in range(g)], axis=1).reshape(n, g * r)
