@@ -190,3 +190,19 @@ def output_path(spec: LayerSpec, o: torch.Tensor, pos0, inv_freq: torch.Tensor,
         y = torch.empty(B, S, G, R, dtype=spec.dtype, device=o.device)
     dsv4_grouped_proj(GprojCfg(G, Kd, R, spec.dtype), o.view(B * S, G, Kd), wo_a, y.view(B * S, G, R))
     return y
+
+
+def compressor_lanes(x: torch.Tensor, w_kv: torch.Tensor, w_gate: torch.Tensor):
+    """A compressor's two lanes from the layer's hidden states: a = x w_kv^T and
+    g = x w_gate^T (the ratio-4 layer's wkv and wgate are [1024, 4096]: [MLXLM-1189]
+    Thump604's fix list).  x [T, hidden]; w_kv, w_gate [coff*D, hidden]; returns a, g
+    [T, coff*D], ready for dsv4_compress_prefill (one sequence's chunk) or, with one token
+    per sequence, dsv4_compress_step.  Two dsv4_grouped_proj calls with one group."""
+    T, Kd = x.shape
+    W = w_kv.shape[0]
+    cfg = GprojCfg(1, Kd, W, x.dtype)
+    a = torch.empty(T, W, dtype=x.dtype, device=x.device)
+    g = torch.empty(T, W, dtype=x.dtype, device=x.device)
+    dsv4_grouped_proj(cfg, x.view(T, 1, Kd), w_kv.view(1, W, Kd), a.view(T, 1, W))
+    dsv4_grouped_proj(cfg, x.view(T, 1, Kd), w_gate.view(1, W, Kd), g.view(T, 1, W))
+    return a, g

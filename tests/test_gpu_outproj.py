@@ -1,7 +1,8 @@
 """The layer's neighbours through the C ABI against the oracle (needs a gfx950 GPU):
-RoPE of per-head vectors and its inverse (dsv4_rope), and the grouped block-diagonal output
+RoPE of per-head vectors and its inverse (dsv4_rope), the grouped block-diagonal output
 projection (dsv4_grouped_proj) on all three of its kernels (up to 32 tokens: weight
-streaming; more: LDS-tiled MFMA; fp32 or other shapes: one thread per output).
+streaming; more: LDS-tiled MFMA; fp32 or other shapes: one thread per output), and the
+compressor lanes projected from hidden states by the same call with one group.
 
 Bars: RoPE as the compressed rows (bf16 within 2 ulp of the pair's norm, fp32 max-rel
 1e-5 per head); projection max-rel per (token, group) row 4e-3 in bf16 (two ulps of the
@@ -14,7 +15,8 @@ import torch
 import oracle
 import synth
 import sparse_attention_dsv4_amd as K
-from sparse_attention_dsv4_amd.layer import LayerSpec, output_path
+import synth.csa as SC
+from sparse_attention_dsv4_amd.layer import LayerSpec, compressor_lanes, output_path
 from tests import gpu_harness as G
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +127,39 @@ def test_output_path_matches_oracle(S):
         ref = oracle.grouped_out_proj(turned, w64).reshape(S, Gr, R)
         mr = G.max_rel_rows(G.f64(y[b]), ref)
         assert mr.max() <= 4e-3, f"sequence {b}: max-rel {mr.max():.3g}"
+
+
+@pytest.mark.parametrize("T", [1, 8, 300], ids=["step", "b8", "chunk300"])
+def test_compressor_lanes_from_hidden_states(T):
+    """hidden [T, 4096] -> a, g [T, 1024] (wkv, wgate [1024, 4096]) -> rows of the ratio-4
+    compressor, against the oracle's matmul (rounded to bf16, the stored lanes) and rows."""
+    spec = LayerSpec(ratio=4)
+    W, hid = spec.coff * spec.dim, 4096
+    x = synth.normal((T, hid), seed=51 + T, stream="hidden", dtype=torch.bfloat16, device="cuda")
+    wkv = synth.normal((W, hid), seed=51, stream="wkv", scale=hid ** -0.5, dtype=torch.bfloat16,
+                       device="cuda")
+    wg = synth.normal((W, hid), seed=51, stream="wgate", scale=hid ** -0.5, dtype=torch.bfloat16,
+                      device="cuda")
+    a, g = compressor_lanes(x, wkv, wg)
+    torch.cuda.synchronize()
+    x64 = G.f64(x)[:, None, :]
+    ra = oracle.grouped_out_proj(x64, G.f64(wkv)[None])
+    rg = oracle.grouped_out_proj(x64, G.f64(wg)[None])
+    for got, ref, n in ((a, ra, "a"), (g, rg, "g")):
+        mr = G.max_rel_rows(G.f64(got), ref)
+        assert mr.max() <= 4e-3, f"lane {n}: max-rel {mr.max():.3g}"
+    if T < 2 * spec.ratio:
+        return
+    # the lanes drive the compressor: rows from the GPU lanes against the oracle's rows from
+    # the same (bf16) lanes
+    par = SC.layer_params(spec, 51, device="cuda")
+    cc = spec.comp_cfg()
+    state = torch.empty(1, K.dsv4_comp_state_bytes(cc, 1), dtype=torch.uint8, device="cuda")
+    rows = torch.empty(1, T // spec.ratio, spec.dim, dtype=torch.bfloat16, device="cuda")
+    K.dsv4_compress_prefill(cc, state, a[None], g[None], [0], par["ape"], par["norm_w"],
+                            par["inv_freq"], rows)
+    torch.cuda.synchronize()
+    ref_rows = oracle.compressor_rows(G.f64(a), G.f64(g), G.f64(par["ape"]), G.f64(par["norm_w"]),
+                                      par["inv_freq"].cpu().numpy(), ratio=spec.ratio,
+                                      overlap=spec.is_overlap, eps=spec.eps, store="bf16")
+    G.assert_rows_match(G.f64(rows[0]), ref_rows, "bf16", "rows from projected lanes", spec.rope_dim)
