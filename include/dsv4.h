@@ -64,6 +64,10 @@ typedef struct {
     int32_t rope_dim;  /* rd, even, 0 <= rd <= D: RoPE on the last rd dims                 */
     float   eps;       /* RMSNorm epsilon (>= 0)                                           */
     int32_t dtype;     /* dsv4_dtype                                                      */
+    int32_t retain;    /* tokens of rollback the frontier state keeps (0..2^20): the state
+                          holds nw = coff + ceil(retain / r) windows, so a trim of up to
+                          `retain` tokens back across window boundaries finds them again
+                          (MTPLX PR #216 speculative-decode comment: exact trim)          */
 } dsv4_comp_cfg;
 
 /* Indexer.  Pages: PR #1189 stepnoy's patch ("Reference scoring") and aidiffuser's indexer
@@ -90,6 +94,10 @@ typedef struct {
     int32_t topk;      /* k: width of sel rows (ignored when sel == NULL)                  */
     float   scale;     /* logit scale applied to q . x                                     */
     int32_t dtype;     /* dsv4_dtype                                                      */
+    int32_t retain;    /* tokens of rollback the window ring keeps (0..2^20): the ring has
+                          W + retain slots, token t in slot t % (W + retain); retention and
+                          attendance are separate, only W tokens are attended (MTPLX PR
+                          #216 speculative-decode comment)                                 */
 } dsv4_attn_cfg;
 
 /* Library identification and the thread-local message of the last failed call. */
@@ -160,7 +168,7 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
 /* Decode attention: one query per sequence at position pos[b].
  *   q        [batch, H, D]     query heads
  *   kv_new   [batch, D]        latent of token pos[b]; written into win_ring slot pos % W
- *   win_ring [batch, W, D]     slot t % W holds token t for the W-1 tokens before pos[b]
+ *   win_ring [batch, W+retain, D] slot t % (W+retain) holds token t for the tokens before pos[b]
  *                              (slots of tokens < 0 are never read)
  *   rows     [batch, row_cap, D] compressed rows (NULL when cfg->ratio == 0)
  *   sel      [batch, k] int32 or NULL: NULL attends every visible row (j < (pos+1)/r);

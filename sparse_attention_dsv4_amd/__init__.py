@@ -45,7 +45,8 @@ class Dsv4Error(RuntimeError):
 
 class _CompCfg(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_int32), ("overlap", ctypes.c_int32), ("dim", ctypes.c_int32),
-                ("rope_dim", ctypes.c_int32), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rope_dim", ctypes.c_int32), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("retain", ctypes.c_int32)]
 
 
 class _IndexCfg(ctypes.Structure):
@@ -56,7 +57,7 @@ class _IndexCfg(ctypes.Structure):
 class _AttnCfg(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("ratio", ctypes.c_int32), ("topk", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("retain", ctypes.c_int32)]
 
 
 class _RopeCfg(ctypes.Structure):
@@ -82,6 +83,7 @@ class CompCfg:
     rope_dim: int
     eps: float = 1e-6
     dtype: torch.dtype = torch.bfloat16
+    retain: int = 0               # tokens of rollback the frontier state keeps
 
     @property
     def coff(self) -> int:
@@ -89,7 +91,7 @@ class CompCfg:
 
     def c(self):
         return _CompCfg(self.ratio, int(self.overlap), self.dim, self.rope_dim, self.eps,
-                        _DTYPES[self.dtype])
+                        _DTYPES[self.dtype], self.retain)
 
 
 @dataclass(frozen=True)
@@ -136,10 +138,15 @@ class AttnCfg:
     topk: int
     scale: float
     dtype: torch.dtype = torch.bfloat16
+    retain: int = 0               # tokens of rollback the window ring keeps (W + retain slots)
+
+    @property
+    def ring_slots(self) -> int:
+        return self.window + self.retain
 
     def c(self):
         return _AttnCfg(self.heads, self.dim, self.window, self.ratio, self.topk, self.scale,
-                        _DTYPES[self.dtype])
+                        _DTYPES[self.dtype], self.retain)
 
 
 _lib = None
@@ -322,7 +329,7 @@ def dsv4_csa_attn_decode(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_rows, p
     B = q.shape[0]
     _need(q, (B, cfg.heads, cfg.dim), cfg.dtype, "q")
     _need(kv_new, (B, cfg.dim), cfg.dtype, "kv_new")
-    _need(win_ring, (B, cfg.window, cfg.dim), cfg.dtype, "win_ring")
+    _need(win_ring, (B, cfg.ring_slots, cfg.dim), cfg.dtype, "win_ring")
     _need(sinks, (cfg.heads,), torch.float32, "sinks")
     _need(out, (B, cfg.heads, cfg.dim), cfg.dtype, "out")
     _attn_common_checks(cfg, rows, sel, n_rows, B, (B, cfg.topk))
@@ -343,7 +350,7 @@ def dsv4_csa_attn_decode_store(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_r
     B = q.shape[0]
     _need(q, (B, cfg.heads, cfg.dim), cfg.dtype, "q")
     _need(kv_new, (B, cfg.dim), cfg.dtype, "kv_new")
-    _need(win_ring, (B, cfg.window, cfg.dim), cfg.dtype, "win_ring")
+    _need(win_ring, (B, cfg.ring_slots, cfg.dim), cfg.dtype, "win_ring")
     _need(sinks, (cfg.heads,), torch.float32, "sinks")
     _need(out, (B, cfg.heads, cfg.dim), cfg.dtype, "out")
     _attn_common_checks(cfg, rows, sel, n_rows, B, (B, cfg.topk))
@@ -372,7 +379,7 @@ def dsv4_csa_attn_prefill(cfg: AttnCfg, q, kv_new, win_ring, rows, sel, n_rows, 
     B, S = q.shape[0], q.shape[1]
     _need(q, (B, S, cfg.heads, cfg.dim), cfg.dtype, "q")
     _need(kv_new, (B, S, cfg.dim), cfg.dtype, "kv_new")
-    _need(win_ring, (B, cfg.window, cfg.dim), cfg.dtype, "win_ring")
+    _need(win_ring, (B, cfg.ring_slots, cfg.dim), cfg.dtype, "win_ring")
     _need(sinks, (cfg.heads,), torch.float32, "sinks")
     _need(out, (B, S, cfg.heads, cfg.dim), cfg.dtype, "out")
     _attn_common_checks(cfg, rows, sel, n_rows, B, (B, S, cfg.topk))

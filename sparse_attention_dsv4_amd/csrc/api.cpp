@@ -49,6 +49,12 @@ constexpr int64_t kPosLimit = (int64_t(1) << 31) - 2;   // positions travel as i
 bool dtype_ok(int32_t d) { return d == DSV4_BF16 || d == DSV4_F32; }
 size_t dtype_size(int32_t d) { return d == DSV4_BF16 ? 2 : 4; }
 
+// Windows of the frontier state: the coff pooled ones plus those a trim of `retain` tokens
+// back can reach.
+int64_t state_windows(const dsv4_comp_cfg* c) {
+    return (c->overlap ? 2 : 1) + (int64_t(c->retain) + c->ratio - 1) / c->ratio;
+}
+
 int check_comp_cfg(const dsv4_comp_cfg* c) {
     if (!c) return fail(DSV4_EINVAL, "cfg is NULL");
     if (c->ratio < 1) return fail(DSV4_EINVAL, "ratio %d < 1", c->ratio);
@@ -58,7 +64,8 @@ int check_comp_cfg(const dsv4_comp_cfg* c) {
         return fail(DSV4_EINVAL, "rope_dim %d must be even and within 0..dim", c->rope_dim);
     if (!(c->eps >= 0.f) || !std::isfinite(c->eps)) return fail(DSV4_EINVAL, "eps must be >= 0");
     if (!dtype_ok(c->dtype)) return fail(DSV4_EINVAL, "unknown dtype %d", c->dtype);
-    if (int64_t(c->ratio) * (c->overlap ? 2 : 1) * 2 * c->dim > (int64_t(1) << 30))
+    if (c->retain < 0 || c->retain > (1 << 20)) return fail(DSV4_EINVAL, "retain %d outside 0..2^20", c->retain);
+    if (int64_t(c->ratio) * state_windows(c) * (c->overlap ? 2 : 1) * 2 * c->dim > (int64_t(1) << 30))
         return fail(DSV4_EUNSUPPORTED, "state per sequence too large");
     return DSV4_OK;
 }
@@ -84,6 +91,7 @@ int check_attn_cfg(const dsv4_attn_cfg* c) {
     if (c->topk < 0) return fail(DSV4_EINVAL, "topk %d < 0", c->topk);
     if (!std::isfinite(c->scale)) return fail(DSV4_EINVAL, "scale is not finite");
     if (!dtype_ok(c->dtype)) return fail(DSV4_EINVAL, "unknown dtype %d", c->dtype);
+    if (c->retain < 0 || c->retain > (1 << 20)) return fail(DSV4_EINVAL, "retain %d outside 0..2^20", c->retain);
     return DSV4_OK;
 }
 
@@ -142,7 +150,8 @@ const char* dsv4_last_error(void) { return g_err.c_str(); }
 size_t dsv4_comp_state_bytes(const dsv4_comp_cfg* cfg, int32_t batch) {
     if (check_comp_cfg(cfg) != DSV4_OK || batch < 0) return 0;
     const int coff = cfg->overlap ? 2 : 1;
-    return size_t(batch) * 2 * coff * size_t(cfg->ratio) * coff * cfg->dim * dtype_size(cfg->dtype);
+    return size_t(batch) * 2 * size_t(state_windows(cfg)) * size_t(cfg->ratio) * coff * cfg->dim *
+           dtype_size(cfg->dtype);
 }
 
 size_t dsv4_index_workspace_bytes(const dsv4_index_cfg* cfg, int32_t batch, int64_t s,
@@ -179,7 +188,8 @@ int dsv4_compress_prefill(const dsv4_comp_cfg* cfg, void* state, const void* kv_
                         (long long)((lb + n_new) / cfg->ratio), (long long)row_cap);
     }
     dsv4::CompressJob j;
-    j.r = cfg->ratio; j.coff = cfg->overlap ? 2 : 1; j.D = cfg->dim; j.rd = cfg->rope_dim;
+    j.r = cfg->ratio; j.coff = cfg->overlap ? 2 : 1; j.nw = int(state_windows(cfg));
+    j.D = cfg->dim; j.rd = cfg->rope_dim;
     j.eps = cfg->eps; j.bf16 = cfg->dtype == DSV4_BF16;
     j.state = state; j.lane_a = kv_lane; j.lane_g = gate_lane; j.ape = ape; j.gamma = norm_w;
     j.inv_freq = inv_freq; j.rows = rows; j.row_cap = row_cap; j.n_new = n_new;
@@ -296,10 +306,12 @@ static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_n
                             (long long)((pos0[b] + 1) / cfg->ratio - 1));
         const int coff = fs.cfg->overlap ? 2 : 1;
         fronts[f].state = fs.state; fronts[f].lane_a = fs.kv_lane; fronts[f].lane_g = fs.gate_lane;
-        fronts[f].r = fs.cfg->ratio; fronts[f].coff = coff; fronts[f].W = coff * fs.cfg->dim;
+        fronts[f].r = fs.cfg->ratio; fronts[f].nw = int(state_windows(fs.cfg));
+        fronts[f].W = coff * fs.cfg->dim;
     }
     dsv4::AttnJob j;
-    j.H = cfg->heads; j.D = cfg->dim; j.W = cfg->window; j.r = cfg->ratio; j.k = cfg->topk;
+    j.H = cfg->heads; j.D = cfg->dim; j.W = cfg->window; j.Wr = cfg->window + cfg->retain;
+    j.r = cfg->ratio; j.k = cfg->topk;
     j.scale = cfg->scale; j.bf16 = cfg->dtype == DSV4_BF16;
     j.q = q; j.kv_new = kv_new; j.ring = win_ring; j.rows = has_rows ? rows : nullptr;
     j.row_cap = row_cap; j.sel = sel; j.sinks = sinks; j.out = out; j.S = s; j.batch = batch;

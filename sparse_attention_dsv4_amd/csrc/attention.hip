@@ -23,8 +23,10 @@
 // that attn_combine_kernel merges with the sink; a query handled by one workgroup normalises
 // and writes its output.
 //
-// The ring update runs after the attention kernel on the stream: writing token t evicts
-// token t - W, which an earlier query of the same call may still need.
+// The window ring holds Wr >= W slots (token t in slot t % Wr): the W attended tokens plus
+// those retained for rollback.  The ring update runs after the attention kernel on the
+// stream: writing token t evicts token t - Wr, which an earlier query of the same call may
+// still need.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -39,6 +41,7 @@ constexpr size_t kAttnLdsMax = 65536 - 1024;   // dynamic LDS: 4 B per latent di
 template <typename T>
 struct AttnArgs {
     int H, D, W, r, k;
+    int Wr;            // ring slots
     float scale;
     const T* q;
     const T* kv_new;
@@ -59,7 +62,7 @@ __device__ __forceinline__ const T* key_row(const AttnArgs<T>& a, int b, int32_t
     if (code >= 0) return a.rows + (size_t(b) * a.row_cap + size_t(code)) * a.D;
     const int64_t t = -int64_t(code) - 1;
     if (t >= pos0) return a.kv_new + (size_t(b) * a.S + size_t(t - pos0)) * a.D;
-    return a.ring + (size_t(b) * a.W + size_t(t % a.W)) * a.D;
+    return a.ring + (size_t(b) * a.Wr + size_t(t % a.Wr)) * a.D;
 }
 
 template <typename T>
@@ -148,11 +151,11 @@ __global__ void __launch_bounds__(kAttnThreads)
 ring_update_kernel(AttnArgs<T> a, SeqInts pos0v) {
     const int b = blockIdx.y;
     const int64_t pos0 = pos0v.v[b];
-    const int64_t first = a.S > a.W ? pos0 + a.S - a.W : pos0;
+    const int64_t first = a.S > a.Wr ? pos0 + a.S - a.Wr : pos0;
     const int64_t t = first + blockIdx.x;
     if (t >= pos0 + a.S) return;
     const T* src = a.kv_new + (size_t(b) * a.S + size_t(t - pos0)) * a.D;
-    T* dst = a.ring + (size_t(b) * a.W + size_t(t % a.W)) * a.D;
+    T* dst = a.ring + (size_t(b) * a.Wr + size_t(t % a.Wr)) * a.D;
     for (int d = threadIdx.x; d < a.D; d += blockDim.x) dst[d] = src[d];
 }
 
@@ -172,10 +175,10 @@ hipError_t run(const AttnJob& j, hipStream_t st) {
         }
         const size_t qoff = size_t(b0) * j.S;
         AttnArgs<T> a;
-        a.H = j.H; a.D = j.D; a.W = j.W; a.r = j.r; a.k = j.k; a.scale = j.scale;
+        a.H = j.H; a.D = j.D; a.W = j.W; a.Wr = j.Wr; a.r = j.r; a.k = j.k; a.scale = j.scale;
         a.q = static_cast<const T*>(j.q) + qoff * j.H * j.D;
         a.kv_new = static_cast<const T*>(j.kv_new) + qoff * j.D;
-        a.ring = static_cast<T*>(j.ring) + size_t(b0) * j.W * j.D;
+        a.ring = static_cast<T*>(j.ring) + size_t(b0) * j.Wr * j.D;
         a.rows = j.rows ? static_cast<const T*>(j.rows) + size_t(b0) * j.row_cap * j.D : nullptr;
         a.row_cap = j.row_cap;
         a.sel = j.sel ? j.sel + qoff * j.k : nullptr;
@@ -188,7 +191,7 @@ hipError_t run(const AttnJob& j, hipStream_t st) {
                            dim3(kAttnThreads), lds, st, a, pos, nr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t nupd = std::min<int64_t>(j.S, j.W);
+        const int64_t nupd = std::min<int64_t>(j.S, j.Wr);
         DSV4_LAUNCH("ring_update", ring_update_kernel<T>, dim3(unsigned(nupd), nb), dim3(kAttnThreads), 0,
                            st, a, pos);
         e = hipGetLastError();
@@ -251,16 +254,17 @@ struct AttnMfmaArgs {
     bf16* out;
     int64_t S;
     int W, r;
+    int Wr;                               // ring slots (W + tokens retained for rollback)
     float scale_log2;                     // logit scale * log2(e)
     int keys_per_split, n_splits;
     float* part_ml;                       // [B][S][n_splits][H][2]  running max, sum
     float* part_o;                        // [B][S][n_splits][H][D]  unnormalised output
     // decode: compressor frontier stores of this token (lanes of a step completing no row)
     struct Front {
-        bf16* state;                      // [B][2][coff][r][W]
+        bf16* state;                      // [B][2][nw][r][W]
         const bf16* a;                    // [B][W] kv lane, then gate lane
         const bf16* g;
-        int r, coff, W;
+        int r, nw, W;
     } fr[2];
     int n_fr;
 };
@@ -292,11 +296,11 @@ struct TileCtx {
 __device__ __forceinline__ void key_ctx(TileCtx& c, const AttnMfmaArgs& a, int b, int t0, int pos0) {
     c.t0 = t0;
     c.pos0 = pos0;
-    c.W = uint32_t(a.W);
+    c.W = uint32_t(a.Wr);
     c.slot0 = uint32_t(t0) % c.W;
     c.sel = a.sel != nullptr;
     c.rows = a.rows ? a.rows + size_t(b) * size_t(a.row_cap) * MD : nullptr;
-    c.ring = a.ring + size_t(b) * size_t(a.W) * MD;
+    c.ring = a.ring + size_t(b) * size_t(a.Wr) * MD;
     c.kv_new = a.kv_new + size_t(b) * size_t(a.S) * MD;
 }
 
@@ -819,7 +823,7 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int nk = c.nrow + nwin;
     const size_t pbase = (size_t(b) * a.n_splits + split) * MH + DHG * hg;
     if (split == 0 && hg == 0) {
-        // store the new latent in its ring slot.  Slot p % W holds token p - W, which this
+        // store the new latent in its ring slot.  Slot p % Wr holds token p - Wr, which this
         // query does not read (its window is p-W+1 .. p, with p itself taken from kv_new),
         // so the store cannot race the key loads of the other workgroups.
         const uint4* src = reinterpret_cast<const uint4*>(c.kv_new);
@@ -830,8 +834,8 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         // the compressor step of this token for lane hg - 1, at a step that completes no row:
         // its kv and gate lanes go to the token's frontier slot (nothing here reads the state)
         const AttnMfmaArgs::Front f = hg == 1 ? a.fr[0] : a.fr[1];
-        bf16* sa = f.state + size_t(b) * (size_t(2) * f.coff * f.r * f.W) + frontier_slot(p, f.r, f.coff, f.W);
-        bf16* sg = sa + size_t(f.coff) * f.r * f.W;
+        bf16* sa = f.state + size_t(b) * (size_t(2) * f.nw * f.r * f.W) + frontier_slot(p, f.r, f.nw, f.W);
+        bf16* sg = sa + size_t(f.nw) * f.r * f.W;
         const bf16* la = f.a + size_t(b) * f.W;
         const bf16* lg = f.g + size_t(b) * f.W;
         for (int c = tid; c < f.W; c += 256) {
@@ -1067,7 +1071,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         AttnMfmaArgs a;
         a.q = static_cast<const bf16*>(j.q) + qoff * MH * MD;
         a.kv_new = static_cast<const bf16*>(j.kv_new) + qoff * MD;
-        a.ring = static_cast<const bf16*>(j.ring) + size_t(b0) * j.W * MD;
+        a.ring = static_cast<const bf16*>(j.ring) + size_t(b0) * j.Wr * MD;
         a.rows = j.rows ? static_cast<const bf16*>(j.rows) + size_t(b0) * j.row_cap * MD : nullptr;
         a.row_cap = j.row_cap;
         a.sel = j.sel ? j.sel + qoff * j.k : nullptr;
@@ -1076,6 +1080,7 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         a.out = static_cast<bf16*>(j.out) + qoff * MH * MD;
         a.S = j.S;
         a.W = j.W;
+        a.Wr = j.Wr;
         a.r = j.r;
         a.scale_log2 = j.scale * kLog2e;
         const bool decode = j.S == 1;
@@ -1086,11 +1091,11 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         a.n_fr = decode ? j.n_fronts : 0;
         for (int f = 0; f < a.n_fr; ++f) {
             const FrontierJob& fj = j.fronts[f];
-            a.fr[f].state = static_cast<bf16*>(fj.state) + size_t(b0) * 2 * fj.coff * fj.r * fj.W;
+            a.fr[f].state = static_cast<bf16*>(fj.state) + size_t(b0) * 2 * fj.nw * fj.r * fj.W;
             a.fr[f].a = static_cast<const bf16*>(fj.lane_a) + size_t(b0) * fj.W;
             a.fr[f].g = static_cast<const bf16*>(fj.lane_g) + size_t(b0) * fj.W;
             a.fr[f].r = fj.r;
-            a.fr[f].coff = fj.coff;
+            a.fr[f].nw = fj.nw;
             a.fr[f].W = fj.W;
         }
         float* ws = static_cast<float*>(j.ws);
@@ -1117,10 +1122,10 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         }
         if (j.S == 1) continue;          // the attention kernel stored the decode token
         AttnArgs<bf16> ra;
-        ra.D = MD; ra.W = j.W; ra.S = j.S;
+        ra.D = MD; ra.W = j.W; ra.Wr = j.Wr; ra.S = j.S;
         ra.kv_new = a.kv_new;
-        ra.ring = static_cast<bf16*>(j.ring) + size_t(b0) * j.W * MD;
-        const int64_t nupd = std::min<int64_t>(j.S, j.W);
+        ra.ring = static_cast<bf16*>(j.ring) + size_t(b0) * j.Wr * MD;
+        const int64_t nupd = std::min<int64_t>(j.S, j.Wr);
         DSV4_LAUNCH("ring_update", ring_update_kernel<bf16>, dim3(unsigned(nupd), nb), dim3(256), 0, st, ra, pos);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

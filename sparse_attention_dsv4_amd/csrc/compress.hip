@@ -9,15 +9,17 @@
 // RoPE'd at birth at j*r); MTPLX PR #216 "Decode path" (pool in fp32, cast to the storage
 // dtype before the norm).
 //
-// Layout of the frontier state of one sequence: [lane (kv, gate)][coff][r][coff*D].  Token t
-// lives in window slot (t / r) % coff at position t % r.  With coff = 2 the state holds the
-// previous complete window and the current partial one; with coff = 1 only the current one.
+// Layout of the frontier state of one sequence: [lane (kv, gate)][nw][r][coff*D].  Token t
+// lives in window slot (t / r) % nw at position t % r.  nw = coff + ceil(retain / r): with
+// coff = 2 the state holds the previous complete window and the current partial one, with
+// coff = 1 only the current one, and `retain` tokens of rollback add older windows that a
+// trim back across a window boundary needs again.
 //
 // Two kernels per call:
 //   compress_rows_kernel  one workgroup per emitted row: reads every slot of the row from
 //                         the state (tokens before the call) or the new lanes, pools per
 //                         channel with an online softmax, then norm and RoPE in LDS;
-//   compress_state_kernel copies the new tokens of the last coff windows into the state.
+//   compress_state_kernel copies the new tokens of the last nw windows into the state.
 // The second runs after the first on the stream, because a row of this call may read a
 // state slot that the update overwrites.  With one new token per sequence (decode) the two
 // fuse into compress_step_kernel.
@@ -33,7 +35,7 @@ constexpr int kStepThreads = 512;     // decode step: one latent channel per thr
 
 template <typename T>
 struct CompArgs {
-    int r, coff, D, rd;
+    int r, coff, nw, D, rd;
     float eps;
     T* state;
     const T* lane_a;
@@ -60,15 +62,15 @@ __device__ __forceinline__ void pool_slot(float logit, float v, float& m, float&
 
 // Row j of sequence b: pooled per channel with an online softmax over its slots, rounded,
 // RMS-normalised, rounded, RoPE'd on the last rd dims at position j*r, rounded.  Slot s of
-// window w is token w*r + s: tokens before the call (t < lb) sit in state window (w % coff)
+// window w is token w*r + s: tokens before the call (t < lb) sit in state window (w % nw)
 // at position s, later ones in the new lanes at t - lb.  All positions fit in 32 bits.
 template <typename T>
 __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int lb,
                                          float* zrow, float* red) {
     const int D = a.D, W = a.coff * a.D, r = a.r;
-    const size_t st = size_t(2) * a.coff * r * W;
+    const size_t st = size_t(2) * a.nw * r * W;
     const T* sa0 = a.state + size_t(b) * st;                 // kv lane of this sequence
-    const T* sg0 = sa0 + size_t(a.coff) * r * W;             // gate lane
+    const T* sg0 = sa0 + size_t(a.nw) * r * W;               // gate lane
     float ss = 0.f;
     for (int c = threadIdx.x; c < D; c += blockDim.x) {
         float m = -INFINITY, l = 0.f, acc = 0.f;
@@ -80,7 +82,7 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
             const int t0 = win * r;
             int n_state = lb - t0;                             // slots taken from the state
             n_state = n_state < 0 ? 0 : (n_state > r ? r : n_state);
-            const size_t wo = size_t(win % a.coff) * r * W + col;
+            const size_t wo = size_t(win % a.nw) * r * W + col;
             const T* sa = sa0 + wo;
             const T* sg = sg0 + wo;
             const T* ap = a.ape + col;
@@ -147,9 +149,9 @@ compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
     const int b = blockIdx.x;
     const int64_t lb = len_before.v[b];
     const int W = a.coff * a.D;
-    const size_t st = size_t(2) * a.coff * a.r * W;
-    T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.coff, W);
-    T* sg = sa + size_t(a.coff) * a.r * W;
+    const size_t st = size_t(2) * a.nw * a.r * W;
+    T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
+    T* sg = sa + size_t(a.nw) * a.r * W;
     for (int c = threadIdx.x; c < W; c += blockDim.x) {
         sa[c] = a.lane_a[size_t(b) * W + c];
         sg[c] = a.lane_g[size_t(b) * W + c];
@@ -163,15 +165,15 @@ compress_state_kernel(CompArgs<T> a, SeqInts len_before) {
     const int b = blockIdx.y;
     const int64_t lb = len_before.v[b];
     const int64_t la = lb + a.n_new;
-    int64_t keep_from = (la / a.r - (a.coff - 1)) * a.r;   // first token of the kept windows
+    int64_t keep_from = (la / a.r - (a.nw - 1)) * a.r;     // first token of the kept windows
     if (keep_from < lb) keep_from = lb;
     const int64_t t = keep_from + blockIdx.x;
     if (t >= la) return;
     const int W = a.coff * a.D;
-    const size_t st = size_t(2) * a.coff * a.r * W;
+    const size_t st = size_t(2) * a.nw * a.r * W;
     const size_t src = (size_t(b) * a.n_new + size_t(t - lb)) * W;
-    T* sa = a.state + size_t(b) * st + frontier_slot(t, a.r, a.coff, W);
-    T* sg = sa + size_t(a.coff) * a.r * W;
+    T* sa = a.state + size_t(b) * st + frontier_slot(t, a.r, a.nw, W);
+    T* sg = sa + size_t(a.nw) * a.r * W;
     for (int c = threadIdx.x; c < W; c += blockDim.x) {
         sa[c] = a.lane_a[src + c];
         sg[c] = a.lane_g[src + c];
@@ -183,9 +185,9 @@ template <typename T>
 __global__ void __launch_bounds__(kCompThreads)
 frontier_store_kernel(FrontierJob f, SeqInts pos) {
     const int b = blockIdx.x;
-    const size_t st = size_t(2) * f.coff * f.r * f.W;
-    T* sa = static_cast<T*>(f.state) + size_t(b) * st + frontier_slot(pos.v[b], f.r, f.coff, f.W);
-    T* sg = sa + size_t(f.coff) * f.r * f.W;
+    const size_t st = size_t(2) * f.nw * f.r * f.W;
+    T* sa = static_cast<T*>(f.state) + size_t(b) * st + frontier_slot(pos.v[b], f.r, f.nw, f.W);
+    T* sg = sa + size_t(f.nw) * f.r * f.W;
     const T* la = static_cast<const T*>(f.lane_a) + size_t(b) * f.W;
     const T* lg = static_cast<const T*>(f.lane_g) + size_t(b) * f.W;
     for (int c = threadIdx.x; c < f.W; c += blockDim.x) {
@@ -197,13 +199,13 @@ frontier_store_kernel(FrontierJob f, SeqInts pos) {
 template <typename T>
 hipError_t run(const CompressJob& j, hipStream_t s) {
     const int W = j.coff * j.D;
-    const size_t st_elems = size_t(2) * j.coff * j.r * W;
+    const size_t st_elems = size_t(2) * j.nw * j.r * W;
     for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
         const int nb = std::min(kSeqSlice, j.batch - b0);
         SeqInts lb{};
         if (j.n_new == 1) {
             CompArgs<T> a;
-            a.r = j.r; a.coff = j.coff; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
+            a.r = j.r; a.coff = j.coff; a.nw = j.nw; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
             a.state = static_cast<T*>(j.state) + size_t(b0) * st_elems;
             a.lane_a = static_cast<const T*>(j.lane_a) + size_t(b0) * W;
             a.lane_g = static_cast<const T*>(j.lane_g) + size_t(b0) * W;
@@ -226,11 +228,11 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
             lb.v[i] = int32_t(l0);
             const int64_t la = l0 + j.n_new;
             max_rows = std::max(max_rows, la / j.r - l0 / j.r);
-            int64_t keep_from = std::max<int64_t>(l0, (la / j.r - (j.coff - 1)) * j.r);
+            int64_t keep_from = std::max<int64_t>(l0, (la / j.r - (j.nw - 1)) * j.r);
             max_keep = std::max(max_keep, la - keep_from);
         }
         CompArgs<T> a;
-        a.r = j.r; a.coff = j.coff; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
+        a.r = j.r; a.coff = j.coff; a.nw = j.nw; a.D = j.D; a.rd = j.rd; a.eps = j.eps;
         a.state = static_cast<T*>(j.state) + size_t(b0) * st_elems;
         a.lane_a = static_cast<const T*>(j.lane_a) + size_t(b0) * j.n_new * W;
         a.lane_g = static_cast<const T*>(j.lane_g) + size_t(b0) * j.n_new * W;
@@ -265,7 +267,7 @@ hipError_t launch_compress(const CompressJob& j, hipStream_t s) {
 hipError_t launch_frontier_store(const FrontierJob& f, bool bf16_, int batch, const int64_t* pos,
                                  hipStream_t s) {
     const size_t es = bf16_ ? sizeof(bf16) : sizeof(float);
-    const size_t st = size_t(2) * f.coff * f.r * f.W;
+    const size_t st = size_t(2) * f.nw * f.r * f.W;
     for (int b0 = 0; b0 < batch; b0 += kSeqSlice) {
         const int nb = std::min(kSeqSlice, batch - b0);
         SeqInts p{};

@@ -8,28 +8,29 @@
 
 namespace dsv4 {
 
-// Frontier state of one compressor lane for one sequence: [lane (kv, gate)][coff][r][coff*D]
-// elements.  Token t sits in window slot (t / r) % coff at position t % r; this is the
-// element offset of its kv-lane entry (the gate lane's is coff * r * coff*D further).
-__host__ __device__ inline size_t frontier_slot(int64_t t, int r, int coff, int W) {
-    return (size_t((t / r) % coff) * size_t(r) + size_t(t % r)) * size_t(W);
+// Frontier state of one compressor lane for one sequence: [lane (kv, gate)][nw][r][coff*D]
+// elements (nw windows: the coff pooled ones plus those retained for rollback).  Token t
+// sits in window slot (t / r) % nw at position t % r; this is the element offset of its
+// kv-lane entry (the gate lane's is nw * r * coff*D further).
+__host__ __device__ inline size_t frontier_slot(int64_t t, int r, int nw, int W) {
+    return (size_t((t / r) % nw) * size_t(r) + size_t(t % r)) * size_t(W);
 }
 
 // One lane's frontier store of a decode step (the token's kv and gate lanes into its slot).
 struct FrontierJob {
-    void* state;               // [B][2][coff][r][coff*D]
+    void* state;               // [B][2][nw][r][coff*D]
     const void* lane_a;        // [B][coff*D]
     const void* lane_g;
-    int r, coff, W;            // W = coff*D
+    int r, nw, W;              // W = coff*D
 };
 hipError_t launch_frontier_store(const FrontierJob& f, bool bf16, int batch, const int64_t* pos,
                                  hipStream_t s);
 
 struct CompressJob {
-    int r, coff, D, rd;
+    int r, coff, nw, D, rd;
     float eps;
     bool bf16;
-    void* state;               // [B][2][coff][r][coff*D]
+    void* state;               // [B][2][nw][r][coff*D]
     const void* lane_a;        // [B][n_new][coff*D]
     const void* lane_g;
     const void* ape;           // [r][coff*D]
@@ -66,11 +67,12 @@ int64_t index_key_stride(int64_t n_max);
 
 struct AttnJob {
     int H, D, W, r, k;
+    int Wr;                    // ring slots: W + the tokens retained for rollback
     float scale;
     bool bf16;
     const void* q;             // [B][S][H][D]
     const void* kv_new;        // [B][S][D]
-    void* ring;                // [B][W][D]
+    void* ring;                // [B][Wr][D]
     const void* rows;          // [B][row_cap][D] or null
     int64_t row_cap;
     const int32_t* sel;        // [B][S][k] or null

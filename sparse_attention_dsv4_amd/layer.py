@@ -42,6 +42,7 @@ class LayerSpec:
     overlap: bool | None = None   # default: ratio == 4
     eps: float = 1e-6
     dtype: torch.dtype = torch.bfloat16
+    rollback: int = 0             # tokens a trim may take back exactly (speculative decode)
 
     @property
     def coff(self) -> int:
@@ -64,18 +65,19 @@ class LayerSpec:
         return self.dim ** -0.5
 
     def comp_cfg(self) -> CompCfg:
-        return CompCfg(self.ratio, self.is_overlap, self.dim, self.rope_dim, self.eps, self.dtype)
+        return CompCfg(self.ratio, self.is_overlap, self.dim, self.rope_dim, self.eps, self.dtype,
+                       self.rollback)
 
     def index_comp_cfg(self) -> CompCfg:
         return CompCfg(self.ratio, self.is_overlap, self.index_dim, self.rope_dim, self.eps,
-                       self.dtype)
+                       self.dtype, self.rollback)
 
     def index_cfg(self) -> IndexCfg:
         return IndexCfg(self.index_heads, self.index_dim, self.topk, self.ratio, self.dtype)
 
     def attn_cfg(self) -> AttnCfg:
         return AttnCfg(self.heads, self.dim, self.window, self.ratio, self.topk, self.scale,
-                       self.dtype)
+                       self.dtype, self.rollback)
 
 
 class CsaLayer:
@@ -87,8 +89,10 @@ class CsaLayer:
         self.fold_stores = fold_stores        # decode: frontier stores ride in the attention
         self.params = params                  # ape, norm_w, ape_i, norm_w_i, inv_freq, sinks
         self.lengths = [0] * batch
+        self.max_lengths = [0] * batch        # furthest position each sequence has written
         dt = spec.dtype
-        self.ring = torch.zeros(batch, spec.window, spec.dim, dtype=dt, device=device)
+        self.ring = torch.zeros(batch, spec.window + spec.rollback, spec.dim, dtype=dt,
+                                device=device)
         self.row_cap = max_tokens // spec.ratio if spec.has_rows else 0
         if spec.has_rows:
             cc = spec.comp_cfg()
@@ -136,7 +140,7 @@ class CsaLayer:
         dsv4_csa_attn_prefill(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
                               self.rows if sp.has_rows else None, sel, self.n_rows(S), pos0,
                               P["sinks"], out, self.ws_attn)
-        self.lengths = [n + S for n in self.lengths]
+        self._advance(S)
         return out
 
     def decode(self, tok: dict, sel_out=None) -> torch.Tensor:
@@ -173,8 +177,41 @@ class CsaLayer:
             dsv4_csa_attn_decode(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
                                  self.rows if sp.has_rows else None, sel, self.n_rows(1), pos,
                                  P["sinks"], out, self.ws_attn)
-        self.lengths = [n + 1 for n in self.lengths]
+        self._advance(1)
         return out
+
+    def _advance(self, n: int):
+        self.lengths = [x + n for x in self.lengths]
+        self.max_lengths = [max(m, x) for m, x in zip(self.max_lengths, self.lengths)]
+
+    # ------------------------------------------------------------------ rollback
+    def rollback_room(self):
+        """Tokens each sequence can take back exactly: the retained depth (spec.rollback)
+        less what earlier trims not yet re-decoded already used."""
+        return [max(0, min(x, self.spec.rollback - (max(m, x) - x)))
+                for x, m in zip(self.lengths, self.max_lengths)]
+
+    def trim(self, n):
+        """Take back the last n[b] tokens of each sequence (an int applies to all), exactly:
+        afterwards every call behaves as if those tokens had never been processed (MTPLX PR
+        #216 speculative-decode comment: emitted rows truncate, the compressor frontiers and
+        the window keep what a rewind needs, and a trim past that bound raises rather than
+        clamps).  Nothing on the device changes: rows past the new count are never read, and
+        the window ring (W + rollback slots) and the frontier states (coff + ceil(rollback / r)
+        windows) still hold every entry the shorter sequences read; re-decoded positions
+        overwrite the stale ones.  Raises ValueError, changing nothing, if any n[b] exceeds
+        rollback_room()[b]."""
+        ns = [int(n)] * self.batch if isinstance(n, int) else [int(v) for v in n]
+        if len(ns) != self.batch:
+            raise ValueError(f"trim takes {self.batch} counts, got {len(ns)}")
+        room = self.rollback_room()
+        for b, (v, r) in enumerate(zip(ns, room)):
+            if v < 0:
+                raise ValueError(f"sequence {b}: negative trim {v}")
+            if v > r:
+                raise ValueError(f"sequence {b}: trim of {v} tokens exceeds the rollback room "
+                                 f"{r} (capacity {self.spec.rollback})")
+        self.lengths = [x - v for x, v in zip(self.lengths, ns)]
 
 
 def output_path(spec: LayerSpec, o: torch.Tensor, pos0, inv_freq: torch.Tensor,
