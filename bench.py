@@ -456,7 +456,7 @@ KERNEL_SOURCES = {"attn": "attention.hip", "ring": "attention.hip", "index": "in
 COPY_CALIB_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
-TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_mfma_ctx65536_chunk2048_ratio4.txt")
+TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_rs_ctx65536_chunk2048_ratio4.txt")
 TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_mfma_decode_ctx262144_b4_stack.txt")
 
 

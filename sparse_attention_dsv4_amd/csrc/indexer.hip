@@ -136,6 +136,7 @@ struct IdxMfmaArgs {
     int r;
     float scale;
     int rows_per_block;
+    int queries_per_group;     // row-stationary kernel: queries one workgroup scores
 };
 
 // Direct global -> LDS copy (16 bytes per lane to lds_base + 16 lane), as inline asm so the
@@ -362,6 +363,105 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             for (int q = 0; q < NQ; ++q)
                 if (hi == 0 && jj < nv[q])
                     a.keys[(size_t(b) * a.S + size_t(qbase + q)) * a.n_stride + size_t(jj)] = score_key(score[v][q]);
+        }
+    }
+}
+
+// Row-stationary scoring for prefill at long context: a workgroup copies a block of RSB rows
+// into LDS once (no copies run while the operands are read) and streams queries through
+// registers: wave w scores queries q_lo + w, q_lo + w + WAVES, ... of the workgroup's
+// group against every 32-row block of the tile a query can see.  Each query's A operand
+// (64 heads x 128 dims) and head weights come from global memory (L2); the two waves of a
+// SIMD hide each other's loads.
+constexpr int RSB = 512;                      // rows held by one workgroup (128 KB of LDS)
+#ifndef DSV4_IDX_RS
+#define DSV4_IDX_RS 1
+#endif
+constexpr bool kIdxRowStationary = DSV4_IDX_RS != 0;
+constexpr int64_t kIdxRsMinRows = 4096;       // below, too few row blocks to fill the chip
+
+struct IdxQ {
+    bf16x8 qa[2][ID / 16];
+    float wsc[2][16];
+};
+
+__device__ __forceinline__ void idx_load_query(const IdxMfmaArgs& a, int b, int64_t s, IdxQ& q) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(s)) * IH + l32) * ID + 8 * hi;
+    const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int ks = 0; ks < ID / 16; ++ks) q.qa[m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {           // heads 32 m + 8 g + 4 hi + 0..3
+            const float4 v = *reinterpret_cast<const float4*>(wr + 32 * m + 8 * g + 4 * hi);
+            q.wsc[m][4 * g + 0] = v.x * a.scale;
+            q.wsc[m][4 * g + 1] = v.y * a.scale;
+            q.wsc[m][4 * g + 2] = v.z * a.scale;
+            q.wsc[m][4 * g + 3] = v.w * a.scale;
+        }
+    }
+}
+
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+index_score_rs_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    __shared__ __attribute__((aligned(16))) unsigned char kt[RSB * IROWB];
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int64_t pos0 = pos0v.v[b];
+    const int64_t q_lo = int64_t(blockIdx.y) * a.queries_per_group;
+    int64_t q_hi = q_lo + a.queries_per_group < a.S ? q_lo + a.queries_per_group : a.S;
+    int64_t nv_max = (pos0 + q_hi) / a.r;                  // rows the group's last query sees
+    if (nv_max > n_rows.v[b]) nv_max = n_rows.v[b];
+    const int64_t j_begin = int64_t(blockIdx.x) * RSB;
+    if (j_begin >= nv_max) return;
+    const int64_t j_end = j_begin + RSB < nv_max ? j_begin + RSB : nv_max;
+#pragma unroll
+    for (int t = 0; t < RSB / IRT; ++t) idx_load_tile<WAVES>(a, b, j_begin + t * IRT, j_end, kt + t * IRT * IROWB);
+    wait_vm_loads<0>();
+    __syncthreads();
+
+    for (int64_t s = q_lo + w; s < q_hi; s += WAVES) {
+        IdxQ cur;
+        idx_load_query(a, b, s, cur);
+        int64_t nvq = (pos0 + s + 1) / a.r;
+        if (nvq > n_rows.v[b]) nvq = n_rows.v[b];
+        const int nblk = nvq > j_begin ? int((nvq - j_begin + 31) / 32) : 0;   // blocks it sees
+        uint32_t* keys = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
+        floatx16 c[2][2];
+#pragma unroll
+        for (int u = 0; u <= RSB / 32; ++u) {
+            if (u < RSB / 32 && u < nblk) {
+                const int row = 32 * (u & (IRT / 32 - 1)) + l32;              // row of its tile
+                const unsigned char* kr = kt + (u / (IRT / 32)) * IRT * IROWB + row * IROWB;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    c[u & 1][0][i] = 0.f;
+                    c[u & 1][1][i] = 0.f;
+                }
+#pragma unroll
+                for (int ks = 0; ks < ID / 16; ++ks) {
+                    const bf16x8 kb = load_bf16x8(kr + swz(row, 2 * ks + hi) * 16);
+                    c[u & 1][0] = mfma32x32x16(cur.qa[0][ks], kb, c[u & 1][0]);
+                    c[u & 1][1] = mfma32x32x16(cur.qa[1][ks], kb, c[u & 1][1]);
+                }
+            }
+            if (u > 0 && u - 1 < nblk) {
+                const int v = u - 1;
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s0 = fmaf(cur.wsc[0][i], relu_bits(c[v & 1][0][i]), s0);
+                    s1 = fmaf(cur.wsc[1][i], relu_bits(c[v & 1][1][i]), s1);
+                }
+                float sc = s0 + s1;
+                sc += __shfl_xor(sc, 32, 64);
+                const int64_t jj = j_begin + 32 * v + l32;
+                if (hi == 0 && jj < nvq) keys[jj] = score_key(sc);
+            }
         }
     }
 }
@@ -755,6 +855,22 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             a.scale = 1.0f / sqrtf(float(j.di)) / sqrtf(float(j.Hi));
             constexpr int QG = kIdxWaves * kIdxQpw;        // queries per prefill workgroup
             const bool perq = j.S >= QG;
+            if (perq && kIdxRowStationary && nv_max >= kIdxRsMinRows) {
+                // row-stationary: RSB-row blocks x query groups, about one workgroup per CU
+                const int64_t rb = (nv_max + RSB - 1) / RSB;
+                int64_t ng = (256 + rb * nb - 1) / (rb * nb);
+                const int64_t max_groups = (j.S + kIdxWaves - 1) / kIdxWaves;
+                if (ng > max_groups) ng = max_groups;
+                if (ng < 1) ng = 1;
+                int64_t qpg = (j.S + ng - 1) / ng;
+                qpg = (qpg + kIdxWaves - 1) / kIdxWaves * kIdxWaves;
+                a.queries_per_group = int(qpg);
+                ng = (j.S + qpg - 1) / qpg;
+                DSV4_LAUNCH("index_score_rs", index_score_rs_kernel<kIdxWaves>, dim3(unsigned(rb), unsigned(ng), nb),
+                            dim3(64 * kIdxWaves), 0, st, a, pos, nr);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            } else {
             const int64_t groups = perq ? (j.S + QG - 1) / QG : j.S;
             // enough row blocks to give the chip >= ~2048 workgroups in prefill; in decode (one
             // query per group) fewer, longer blocks, so each streams several tiles through
@@ -774,6 +890,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                             dim3(gx, unsigned(groups), nb), dim3(256), 0, st, a, pos, nr);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
+            }
         } else if (nv_max > j.k) {
             ScoreArgs<T> a;
             a.Hi = j.Hi; a.di = j.di; a.r = j.r;
