@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 import sparse_attention_dsv4_amd as K  # noqa: E402
 import synth.csa as SC  # noqa: E402
-from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec, output_path  # noqa: E402
+from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec, compressor_lanes, output_path  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
@@ -442,6 +442,32 @@ def bench_output_path(args, seed=41):
         entry["us_per_call"] = us_g + ms_r / n_r * 1e3
         out[name] = entry
         del o, y
+    # the ratio-4 compressor's lanes of a 2048-token chunk from hidden states (wkv, wgate
+    # [1024, 4096]): two one-group projections of 128 x 128 tiles
+    T, hid, W = args.chunk, 4096, spec.coff * spec.dim
+    x = synth.normal((T, hid), seed=seed, stream="hidden", dtype=torch.bfloat16, device="cuda")
+    wkv = synth.normal((W, hid), seed=seed, stream="wkv", scale=hid ** -0.5, dtype=torch.bfloat16,
+                       device="cuda")
+    wg = synth.normal((W, hid), seed=seed, stream="wgate", scale=hid ** -0.5, dtype=torch.bfloat16,
+                      device="cuda")
+    for _ in range(3):
+        compressor_lanes(x, wkv, wg)
+    torch.cuda.synchronize()
+    K.dsv4_trace_reset()
+    K.dsv4_trace_enable(True)
+    for _ in range(10):
+        compressor_lanes(x, wkv, wg)
+    torch.cuda.synchronize()
+    K.dsv4_trace_enable(False)
+    n_g, ms_g = kernel_time("gproj")
+    us = ms_g / n_g * 1e3
+    fl = 2.0 * T * W * hid
+    ach = fl / (us * 1e-6) / 1e12
+    out["lanes_prefill_2048"] = {
+        "tokens": T, "us_per_call": 2 * us,
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "gproj_tile",
+                     "flops_per_launch": fl}}
     return out
 
 
@@ -655,7 +681,8 @@ def main():
         outp = bench_output_path(args)
         log(f"[output path] decode b8 {outp['decode_b8']['us_per_call']:.1f} us "
             f"({outp['decode_b8']['roofline']['frac'] * 100:.0f}% of HBM in the projection); prefill 2048 "
-            f"{outp['prefill_2048']['us_per_call']:.1f} us ({outp['prefill_2048']['roofline']['frac'] * 100:.0f}% of MFMA)")
+            f"{outp['prefill_2048']['us_per_call']:.1f} us ({outp['prefill_2048']['roofline']['frac'] * 100:.0f}% of MFMA); "
+            f"compressor lanes of 2048 tokens {outp['lanes_prefill_2048']['us_per_call']:.1f} us")
     stack = None
     if not args.skip_stack and args.only is None:
         stack = bench_stack(args)

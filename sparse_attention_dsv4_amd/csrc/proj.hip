@@ -6,9 +6,10 @@
 //                        (decode): weight streaming, HBM-bound -- each 32-row block of a
 //                        group's weight is read once, straight into registers, by 8 waves
 //                        that split K and meet in LDS;
-//   gproj_tile_kernel    the same for more tokens (prefill): MFMA-bound 256-token x
-//                        256-row tiles (8 waves), both operands staged in LDS by direct
-//                        global-to-LDS copies, k blocks of 64 double-buffered;
+//   gproj_tile_kernel    the same for more tokens (prefill): MFMA-bound 256 x 256 tiles of
+//                        8 waves (128 x 128 of 4 waves for smaller grids), both operands
+//                        staged in LDS by direct global-to-LDS copies, k blocks of 64
+//                        double-buffered;
 //   gproj_generic_kernel any shape or fp32: one thread per output.
 // Every product accumulates in fp32 (v_mfma_f32_32x32x16_bf16 on the bf16 paths); outputs
 // are rounded once to the storage type.
@@ -122,31 +123,26 @@ __global__ void __launch_bounds__(64 * kSmallWaves) gproj_small_kernel(GprojArgs
     }
 }
 
-// More tokens: workgroup tile 64 WT tokens x 256 rows of one group, 2 WT waves of 64 x 128
-// (2 x 4 MFMA blocks; C[token][row]), k in blocks of BK through an NST-stage LDS ring.  A
-// stage holds 128 token rows and 256 weight rows of 2 BK bytes; the 16-byte chunk c of row r
-// sits at chunk c ^ ((r / (16 / CPR)) % CPR) (CPR chunks per row), so the 16 rows of one
-// MFMA operand read phase hit 16 different 16-byte bank groups.  Token rows past T load row
-// T - 1 (finite values whose outputs are not stored).
-#ifndef DSV4_GPROJ_BK
-#define DSV4_GPROJ_BK 64
-#endif
-#ifndef DSV4_GPROJ_STAGES
-#define DSV4_GPROJ_STAGES 2
-#endif
-#ifndef DSV4_GPROJ_WT
-#define DSV4_GPROJ_WT 4
-#endif
-constexpr int kTileWt = DSV4_GPROJ_WT;                   // waves along the tokens (64 each)
-constexpr int kTileWaves = 2 * kTileWt;                  // and two along the rows (128 each)
-constexpr int kTileT = 64 * kTileWt, kTileR = 256;
-constexpr int kTileK = DSV4_GPROJ_BK, kTileStages = DSV4_GPROJ_STAGES;
+// More tokens: workgroup tile 64 WT tokens x 64 WRB rows of one group, 2 WT waves of
+// 64 x 32 WRB (2 x WRB MFMA blocks; C[token][row]): WT = WRB = 4 (256 x 256, 8 waves) where
+// that gives the chip about a workgroup per CU or more, WT = WRB = 2 (128 x 128, 4 waves)
+// for smaller grids.  k in blocks of 64, double-buffered in LDS.  A stage holds the tile's
+// token rows and weight rows of 128 bytes; the 16-byte chunk c of row r sits at chunk
+// c ^ ((r / 2) % 8), so the 16 rows of one MFMA operand read phase hit 16 different 16-byte
+// bank groups.  Token rows past T load row T - 1 (finite values whose outputs are not stored).
+constexpr int kTileK = 64, kTileStages = 2;
 constexpr int kRowB = kTileK * 2;                        // bytes per staged row
 constexpr int kCpr = kRowB / 16;                         // 16-byte chunks per row
 constexpr int kRowsPerOp = 1024 / kRowB;                 // rows per 1 KB copy
-constexpr int kStageB = (kTileT + kTileR) * kRowB;
-constexpr int kTileOps = (kTileT + kTileR) / kRowsPerOp / kTileWaves;   // copies per wave per stage
-static_assert(kCpr == 4 || kCpr == 8, "k block of 32 or 64");
+
+template <int WT, int WRB>
+struct TileShape {
+    static constexpr int waves = 2 * WT;
+    static constexpr int T = 64 * WT, R = 64 * WRB;
+    static constexpr int stage_bytes = (T + R) * kRowB;
+    static constexpr int ops = (T + R) / kRowsPerOp / waves;   // 1 KB copies per wave per stage
+    static_assert((T + R) % (kRowsPerOp * waves) == 0, "whole copies per wave");
+};
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -169,76 +165,71 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ ((row / (16 / kCpr)) % kCpr); }
 
 // Copy k block kb of the tile into stage buffer buf: 1 KB copies of kRowsPerOp rows; wave w
-// takes copies w, w + 2 WT, ... (the token rows first, then the weight rows).
+// takes copies w, w + waves, ... (the token rows first, then the weight rows).
+template <class SH>
 __device__ __forceinline__ void tile_load(const GprojArgs& a, int g, int64_t t0, int r0, int kb,
                                           unsigned char* buf) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kTileOps; ++i) {
-        const int op = w + kTileWaves * i;
+    for (int i = 0; i < SH::ops; ++i) {
+        const int op = w + SH::waves * i;
         const int row = kRowsPerOp * op + lane / kCpr;   // row of the stage
         const int c = tswz(row, lane % kCpr);            // logical chunk landing at lane % kCpr
         const bf16* src;
-        if (row < kTileT) {
+        if (row < SH::T) {
             int64_t t = t0 + row;
             t = t < a.T ? t : a.T - 1;
             src = a.x + (size_t(t) * a.G + g) * a.K + size_t(kb) * kTileK + 8 * c;
         } else {
-            const int r = r0 + row - kTileT;
+            const int r = r0 + row - SH::T;
             src = a.w + (size_t(g) * a.R + r) * a.K + size_t(kb) * kTileK + 8 * c;
         }
         dma16(src, buf + op * 1024);
     }
 }
 
-__global__ void __launch_bounds__(64 * kTileWaves) gproj_tile_kernel(GprojArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char st[kTileStages][kStageB];
+template <int WT, int WRB>
+__global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
+    using SH = TileShape<WT, WRB>;
+    __shared__ __attribute__((aligned(16))) unsigned char st[kTileStages][SH::stage_bytes];
     const int g = blockIdx.z;
-    const int64_t t0 = int64_t(blockIdx.x) * kTileT;
-    const int r0 = int(blockIdx.y) * kTileR;
+    const int64_t t0 = int64_t(blockIdx.x) * SH::T;
+    const int r0 = int(blockIdx.y) * SH::R;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 31, hh = lane >> 5;
-    const int wt = w % kTileWt, wr = w / kTileWt;        // wave tile: tokens 64 wt, rows 128 wr
+    const int wt = w % WT, wr = w / WT;                  // wave tile: tokens 64 wt, rows 32 WRB wr
     const int nk = a.K / kTileK;
-    floatx16 acc[2][4];
+    floatx16 acc[2][WRB];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < WRB; ++v)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kTileStages - 1; ++s)
-        if (s < nk) tile_load(a, g, t0, r0, s, st[s]);
+    tile_load<SH>(a, g, t0, r0, 0, st[0]);
     for (int kb = 0; kb < nk; ++kb) {
-        // stage kb has landed once at most the copies of the stages issued after it are
-        // pending: min(NST - 2, blocks left after kb) stages
-        const int later = nk - 1 - kb < kTileStages - 2 ? nk - 1 - kb : kTileStages - 2;
-        if (later >= 2) wait_vm<2 * kTileOps>();
-        else if (later == 1) wait_vm<kTileOps>();
-        else wait_vm<0>();
-        lds_barrier();                                   // stage kb visible; kb-1 fully read
-        if (kb + kTileStages - 1 < nk)
-            tile_load(a, g, t0, r0, kb + kTileStages - 1, st[(kb + kTileStages - 1) % kTileStages]);
+        wait_vm<0>();                                    // block kb (the only copies in flight)
+        lds_barrier();                                   // block kb visible; kb-1 fully read
+        if (kb + 1 < nk) tile_load<SH>(a, g, t0, r0, kb + 1, st[(kb + 1) % kTileStages]);
         const unsigned char* buf = st[kb % kTileStages];
 #pragma unroll
         for (int j = 0; j < kTileK / 16; ++j) {          // MFMA k steps of this block
             const int lc = 2 * j + hh;                   // logical chunk of this lane
-            bf16x8 xa[2], wb[4];
+            bf16x8 xa[2], wb[WRB];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = 64 * wt + 32 * u + m;
                 xa[u] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
             }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = kTileT + 128 * wr + 32 * v + m;
+            for (int v = 0; v < WRB; ++v) {
+                const int row = SH::T + 32 * WRB * wr + 32 * v + m;
                 wb[v] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = mfma32x32x16(xa[u], wb[v], acc[u][v]);
+                for (int v = 0; v < WRB; ++v) acc[u][v] = mfma32x32x16(xa[u], wb[v], acc[u][v]);
         }
     }
     // C[token][row]: register i of lane l is token c_row(i, l), row l % 32
@@ -248,9 +239,9 @@ __global__ void __launch_bounds__(64 * kTileWaves) gproj_tile_kernel(GprojArgs a
         for (int i = 0; i < 16; ++i) {
             const int64_t t = t0 + 64 * wt + 32 * u + c_row(i, lane);
             if (t >= a.T) continue;
-            bf16* yr = a.y + (size_t(t) * a.G + g) * a.R + r0 + 128 * wr + m;
+            bf16* yr = a.y + (size_t(t) * a.G + g) * a.R + r0 + 32 * WRB * wr + m;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
+            for (int v = 0; v < WRB; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
         }
 }
 
@@ -324,11 +315,19 @@ hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    if (j.bf16 && j.K % kTileK == 0 && j.R % kTileR == 0) {
+    if (j.bf16 && j.K % kTileK == 0 && j.R % 128 == 0) {
         GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
                     static_cast<bf16*>(j.y), j.T};
-        const dim3 grid(unsigned((j.T + kTileT - 1) / kTileT), unsigned(j.R / kTileR), unsigned(j.G));
-        DSV4_LAUNCH("gproj_tile", gproj_tile_kernel, grid, dim3(64 * kTileWaves), 0, s, a);
+        using Big = TileShape<4, 4>;
+        using Small = TileShape<2, 2>;
+        const int64_t big_tiles = (j.T + Big::T - 1) / Big::T * (j.R / Big::R) * j.G;
+        if (j.R % Big::R == 0 && big_tiles >= 256) {
+            const dim3 grid(unsigned((j.T + Big::T - 1) / Big::T), unsigned(j.R / Big::R), unsigned(j.G));
+            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<4, 4>), grid, dim3(64 * Big::waves), 0, s, a);
+        } else {
+            const dim3 grid(unsigned((j.T + Small::T - 1) / Small::T), unsigned(j.R / Small::R), unsigned(j.G));
+            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<2, 2>), grid, dim3(64 * Small::waves), 0, s, a);
+        }
         return hipGetLastError();
     }
     const int64_t n = j.T * j.G * j.R;

@@ -92,9 +92,10 @@ def test_grouped_proj_tiled(T):
 
 
 def test_grouped_proj_other_k():
-    """Smaller K on both MFMA kernels (K = 512 and 1536)."""
+    """Smaller K on both MFMA kernels (K = 512 and 1536), and 128-row tiles (R = 384)."""
     _proj_case(5, 2, 512, 64, torch.bfloat16, seed=7)
     _proj_case(300, 3, 1536, 256, torch.bfloat16, seed=8)
+    _proj_case(40, 2, 512, 384, torch.bfloat16, seed=11)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
