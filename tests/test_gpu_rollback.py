@@ -41,6 +41,13 @@ CASES = {
     # capacity exactly used: 8 of 8, across two ratio-4 windows
     "ratio4_full_room": (LayerSpec(ratio=4, rollback=8), 1030,
                          [("dec", 1, 8), ("trim", 8), ("dec", 2, 9)]),
+    # the generic kernels (fp32, small shapes): a rollback deeper than the window ring's
+    # 16 tokens and than two ratio-4 windows, across the top-8 threshold (36 visible rows)
+    "small_fp32_generic": (LayerSpec(ratio=4, heads=4, dim=64, rope_dim=16, window=16,
+                                     index_heads=2, index_dim=32, topk=8,
+                                     dtype=torch.float32, rollback=20), 29,
+                           [("dec", 1, 12), ("trim", 7), ("dec", 2, 3), ("trim", 8),
+                            ("dec", 3, 10)]),
 }
 
 
@@ -60,6 +67,7 @@ def test_trim_equals_never_decoded(name):
     outs = {}                                        # position -> draft's output, last decode
     for op in script:
         if op[0] == "trim":
+            assert op[1] <= len(committed), "the scripts take back decoded tokens only"
             draft.trim(op[1])
             del committed[len(committed) - op[1]:]
             continue
