@@ -48,9 +48,6 @@ struct ScoreArgs {
     uint32_t* keys;
 };
 
-#ifndef DSV4_IDX_ILV
-#define DSV4_IDX_ILV 0                    // VALU instructions placed after each MFMA (0: compiler's order)
-#endif
 
 // max(x, 0) for finite x as an integer max of the bit pattern (negative floats, -0 included,
 // have the sign bit set and compare below 0): one instruction, no IEEE canonicalisation.
@@ -164,37 +161,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 1
 
 // Stage rows [j0, j0 + IRT) of the lane (zeros past j_end): each wave instruction moves 4
 // rows; lane l fetches chunk swz(row, l%16) of row l/16 so that it lands at position l%16.
-#ifndef DSV4_IDX_REGSTAGE
-#define DSV4_IDX_REGSTAGE 0
-#endif
-
-// Register-staged tile copy: idx_fetch_tile loads this wave's rows of a tile into registers
-// (rows past j_end read the last row), idx_put_tile writes them to LDS (zeros past j_end).
-template <int WAVES>
-__device__ __forceinline__ void idx_fetch_tile(const IdxMfmaArgs& a, int b, int64_t j0, int64_t j_end,
-                                               uint4 (&v)[IRT / 4 / WAVES]) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < IRT / 4 / WAVES; ++i) {
-        const int row = 4 * (w + WAVES * i) + (lane >> 4);
-        const int64_t jj = j0 + row;
-        const int64_t js = jj < j_end ? jj : j_end - 1;
-        v[i] = *reinterpret_cast<const uint4*>(a.rows + (size_t(b) * a.row_cap + size_t(js)) * ID +
-                                               swz(row, lane & 15) * 8);
-    }
-}
-template <int WAVES>
-__device__ __forceinline__ void idx_put_tile(int64_t j0, int64_t j_end, const uint4 (&v)[IRT / 4 / WAVES],
-                                             unsigned char* buf) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < IRT / 4 / WAVES; ++i) {
-        const int row0 = 4 * (w + WAVES * i);
-        const bool in = j0 + row0 + (lane >> 4) < j_end;
-        store16(buf + row0 * IROWB + lane * 16, in ? v[i] : make_uint4(0, 0, 0, 0));
-    }
-}
-
 template <int WAVES>
 __device__ __forceinline__ void idx_load_tile(const IdxMfmaArgs& a, int b, int64_t j0,
                                               int64_t j_end, unsigned char* buf) {
@@ -271,20 +237,6 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     // between can only make the counted wait stricter).
     constexpr int OPS = IRT / 4 / WAVES;
     const int ntiles = int((j_end - j_begin + IRT - 1) / IRT);
-#if DSV4_IDX_REGSTAGE
-    // tile t+1 goes from registers to LDS at the start of tile t, tile t+2 is fetched into
-    // registers right after: each fetch has a whole tile of compute to land
-    uint4 stage[OPS];
-    idx_fetch_tile<WAVES>(a, b, j_begin, j_end, stage);
-    idx_put_tile<WAVES>(j_begin, j_end, stage, kt[0]);
-    if (ntiles > 1) idx_fetch_tile<WAVES>(a, b, j_begin + IRT, j_end, stage);
-    for (int t = 0; t < ntiles; ++t) {
-        const int64_t j0 = j_begin + int64_t(t) * IRT;
-        __syncthreads();                               // tile t visible; tile t-1 fully read
-        if (t + 1 < ntiles) idx_put_tile<WAVES>(j0 + IRT, j_end, stage, kt[(t + 1) & 1]);
-        if (t + 2 < ntiles) idx_fetch_tile<WAVES>(a, b, j0 + 2 * IRT, j_end, stage);
-        const unsigned char* buf = kt[t & 1];
-#else
 #pragma unroll
     for (int t = 0; t < NSTAGE - 1; ++t)
         if (t < ntiles) idx_load_tile<WAVES>(a, b, j_begin + int64_t(t) * IRT, j_end, kt[t]);
@@ -298,7 +250,6 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         if (t + NSTAGE - 1 < ntiles)
             idx_load_tile<WAVES>(a, b, j0 + int64_t(NSTAGE - 1) * IRT, j_end, kt[(t + NSTAGE - 1) % NSTAGE]);
         const unsigned char* buf = kt[t % NSTAGE];
-#endif
         // 32-row blocks of the tile: prefill waves take all 4 (their own queries), decode waves
         // one each.  The MFMAs of block u+1 are issued before the epilogue of block u, so the
         // matrix pipe stays busy while the VALU reduces the previous block.
@@ -344,16 +295,6 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
                     score[v][q] = sc + __shfl_xor(sc, 32, 64);
                 }
             }
-#if DSV4_IDX_ILV > 0
-            // interleave the epilogue's VALU work between this block's MFMAs
-            if (u > 0 && u < NB) {
-#pragma unroll
-                for (int i = 0; i < 2 * ID / 16 * NQ; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, DSV4_IDX_ILV, 0);
-                }
-            }
-#endif
         }
 #pragma unroll
         for (int v = 0; v < NB; ++v) {
