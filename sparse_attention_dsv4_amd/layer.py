@@ -118,13 +118,32 @@ class CsaLayer:
         return [(n + extra) // r for n in self.lengths] if r > 0 else None
 
     # ------------------------------------------------------------------ steps
-    def prefill(self, tok: dict, sel_out=None) -> torch.Tensor:
+    def rope_inputs(self, tok: dict, pos0, S: int):
+        """RoPE of the per-head inputs of S tokens at positions pos0[b] + t, in place: q
+        [B,S,H,D] and kv [B,S,D] (the last rope_dim dims of every head), and the indexer's qi
+        [B,S,Hi,di] -- the rotation the boundary otherwise expects the caller to have applied
+        (q, kv and qi turn at the token's absolute position with the layer's inv_freq, the
+        same frequencies the compressed rows use: [MLXLM-1189] OmarB97's RoPE notes)."""
+        sp, inv = self.spec, self.params["inv_freq"]
+        B = len(pos0)
+        dsv4_rope(RopeCfg(sp.heads, sp.dim, sp.rope_dim, False, sp.dtype),
+                  tok["q"].view(B, S, sp.heads, sp.dim), pos0, inv)
+        dsv4_rope(RopeCfg(1, sp.dim, sp.rope_dim, False, sp.dtype),
+                  tok["kv"].view(B, S, 1, sp.dim), pos0, inv)
+        if sp.has_indexer:
+            dsv4_rope(RopeCfg(sp.index_heads, sp.index_dim, sp.rope_dim, False, sp.dtype),
+                      tok["qi"].view(B, S, sp.index_heads, sp.index_dim), pos0, inv)
+
+    def prefill(self, tok: dict, sel_out=None, rope: bool = False) -> torch.Tensor:
         """Process S new tokens of every sequence.  ``tok`` holds q [B,S,H,D], kv [B,S,D],
         a, g [B,S,coff*D], and with an indexer ai, gi [B,S,coff*di], qi [B,S,Hi,di],
-        w [B,S,Hi].  Returns out [B,S,H,D]; writes the selection into ``sel_out`` if given."""
+        w [B,S,Hi].  Returns out [B,S,H,D]; writes the selection into ``sel_out`` if given.
+        With ``rope``, q, kv and qi arrive unrotated and are rotated in place first."""
         sp, P = self.spec, self.params
         S = tok["q"].shape[1]
         pos0 = list(self.lengths)
+        if rope:
+            self.rope_inputs(tok, pos0, S)
         out = torch.empty_like(tok["q"])
         sel = None
         if sp.has_rows:
@@ -143,10 +162,13 @@ class CsaLayer:
         self._advance(S)
         return out
 
-    def decode(self, tok: dict, sel_out=None) -> torch.Tensor:
-        """One token per sequence; ``tok`` tensors have no S axis (q [B,H,D], kv [B,D], ...)."""
+    def decode(self, tok: dict, sel_out=None, rope: bool = False) -> torch.Tensor:
+        """One token per sequence; ``tok`` tensors have no S axis (q [B,H,D], kv [B,D], ...).
+        With ``rope``, q, kv and qi arrive unrotated and are rotated in place first."""
         sp, P = self.spec, self.params
         pos = list(self.lengths)
+        if rope:
+            self.rope_inputs(tok, pos, 1)
         out = torch.empty_like(tok["q"])
         sel = None
         fold = (self.fold_stores and sp.has_rows and

@@ -16,7 +16,7 @@ import oracle
 import synth
 import sparse_attention_dsv4_amd as K
 import synth.csa as SC
-from sparse_attention_dsv4_amd.layer import LayerSpec, compressor_lanes, output_path
+from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec, compressor_lanes, output_path
 from tests import gpu_harness as G
 
 pytestmark = pytest.mark.gpu
@@ -164,3 +164,48 @@ def test_compressor_lanes_from_hidden_states(T):
                                       par["inv_freq"].cpu().numpy(), ratio=spec.ratio,
                                       overlap=spec.is_overlap, eps=spec.eps, store="bf16")
     G.assert_rows_match(G.f64(rows[0]), ref_rows, "bf16", "rows from projected lanes", spec.rope_dim)
+
+
+@pytest.mark.parametrize("spec", [LayerSpec(ratio=4), LayerSpec(ratio=4, heads=4, dim=64, rope_dim=16,
+                                  window=16, index_heads=2, index_dim=32, topk=8,
+                                  dtype=torch.float32)], ids=["v4_bf16", "small_fp32"])
+def test_layer_rotates_its_inputs(spec):
+    """A layer given unrotated q / kv / qi (rope=True) equals one given the same inputs
+    rotated beforehand (by the oracle's rotation, rounded to storage), through prefill and
+    decode: the wiring of the inputs' RoPE (positions, head shapes, which tensors)."""
+    B, seed, prefix, steps = 2, 71, 300, 5
+    params = SC.layer_params(spec, seed, device="cuda")
+    layers = [CsaLayer(spec, B, prefix + steps + 8, params, device="cuda", max_chunk=prefix)
+              for _ in range(2)]
+    inv = params["inv_freq"].cpu().numpy()
+    store = "bf16" if spec.dtype == torch.bfloat16 else "f32"
+
+    def pre_rotated(tok, pos_rows):
+        out = {}
+        for k, v in tok.items():
+            if k in ("q", "kv", "qi"):
+                x = G.f64(v)
+                shp = x.shape
+                x = x.reshape(-1, 1 if k == "kv" else shp[-2], shp[-1])
+                r = oracle.rope_heads(x, pos_rows, inv)
+                r = oracle.round_store(r, store).reshape(shp)
+                out[k] = torch.tensor(r, dtype=spec.dtype, device="cuda")
+            else:
+                out[k] = v.clone()
+        return out
+
+    tok = SC.batch_token_inputs(spec, seed, [0] * B, prefix, device="cuda")
+    pos_rows = np.tile(np.arange(prefix), B)
+    o_ref = layers[0].prefill(pre_rotated(tok, pos_rows))
+    o_rot = layers[1].prefill({k: v.clone() for k, v in tok.items()}, rope=True)
+    torch.cuda.synchronize()
+    bar = 2e-2 if spec.dtype == torch.bfloat16 else 1e-5
+    assert G.max_rel_rows(G.f64(o_rot), G.f64(o_ref)).max() <= bar
+    for i in range(steps):
+        p = prefix + i
+        t = SC.batch_token_inputs(spec, seed, [p] * B, 1, device="cuda")
+        t = {k: v[:, 0].contiguous() for k, v in t.items()}
+        o_ref = layers[0].decode(pre_rotated(t, np.full(B, p)))
+        o_rot = layers[1].decode({k: v.clone() for k, v in t.items()}, rope=True)
+        torch.cuda.synchronize()
+        assert G.max_rel_rows(G.f64(o_rot), G.f64(o_ref)).max() <= bar, f"decode step {i}"
