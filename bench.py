@@ -248,7 +248,7 @@ def bench_stack(args, seed=23):
     g_wall = time.perf_counter() - t0
     spec4 = specs[1]
     nv = (L + warm) // spec4.ratio
-    n_l, ms_l = per_kernel["index_score_mfma"]
+    n_l, ms_l = per_kernel["index_score_stream"]
     # algorithmic bytes of one scan: every visible indexer row, the queries and head weights
     bytes_launch = B * (nv * spec4.index_dim * 2 + spec4.index_heads * (spec4.index_dim * 2 + 4))
     achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
@@ -261,8 +261,8 @@ def bench_stack(args, seed=23):
         "kernels_ratio4_layer": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
                                  for n, v in per_kernel.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(TRAFFIC_STACK, "index_score_mfma"),
-                     "kernel": "index_score_mfma",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(TRAFFIC_STACK, "index_score_stream"),
+                     "kernel": "index_score_stream",
                      "bytes_per_launch": bytes_launch},
     }
 
@@ -483,7 +483,7 @@ COPY_CALIB_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
 TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_rs_ctx65536_chunk2048_ratio4.txt")
-TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_mfma_decode_ctx262144_b4_stack.txt")
+TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_stream_decode_ctx262144_b4_stack.txt")
 
 
 def kernel_source_digest(kernel: str) -> str:

@@ -407,6 +407,118 @@ index_score_rs_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 }
 
+// Decode scoring (each query's rows read once, no sharing between queries): the workgroup
+// stages its query's 64 x 128 fragment in LDS once (16-byte chunks XOR-swizzled by head),
+// then every wave streams its own contiguous run of 32-row blocks straight into registers,
+// with the next block's loads in flight while the current one is scored.  MFMA k slots are
+// ordered so that a lane holds 64 contiguous bytes of its row per 64-dim half: k slot
+// 8 hi + e of MFMA ks = 4 d + j is dim 64 d + 32 hi + 8 j + e, in the query operand alike.
+constexpr int kStreamWaves = 8;
+#ifndef DSV4_IDX_STREAM
+#define DSV4_IDX_STREAM 1
+#endif
+constexpr bool kIdxStream = DSV4_IDX_STREAM != 0;
+
+__device__ __forceinline__ void idx_stream_block(const bf16* rows, int64_t blk, int64_t nv, uint4 (&kb)[8]) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    int64_t j = blk * 32 + l32;
+    j = j < nv ? j : nv - 1;                          // rows past the visible ones: scores not stored
+    const bf16* rp = rows + size_t(j) * ID + 32 * hi;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        kb[c] = *reinterpret_cast<const uint4*>(rp + 8 * c);
+        kb[4 + c] = *reinterpret_cast<const uint4*>(rp + 64 + 8 * c);
+    }
+}
+
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    const int b = blockIdx.z;
+    const int64_t s = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int64_t nv = (int64_t(pos0v.v[b]) + s + 1) / a.r;
+    if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    const int64_t nbt = (nv + 31) / 32;                // 32-row blocks of this query
+    const int bpw = a.rows_per_block / (32 * WAVES);   // blocks per wave
+    if (int64_t(blockIdx.x) * WAVES * bpw >= nbt) return;   // whole workgroup
+    __shared__ __attribute__((aligned(16))) unsigned char qs[IH * IROWB];
+    {
+        const bf16* qg = a.qi + (size_t(b) * a.S + size_t(s)) * IH * ID;
+        for (int i = threadIdx.x; i < IH * 16; i += 64 * WAVES) {
+            const int h = i >> 4, c = i & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(qg + h * ID + c * 8);
+            store16(qs + h * IROWB + ((c ^ (h & 15)) * 16), v);
+        }
+    }
+    __syncthreads();
+    const int64_t blk0 = (int64_t(blockIdx.x) * WAVES + w) * bpw;
+    if (blk0 >= nbt) return;
+    const int nb = int(nbt - blk0 < bpw ? nbt - blk0 : bpw);
+    // query operand in the permuted k order, head weights
+    bf16x8 qa[2][8];
+    float wsc[2][16];
+    {
+        const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(s)) * IH + l32) * ID + 32 * hi;
+        const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int h = 32 * m + l32, c = 8 * (ks >> 2) + 4 * hi + (ks & 3);
+                const uint4 v = *reinterpret_cast<const uint4*>(qs + h * IROWB + ((c ^ (h & 15)) * 16));
+                __builtin_memcpy(&qa[m][ks], &v, 16);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(wr + 32 * m + 8 * g + 4 * hi);
+                wsc[m][4 * g + 0] = v.x * a.scale;
+                wsc[m][4 * g + 1] = v.y * a.scale;
+                wsc[m][4 * g + 2] = v.z * a.scale;
+                wsc[m][4 * g + 3] = v.w * a.scale;
+            }
+        }
+    }
+    const bf16* rows = a.rows + size_t(b) * a.row_cap * ID;
+    uint32_t* keys = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
+    auto score = [&](const uint4 (&kb)[8], int64_t blk) {
+        floatx16 c0, c1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            c0[i] = 0.f;
+            c1[i] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            bf16x8 kv;
+            __builtin_memcpy(&kv, &kb[ks], 16);
+            c0 = mfma32x32x16(qa[0][ks], kv, c0);
+            c1 = mfma32x32x16(qa[1][ks], kv, c1);
+        }
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0 = fmaf(wsc[0][i], relu_bits(c0[i]), s0);
+            s1 = fmaf(wsc[1][i], relu_bits(c1[i]), s1);
+        }
+        float sc = s0 + s1;
+        sc += __shfl_xor(sc, 32, 64);
+        const int64_t jj = blk * 32 + l32;
+        if (hi == 0 && jj < nv) keys[jj] = score_key(sc);
+    };
+    uint4 kb0[8], kb1[8];
+    idx_stream_block(rows, blk0, nv, kb0);
+    for (int u = 0; u < nb; u += 2) {
+        if (u + 1 < nb) idx_stream_block(rows, blk0 + u + 1, nv, kb1);
+        score(kb0, blk0 + u);
+        if (u + 1 < nb) {
+            if (u + 2 < nb) idx_stream_block(rows, blk0 + u + 2, nv, kb0);
+            score(kb1, blk0 + u + 1);
+        }
+    }
+}
+
 bool use_index_mfma(bool bf16_, int Hi, int di) { return bf16_ && Hi == IH && di == ID; }
 
 struct SelArgs {
@@ -826,7 +938,16 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             if (perq)
                 DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<kIdxQpw, kIdxWaves, kIdxStages>),
                             dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
-            else
+            else if (kIdxStream) {
+                // decode: blocks per wave so the chip gets about 256 workgroups
+                const int64_t nbt = (nv_max + 31) / 32;
+                int64_t bpw = (nbt * j.S * nb + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
+                if (bpw < 1) bpw = 1;
+                a.rows_per_block = int(bpw * 32 * kStreamWaves);
+                const unsigned sx = unsigned((nbt + bpw * kStreamWaves - 1) / (bpw * kStreamWaves));
+                DSV4_LAUNCH("index_score_stream", index_score_stream_kernel<kStreamWaves>,
+                            dim3(sx, unsigned(j.S), nb), dim3(64 * kStreamWaves), 0, st, a, pos, nr);
+            } else
                 DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<0, 4, kIdxStages>),
                             dim3(gx, unsigned(groups), nb), dim3(256), 0, st, a, pos, nr);
             hipError_t e = hipGetLastError();
@@ -880,11 +1001,22 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<64, MT, SEL_MERGE>),
                             dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
         } else if (nv_max <= 512 * 32) {
-            // keys in registers: 512 threads x 32 or 64 keys, 1024 threads x 68 keys (69,632
+            // keys in registers: 512 threads x 4 .. 64 keys, 1024 threads x 68 keys (69,632
             // rows, which covers a 262,144-token ratio-4 lane plus its decode steps); beyond,
-            // in memory
-            DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<32, 512, SEL_DIRECT>),
-                        dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
+            // in memory.  Wave w holds rows 64 KPT w .. 64 KPT (w + 1) - 1, so KPT follows the
+            // row count: every wave of the workgroup shares the histogram atomics
+            if (nv_max <= 512 * 4)
+                DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<4, 512, SEL_DIRECT>),
+                            dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
+            else if (nv_max <= 512 * 8)
+                DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<8, 512, SEL_DIRECT>),
+                            dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
+            else if (nv_max <= 512 * 16)
+                DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<16, 512, SEL_DIRECT>),
+                            dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
+            else
+                DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<32, 512, SEL_DIRECT>),
+                            dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);
         } else if (nv_max <= 512 * 64) {
             DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<64, 512, SEL_DIRECT>),
                         dim3(unsigned(j.S), nb), dim3(512), 0, st, sa, pos, nr);

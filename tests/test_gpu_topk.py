@@ -1,5 +1,5 @@
 """Indexer top-k through the C ABI at row counts that reach every selection kernel (keys in
-registers up to 16,384 / 32,768 / 69,632 rows, in memory beyond), and with massive exact ties
+registers up to 2048 / 4096 / 8192 / 16,384 / 32,768 / 69,632 rows, in memory beyond), and with massive exact ties
 (needs a gfx950 GPU).
 
 The indexer rows are drawn directly (the index call takes them as input), so the oracle only
@@ -54,11 +54,13 @@ def _check(rows_i, qi, w, positions, sel, exact):
 
 
 @pytest.mark.parametrize("queries", ["few", "many"])
-@pytest.mark.parametrize("n_vis", [16384, 16684, 20001, 32768, 33001, 65600, 69632, 69633])
+@pytest.mark.parametrize("n_vis", [600, 2048, 2049, 4096, 5000, 8192, 12000,
+                                   16384, 16684, 20001, 32768, 33001, 65600, 69632, 69633])
 def test_topk_large_lanes(n_vis, queries):
     """Few queries (6) over more than 16,384 rows take the split selection (k best per
     8192-row chunk, then of the candidates; 16,684 leaves a last chunk of k rows or fewer);
-    many (65 in one sequence) take one workgroup per query."""
+    many (65 in one sequence) take one workgroup per query.  Up to 16,384 rows the keys per
+    thread follow the row count (4, 8, 16 or 32: the counts below reach each and its edge)."""
     B, S = (2, 3) if queries == "few" else (1, 65)
     cap = n_vis + 8
     g = 11 + n_vis
@@ -74,8 +76,8 @@ def test_topk_large_lanes(n_vis, queries):
     _check(rows_i, qi, w, positions, sel, exact=False)
 
 
-@pytest.mark.parametrize("n_vis,S", [(12000, 2), (30000, 2), (80000, 2), (30000, 40),
-                                     (60000, 40), (80000, 40)])
+@pytest.mark.parametrize("n_vis,S", [(2000, 2), (4000, 2), (7000, 40), (12000, 2), (30000, 2),
+                                     (80000, 2), (30000, 40), (60000, 40), (80000, 40)])
 def test_topk_exact_ties_take_lower_rows(n_vis, S):
     """Rows repeat with period 7, so the scores take 7 values and the k-th score sits inside
     a block of ~1/7 of the rows: the selection must take the lowest rows of that block.  The
