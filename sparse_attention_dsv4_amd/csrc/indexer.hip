@@ -943,6 +943,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 const int64_t nbt = (nv_max + 31) / 32;
                 int64_t bpw = (nbt * j.S * nb + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
                 if (bpw < 1) bpw = 1;
+                if (bpw > (int64_t(1) << 20)) bpw = int64_t(1) << 20;   // rows_per_block fits an int
                 a.rows_per_block = int(bpw * 32 * kStreamWaves);
                 const unsigned sx = unsigned((nbt + bpw * kStreamWaves - 1) / (bpw * kStreamWaves));
                 DSV4_LAUNCH("index_score_stream", index_score_stream_kernel<kStreamWaves>,

@@ -309,3 +309,16 @@ def test_v4_attention_with_ragged_selection():
     ref = G.oracle_attention(spec, tk, par, rows, np.array(ref_sel), pos)
     mr = G.max_rel_rows(G.f64(out[0]), ref)
     assert mr.max() <= 2e-2, mr.max()
+
+
+@pytest.mark.parametrize("spec_name", ["small_bf16", "v4_ratio4"])
+def test_batch_beyond_one_launch_slice(spec_name):
+    """130 sequences: every launcher walks the batch in slices of 128 sequences, so
+    sequences 127, 128 and 129 sit on either side of a slice edge (the generic kernels at the
+    small shape, sparse regime; the MFMA kernels at the V4 shape, dense regime)."""
+    spec, chunks, n_dec = (SMALL_BF16, [120, 50], 30) if spec_name == "small_bf16" else (V4_R4, [40], 4)
+    res = G.run_gpu(spec, 21, 130, chunks, n_dec)
+    T = sum(chunks) + n_dec
+    pos = sorted(set(list(range(0, T, 7)) + list(range(T - 6, T))))
+    for b in (0, 127, 128, 129):
+        _check_layer(spec, res, b, pos, 21)
