@@ -228,7 +228,7 @@ int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* k
                           const float* sinks, void* out, int32_t batch, int64_t s, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* The layer's neighbours on either side of the attention (survey's next rows).
+/* The layer's neighbours on either side of the attention.
  * Pages: mlx-lm PR #1189 (OmarB97's note 2 and stepnoy's patch: the rotary dims are the last
  * rd of each head, interleaved pairs turned by position * inv_freq; Thump604's fix list:
  * inverse output rotation of the post-attention rope dims); MTPLX PR #216 opening ("What V4

@@ -13,7 +13,7 @@ Sources ("the pages"):
                stepnoy's index-space fix).
   [V41-MLX]    "deepseek-v41-mlx" (section "Why this exists": the landmines kept from V4).
 
-Readings where the pages leave a step open are marked READING and listed in the design doc.
+Readings where the pages leave a step open are marked READING.
 Every parity claim of the HIP path is against these functions.
 """
 from __future__ import annotations
