@@ -179,28 +179,34 @@ def bench_decode(args, seed=0):
     return res, layer_state
 
 
-def bench_stack(args, seed=23):
-    """Decode of the [0, 4, 128] stack at 262,144 tokens, batch 4: a window-only layer, a
-    ratio-4 layer (65,536 rows, indexer top-512) and a ratio-128 layer (2048 rows, top-512).
-    A step is one decode token of every sequence through all three layers; the K steps are
-    replayed as a HIP graph like the headline decode.  The roofline is the ratio-4 layer's
-    indexer scan (HBM-bound: every visible indexer row is read once per step)."""
+def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=None):
+    """Decode of a layer stack at 262,144 tokens, batch 4.  The default is V4-Flash's head
+    [0, 4, 128]: a window-only layer, a ratio-4 layer (65,536 rows, indexer top-512) and a
+    ratio-128 layer (2048 rows, top-512); ratios (128, 128, 4, 128) with topk 1024 is
+    V4-Pro's head (no window-only layer, top-1024).  A step is one decode token of every
+    sequence through all layers; the K steps are replayed as a HIP graph like the headline
+    decode.  The roofline is the ratio-4 layer's indexer scan (HBM-bound: every visible
+    indexer row is read once per step); its HBM traffic is read from ``traffic_profile`` (the
+    counters of that stack's run), None when no such profile is given."""
     B, L = 4, 262144
     steps, warm = min(args.steps, 64), args.warmup
-    specs = [LayerSpec(ratio=0, indexer=False, topk=0), LayerSpec(ratio=4), LayerSpec(ratio=128)]
+    specs = [LayerSpec(ratio=0, indexer=False, topk=0) if r == 0 else LayerSpec(ratio=r, topk=topk)
+             for r in ratios]
+    i4 = list(ratios).index(4)
     layers, toks = [], []
     t_setup = time.time()
     for i, spec in enumerate(specs):
-        params = SC.layer_params(spec, seed + spec.ratio, device="cuda")
+        lseed = seed + spec.ratio + 1000 * list(ratios[:i]).count(spec.ratio)
+        params = SC.layer_params(spec, lseed, device="cuda")
         layer = CsaLayer(spec, B, L + warm + 3 * steps + 8, params, device="cuda", max_chunk=spec.window)
-        build_prefix(layer, spec, seed + spec.ratio, L)
+        build_prefix(layer, spec, lseed, L)
         layers.append(layer)
         tl = []
         for j in range(warm + steps):
-            t = SC.batch_token_inputs(spec, seed + spec.ratio, [L + j] * B, 1, device="cuda")
+            t = SC.batch_token_inputs(spec, lseed, [L + j] * B, 1, device="cuda")
             tl.append({k: v[:, 0].contiguous() for k, v in t.items()})
         toks.append(tl)
-    log(f"[stack] three layers at {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
+    log(f"[stack] {list(ratios)} (top-{topk}) at {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
 
     def step(j, trace_layer=None):
         for i, layer in enumerate(layers):
@@ -221,7 +227,7 @@ def bench_stack(args, seed=23):
     # kernel durations of the ratio-4 layer, in a second identical pass with the trace on
     K.dsv4_trace_reset()
     for j in range(warm, warm + steps):
-        step(j, trace_layer=1)
+        step(j, trace_layer=i4)
     torch.cuda.synchronize()
     per_kernel = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
     # graph replay of the K steps (state restored outside the timed region)
@@ -246,22 +252,25 @@ def bench_stack(args, seed=23):
     graph.replay()
     torch.cuda.synchronize()
     g_wall = time.perf_counter() - t0
-    spec4 = specs[1]
+    spec4 = specs[i4]
     nv = (L + warm) // spec4.ratio
     n_l, ms_l = per_kernel["index_score_stream"]
     # algorithmic bytes of one scan: every visible indexer row, the queries and head weights
     bytes_launch = B * (nv * spec4.index_dim * 2 + spec4.index_heads * (spec4.index_dim * 2 + 4))
     achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
     return {
-        "workload": f"decode, [0, 4, 128] stack (window-only, ratio-4 with top-512 over ~{nv} rows, "
-                    f"ratio-128 with top-512 over ~{L // 128} rows), batch {B}, context {L}",
+        "workload": f"decode, {list(ratios)} stack ("
+                    + ", ".join("window-only" if r == 0 else
+                                f"ratio-{r} with top-{topk} over ~{(L + warm) // r} rows" for r in ratios)
+                    + f"), batch {B}, context {L}",
         "tok_s": B * steps / g_wall, "ms_per_step": g_wall / steps * 1e3,
-        "mode": "hip-graph replay of the K captured steps (three layers per step)",
+        "mode": f"hip-graph replay of the K captured steps ({len(ratios)} layers per step)",
         "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3},
         "kernels_ratio4_layer": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
                                  for n, v in per_kernel.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(TRAFFIC_STACK, "index_score_stream"),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": (traffic_from_profile(traffic_profile, "index_score_stream")
+                                                                  if traffic_profile else None),
                      "kernel": "index_score_stream",
                      "bytes_per_launch": bytes_launch},
     }
@@ -664,7 +673,7 @@ def main():
         sys.exit(2)
     K.lib()
     if args.only == "stack":             # stack-only profiler run
-        stack = bench_stack(args)
+        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step")
         print(json.dumps({"workload": "stack", "decode_262k_stack": stack}), flush=True)
         return
@@ -683,11 +692,14 @@ def main():
             f"({outp['decode_b8']['roofline']['frac'] * 100:.0f}% of HBM in the projection); prefill 2048 "
             f"{outp['prefill_2048']['us_per_call']:.1f} us ({outp['prefill_2048']['roofline']['frac'] * 100:.0f}% of MFMA); "
             f"compressor lanes of 2048 tokens {outp['lanes_prefill_2048']['us_per_call']:.1f} us")
-    stack = None
+    stack = pro = None
     if not args.skip_stack and args.only is None:
-        stack = bench_stack(args)
+        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step; index scan "
             f"{stack['roofline']['achieved']:.0f} GB/s ({stack['roofline']['frac'] * 100:.1f}% of HBM)")
+        pro = bench_stack(args, ratios=(128, 128, 4, 128), topk=1024)
+        log(f"[pro stack] graph {pro['tok_s']:.0f} tok/s, {pro['ms_per_step']:.4f} ms/step; index scan "
+            f"{pro['roofline']['achieved']:.0f} GB/s ({pro['roofline']['frac'] * 100:.1f}% of HBM)")
     if dec is None:                      # prefill-only profiler run
         print(json.dumps({"workload": "prefill", "prefill": pre}), flush=True)
         return
@@ -721,6 +733,7 @@ def main():
         "kernels": dec["kernels"],
         "prefill": pre,
         "decode_262k_stack": stack,
+        "decode_262k_pro_stack": pro,
         "output_path": outp,
         "cpu_baseline": cpu,
     }

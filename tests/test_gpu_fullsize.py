@@ -244,6 +244,28 @@ def test_config_stack_262k_batch4(ratio):
     print(f"  262K ratio-{ratio} decode: worst max-rel {worst:.3g}; top-k exact {ne} of {len(samples)}")
 
 
+@pytest.mark.parametrize("ratio", [4, 128])
+def test_pro_stack_262k_batch4(ratio):
+    """V4-Pro's head [128, 128, 4, 128] at 262,144 tokens, batch 4, top-1024: its two layer
+    kinds, a ratio-128 layer (2048 rows, so the selection is sparse) and a ratio-4 layer
+    (65,536 rows).  128 decode steps (a ratio-128 row is born on the way); sampled steps are
+    checked for every sequence."""
+    spec = LayerSpec(ratio=ratio, topk=1024)
+    seed, B, L, steps = 51 + ratio, 4, 262144, 128
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, B, L + steps + 8, params, device="cuda", max_chunk=spec.window)
+    bench.build_prefix(layer, spec, seed, L)
+    outs, sels = _decode_steps(layer, spec, seed, B, L, steps)
+    n = (L + steps) // spec.ratio
+    js = [0, L // spec.ratio - 1, L // spec.ratio, n - 1]
+    for b in (0, 3):
+        _check_rows(spec, seed, layer.rows.cpu(), b, js)
+        _check_rows(spec, seed, layer.rows_i.cpu(), b, js, index_lane=True)
+    samples = [(i, b) for i in (0, 127) for b in range(B)]
+    worst, ne = _check_decode_queries(spec, seed, layer, outs, sels, L, samples)
+    print(f"  262K Pro ratio-{ratio} decode: worst max-rel {worst:.3g}; top-k exact {ne} of {len(samples)}")
+
+
 @pytest.mark.parametrize("case", ["dense_ratio4_b8", "selected_b16"])
 def test_decode_splits_longer_than_one_lds_chunk(case):
     """Decode splits that hold more keys than one LDS chunk (128 keys), so the attention

@@ -322,3 +322,13 @@ def test_batch_beyond_one_launch_slice(spec_name):
     pos = sorted(set(list(range(0, T, 7)) + list(range(T - 6, T))))
     for b in (0, 127, 128, 129):
         _check_layer(spec, res, b, pos, 21)
+
+
+def test_v4_pro_top1024_sparse():
+    """V4-Pro's selection size (top-1024; the layer shape otherwise as Flash's ratio-4 layer):
+    1135 rows by the end, so queries from p = 4099 on select 1024 of their rows (chunked
+    prefill, then decode steps)."""
+    spec = LayerSpec(ratio=4, topk=1024)
+    res = G.run_gpu(spec, 31, 1, [2500, 2000], 40)
+    pos = sorted(set(list(range(0, 4540, 131)) + list(range(4090, 4110)) + list(range(4520, 4540))))
+    _check_layer(spec, res, 0, pos, 31)

@@ -27,11 +27,11 @@ def _need_gpu(request):
     print(f"\n[case] {request.node.name}", flush=True)
 
 
-def _run(rows_i, qi, w, positions, n_rows):
+def _run(rows_i, qi, w, positions, n_rows, spec=SPEC):
     """rows_i [B, cap, di] bf16, qi [B, S, Hi, di] bf16, w [B, S, Hi] fp32 (GPU tensors)."""
     B, S = qi.shape[0], qi.shape[1]
-    cfg = SPEC.index_cfg()
-    sel = torch.full((B, S, SPEC.topk), -2, dtype=torch.int32, device="cuda")
+    cfg = spec.index_cfg()
+    sel = torch.full((B, S, spec.topk), -2, dtype=torch.int32, device="cuda")
     nb = K.dsv4_index_workspace_bytes(cfg, B, S, max(n_rows))
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     K.dsv4_index_topk(cfg, qi, w, rows_i, n_rows, [p[0] for p in positions], sel, ws)
@@ -39,16 +39,16 @@ def _run(rows_i, qi, w, positions, n_rows):
     return sel.cpu().numpy()
 
 
-def _check(rows_i, qi, w, positions, sel, exact):
+def _check(rows_i, qi, w, positions, sel, exact, spec=SPEC):
     for b in range(qi.shape[0]):
         P = positions[b]
         rows = G.f64(rows_i[b])
         scores = oracle.index_scores(G.f64(qi[b]), G.f64(w[b]), rows)
-        ref = oracle.select_topk(scores, P, ratio=SPEC.ratio, k=SPEC.topk)
+        ref = oracle.select_topk(scores, P, ratio=spec.ratio, k=spec.topk)
         if exact:
             assert np.array_equal(sel[b], ref), f"sequence {b}: selection differs"
         else:
-            ne, nb, nbad, bad = G.topk_band_ok(sel[b], ref, scores, P, SPEC)
+            ne, nb, nbad, bad = G.topk_band_ok(sel[b], ref, scores, P, spec)
             print(f"  seq {b}: exact {ne}, in band {nb}")
             assert nbad == 0, bad[:4]
 
@@ -95,3 +95,24 @@ def test_topk_exact_ties_take_lower_rows(n_vis, S):
     n_rows = [cap] * B
     sel = _run(rows_i, qi, w, positions, n_rows)
     _check(rows_i, qi, w, positions, sel, exact=True)
+
+
+@pytest.mark.parametrize("queries", ["few", "many"])
+@pytest.mark.parametrize("n_vis", [1500, 3000, 20001, 70001])
+def test_topk_1024_pro_shape(n_vis, queries):
+    """V4-Pro keeps the top-1024 (the indexer shape otherwise as Flash): a selection longer
+    than the rows of the smaller kernels' first pass, the split selection with 1024
+    candidates per chunk (20,001 rows, few queries) and the in-memory kernel (70,001)."""
+    spec = LayerSpec(ratio=4, topk=1024)
+    B, S = (2, 3) if queries == "few" else (1, 65)
+    cap = n_vis + 8
+    g = 41 + n_vis
+    rows_i = synth.normal((B, cap, spec.index_dim), seed=g, stream="rows_i", dtype=torch.bfloat16,
+                          device="cuda")
+    qi = synth.normal((B, S, spec.index_heads, spec.index_dim), seed=g, stream="qi",
+                      dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, spec.index_heads), seed=g, stream="w", device="cuda")
+    positions = [[4 * n_vis - S - b + i for i in range(S)] for b in range(B)]
+    n_rows = [min(cap, (positions[b][-1] + 1) // 4) for b in range(B)]
+    sel = _run(rows_i, qi, w, positions, n_rows, spec)
+    _check(rows_i, qi, w, positions, sel, exact=False, spec=spec)
