@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 import sparse_attention_dsv4_amd as K  # noqa: E402
 import synth.csa as SC  # noqa: E402
-from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec, compressor_lanes, output_path  # noqa: E402
+from sparse_attention_dsv4_amd.layer import (CsaLayer, LayerSpec, SharedCsaLayer, compressor_lanes,  # noqa: E402
+                                             output_path)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
@@ -275,6 +276,108 @@ def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=Non
                      "bytes_per_launch": bytes_launch},
     }
 
+
+
+def bench_shared(args, seed=71, n_own=2, n_sel=1):
+    """Decode of a cross-layer-sharing group at 262,144 tokens, batch 4 (V4.1's layout: one
+    ratio-4 layer owns the compressors and index keys; ``n_own`` index-source layers score
+    their own queries against its keys and ``n_sel`` layers attend its selection).  A step is
+    one token through the owner and every consumer, replayed as a HIP graph.  The roofline is
+    the index scan (owner and index-source layers: the same rows, read once per launch)."""
+    B, L = 4, 262144
+    steps, warm = min(args.steps, 64), args.warmup
+    spec = LayerSpec(ratio=4)
+    t_setup = time.time()
+    owner = CsaLayer(spec, B, L + warm + 3 * steps + 8, SC.layer_params(spec, seed, device="cuda"),
+                     device="cuda", max_chunk=spec.window)
+    build_prefix(owner, spec, seed, L)
+    cons = []
+    for i in range(n_own + n_sel):
+        c = SharedCsaLayer(spec, owner, SC.layer_params(spec, seed + 1 + i, device="cuda"),
+                           index="own" if i < n_own else "owner", max_chunk=spec.window)
+        c.ring.copy_(owner.ring)          # the owner's last W token latents
+        cons.append(c)
+    toks = []
+    for j in range(warm + steps):
+        to = {k: v[:, 0].contiguous() for k, v in
+              SC.batch_token_inputs(spec, seed, [L + j] * B, 1, device="cuda").items()}
+        tc = []
+        for i in range(len(cons)):
+            t = {k: v[:, 0].contiguous() for k, v in
+                 SC.batch_token_inputs(spec, seed + 1 + i, [L + j] * B, 1, device="cuda",
+                                       fields=["q", "qi", "w"]).items()}
+            t["kv"] = to["kv"]
+            tc.append(t)
+        toks.append((to, tc))
+    sel = torch.empty(B, 1, spec.topk, dtype=torch.int32, device="cuda")
+    log(f"[shared] owner + {n_own} index-source + {n_sel} selection-sharing layers at {L} tokens x {B} "
+        f"built in {time.time() - t_setup:.1f}s")
+
+    def step(j):
+        to, tc = toks[j]
+        owner.decode(to, sel_out=sel)
+        for c, t in zip(cons, tc):
+            c.decode(t) if c.index == "own" else c.decode(t, sel=sel[:, 0])
+
+    for j in range(warm):
+        step(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(warm, warm + steps):
+        step(j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # kernel durations in a second pass with the trace on (positions keep advancing, as in
+    # bench_stack: the layers hold room for the three passes)
+    K.dsv4_trace_reset()
+    K.dsv4_trace_enable(True)
+    for j in range(warm, warm + steps):
+        step(j)
+    torch.cuda.synchronize()
+    K.dsv4_trace_enable(False)
+    per_kernel = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+    names = ("ring", "state", "rows", "state_i", "rows_i")
+    snap = [{n: getattr(l, n).clone() for n in names if hasattr(l, n)} for l in [owner] + cons]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(warm, warm + steps):
+            step(j)
+
+    def restore():
+        for l, sn in zip([owner] + cons, snap):
+            for n, v in sn.items():
+                getattr(l, n).copy_(v)
+        torch.cuda.synchronize()
+
+    restore()
+    graph.replay()
+    torch.cuda.synchronize()
+    restore()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    g_wall = time.perf_counter() - t0
+    nv = (L + warm) // spec.ratio
+    n_l, ms_l = per_kernel["index_score_stream"]
+    bytes_launch = B * (nv * spec.index_dim * 2 + spec.index_heads * (spec.index_dim * 2 + 4))
+    achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
+    owner_bytes = sum(getattr(owner, n).numel() * getattr(owner, n).element_size() for n in names)
+    cons_bytes = cons[0].ring.numel() * cons[0].ring.element_size()
+    n_layers = 1 + len(cons)
+    return {
+        "workload": f"decode, cross-layer KV sharing at context {L}, batch {B}: one ratio-4 owner "
+                    f"(compressors, ~{nv} rows, top-512), {n_own} layers scoring their own queries "
+                    f"against its index keys, {n_sel} attending its selection",
+        "tok_s": B * steps / g_wall, "ms_per_step": g_wall / steps * 1e3,
+        "us_per_layer": g_wall / steps / n_layers * 1e6,
+        "mode": f"hip-graph replay of the K captured steps ({n_layers} layers per step)",
+        "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3},
+        "cache_bytes": {"owner": owner_bytes, "per_sharing_layer": cons_bytes},
+        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "index_score_stream",
+                     "bytes_per_launch": bytes_launch},
+    }
 
 
 def cpu_baseline_decode(layer_state, sample_steps):
@@ -660,7 +763,7 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-stack", action="store_true",
                     help="leave out the 262,144-token [0, 4, 128] stack decode sub-line")
-    ap.add_argument("--only", choices=["decode", "prefill", "stack"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "stack", "shared"], default=None,
                     help="run one workload (for per-workload profiler runs); the JSON line "
                          "then carries that workload's numbers only")
     args = ap.parse_args()
@@ -677,6 +780,9 @@ def main():
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step")
         print(json.dumps({"workload": "stack", "decode_262k_stack": stack}), flush=True)
         return
+    if args.only == "shared":            # shared-KV-only run
+        print(json.dumps({"workload": "shared", "decode_262k_shared_kv": bench_shared(args)}), flush=True)
+        return
     dec = pre = None
     if args.only != "prefill":
         dec, dec_state = bench_decode(args)
@@ -692,7 +798,7 @@ def main():
             f"({outp['decode_b8']['roofline']['frac'] * 100:.0f}% of HBM in the projection); prefill 2048 "
             f"{outp['prefill_2048']['us_per_call']:.1f} us ({outp['prefill_2048']['roofline']['frac'] * 100:.0f}% of MFMA); "
             f"compressor lanes of 2048 tokens {outp['lanes_prefill_2048']['us_per_call']:.1f} us")
-    stack = pro = None
+    stack = pro = shared = None
     if not args.skip_stack and args.only is None:
         stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step; index scan "
@@ -700,6 +806,9 @@ def main():
         pro = bench_stack(args, ratios=(128, 128, 4, 128), topk=1024)
         log(f"[pro stack] graph {pro['tok_s']:.0f} tok/s, {pro['ms_per_step']:.4f} ms/step; index scan "
             f"{pro['roofline']['achieved']:.0f} GB/s ({pro['roofline']['frac'] * 100:.1f}% of HBM)")
+        shared = bench_shared(args)
+        log(f"[shared] graph {shared['tok_s']:.0f} tok/s, {shared['ms_per_step']:.4f} ms/step "
+            f"({shared['us_per_layer']:.1f} us per layer); index scan {shared['roofline']['achieved']:.0f} GB/s")
     if dec is None:                      # prefill-only profiler run
         print(json.dumps({"workload": "prefill", "prefill": pre}), flush=True)
         return
@@ -734,6 +843,7 @@ def main():
         "prefill": pre,
         "decode_262k_stack": stack,
         "decode_262k_pro_stack": pro,
+        "decode_262k_shared_kv": shared,
         "output_path": outp,
         "cpu_baseline": cpu,
     }

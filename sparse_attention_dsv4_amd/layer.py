@@ -236,6 +236,108 @@ class CsaLayer:
         self.lengths = [x - v for x, v in zip(self.lengths, ns)]
 
 
+class SharedCsaLayer:
+    """A layer that owns no compressor (V4.1 cross-layer KV sharing: [V41-MLX] "Why this
+    exists", the cross-layer sharing item: a few layers own the KV compressors and index keys
+    and every other layer consumes the most recent owner's caches; the index-source layers
+    among them score their own queries against the owner's keys).
+
+    ``owner`` is the CsaLayer whose compressed lanes this layer reads; ``spec`` gives this
+    layer's own attention shape (heads, window, top-k) and must match the owner's latent
+    width, ratio and dtype.  Each token, after the owner's call for it:
+      * index="own" (an index-source layer): its own qi, w scored against the owner's index
+        keys (the rows visible to the token, as for the owner) -> its own top-k;
+      * index="owner": the selection the owner's indexer made for the same token, passed as
+        ``sel`` (or, when the owner has no indexer, every visible row).
+    The window holds the owner's token latents (the caller passes the owner's kv): the layer
+    keeps them in a ring of its own, because a prefill call advances the ring it is given
+    after attending, so two layers cannot take turns on one ring within a chunk.  Lengths
+    follow the owner's: from a sequence's first token on, call ``prefill``/``decode`` with
+    the same tokens right after the owner's call, while ``owner.lengths`` already counts
+    them.  Every step runs in the library (index_topk, attention), as for the owner."""
+
+    def __init__(self, spec: LayerSpec, owner: CsaLayer, params: dict, index: str = "own",
+                 device="cuda", max_chunk: int = 2048):
+        o = owner.spec
+        if spec.ratio != o.ratio or spec.dim != o.dim or spec.dtype != o.dtype:
+            raise ValueError("a sharing layer reads the owner's rows: ratio, dim and dtype must match")
+        if index not in ("own", "owner"):
+            raise ValueError(f"index must be 'own' or 'owner', not {index!r}")
+        if index == "own" and spec.has_indexer and not (
+                o.has_indexer and (spec.index_heads, spec.index_dim) == (o.index_heads, o.index_dim)):
+            raise ValueError("index='own' scores against the owner's index keys: the owner needs "
+                             "an indexer of the same width")
+        if index == "owner" and spec.has_indexer and not o.has_indexer:
+            raise ValueError("index='owner' needs an owner with an indexer")
+        if index == "owner" and o.has_indexer and spec.topk != o.topk:
+            raise ValueError("index='owner' attends the owner's selection: top-k must match")
+        self.spec, self.owner, self.params, self.index = spec, owner, params, index
+        self.batch, self.device = owner.batch, device
+        self.ring = torch.zeros(owner.batch, spec.window + spec.rollback, spec.dim, dtype=spec.dtype,
+                                device=device)
+        if index == "own" and spec.has_indexer:
+            nb = dsv4_index_workspace_bytes(spec.index_cfg(), owner.batch, max_chunk, max(1, owner.row_cap))
+            self.ws_index = torch.empty(nb, dtype=torch.uint8, device=device)
+        ac = spec.attn_cfg()
+        nb = max(dsv4_attn_workspace_bytes(ac, owner.batch, s) for s in range(1, min(max_chunk, 1024) + 1))
+        self.ws_attn = torch.empty(max(1, nb), dtype=torch.uint8, device=device)
+
+    def _positions(self, S: int):
+        # the owner has already advanced past these S tokens
+        return [n - S for n in self.owner.lengths]
+
+    def _select(self, tok: dict, pos0, S: int, sel, sel_out):
+        sp, ow = self.spec, self.owner
+        if not (sp.has_indexer and ow.spec.has_indexer):
+            return None
+        if self.index == "owner":
+            if sel is None:
+                raise ValueError("index='owner': pass the owner's selection for these tokens")
+            return sel
+        out = sel_out if sel_out is not None else torch.empty(
+            self.batch, S, sp.topk, dtype=torch.int32, device=self.device)
+        dsv4_index_topk(sp.index_cfg(), tok["qi"], tok["w"], ow.rows_i, ow.n_rows(), pos0, out,
+                        self.ws_index)
+        return out
+
+    def prefill(self, tok: dict, sel=None, sel_out=None) -> torch.Tensor:
+        """S tokens of every sequence: q [B,S,H,D], kv [B,S,D] (the owner's), and for
+        index='own' qi [B,S,Hi,di], w [B,S,Hi]; for index='owner' ``sel`` [B,S,k] is the
+        owner's selection of these tokens.  Returns out [B,S,H,D]."""
+        sp, ow = self.spec, self.owner
+        S = tok["q"].shape[1]
+        pos0 = self._positions(S)
+        chosen = self._select(tok, pos0, S, sel, sel_out)
+        out = torch.empty_like(tok["q"])
+        dsv4_csa_attn_prefill(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
+                              ow.rows if sp.has_rows else None, chosen, ow.n_rows(), pos0,
+                              self.params["sinks"], out, self.ws_attn)
+        return out
+
+    def decode(self, tok: dict, sel=None, sel_out=None) -> torch.Tensor:
+        """One token per sequence (no S axis: q [B,H,D], kv [B,D], qi [B,Hi,di], w [B,Hi];
+        ``sel`` [B,k] for index='owner')."""
+        sp, ow = self.spec, self.owner
+        pos = self._positions(1)
+        chosen = None
+        if sp.has_indexer and ow.spec.has_indexer:
+            if self.index == "owner":
+                if sel is None:
+                    raise ValueError("index='owner': pass the owner's selection for this token")
+                chosen = sel
+            else:
+                s3 = sel_out if sel_out is not None else torch.empty(
+                    self.batch, 1, sp.topk, dtype=torch.int32, device=self.device)
+                dsv4_index_topk(sp.index_cfg(), tok["qi"][:, None], tok["w"][:, None], ow.rows_i,
+                                ow.n_rows(), pos, s3, self.ws_index)
+                chosen = s3[:, 0]
+        out = torch.empty_like(tok["q"])
+        dsv4_csa_attn_decode(sp.attn_cfg(), tok["q"], tok["kv"], self.ring,
+                             ow.rows if sp.has_rows else None, chosen, ow.n_rows(), pos,
+                             self.params["sinks"], out, self.ws_attn)
+        return out
+
+
 def output_path(spec: LayerSpec, o: torch.Tensor, pos0, inv_freq: torch.Tensor,
                 wo_a: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     """The attention output's way out of the layer: the rotary dims of every head turned back
