@@ -763,7 +763,7 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-stack", action="store_true",
                     help="leave out the 262,144-token [0, 4, 128] stack decode sub-line")
-    ap.add_argument("--only", choices=["decode", "prefill", "stack", "shared"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "stack", "pro", "shared"], default=None,
                     help="run one workload (for per-workload profiler runs); the JSON line "
                          "then carries that workload's numbers only")
     args = ap.parse_args()
@@ -779,6 +779,10 @@ def main():
         stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step")
         print(json.dumps({"workload": "stack", "decode_262k_stack": stack}), flush=True)
+        return
+    if args.only == "pro":               # V4-Pro-stack-only run
+        print(json.dumps({"workload": "pro", "decode_262k_pro_stack":
+                          bench_stack(args, ratios=(128, 128, 4, 128), topk=1024)}), flush=True)
         return
     if args.only == "shared":            # shared-KV-only run
         print(json.dumps({"workload": "shared", "decode_262k_shared_kv": bench_shared(args)}), flush=True)
