@@ -84,7 +84,7 @@ def build_prefix(layer: CsaLayer, spec: LayerSpec, seed: int, L: int):
 
 
 def kernel_time(name: str):
-    n, ms = K.dsv4_trace_read(name)
+    n, ms = K.dsv4_trace_read("=" + name)
     return n, ms
 
 
@@ -96,13 +96,161 @@ def cpu_threads() -> int:
         return os.cpu_count() or 1
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _sleep_ms(ms: float):
+    """Hold the stream for about ``ms`` on the GPU (torch's spin kernel), so that the host can
+    enqueue the launches that follow before the GPU reaches them."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(1e-3, e0.elapsed_time(e1))
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
+def traced(run, launches_hint: int):
+    """Kernel durations of the library launches that ``run()`` enqueues, from the library's
+    event trace.  A GPU-side wait goes first, long enough for the host to enqueue every
+    launch, so the kernels then run back to back as they do in a graph replay (not each
+    from an idle GPU).  Returns {kernel: (launches, total_ms)}."""
+    torch.cuda.synchronize()
+    K.dsv4_trace_reset()
+    K.dsv4_trace_enable(True)
+    _sleep_ms(0.05 * launches_hint + 2.0)
+    run()
+    torch.cuda.synchronize()
+    K.dsv4_trace_enable(False)
+    return {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+
+
+def kernel_table(per_kernel, per=1):
+    return {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3,
+                "us_per_step": v[1] / per * 1e3} for n, v in per_kernel.items() if v[0]}
+
+
+def graph_of(fn):
+    """Capture ``fn()`` (library launches on the current stream) as a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def replay_ms(graph, restore, reps: int = 1):
+    """Wall time of one replay (the mean over ``reps``), the state restored before each."""
+    t = 0.0
+    for _ in range(reps):
+        restore()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t += time.perf_counter() - t0
+    return t / reps * 1e3
+
+
+# ------------------------------------------------------------------ algorithmic work
+def decode_step_bytes(spec: LayerSpec, batch: int, step_positions) -> dict:
+    """Algorithmic HBM bytes of one decode step of one layer for ``batch`` sequences, averaged
+    over the steps at ``step_positions`` (every sequence at that position): inputs read once
+    and outputs written once, no re-reads counted.  A row emission, which happens at one step
+    in r, is counted as 1/r of its bytes at every step (its natural rate)."""
+    e = 2 if spec.dtype == torch.bfloat16 else 4
+    H, D, W = spec.heads, spec.dim, spec.window
+    out = defaultdict(float)
+    for p in step_positions:
+        n = (p + 1) // spec.ratio if spec.has_rows else 0
+        keys = W + ((min(n, spec.topk) if spec.has_indexer else n) if spec.has_rows else 0)
+        # q, out, the attended keys (the window's newest from kv_new), the ring slot store
+        out["attention"] += 2 * H * D * e + keys * D * e + D * e
+        if spec.has_rows:
+            lanes = [(spec.coff * spec.dim, spec.dim)]
+            if spec.has_indexer:
+                lanes.append((spec.coff * spec.index_dim, spec.index_dim))
+            for width, dim in lanes:
+                out["compressor"] += 2 * width * e * 2            # a, g read; frontier store
+                # an emission reads value and gate of coff*r slots per channel, writes the row
+                out["compressor"] += (2 * spec.coff * spec.ratio * dim * e + dim * e) / spec.ratio
+        if spec.has_indexer:
+            out["indexer"] += (n * spec.index_dim * e + spec.index_heads * (spec.index_dim * e + 4)
+                               + spec.topk * 4)
+    out = {k: v * batch / len(step_positions) for k, v in out.items()}
+    out["total"] = sum(out.values())
+    return out
+
+
+def prefill_chunk_flops(spec: LayerSpec, start: int, S: int) -> dict:
+    """Algorithmic flops of one prefill chunk (queries start .. start+S-1): the indexer's
+    2*H_i*d_i per (query, visible row), attention's 4*H*D per (query, attended key)."""
+    idx = att = 0.0
+    for p in range(start, start + S):
+        n = (p + 1) // spec.ratio
+        idx += 2.0 * spec.index_heads * spec.index_dim * n
+        att += 4.0 * spec.heads * spec.dim * (min(p + 1, spec.window) + min(spec.topk, n))
+    return {"indexer": idx, "attention": att, "total": idx + att}
+
+
+def emission_positions(p0: int, n: int, ratio: int) -> int:
+    """Steps among positions p0 .. p0+n-1 at which a row completes."""
+    return sum(1 for p in range(p0, p0 + n) if (p + 1) % ratio == 0) if ratio > 0 else 0
+
+
+def emission_cost(layer: CsaLayer, tok: dict, reps: int = 32):
+    """Extra cost of a decode step that completes a row over one that does not, for one
+    layer: each step is captured ``reps`` times in one graph at a fixed position (a step at a
+    fixed position rewrites the same ring slot, frontier slot and row, so repeats are
+    identical work) and replayed; kernel durations come from a traced run of the same repeats.
+    Returns (extra wall ms per emission, extra kernel ms per emission, kernel table)."""
+    r = layer.spec.ratio
+    p_now = layer.lengths[0]
+    p_emit = p_now + (r - 1 - p_now % r)           # (p + 1) % r == 0
+    p_plain = p_emit - 1 if r > 1 else None
+    res = {}
+    for name, p in (("emit", p_emit), ("plain", p_plain)):
+        if p is None:
+            continue
+
+        def run(p=p):
+            for _ in range(reps):
+                layer.lengths = [p] * layer.batch
+                layer.decode(tok)
+        g = graph_of(run)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = replay_ms(g, lambda: None, reps=5) / reps
+        kern = traced(run, 4 * reps)
+        res[name] = (ms, sum(v[1] for v in kern.values()) / reps, kern)
+        del g
+    layer.lengths = [p_now] * layer.batch
+    if "plain" not in res:
+        return 0.0, 0.0, {}
+    return (res["emit"][0] - res["plain"][0], res["emit"][1] - res["plain"][1],
+            kernel_table(res["emit"][2], reps))
+
+
+def step_roofline(bytes_per_step: float, kernel_ms_per_step: float, dominant: dict):
+    ach = bytes_per_step / (kernel_ms_per_step * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS, "scope": "whole step: algorithmic bytes per step over "
+                                                 "the summed kernel time of one step",
+            "bytes_per_step": bytes_per_step, "kernel_us_per_step": kernel_ms_per_step * 1e3,
+            "traffic": dominant.pop("step_traffic", None), "dominant_kernel": dominant}
+
+
 # ------------------------------------------------------------------ decode @ 64K
 def bench_decode(args, seed=0):
     spec = LayerSpec(ratio=128, indexer=False, topk=0)
     B, L = args.decode_batch, args.context
     steps, warm = args.steps, args.warmup
+    r = spec.ratio
     params = SC.layer_params(spec, seed, device="cuda")
-    layer = CsaLayer(spec, B, L + warm + 3 * steps + 8, params, device="cuda", max_chunk=spec.window)
+    layer = CsaLayer(spec, B, L + warm + 3 * steps + 2 * r + 8, params, device="cuda",
+                     max_chunk=spec.window)
     t_setup = time.time()
     build_prefix(layer, spec, seed, L)
     log(f"[decode] prefix of {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
@@ -115,31 +263,23 @@ def bench_decode(args, seed=0):
     for i in range(warm):
         layer.decode(toks[i])
     torch.cuda.synchronize()
-    K.dsv4_trace_reset()
+    # eager: one library call at a time from Python
+    p_eager = layer.lengths[0]
     t0 = time.perf_counter()
     for i in range(warm, warm + steps):
         layer.decode(toks[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # kernel durations, measured in a second identical pass with the event trace on
-    K.dsv4_trace_enable(True)
-    K.dsv4_trace_reset()
-    pos = list(layer.lengths)
-    for i in range(warm, warm + steps):
-        layer.decode(toks[i])
-    torch.cuda.synchronize()
-    names = K.dsv4_trace_kernels()
-    per_kernel = {n: kernel_time(n) for n in names}
-    K.dsv4_trace_enable(False)
-    # the same steps captured once as a HIP graph and replayed: every launch and argument of
-    # the K steps is recorded, so a replay costs no host work per launch.  The state is
-    # restored before each replay (outside the timed region), so the replay recomputes
-    # exactly the captured positions.
+    # kernel durations of the same K steps, run back to back
+    p_trace = layer.lengths[0]
+    per_kernel = traced(lambda: [layer.decode(toks[i]) for i in range(warm, warm + steps)],
+                        3 * steps)
+    # the K steps captured once as a HIP graph and replayed: every launch and argument is
+    # recorded, so a replay costs no host work per launch.  The state is restored before each
+    # replay (outside the timed region), so every replay recomputes the captured positions.
     snap = {n: getattr(layer, n).clone() for n in ("ring", "state", "rows")}
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(warm, warm + steps):
-            layer.decode(toks[i])
+    p_graph = layer.lengths[0]
+    graph = graph_of(lambda: [layer.decode(toks[i]) for i in range(warm, warm + steps)])
 
     def restore():
         for n, v in snap.items():
@@ -158,37 +298,59 @@ def bench_decode(args, seed=0):
     torch.cuda.synchronize()
     g_wall = time.perf_counter() - t0
     g_ev = g0.elapsed_time(g1) * 1e-3
+    del graph
+    # a row completes once every r steps; the K-step window holds n_e such steps, not K/r.
+    # The emission step's extra cost is measured on its own and the window corrected to the
+    # natural rate.
+    layer.lengths = [p_graph + steps] * B
+    emit_wall_ms, emit_kernel_ms, emit_kernels = emission_cost(layer, toks[warm])
+    n_e_graph = emission_positions(p_graph, steps, r)
+    n_e_trace = emission_positions(p_trace, steps, r)
+    corr_graph = (steps / r - n_e_graph) * emit_wall_ms * 1e-3
+    corr_trace = (steps / r - n_e_trace) * emit_kernel_ms
+    g_amort = g_wall + corr_graph
+    kernel_ms_step = (sum(v[1] for v in per_kernel.values()) + corr_trace) / steps
+    # algorithmic bytes per step at the traced positions (the emission at 1/r)
+    by = decode_step_bytes(spec, B, range(p_trace, p_trace + steps))
     attn_name = max((n for n in per_kernel if n.startswith("attn")), key=lambda n: per_kernel[n][1])
     n_l, ms_l = per_kernel[attn_name]
-    # algorithmic bytes of one decode attention launch: q and out (bf16) + every attended key
-    keys = spec.window + (L + warm) // spec.ratio
-    bytes_launch = B * (2 * spec.heads * spec.dim * 2 + keys * spec.dim * 2)
+    keys = spec.window + (p_trace + steps // 2 + 1) // r
+    bytes_launch = B * (2 * spec.heads * spec.dim * 2 + keys * spec.dim * 2 + 2 * spec.dim * 2)
     achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
+    dominant = {"kernel": attn_name, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic_from_profile(TRAFFIC_DECODE, attn_name),
+                "bytes_per_launch": bytes_launch, "avg_us": ms_l / n_l * 1e3}
+    dominant["step_traffic"] = step_traffic_from_profile(TRAFFIC_DECODE_STEP, per_kernel, steps)
     res = {
-        "tok_s": B * steps / g_wall, "ms_per_step": g_wall / steps * 1e3,
-        "mode": "hip-graph replay of the K captured steps",
-        "graph_events_ms_per_step": g_ev / steps * 1e3,
+        "tok_s": B * steps / g_amort, "ms_per_step": g_amort / steps * 1e3,
+        "mode": "hip-graph replay of the K captured steps; the row emission (one step in "
+                f"{r}) amortized at its natural rate",
+        "raw": {"ms_per_step": g_wall / steps * 1e3, "emission_steps_in_window": n_e_graph,
+                "graph_events_ms_per_step": g_ev / steps * 1e3},
+        "emission": {"extra_us_per_emission": emit_wall_ms * 1e3,
+                     "extra_kernel_us_per_emission": emit_kernel_ms * 1e3,
+                     "kernels_of_an_emission_step": emit_kernels},
         "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3,
                   "mode": "one library call per lane per step from Python"},
-        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profile(TRAFFIC_DECODE, attn_name), "kernel": attn_name,
-                     "bytes_per_launch": bytes_launch},
+        "kernels": kernel_table(per_kernel, steps),
+        "bytes_per_step": by,
+        "roofline": step_roofline(by["total"], kernel_ms_step, dominant),
     }
-    layer_state = (layer, toks, spec, params, pos)
-    return res, layer_state
+    return res, (spec, seed)
 
 
-def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=None):
+def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=None,
+                step_traffic_profile=None):
     """Decode of a layer stack at 262,144 tokens, batch 4.  The default is V4-Flash's head
     [0, 4, 128]: a window-only layer, a ratio-4 layer (65,536 rows, indexer top-512) and a
     ratio-128 layer (2048 rows, top-512); ratios (128, 128, 4, 128) with topk 1024 is
     V4-Pro's head (no window-only layer, top-1024).  A step is one decode token of every
     sequence through all layers; the K steps are replayed as a HIP graph like the headline
-    decode.  The roofline is the ratio-4 layer's indexer scan (HBM-bound: every visible
-    indexer row is read once per step); its HBM traffic is read from ``traffic_profile`` (the
-    counters of that stack's run), None when no such profile is given."""
+    decode, with each layer's row emission amortized at its natural rate.  The roofline is
+    the whole step's (algorithmic bytes of every layer over the summed kernel time of a step);
+    the dominant kernel beside it is the ratio-4 layer's indexer scan (every visible indexer
+    row is read once per step), whose HBM traffic comes from ``traffic_profile``."""
     B, L = 4, 262144
     steps, warm = min(args.steps, 64), args.warmup
     specs = [LayerSpec(ratio=0, indexer=False, topk=0) if r == 0 else LayerSpec(ratio=r, topk=topk)
@@ -199,7 +361,8 @@ def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=Non
     for i, spec in enumerate(specs):
         lseed = seed + spec.ratio + 1000 * list(ratios[:i]).count(spec.ratio)
         params = SC.layer_params(spec, lseed, device="cuda")
-        layer = CsaLayer(spec, B, L + warm + 3 * steps + 8, params, device="cuda", max_chunk=spec.window)
+        layer = CsaLayer(spec, B, L + warm + 3 * steps + 2 * max(ratios) + 8, params, device="cuda",
+                         max_chunk=spec.window)
         build_prefix(layer, spec, lseed, L)
         layers.append(layer)
         tl = []
@@ -209,13 +372,11 @@ def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=Non
         toks.append(tl)
     log(f"[stack] {list(ratios)} (top-{topk}) at {L} tokens x {B} built in {time.time() - t_setup:.1f}s")
 
-    def step(j, trace_layer=None):
+    def step(j, only=None):
         for i, layer in enumerate(layers):
-            if trace_layer is not None:
-                K.dsv4_trace_enable(i == trace_layer)
+            if only is not None:
+                K.dsv4_trace_enable(i == only)
             layer.decode(toks[i][j])
-        if trace_layer is not None:
-            K.dsv4_trace_enable(False)
 
     for j in range(warm):
         step(j)
@@ -225,19 +386,18 @@ def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=Non
         step(j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # kernel durations of the ratio-4 layer, in a second identical pass with the trace on
-    K.dsv4_trace_reset()
-    for j in range(warm, warm + steps):
-        step(j, trace_layer=i4)
-    torch.cuda.synchronize()
-    per_kernel = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+    # kernel durations of the whole step, then of the ratio-4 layer alone, back to back
+    p_trace = layers[0].lengths[0]
+    per_kernel = traced(lambda: [step(j) for j in range(warm, warm + steps)], 6 * len(layers) * steps)
+    for l in layers:
+        l.lengths = [p_trace] * B
+    per_kernel4 = traced(lambda: [step(j, only=i4) for j in range(warm, warm + steps)],
+                         6 * len(layers) * steps)
     # graph replay of the K steps (state restored outside the timed region)
     names = ("ring", "state", "rows", "state_i", "rows_i")
     snap = [{n: getattr(l, n).clone() for n in names if hasattr(l, n)} for l in layers]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for j in range(warm, warm + steps):
-            step(j)
+    p_graph = layers[0].lengths[0]
+    graph = graph_of(lambda: [step(j) for j in range(warm, warm + steps)])
 
     def restore():
         for l, sn in zip(layers, snap):
@@ -253,29 +413,59 @@ def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=Non
     graph.replay()
     torch.cuda.synchronize()
     g_wall = time.perf_counter() - t0
+    del graph
+    # each layer's row emissions at their natural rate (the window holds n_e of them, not K/r)
+    corr_wall = corr_kernel = 0.0
+    emissions = {}
+    for i, (spec, layer) in enumerate(zip(specs, layers)):
+        if not spec.has_rows:
+            continue
+        n_g = emission_positions(p_graph, steps, spec.ratio)
+        n_t = emission_positions(p_trace, steps, spec.ratio)
+        if n_g == steps / spec.ratio and n_t == steps / spec.ratio:
+            continue
+        layer.lengths = [p_graph + steps] * B
+        ew, ek, _ = emission_cost(layer, toks[i][warm])
+        corr_wall += (steps / spec.ratio - n_g) * ew * 1e-3
+        corr_kernel += (steps / spec.ratio - n_t) * ek
+        emissions[f"layer{i}_ratio{spec.ratio}"] = {"extra_us_per_emission": ew * 1e3,
+                                                    "extra_kernel_us_per_emission": ek * 1e3,
+                                                    "emission_steps_in_window": n_g}
+    g_amort = g_wall + corr_wall
+    kernel_ms_step = (sum(v[1] for v in per_kernel.values()) + corr_kernel) / steps
+    by = defaultdict(float)
+    for i, spec in enumerate(specs):
+        for k, v in decode_step_bytes(spec, B, range(p_trace, p_trace + steps)).items():
+            by[f"layer{i}_ratio{spec.ratio}.{k}" if k != "total" else "total"] += v
     spec4 = specs[i4]
-    nv = (L + warm) // spec4.ratio
-    n_l, ms_l = per_kernel["index_score_stream"]
+    nv = (p_trace + steps // 2 + 1) // spec4.ratio
+    n_l, ms_l = per_kernel4["index_score_stream"]
     # algorithmic bytes of one scan: every visible indexer row, the queries and head weights
     bytes_launch = B * (nv * spec4.index_dim * 2 + spec4.index_heads * (spec4.index_dim * 2 + 4))
     achieved = bytes_launch / (ms_l / n_l * 1e-3) / 1e9
+    dominant = {"kernel": "index_score_stream (ratio-4 layer)", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": (traffic_from_profile(traffic_profile, "index_score_stream")
+                            if traffic_profile else None),
+                "bytes_per_launch": bytes_launch, "avg_us": ms_l / n_l * 1e3}
+    dominant["step_traffic"] = (step_traffic_from_profile(step_traffic_profile, per_kernel, steps)
+                                if step_traffic_profile else None)
     return {
         "workload": f"decode, {list(ratios)} stack ("
                     + ", ".join("window-only" if r == 0 else
                                 f"ratio-{r} with top-{topk} over ~{(L + warm) // r} rows" for r in ratios)
                     + f"), batch {B}, context {L}",
-        "tok_s": B * steps / g_wall, "ms_per_step": g_wall / steps * 1e3,
-        "mode": f"hip-graph replay of the K captured steps ({len(ratios)} layers per step)",
+        "tok_s": B * steps / g_amort, "ms_per_step": g_amort / steps * 1e3,
+        "mode": f"hip-graph replay of the K captured steps ({len(ratios)} layers per step), row "
+                "emissions amortized at their natural rate",
+        "raw_ms_per_step": g_wall / steps * 1e3,
+        "emission": emissions,
         "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3},
-        "kernels_ratio4_layer": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3}
-                                 for n, v in per_kernel.items()},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": (traffic_from_profile(traffic_profile, "index_score_stream")
-                                                                  if traffic_profile else None),
-                     "kernel": "index_score_stream",
-                     "bytes_per_launch": bytes_launch},
+        "kernels": kernel_table(per_kernel, steps),
+        "kernels_ratio4_layer": kernel_table(per_kernel4, steps),
+        "bytes_per_step": dict(by),
+        "roofline": step_roofline(by["total"], kernel_ms_step, dominant),
     }
-
 
 
 def bench_shared(args, seed=71, n_own=2, n_sel=1):
@@ -327,15 +517,9 @@ def bench_shared(args, seed=71, n_own=2, n_sel=1):
         step(j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # kernel durations in a second pass with the trace on (positions keep advancing, as in
+    # kernel durations in a second pass, back to back (positions keep advancing, as in
     # bench_stack: the layers hold room for the three passes)
-    K.dsv4_trace_reset()
-    K.dsv4_trace_enable(True)
-    for j in range(warm, warm + steps):
-        step(j)
-    torch.cuda.synchronize()
-    K.dsv4_trace_enable(False)
-    per_kernel = {n: kernel_time(n) for n in K.dsv4_trace_kernels()}
+    per_kernel = traced(lambda: [step(j) for j in range(warm, warm + steps)], 12 * steps)
     names = ("ring", "state", "rows", "state_i", "rows_i")
     snap = [{n: getattr(l, n).clone() for n in names if hasattr(l, n)} for l in [owner] + cons]
     graph = torch.cuda.CUDAGraph()
@@ -373,40 +557,85 @@ def bench_shared(args, seed=71, n_own=2, n_sel=1):
         "mode": f"hip-graph replay of the K captured steps ({n_layers} layers per step)",
         "eager": {"tok_s": B * steps / wall, "ms_per_step": wall / steps * 1e3},
         "cache_bytes": {"owner": owner_bytes, "per_sharing_layer": cons_bytes},
-        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
+        "kernels": kernel_table(per_kernel, steps),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "index_score_stream",
                      "bytes_per_launch": bytes_launch},
     }
 
 
-def cpu_baseline_decode(layer_state, sample_steps):
-    """The oracle doing the same decode work (window + all visible rows, per sequence) on
-    the host, for ``sample_steps`` steps of every sequence.  Rows and ring are the GPU
-    caches copied to the host (the oracle consumes them as inputs)."""
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_prefix_rows(spec: LayerSpec, seed: int, b: int, n_tok: int, index_lane: bool = False,
+                       device="cpu", block: int = 8192) -> np.ndarray:
+    """Compressed rows of sequence ``b`` after ``n_tok`` tokens, by the oracle, block by block
+    from the seeded lanes (drawn on ``device`` by the input generator, read on the host)."""
     import oracle
-    layer, toks, spec, params, pos = layer_state
-    B = layer.batch
-    rows = layer.rows.float().cpu().numpy().astype(np.float64)
-    sinks = params["sinks"].cpu().numpy()
-    n = pos[0]
-    kv_hist = np.random.default_rng(0).standard_normal((spec.window, spec.dim))
+    r = spec.ratio
+    fa, fg = ("ai", "gi") if index_lane else ("a", "g")
+    P = {k: _host(v) for k, v in SC.layer_params(spec, seed).items()}
+    ape, gamma = (P["ape_i"], P["norm_w_i"]) if index_lane else (P["ape"], P["norm_w"])
+    dim = spec.index_dim if index_lane else spec.dim
+    store = "bf16" if spec.dtype == torch.bfloat16 else "f32"
+    end = n_tok - n_tok % r
+    block = max(r, block - block % r)
+    out = [np.zeros((0, dim))]
+    for t0 in range(0, end, block):
+        t1 = min(end, t0 + block)
+        s0 = max(0, t0 - r) if spec.is_overlap else t0          # the previous window, overlapping
+        lanes = SC.token_inputs(spec, seed, b, s0, t1, device=device, fields=[fa, fg])
+        out.append(oracle.compressor_rows(_host(lanes[fa]), _host(lanes[fg]), ape, gamma,
+                                          P["inv_freq"], ratio=r, overlap=spec.is_overlap,
+                                          eps=spec.eps, store=store, rows=range(t0 // r, t1 // r),
+                                          token0=s0))
+    return np.concatenate(out)
+
+
+def cpu_baseline_decode(spec: LayerSpec, seed: int, L: int, n_seq: int, steps: int, device="cpu"):
+    """The oracle doing the decode work of ``steps`` steps of ``n_seq`` sequences from
+    position L on: at each step the row emission when one completes ((p + 1) % r == 0: the
+    oracle's compressor over that row's window), then attention over the window and every
+    visible row.  The cache it starts from (rows of the first L tokens) is built by the
+    oracle from the same seeded inputs before the clock starts; nothing comes from the GPU."""
+    import oracle
+    r, W = spec.ratio, spec.window
+    store = "bf16" if spec.dtype == torch.bfloat16 else "f32"
+    P = {k: _host(v) for k, v in SC.layer_params(spec, seed).items()}
+    t_lo = max(0, L - W + 1 - spec.coff * r)
+    seqs = []
+    for b in range(n_seq):
+        rows = oracle_prefix_rows(spec, seed, b, L, device=device)
+        tok = {k: _host(v) for k, v in SC.token_inputs(spec, seed, b, t_lo, L + steps, device=device,
+                                                       fields=["q", "kv", "a", "g"]).items()}
+        seqs.append([rows, tok])
+    emitted = 0
     t0 = time.perf_counter()
-    done = 0
-    for i in range(sample_steps):
-        for b in range(B):
-            q = toks[i]["q"][b].float().cpu().numpy()[None].astype(np.float64)
-            p = n + i
-            kv = np.concatenate([kv_hist[1:], toks[i]["kv"][b].float().cpu().numpy()[None]])
-            nv = min(oracle.visible_rows(p, spec.ratio), rows.shape[1])
-            oracle.csa_attention(q, kv, rows[b, :nv], None, [p], window=spec.window,
-                                 ratio=spec.ratio, sinks=sinks, scale=spec.scale, store="bf16",
-                                 kv_offset=p - spec.window + 1)
-            done += 1
+    for i in range(steps):
+        p = L + i
+        for rows_tok in seqs:
+            rows, tok = rows_tok
+            if (p + 1) % r == 0:
+                j = (p + 1) // r - 1
+                s0 = max(0, (j - 1) * r) if spec.is_overlap else j * r
+                row = oracle.compressor_rows(tok["a"][s0 - t_lo:p + 1 - t_lo],
+                                             tok["g"][s0 - t_lo:p + 1 - t_lo], P["ape"],
+                                             P["norm_w"], P["inv_freq"], ratio=r,
+                                             overlap=spec.is_overlap, eps=spec.eps, store=store,
+                                             rows=[j], token0=s0)
+                rows = rows_tok[0] = np.concatenate([rows, row])
+                emitted += 1
+            lo = max(0, p - W + 1)
+            oracle.csa_attention(tok["q"][p - t_lo][None], tok["kv"][lo - t_lo:p + 1 - t_lo],
+                                 rows, None, [p], window=W, ratio=r, sinks=P["sinks"],
+                                 scale=spec.scale, store=store, kv_offset=lo)
     dt = time.perf_counter() - t0
+    done = steps * n_seq
     return {"value": done / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{sample_steps} decode steps x {B} sequences of the 64K ratio-128 layer "
-                      f"(window + {rows.shape[1]} rows per query), numpy fp32 oracle"}
+            "sample": f"{steps} decode steps x {n_seq} sequences from position {L} "
+                      f"({done} tokens, {emitted} row emissions at the natural rate), window + "
+                      f"every visible row per query; oracle in numpy, cache built by the oracle"}
 
 
 # ------------------------------------------------------------------ prefill @ 64K
@@ -439,67 +668,83 @@ def bench_prefill(args, seed=1):
         step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / reps
-    K.dsv4_trace_enable(True)
-    K.dsv4_trace_reset()
-    for _ in range(reps):
-        step()
-    torch.cuda.synchronize()
-    names = K.dsv4_trace_kernels()
-    per_kernel = {n: kernel_time(n) for n in names}
-    K.dsv4_trace_enable(False)
+    per_kernel = traced(lambda: [step() for _ in range(reps)], 10 * reps)
     # algorithmic flops of the chunk: indexer q.k over every visible row, attention QK^T and PV
-    idx_pairs = sum(min((p + 1) // 4, L // 4) for p in range(start, L))
-    idx_flops = 2.0 * spec.index_heads * spec.index_dim * idx_pairs
-    keys = sum(spec.window + min(spec.topk, (p + 1) // 4) for p in range(start, L))
-    attn_flops = 4.0 * spec.heads * spec.dim * keys
+    fl = prefill_chunk_flops(spec, start, S)
     dom = max(per_kernel, key=lambda n: per_kernel[n][1])
     n_d, ms_d = per_kernel[dom]
-    dom_flops = idx_flops if "index" in dom else attn_flops if "attn" in dom else 0.0
+    dom_flops = fl["indexer"] if "index" in dom else fl["attention"] if "attn" in dom else 0.0
     achieved = dom_flops / (ms_d / n_d * 1e-3) / 1e12
     total_ms = sum(v[1] for v in per_kernel.values()) / reps
+    whole = fl["total"] / (total_ms * 1e-3) / 1e12
     res = {
         "tok_s": S / wall, "ms_per_chunk": wall * 1e3,
         "workload": f"ratio-4 layer, chunk {start}->{L} (S={S}), indexer top-{spec.topk}, "
                     f"64 heads x 512 latent, bf16",
-        "flops_per_chunk": idx_flops + attn_flops,
-        "tflops_whole_chunk": (idx_flops + attn_flops) / (total_ms * 1e-3) / 1e12,
-        "kernels": {n: {"launches": v[0], "avg_us": v[1] / max(1, v[0]) * 1e3} for n, v in per_kernel.items()},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
-                     "traffic": traffic_from_profile(TRAFFIC_PREFILL, dom),
-                     "kernel": dom, "flops_per_launch": dom_flops},
+        "flops_per_chunk": fl,
+        "kernels": kernel_table(per_kernel, reps),
+        "roofline": {"bound": "mfma", "achieved": whole, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": whole / BF16_MFMA_PEAK_TFLOPS,
+                     "scope": "whole chunk: algorithmic flops over the summed kernel time of the "
+                              "chunk (compressor lanes, indexer, top-k, attention, ring update)",
+                     "flops_per_chunk": fl["total"], "kernel_us_per_chunk": total_ms * 1e3,
+                     "traffic": None,
+                     "dominant_kernel": {"kernel": dom, "bound": "mfma", "achieved": achieved,
+                                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                                         "traffic": traffic_from_profile(TRAFFIC_PREFILL, dom),
+                                         "flops_per_launch": dom_flops,
+                                         "avg_us": ms_d / n_d * 1e3}},
     }
-    return res, (layer, tok, spec, params, start, sel)
+    return res, (spec, seed, start, S)
 
 
-def cpu_baseline_prefill(state, n_queries):
-    """The oracle on ``n_queries`` queries of the same chunk: indexer scores over every
-    visible row, top-k, attention over window + selected rows (rows from the GPU cache)."""
+def cpu_baseline_prefill(spec: LayerSpec, seed: int, start: int, S: int, n_queries: int,
+                         device="cpu"):
+    """The oracle on the chunk start .. start+S-1 of one sequence: the chunk's compressed rows
+    (both lanes; timed, charged to the sample at n_queries / S of their cost), then for
+    ``n_queries`` queries spread over the chunk the indexer scores over every visible row,
+    the top-k and attention over window + selected rows.  The rows of the first ``start``
+    tokens are built by the oracle before the clock starts."""
     import oracle
-    layer, tok, spec, params, start, _ = state
-    rows = layer.rows[0].float().cpu().numpy().astype(np.float64)
-    rows_i = layer.rows_i[0].float().cpu().numpy().astype(np.float64)
-    sinks = params["sinks"].cpu().numpy()
-    S = tok["q"].shape[1]
-    idx = np.linspace(spec.window - 1, S - 1, n_queries).astype(int)   # windows inside the chunk
-    q = tok["q"][0].float().cpu().numpy().astype(np.float64)
-    kv = tok["kv"][0].float().cpu().numpy().astype(np.float64)
-    qi = tok["qi"][0].float().cpu().numpy()
-    w = tok["w"][0].cpu().numpy()
-    t0 = time.perf_counter()
+    r, W = spec.ratio, spec.window
+    store = "bf16" if spec.dtype == torch.bfloat16 else "f32"
+    P = {k: _host(v) for k, v in SC.layer_params(spec, seed).items()}
+    rows = oracle_prefix_rows(spec, seed, 0, start, device=device)
+    rows_i = oracle_prefix_rows(spec, seed, 0, start, index_lane=True, device=device)
+    s0 = max(0, start - r) if spec.is_overlap else start
+    lanes = {k: _host(v) for k, v in SC.token_inputs(spec, seed, 0, s0, start + S, device=device,
+                                                     fields=["a", "g", "ai", "gi"]).items()}
+    idx = np.linspace(0, S - 1, n_queries).astype(int)
+    qs = []
     for i in idx:
         p = start + int(i)
-        nv = oracle.visible_rows(p, spec.ratio)
-        sc = oracle.index_scores(qi[i:i + 1], w[i:i + 1], rows_i[:nv])
-        sel = oracle.select_topk(sc, [p], ratio=spec.ratio, k=spec.topk)
-        lo = int(i) - spec.window + 1
-        oracle.csa_attention(q[i:i + 1], kv[lo:i + 1], rows, sel, [p], window=spec.window,
-                             ratio=spec.ratio, sinks=sinks, scale=spec.scale, store="bf16",
-                             kv_offset=start + lo)
-    dt = time.perf_counter() - t0
+        lo = max(0, p - W + 1)
+        t = {k: _host(v) for k, v in SC.token_inputs(spec, seed, 0, p, p + 1, device=device,
+                                                     fields=["q", "qi", "w"]).items()}
+        t["kv"] = _host(SC.token_inputs(spec, seed, 0, lo, p + 1, device=device, fields=["kv"])["kv"])
+        qs.append((p, lo, t))
+    kw = dict(ratio=r, overlap=spec.is_overlap, eps=spec.eps, store=store,
+              rows=range(start // r, (start + S) // r), token0=s0)
+    t0 = time.perf_counter()
+    rows = np.concatenate([rows, oracle.compressor_rows(lanes["a"], lanes["g"], P["ape"], P["norm_w"],
+                                                        P["inv_freq"], **kw)])
+    rows_i = np.concatenate([rows_i, oracle.compressor_rows(lanes["ai"], lanes["gi"], P["ape_i"],
+                                                            P["norm_w_i"], P["inv_freq"], **kw)])
+    t_comp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for p, lo, t in qs:
+        nv = oracle.visible_rows(p, r)
+        sc = oracle.index_scores(t["qi"], t["w"], rows_i[:nv])
+        sel = oracle.select_topk(sc, [p], ratio=r, k=spec.topk)
+        oracle.csa_attention(t["q"], t["kv"], rows, sel, [p], window=W, ratio=r, sinks=P["sinks"],
+                             scale=spec.scale, store=store, kv_offset=lo)
+    t_q = time.perf_counter() - t0
+    dt = t_q + t_comp * n_queries / S
     return {"value": n_queries / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{n_queries} of the {S} queries of the 64K prefill chunk (indexer over "
-                      f"~16K rows, top-512, attention), numpy fp32 oracle"}
+            "sample": f"{n_queries} of the {S} queries of the chunk {start}->{start + S} (indexer over "
+                      f"~{(start + S) // r} rows, top-{spec.topk}, attention) plus {n_queries}/{S} of the "
+                      f"chunk's compressor work; oracle in numpy, prefix rows built by the oracle"}
 
 
 def bench_output_path(args, seed=41):
@@ -571,14 +816,16 @@ def bench_output_path(args, seed=41):
         compressor_lanes(x, wkv, wg)
     torch.cuda.synchronize()
     K.dsv4_trace_enable(False)
-    n_g, ms_g = kernel_time("gproj")
+    gname = max((n for n in K.dsv4_trace_kernels() if n.startswith("gproj")),
+                key=lambda n: kernel_time(n)[0])
+    n_g, ms_g = kernel_time(gname)
     us = ms_g / n_g * 1e3
     fl = 2.0 * T * W * hid
     ach = fl / (us * 1e-6) / 1e12
     out["lanes_prefill_2048"] = {
         "tokens": T, "us_per_call": 2 * us,
         "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "gproj_tile",
+                     "frac": ach / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": gname,
                      "flops_per_launch": fl}}
     return out
 
@@ -590,12 +837,15 @@ def bench_output_path(args, seed=41):
 # sources still match (a changed kernel reports null until it is measured again).
 CSRC = os.path.join(ROOT, "sparse_attention_dsv4_amd", "csrc")
 KERNEL_SOURCES = {"attn": "attention.hip", "ring": "attention.hip", "index": "indexer.hip",
-                  "topk": "indexer.hip", "compress": "compress.hip"}
+                  "topk": "indexer.hip", "compress": "compress.hip", "frontier": "compress.hip",
+                  "gproj": "proj.hip", "rope": "proj.hip"}
 COPY_CALIB_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
 TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_rs_ctx65536_chunk2048_ratio4.txt")
 TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_stream_decode_ctx262144_b4_stack.txt")
+TRAFFIC_DECODE_STEP = os.path.join(PROFILES, "traffic_step_decode_ctx65536_b8_ratio128.txt")
+TRAFFIC_STACK_STEP = os.path.join(PROFILES, "traffic_step_stack_decode_ctx262144_b4.txt")
 
 
 def kernel_source_digest(kernel: str) -> str:
@@ -707,6 +957,63 @@ def traffic_from_profile(path: str, kernel: str):
     return float(kv["traffic_bytes_per_launch"])
 
 
+def write_step_traffic_profile(a):
+    """HBM bytes per dispatch of every library kernel launched at least 8 times in the run
+    (the timed steps; the one-off prefix build falls below), one line per kernel: the
+    per-step traffic of a workload is then the sum over its kernels of launches per step
+    times bytes per dispatch."""
+    cf = _main_group(_pmc(a.calib_fetch, "FETCH_SIZE"), "copy")[1]
+    cw = _main_group(_pmc(a.calib_write, "WRITE_SIZE"), "copy")[1]
+    ff = COPY_CALIB_BYTES / (np.mean(cf) * 1024.0)
+    wf = COPY_CALIB_BYTES / (np.mean(cw) * 1024.0)
+    fetch, write = _pmc(a.fetch, "FETCH_SIZE"), _pmc(a.write, "WRITE_SIZE")
+    per = defaultdict(lambda: [[], []])
+    for (k, g), v in fetch.items():
+        if len(v) >= 8 and k != "copy":
+            per[k][0] += list(v.values())
+    for (k, g), v in write.items():
+        if len(v) >= 8 and k != "copy":
+            per[k][1] += list(v.values())
+    with open(a.out, "w") as f:
+        f.write(f"# HBM traffic per dispatch of each kernel of a step: {a.title}\n")
+        f.write("# commands (run on the MI355X box from the repository root; each --pmc pass its own run):\n")
+        for c in a.command:
+            f.write(f"#   {c}\n")
+        f.write(f"# copy_calibration: {COPY_CALIB_BYTES} bytes; FETCH_SIZE {np.mean(cf):.1f} KiB, WRITE_SIZE "
+                f"{np.mean(cw):.1f} KiB -> scale {ff:.4f} (fetch), {wf:.4f} (write)\n")
+        f.write("# kernel | source_digest | dispatches | fetch_kib | write_kib | bytes_per_dispatch\n")
+        for k, (fv, wv) in sorted(per.items()):
+            if not fv or not wv:
+                continue
+            byts = np.mean(fv) * 1024.0 * ff + np.mean(wv) * 1024.0 * wf
+            f.write(f"step_kernel: {k} | {kernel_source_digest(k)} | {len(fv)} | {np.mean(fv):.1f} | "
+                    f"{np.mean(wv):.1f} | {byts:.0f}\n")
+    print(open(a.out).read())
+
+
+def step_traffic_from_profile(path: str, per_kernel: dict, steps: int):
+    """HBM bytes per step: the launches per step of each traced kernel times its bytes per
+    dispatch from a committed step-traffic summary; None when the summary is absent, lacks a
+    kernel, or was measured on other sources of one."""
+    try:
+        lines = [l.split(": ", 1)[1] for l in open(path).read().splitlines()
+                 if l.startswith("step_kernel: ")]
+    except OSError:
+        return None
+    table = {}
+    for l in lines:
+        k, digest, _, _, _, byts = [x.strip() for x in l.split("|")]
+        table[k] = (digest, float(byts))
+    total = 0.0
+    for name, (n, _) in per_kernel.items():
+        if not n:
+            continue
+        if name not in table or table[name][0] != kernel_source_digest(name):
+            return None
+        total += n / steps * table[name][1]
+    return total
+
+
 def write_kernel_profile(a):
     groups = defaultdict(list)
     for r in _csv_rows(a.trace_dir, "*kernel_trace.csv"):
@@ -729,7 +1036,8 @@ def write_kernel_profile(a):
 
 
 def main():
-    if len(sys.argv) > 1 and sys.argv[1] in ("--write-traffic-profile", "--write-kernel-profile"):
+    if len(sys.argv) > 1 and sys.argv[1] in ("--write-traffic-profile", "--write-kernel-profile",
+                                              "--write-step-traffic-profile"):
         mode = sys.argv[1]
         pp = argparse.ArgumentParser(prog=f"bench.py {mode}")
         pp.add_argument("--out", required=True)
@@ -744,7 +1052,8 @@ def main():
         pp.add_argument("--largest-grid", action="store_true",
                         help="take the kernel's dispatches of the largest grid launched 8+ times")
         a = pp.parse_args(sys.argv[2:])
-        (write_traffic_profile if mode == "--write-traffic-profile" else write_kernel_profile)(a)
+        {"--write-traffic-profile": write_traffic_profile, "--write-kernel-profile": write_kernel_profile,
+         "--write-step-traffic-profile": write_step_traffic_profile}[mode](a)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--copy-calibration":
         copy_calibration()
@@ -757,8 +1066,10 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=8)
     ap.add_argument("--chunk", type=int, default=2048)
     ap.add_argument("--prefill-reps", type=int, default=5)
-    ap.add_argument("--cpu-decode-steps", type=int, default=64)
-    ap.add_argument("--cpu-prefill-queries", type=int, default=64)
+    ap.add_argument("--cpu-decode-steps", type=int, default=512,
+                    help="decode steps of the oracle's sample (a multiple of 128: row emissions at their natural rate)")
+    ap.add_argument("--cpu-decode-seqs", type=int, default=8)
+    ap.add_argument("--cpu-prefill-queries", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-stack", action="store_true",
@@ -776,7 +1087,7 @@ def main():
         sys.exit(2)
     K.lib()
     if args.only == "stack":             # stack-only profiler run
-        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
+        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK, step_traffic_profile=TRAFFIC_STACK_STEP)
         log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step")
         print(json.dumps({"workload": "stack", "decode_262k_stack": stack}), flush=True)
         return
@@ -790,11 +1101,17 @@ def main():
     dec = pre = None
     if args.only != "prefill":
         dec, dec_state = bench_decode(args)
-        log(f"[decode] graph {dec['tok_s']:.0f} tok/s, {dec['ms_per_step']:.4f} ms/step; "
-            f"eager {dec['eager']['tok_s']:.0f} tok/s, {dec['eager']['ms_per_step']:.4f} ms/step")
+        log(f"[decode] graph {dec['tok_s']:.0f} tok/s, {dec['ms_per_step']:.4f} ms/step "
+            f"(raw {dec['raw']['ms_per_step']:.4f}); eager {dec['eager']['tok_s']:.0f} tok/s; whole step "
+            f"{dec['roofline']['frac'] * 100:.1f}% of HBM ({dec['roofline']['kernel_us_per_step']:.2f} us of "
+            f"kernels); {dec['roofline']['dominant_kernel']['kernel']} "
+            f"{dec['roofline']['dominant_kernel']['frac'] * 100:.1f}%")
     if not args.skip_prefill and args.only != "decode":
         pre, pre_state = bench_prefill(args)
-        log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk")
+        log(f"[prefill] {pre['tok_s']:.0f} tok/s, {pre['ms_per_chunk']:.3f} ms/chunk; whole chunk "
+            f"{pre['roofline']['frac'] * 100:.1f}% of MFMA ({pre['roofline']['kernel_us_per_chunk']:.0f} us "
+            f"of kernels); {pre['roofline']['dominant_kernel']['kernel']} "
+            f"{pre['roofline']['dominant_kernel']['frac'] * 100:.1f}%")
     outp = None
     if args.only is None:
         outp = bench_output_path(args)
@@ -804,12 +1121,13 @@ def main():
             f"compressor lanes of 2048 tokens {outp['lanes_prefill_2048']['us_per_call']:.1f} us")
     stack = pro = shared = None
     if not args.skip_stack and args.only is None:
-        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK)
-        log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step; index scan "
-            f"{stack['roofline']['achieved']:.0f} GB/s ({stack['roofline']['frac'] * 100:.1f}% of HBM)")
+        stack = bench_stack(args, traffic_profile=TRAFFIC_STACK, step_traffic_profile=TRAFFIC_STACK_STEP)
+        log(f"[stack] graph {stack['tok_s']:.0f} tok/s, {stack['ms_per_step']:.4f} ms/step; whole step "
+            f"{stack['roofline']['frac'] * 100:.1f}% of HBM; index scan "
+            f"{stack['roofline']['dominant_kernel']['frac'] * 100:.1f}%")
         pro = bench_stack(args, ratios=(128, 128, 4, 128), topk=1024)
-        log(f"[pro stack] graph {pro['tok_s']:.0f} tok/s, {pro['ms_per_step']:.4f} ms/step; index scan "
-            f"{pro['roofline']['achieved']:.0f} GB/s ({pro['roofline']['frac'] * 100:.1f}% of HBM)")
+        log(f"[pro stack] graph {pro['tok_s']:.0f} tok/s, {pro['ms_per_step']:.4f} ms/step; whole step "
+            f"{pro['roofline']['frac'] * 100:.1f}% of HBM")
         shared = bench_shared(args)
         log(f"[shared] graph {shared['tok_s']:.0f} tok/s, {shared['ms_per_step']:.4f} ms/step "
             f"({shared['us_per_layer']:.1f} us per layer); index scan {shared['roofline']['achieved']:.0f} GB/s")
@@ -818,11 +1136,17 @@ def main():
         return
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = {"decode": cpu_baseline_decode(dec_state, args.cpu_decode_steps)}
+        t_cpu = time.time()
+        dspec, dseed = dec_state
+        cpu = cpu_baseline_decode(dspec, dseed, args.context, args.cpu_decode_seqs,
+                                  args.cpu_decode_steps, device="cuda")
         if pre is not None:
-            cpu["prefill"] = cpu_baseline_prefill(pre_state, args.cpu_prefill_queries)
-        cpu = dict(cpu["decode"], prefill=cpu.get("prefill"),
-                   host=platform.processor() or platform.machine())
+            pspec, pseed, pstart, pS = pre_state
+            cpu["prefill"] = cpu_baseline_prefill(pspec, pseed, pstart, pS, args.cpu_prefill_queries,
+                                                  device="cuda")
+        cpu["host"] = platform.processor() or platform.machine()
+        log(f"[cpu baseline] decode {cpu['value']:.1f} tok/s on {cpu['cores']} threads "
+            f"({time.time() - t_cpu:.1f}s with setup)")
     line = {
         "metric": "CSA decode tokens/s and prefill tokens/s at 64K ctx; % HBM/MFMA peak",
         "value": dec["tok_s"],

@@ -275,7 +275,8 @@ int dsv4_grouped_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w, v
  * a start/stop HIP event pair attached to its own dispatch (hipExtLaunchKernelGGL), so each
  * record is that kernel's execution time on its launch stream.  dsv4_trace_read() waits for the
  * recorded events and returns, for the kernels whose name contains `name_substr` (all when
- * NULL or ""), the launch count and the summed GPU duration in milliseconds.  Tracing
+ * NULL or ""; "=name" selects the kernel of exactly that name), the launch count and the
+ * summed GPU duration in milliseconds.  Tracing
  * creates HIP events (it is the one facility that allocates); leave it off in production. */
 int dsv4_trace_enable(int32_t on);
 int dsv4_trace_reset(void);

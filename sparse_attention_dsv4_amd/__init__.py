@@ -402,7 +402,8 @@ def dsv4_trace_reset():
 
 
 def dsv4_trace_read(name_substr: str = ""):
-    """(launches, total_ms) of traced kernels whose name contains ``name_substr``."""
+    """(launches, total_ms) of traced kernels whose name contains ``name_substr`` (or, for
+    "=name", of the kernel of exactly that name)."""
     n = ctypes.c_int64(0)
     ms = ctypes.c_double(0.0)
     _check(lib().dsv4_trace_read(name_substr.encode(), ctypes.byref(n), ctypes.byref(ms)))

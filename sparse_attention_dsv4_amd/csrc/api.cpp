@@ -415,7 +415,11 @@ int dsv4_trace_read(const char* name_substr, int64_t* launches, double* total_ms
     int64_t n = 0;
     double ms = 0.0;
     for (auto& r : g_recs) {
-        if (name_substr && *name_substr && !std::strstr(r.name, name_substr)) continue;
+        if (name_substr && name_substr[0] == '=') {          // "=name": that kernel only
+            if (std::strcmp(r.name, name_substr + 1) != 0) continue;
+        } else if (name_substr && *name_substr && !std::strstr(r.name, name_substr)) {
+            continue;
+        }
         if (!r.start || !r.stop) return fail(DSV4_EHIP, "trace record without events");
         hipError_t e = hipEventSynchronize(r.stop);
         if (e != hipSuccess) return hip_status(e, "trace sync");
