@@ -247,8 +247,7 @@ def select_topk(scores, positions, *, ratio: int, k: int) -> np.ndarray:
 # Attention
 # --------------------------------------------------------------------------------------
 def csa_attention(q, kv, rows, sel, positions, *, window: int, ratio: int, sinks,
-                  scale: float, store: str, work=np.float32, p_round: bool = False,
-                  kv_offset: int = 0) -> np.ndarray:
+                  scale: float, store: str, work=np.float32, kv_offset: int = 0) -> np.ndarray:
     """MQA attention of each query over its sliding window plus its compressed rows.
 
     [MTPLX-216] "What V4 adds" and its opening: 64 query heads over one 512-dim latent that
@@ -263,8 +262,8 @@ def csa_attention(q, kv, rows, sel, positions, *, window: int, ratio: int, sinks
       l_x = scale * q_h . x;  m = max(z_h, max l);
       o_h = sum_x e^(l_x - m) x / (e^(z_h - m) + sum_x e^(l_x - m)).
     READING: the window is the W tokens ending at p, self included; a token may count both
-    as a window key and inside a compressed row (no de-duplication).
-    ``p_round`` rounds e^(l - m) to bf16 before the weighted sum (kernel-faithful mode).
+    as a window key and inside a compressed row (no de-duplication).  The probabilities are
+    not rounded before the weighted sum (the bf16 tolerance covers kernels that round them).
 
     q: [S, H, D]; kv: [T, D] with kv[i] the latent of token kv_offset + i; rows: [N, D] or
     None (ratio 0); sel: [S, k] int or None; positions: [S]; sinks: [H].
@@ -295,8 +294,6 @@ def csa_attention(q, kv, rows, sel, positions, *, window: int, ratio: int, sinks
         m = np.maximum(sinks, logits.max(axis=1))
         e = np.exp(logits - m[:, None])
         denom = np.exp(sinks - m) + e.sum(axis=1, dtype=work)
-        if p_round:
-            e = bf16_round(e).astype(work)
         o = np.matmul(e, X) / denom[:, None]
         out[i] = round_store(o, store)
     return out

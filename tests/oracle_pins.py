@@ -209,6 +209,66 @@ def pin_compress_prefix_invariance():
         assert np.array_equal(part, full[:T2 // r])
 
 
+def pin_compress_lane_slice_with_token0():
+    """Rows computed from a slice of the lane that starts at token t0 (``token0=t0`` and a
+    ``rows=`` subset) equal the same rows of the whole-lane call, bit for bit: overlapping
+    and plain windows, t0 on and off a window boundary, ordered and unordered subsets."""
+    rng = _rng(31)
+    D = 8
+    for overlap, r in [(True, 4), (False, 4), (True, 3), (False, 5)]:
+        T = 12 * r + 3
+        a, g, ape = _lanes(rng, T, r, D, overlap)
+        gamma = rng.standard_normal(D)
+        inv = _inv_freq(4)
+        kw = dict(ratio=r, overlap=overlap, eps=1e-6, store="bf16")
+        full = O.compressor_rows(a, g, ape, gamma, inv, **kw)
+        for t0 in (1, r, r + 1, 2 * r - 1, 5 * r + 2):
+            first = -(-t0 // r) + (1 if overlap else 0)    # first row with every slot at or after t0
+            js = list(range(first, T // r))
+            part = O.compressor_rows(a[t0:], g[t0:], ape, gamma, inv, rows=js, token0=t0, **kw)
+            assert np.array_equal(part, full[js]), (overlap, r, t0)
+            sub = js[::-3]
+            part = O.compressor_rows(a[t0:], g[t0:], ape, gamma, inv, rows=sub, token0=t0, **kw)
+            assert np.array_equal(part, full[sub]), (overlap, r, t0, sub)
+
+
+def pin_compress_bf16_rounding_points():
+    """bf16 storage at r = 1 (one slot: the pooled value is the token's own value):
+    row t = bf16(RoPE_t(bf16(RMSNorm(bf16(a_t)) * gamma))), each rounding torch's
+    fp32 -> bfloat16 conversion, at exactly the three points the storage rule names (the
+    pooled value before the norm, the normed row, the rotated row).  The norm and the rotation
+    are taken in fp64 here (torch), so only the rounding points decide the bits."""
+    rng = _rng(33)
+    T, D, rd, eps = 24, 32, 16, 1e-6
+    a = rng.standard_normal((T, D)) * 3.0
+    g = rng.standard_normal((T, D))
+    ape = rng.standard_normal((1, D))
+    gamma = rng.standard_normal(D)
+    inv = _inv_freq(rd, theta=10.0)
+    rows = O.compressor_rows(a, g, ape, gamma, inv, ratio=1, overlap=False, eps=eps, store="bf16",
+                             work=F64)
+
+    def bf(x):
+        return torch.as_tensor(x, dtype=torch.float64).float().bfloat16().double()
+
+    def closed_form(t, round_pooled=True):
+        y = bf(a[t]) if round_pooled else torch.as_tensor(a[t], dtype=torch.float64)
+        y = bf(y / torch.sqrt(torch.linalg.vector_norm(y) ** 2 / D + eps) * torch.as_tensor(gamma))
+        th = torch.as_tensor(np.float32(t) * inv, dtype=torch.float32).double()   # fp32 angle
+        z = torch.complex(y[D - rd::2], y[D - rd + 1::2]) * torch.polar(torch.ones_like(th), th)
+        out = y.clone()
+        out[D - rd::2] = z.real
+        out[D - rd + 1::2] = z.imag
+        return bf(out).numpy()
+
+    differs = 0
+    for t in range(T):
+        expect = closed_form(t)
+        assert np.array_equal(rows[t], expect), (t, np.abs(rows[t] - expect).max())
+        differs += int((closed_form(t, round_pooled=False) != expect).any())
+    assert differs > T // 2            # the data is such that the first rounding point shows
+
+
 def pin_compress_softmax_is_convex():
     """Pooled values lie inside the range of the slot values (softmax weights are a convex
     mix).  A huge eps makes the RMSNorm a fixed scale 1/sqrt(eps), so the pooled value is
@@ -417,6 +477,13 @@ def pin_attention_rows_and_sparse_equal_dense():
         sel[i, :nv] = np.arange(nv)
     sparse = O.csa_attention(q, kv, rows, sel, pos, **kw)
     np.testing.assert_allclose(sparse, dense, rtol=1e-12, atol=1e-12)
+    # the same sets in another order with -1 entries between them
+    ragged = np.full((S, 40), -1)
+    for i, p in enumerate(pos):
+        nv = O.visible_rows(p, r)
+        ragged[i, 1:2 * nv + 1:2] = np.arange(nv)[::-1]
+    np.testing.assert_allclose(O.csa_attention(q, kv, rows, ragged, pos, **kw), dense,
+                               rtol=1e-12, atol=1e-12)
     # dominance probes around the visibility edge of query p = 17 (4 rows visible)
     q1 = np.zeros((1, 1, D))
     q1[0, 0, 0] = 1.0
@@ -427,6 +494,47 @@ def pin_attention_rows_and_sparse_equal_dense():
         rr[j, 0] = 50.0
         o = O.csa_attention(q1, np.zeros((64, D)), rr, None, [17], **kw1)
         assert (o[0, 0, 0] > 25.0) == expect, (j, o[0, 0, 0])
+
+
+def pin_attention_kv_slice_with_offset():
+    """kv handed over from token lo on (``kv_offset=lo``) equals the call with the whole kv,
+    bit for bit, for queries whose window lies inside the slice (including one whose window
+    starts exactly at lo)."""
+    rng = _rng(32)
+    H, D, W, r = 2, 8, 6, 4
+    kv = rng.standard_normal((60, D))
+    rows = rng.standard_normal((15, D))
+    pos = [20, 33, 40, 59, 59]
+    q = rng.standard_normal((len(pos), H, D))
+    kw = dict(window=W, ratio=r, sinks=np.array([0.3, -1.1]), scale=0.4, store="f32", work=F64)
+    for sel in (None, np.array([[0, 2, -1], [1, 6, 7], [-1, 3, 9], [0, 13, 14], [14, -1, -1]])):
+        full = O.csa_attention(q, kv, rows, sel, pos, **kw)
+        for lo in (1, 7, 15):
+            part = O.csa_attention(q, kv[lo:], rows, sel, pos, kv_offset=lo, **kw)
+            assert np.array_equal(part, full), lo
+
+
+def pin_fp32_work_within_rounding_bound():
+    """The fp32 working precision (pooling, scoring, softmax) stays within a small multiple of
+    fp32 rounding of the same computation in fp64: the error of an fp32 sum of n terms is
+    bounded by about n * 2^-24 of the sum of magnitudes."""
+    rng = _rng(34)
+    D, r, T = 64, 4, 48
+    a, g, ape = _lanes(rng, T, r, D, True)
+    gamma, inv = rng.standard_normal(D), _inv_freq(16)
+    kw = dict(ratio=r, overlap=True, eps=1e-6, store="f32")
+    r32 = O.compressor_rows(a, g, ape, gamma, inv, **kw)
+    r64 = O.compressor_rows(a, g, ape, gamma, inv, work=F64, **kw)
+    assert np.abs(r32 - r64).max() <= 1e-5 * np.abs(r64).max()
+    qi, w, Kr = rng.standard_normal((3, 4, 32)), rng.standard_normal((3, 4)), rng.standard_normal((50, 32))
+    s32, s64 = O.index_scores(qi, w, Kr), O.index_scores(qi, w, Kr, F64)
+    assert np.abs(s32 - s64).max() <= 1e-5 * np.abs(s64).max()
+    q, kv = rng.standard_normal((4, 3, D)), rng.standard_normal((40, D))
+    pos = [10, 20, 30, 39]
+    akw = dict(window=8, ratio=r, sinks=rng.standard_normal(3), scale=D ** -0.5, store="f32")
+    o32 = O.csa_attention(q, kv, r64, None, pos, **akw)
+    o64 = O.csa_attention(q, kv, r64, None, pos, work=F64, **akw)
+    assert (np.abs(o32 - o64).max(-1) / np.abs(o64).max(-1)).max() <= 1e-5
 
 
 def pin_attention_bruteforce_layer():

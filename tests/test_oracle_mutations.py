@@ -2,6 +2,8 @@
 at least one pin fails.  This is what makes the pins worth trusting: each mistake below is
 one a transcription of the pages could plausibly make.
 """
+import inspect
+
 import numpy as np
 import pytest
 
@@ -132,6 +134,36 @@ def _groups_reversed(o, wo_a):                 # group g takes the weight of gro
     return _orig["grouped_out_proj"](o, np.asarray(wo_a)[::-1])
 
 
+def _planted(name, old, new):
+    """The oracle function ``name`` compiled from its own source with one text substitution
+    (the text must be there, so a planted mistake cannot silently stop applying)."""
+    src = inspect.getsource(_orig[name])
+    assert old in src, (name, old)
+    ns = dict(vars(C))
+    exec(compile(src.replace(old, new), f"<planted {name}>", "exec"), ns)
+    return ns[name]
+
+
+def _token0_off_by_one(a, g, ape, gamma, inv_freq, **kw):
+    # a lane handed over from token t0 > 0 read one token early: entry i taken as token t0 + i - 1
+    if kw.get("token0", 0):
+        a, g = np.asarray(a), np.asarray(g)
+        a, g = np.concatenate([a[:1], a[:-1]]), np.concatenate([g[:1], g[:-1]])
+    return _orig["compressor_rows"](a, g, ape, gamma, inv_freq, **kw)
+
+
+def _kv_offset_off_by_one(q, kv, rows, sel, positions, **kw):
+    # kv handed over from token lo > 0 read one token late: entry i taken as token lo + i + 1
+    if kw.get("kv_offset", 0):
+        kv = np.asarray(kv)
+        kv = np.concatenate([kv[1:], kv[-1:]])
+    return _orig["csa_attention"](q, kv, rows, sel, positions, **kw)
+
+
+_round_after_the_norm = _planted("compressor_rows", "y = round_store(pooled, store)",
+                                 "y = np.asarray(pooled, dtype=np.float64)")
+
+
 MUTATIONS = {
     "visibility (j+1)r <= p": ("visible_rows", _visibility_off_by_one),
     "window one token longer": ("csa_attention", _window_one_longer),
@@ -152,6 +184,9 @@ MUTATIONS = {
     "inverse rotation turns forward": ("rope_heads", _inverse_turns_forward),
     "output groups interleaved": ("grouped_out_proj", _groups_interleaved),
     "output groups reversed": ("grouped_out_proj", _groups_reversed),
+    "lane slice read one token early (token0 - 1)": ("compressor_rows", _token0_off_by_one),
+    "kv slice read one token late (kv_offset + 1)": ("csa_attention", _kv_offset_off_by_one),
+    "pooled row rounded after the norm, not before": ("compressor_rows", _round_after_the_norm),
 }
 
 
