@@ -171,3 +171,56 @@ def topk_band_ok(sel_gpu: np.ndarray, sel_ref: np.ndarray, scores: np.ndarray, p
             n_bad += 1
             bad.append((p, sorted(diff)[:8]))
     return n_exact, n_band, n_bad, bad
+
+
+def check_against_oracle(spec: LayerSpec, tok: dict, par: dict, got: dict, b: int, positions,
+                         end_to_end: bool = False, label: str = ""):
+    """Compare sequence ``b`` of a GPU run (``got``: rows, rows_i [B, n, .], sel [B, T, k],
+    out [B, T, H, D], cpu tensors) with the oracle run on the inputs ``tok`` / ``par`` (numpy,
+    indexed by absolute position) at the query ``positions``.
+
+    Stage-isolated (default): the rows are compared with the oracle's, then the oracle scores
+    and selects over the GPU's index rows and attends over the GPU's rows with the GPU's
+    selection, so every query's attention is comparable.  End to end: the oracle runs on its
+    own rows and selection throughout; queries whose selection differs from the GPU's (only
+    inside the top-k band) are left out of the attention comparison."""
+    store = store_of(spec)
+    rows = sel = None
+    report = {}
+    P = np.asarray(positions)
+    if spec.has_rows:
+        rows_ref = oracle_rows(spec, tok, par)
+        rows = f64(got["rows"][b])
+        report["rows_maxabs"] = assert_rows_match(rows, rows_ref, store, "attention-lane rows",
+                                                  spec.rope_dim)
+        if end_to_end:
+            rows = rows_ref
+    agree = np.ones(len(positions), dtype=bool)
+    if spec.has_indexer:
+        rows_i_ref = oracle_rows(spec, tok, par, index_lane=True)
+        rows_i = f64(got["rows_i"][b])
+        report["rows_i_maxabs"] = assert_rows_match(rows_i, rows_i_ref, store, "indexer-lane rows",
+                                                    spec.rope_dim)
+        if end_to_end:
+            rows_i = rows_i_ref
+        scores = oracle_scores(spec, tok, rows_i, positions)
+        sel_ref = oracle_select(spec, scores, positions)
+        sel_gpu = got["sel"][b].numpy()[P]
+        ne, nb, nbad, bad = topk_band_ok(sel_gpu, sel_ref, scores, positions, spec)
+        report.update(topk_exact=ne, topk_band=nb)
+        assert nbad == 0, f"top-k mismatches outside the band: {bad[:5]}"
+        if end_to_end:
+            sel = sel_ref
+            agree = np.array([np.array_equal(sel_gpu[i], sel_ref[i]) for i in range(len(positions))])
+        else:
+            sel = sel_gpu
+    ref = oracle_attention(spec, tok, par, rows, sel, positions)
+    gpu = f64(got["out"][b])[P]
+    mr = max_rel_rows(gpu, ref)[agree]
+    bar = 1e-5 if store == "f32" else 2e-2
+    report["attn_maxrel"] = float(mr.max()) if mr.size else 0.0
+    report["attn_compared"] = f"{int(agree.sum())}/{len(positions)}"
+    assert mr.size == 0 or mr.max() <= bar, f"attention max-rel {mr.max():.3g} > {bar}"
+    print(f"  {label}seq {b}: {report}", flush=True)
+    return report
+

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import synth.csa as SC
 from sparse_attention_dsv4_amd.layer import LayerSpec
 from tests import gpu_harness as G
 
@@ -28,44 +29,10 @@ def _need_gpu(request):
 
 
 def _check_layer(spec, res, b, positions, seed, end_to_end=False):
-    """Stage-isolated comparison of sequence b at the given query positions."""
-    T = res["T"]
-    tok, par = G.oracle_inputs(spec, seed, b, T)
-    store = G.store_of(spec)
-    rows = sel = None
-    report = {}
-    if spec.has_rows:
-        rows_ref = G.oracle_rows(spec, tok, par)
-        rows = G.f64(res["rows"][b])
-        report["rows_maxabs"] = G.assert_rows_match(rows, rows_ref, store, "attention-lane rows",
-                                                    spec.rope_dim)
-        if end_to_end:
-            rows = rows_ref
-    if spec.has_indexer:
-        rows_i_ref = G.oracle_rows(spec, tok, par, index_lane=True)
-        rows_i = G.f64(res["rows_i"][b])
-        report["rows_i_maxabs"] = G.assert_rows_match(rows_i, rows_i_ref, store, "indexer-lane rows",
-                                                      spec.rope_dim)
-        if end_to_end:
-            rows_i = rows_i_ref
-        scores = G.oracle_scores(spec, tok, rows_i, positions)
-        sel_ref = G.oracle_select(spec, scores, positions)
-        sel_gpu = res["sel"][b].numpy()[np.asarray(positions)]
-        ne, nb, nbad, bad = G.topk_band_ok(sel_gpu, sel_ref, scores, positions, spec)
-        report.update(topk_exact=ne, topk_band=nb)
-        assert nbad == 0, f"top-k mismatches outside the band: {bad[:5]}"
-        sel = sel_gpu if not end_to_end else sel_ref
-        agree = np.array([np.array_equal(sel_gpu[i], sel_ref[i]) for i in range(len(positions))])
-    else:
-        agree = np.ones(len(positions), dtype=bool)
-    ref = G.oracle_attention(spec, tok, par, rows, sel, positions)
-    gpu = G.f64(res["out"][b])[np.asarray(positions)]
-    mr = G.max_rel_rows(gpu, ref)[agree]
-    bar = 1e-5 if store == "f32" else 2e-2
-    report["attn_maxrel"] = float(mr.max()) if mr.size else 0.0
-    assert mr.size == 0 or mr.max() <= bar, f"attention max-rel {mr.max():.3g} > {bar}"
-    print(f"  seq {b}: {report}", flush=True)
-    return report
+    """Sequence b at the given query positions against the oracle on the same seeded inputs
+    (stage-isolated unless ``end_to_end``; see gpu_harness.check_against_oracle)."""
+    tok, par = G.oracle_inputs(spec, seed, b, res["T"])
+    return G.check_against_oracle(spec, tok, par, res, b, positions, end_to_end=end_to_end)
 
 
 def test_tiny_fp32_prefill_end_to_end():
@@ -95,6 +62,71 @@ def test_tiny_fp32_config_prefill_256_then_64_decode():
     every position against the oracle from the raw inputs."""
     res = G.run_gpu(TINY, 0, 1, [256], 64)
     _check_layer(TINY, res, 0, list(range(320)), 0, end_to_end=True)
+
+
+def test_tiny_config_literal_shapes():
+    """The tiny fp32 configuration with its stated shapes and recipe: token states
+    x ~ N(0, 1) [320, 64] and weights N(0, 1)/sqrt(64) projecting q (64 -> 4 x 64) and kv
+    (64 -> 64); the overlapping compressor (window 8, stride 4) whose kv and gate lanes are each
+    ONE 64 -> 64 projection feeding both halves of the 128-wide lane, with its (8, 64) APE laid
+    out as ape[s, h*64 + c] = APE8[h*4 + s, c] (the previous window's 4 slots take APE8 rows
+    0..3, the row's own window rows 4..7); the indexer's qi (64 -> 2 x 32), head weights
+    (64 -> 2) and lanes (64 -> 32 into both halves) with an (8, 32) APE; q, kv and qi turned by
+    RoPE at their positions inside the library (rope=True).  Prefill of 256 tokens, then 64
+    decode steps; every position against the oracle end to end (the oracle rotates q, kv and
+    qi itself)."""
+    import synth
+    T0, ND = 256, 64
+    T = T0 + ND
+
+    def nrm(shape, name, scale=1.0):
+        return synth.normal(shape, seed=0, stream=f"tiny.{name}", scale=scale, dtype=torch.float64)
+
+    x = nrm((T, 64), "x")
+
+    def proj(out, name):
+        return (x @ nrm((out, 64), name, 64 ** -0.5).T).float()
+
+    def both_halves(t):
+        return torch.cat([t, t], dim=-1).contiguous()
+
+    def ape_of(a8):                      # [8, D] -> [4, 2D]
+        return torch.cat([a8[0:4], a8[4:8]], dim=1).float().contiguous()
+
+    tok = {"q": proj(256, "wq").view(T, 4, 64), "kv": proj(64, "wkv"),
+           "a": both_halves(proj(64, "wa")), "g": both_halves(proj(64, "wg")),
+           "qi": proj(64, "wqi").view(T, 2, 32), "w": proj(2, "ww"),
+           "ai": both_halves(proj(32, "wai")), "gi": both_halves(proj(32, "wgi"))}
+    params = {"ape": ape_of(nrm((8, 64), "ape8")), "ape_i": ape_of(nrm((8, 32), "ape8_i")),
+              "norm_w": nrm((64,), "gamma").float(), "norm_w_i": nrm((32,), "gamma_i").float(),
+              "sinks": nrm((4,), "sinks").float(), "inv_freq": SC.inv_freq(16)}
+    from sparse_attention_dsv4_amd.layer import CsaLayer
+    layer = CsaLayer(TINY, 1, T, {k: v.cuda() for k, v in params.items()}, device="cuda",
+                     max_chunk=T0)
+    out = torch.empty(1, T, 4, 64)
+    sel = torch.empty(1, T, TINY.topk, dtype=torch.int32)
+    s_buf = torch.empty(1, T0, TINY.topk, dtype=torch.int32, device="cuda")
+    pre = {k: v[:T0][None].cuda().contiguous() for k, v in tok.items()}
+    out[:, :T0] = layer.prefill(pre, sel_out=s_buf, rope=True).cpu()
+    sel[:, :T0] = s_buf.cpu()
+    for t in range(T0, T):
+        s1 = torch.empty(1, 1, TINY.topk, dtype=torch.int32, device="cuda")
+        step = {k: v[t:t + 1].cuda().contiguous() for k, v in tok.items()}
+        out[:, t] = layer.decode(step, sel_out=s1, rope=True).cpu()
+        sel[:, t] = s1[:, 0].cpu()
+    torch.cuda.synchronize()
+    got = {"out": out, "sel": sel, "rows": layer.rows[:, :T // 4].cpu(),
+           "rows_i": layer.rows_i[:, :T // 4].cpu()}
+    pos = np.arange(T)
+    inv = params["inv_freq"].numpy()
+    otok = {k: G.f64(v) for k, v in tok.items()}
+    for k, h in (("q", 4), ("kv", None), ("qi", 2)):
+        x3 = otok[k] if h else otok[k][:, None]
+        r = oracle.round_store(oracle.rope_heads(x3, pos, inv), "f32")
+        otok[k] = r if h else r[:, 0]
+    par = {k: G.f64(v) for k, v in params.items()}
+    G.check_against_oracle(TINY, otok, par, got, 0, list(range(T)), end_to_end=True)
+    G.check_against_oracle(TINY, otok, par, got, 0, list(range(T)))
 
 
 def test_tiny_fp32_dense_to_sparse_crossing():

@@ -1,13 +1,16 @@
 """Exact trim for speculative decode on the GPU: decode draft tokens, take some back with
-CsaLayer.trim, decode other tokens -- every output, selection and compressed row must equal,
-bit for bit, those of a layer that only ever saw the committed tokens (MTPLX PR #216
-speculative-decode comment: rollback exactness across a ratio-4 emission boundary, the
-ratio-128 boundary and the indexer's dense-to-sparse threshold).  Needs a gfx950 GPU."""
+CsaLayer.trim, decode other tokens.  Every output, selection and compressed row must equal,
+bit for bit, those of a layer that only ever saw the committed tokens, and must match the
+oracle run on the committed token stream (MTPLX PR #216, speculative-decode comment: the
+rewind is exact across a ratio-4 emission, the ratio-128 boundary and the indexer's
+dense-to-sparse threshold).  Needs a gfx950 GPU."""
+import numpy as np
 import pytest
 import torch
 
 import synth.csa as SC
 from sparse_attention_dsv4_amd.layer import CsaLayer, LayerSpec
+from tests import gpu_harness as G
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +98,30 @@ def test_trim_equals_never_decoded(name):
         if hasattr(ref, lane):
             a, b = getattr(draft, lane)[:, :n], getattr(ref, lane)[:, :n]
             assert torch.equal(_bits(a), _bits(b)), f"{lane} differ"
+    # the trimmed layer against the oracle on the committed stream: prefix tokens, then the
+    # kept draft token at every decoded position
+    T = draft.lengths[0]
+    positions = [p for _, p in committed]
+    got = {"out": torch.zeros(B, T, spec.heads, spec.dim, dtype=spec.dtype),
+           "sel": torch.full((B, T, max(1, spec.topk)), -2, dtype=torch.int32)}
+    for p in positions:
+        got["out"][:, p] = outs[p][0].cpu()
+        if spec.has_indexer:
+            got["sel"][:, p] = outs[p][1][:, 0].cpu()
+    if spec.has_rows:
+        got["rows"] = draft.rows[:, :n].cpu()
+        if spec.has_indexer:
+            got["rows_i"] = draft.rows_i[:, :n].cpu()
+    par = {k: G.f64(v) for k, v in SC.layer_params(spec, seed).items()}
+    for b in range(B):
+        parts = [SC.token_inputs(spec, seed, b, 0, prefix, device="cuda")]
+        parts += [SC.token_inputs(spec, seed + 100 * s_, b, p, p + 1, device="cuda")
+                  for s_, p in committed]
+        tok = {k: np.concatenate([G.f64(x[k]) for x in parts]) for k in parts[0]}
+        G.check_against_oracle(spec, tok, par, got, b, positions, label="trimmed ")
+        if spec.dtype == torch.float32:
+            G.check_against_oracle(spec, tok, par, got, b, positions, end_to_end=True,
+                                   label="trimmed, end to end ")
 
 
 def test_trim_beyond_room_raises_on_a_live_layer():
