@@ -165,6 +165,24 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
                     const int64_t* pos0, int32_t batch, int64_t s, int32_t* sel, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* dsv4_index_topk without the workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The scratch is a fixed array inside the library, one per GPU, of
+ * dsv4_index_topk_noalloc_scratch_bytes() bytes (16 MiB), held by each GPU the library runs
+ * on until the process ends; its address is looked up on the first call on a device.  The
+ * call allocates nothing: no hipMalloc, hipFree or allocating library routine.  Same
+ * arguments, results and errors as dsv4_index_topk, and EWORKSPACE, before any launch, when
+ * dsv4_index_workspace_bytes() of the call exceeds the fixed size (about four million
+ * (query, row) score keys: e.g. decode of 64 sequences over 65,536 rows fits, a 2048-query
+ * prefill chunk over 16K rows does not).  Every call on one GPU uses that GPU's one array,
+ * which keeps the last call's contents (the call writes every entry it reads): calls that
+ * overlap on one GPU, on any streams, race and must not be issued. */
+size_t dsv4_index_topk_noalloc_scratch_bytes(void);
+int dsv4_index_topk_noalloc(const dsv4_index_cfg* cfg, const void* qi, const float* w,
+                            const void* idx_rows, int64_t row_cap, const int64_t* n_rows,
+                            const int64_t* pos0, int32_t batch, int64_t s, int32_t* sel,
+                            void* stream);
+
 /* Decode attention: one query per sequence at position pos[b].
  *   q        [batch, H, D]     query heads
  *   kv_new   [batch, D]        latent of token pos[b]; written into win_ring slot pos % W

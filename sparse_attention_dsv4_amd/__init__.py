@@ -18,7 +18,8 @@ __all__ = [
     "Dsv4Error", "CompCfg", "IndexCfg", "AttnCfg", "lib", "lib_path",
     "dsv4_version", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
-    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
+    "dsv4_index_topk", "dsv4_index_topk_noalloc", "dsv4_index_topk_noalloc_scratch_bytes",
+    "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
     "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "RopeCfg", "GprojCfg",
     "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
     "EXPORTED_SYMBOLS",
@@ -31,7 +32,8 @@ lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4.so"
 EXPORTED_SYMBOLS = (
     "dsv4_version", "dsv4_last_error", "dsv4_comp_state_bytes", "dsv4_index_workspace_bytes",
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
-    "dsv4_index_topk", "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
+    "dsv4_index_topk", "dsv4_index_topk_noalloc", "dsv4_index_topk_noalloc_scratch_bytes",
+    "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
     "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "dsv4_trace_enable",
     "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernel_name",
 )
@@ -165,7 +167,8 @@ def lib():
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_trace_kernel_name.restype = ctypes.c_char_p
         L.dsv4_trace_kernel_name.argtypes = [ctypes.c_int32]
-        for n in ("dsv4_comp_state_bytes", "dsv4_index_workspace_bytes", "dsv4_attn_workspace_bytes"):
+        for n in ("dsv4_comp_state_bytes", "dsv4_index_workspace_bytes", "dsv4_attn_workspace_bytes",
+                  "dsv4_index_topk_noalloc_scratch_bytes"):
             getattr(L, n).restype = ctypes.c_size_t
         L.dsv4_comp_state_bytes.argtypes = [ctypes.POINTER(_CompCfg), ctypes.c_int32]
         L.dsv4_index_workspace_bytes.argtypes = [ctypes.POINTER(_IndexCfg), ctypes.c_int32,
@@ -177,6 +180,8 @@ def lib():
                                          _I64P, _P, _P, _P, _P, ctypes.c_int64, _P]
         L.dsv4_index_topk.argtypes = [ctypes.POINTER(_IndexCfg), _P, _P, _P, ctypes.c_int64, _I64P,
                                       _I64P, ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]
+        L.dsv4_index_topk_noalloc.argtypes = [ctypes.POINTER(_IndexCfg), _P, _P, _P, ctypes.c_int64,
+                                              _I64P, _I64P, ctypes.c_int32, ctypes.c_int64, _P, _P]
         L.dsv4_csa_attn_decode.argtypes = [ctypes.POINTER(_AttnCfg), _P, _P, _P, _P, ctypes.c_int64,
                                            _P, _I64P, _I64P, _P, _P, ctypes.c_int32, _P,
                                            ctypes.c_size_t, _P]
@@ -309,6 +314,27 @@ def dsv4_index_topk(cfg: IndexCfg, qi, w, idx_rows, n_rows, pos0, sel, ws, strea
         ctypes.byref(c), _ptr(qi), _ptr(w), _ptr(idx_rows), idx_rows.shape[1],
         _host_i64(n_rows, B, "n_rows"), _host_i64(pos0, B, "pos0"), B, S, _ptr(sel), _ptr(ws),
         ws.numel(), _stream(stream)))
+
+
+def dsv4_index_topk_noalloc_scratch_bytes() -> int:
+    return int(lib().dsv4_index_topk_noalloc_scratch_bytes())
+
+
+def dsv4_index_topk_noalloc(cfg: IndexCfg, qi, w, idx_rows, n_rows, pos0, sel, stream=None):
+    """dsv4_index_topk with the library's fixed per-GPU scratch instead of a workspace (no
+    allocation; calls that overlap on one GPU race)."""
+    B, S = qi.shape[0], qi.shape[1]
+    _need(qi, (B, S, cfg.heads, cfg.dim), cfg.dtype, "qi")
+    _need(w, (B, S, cfg.heads), torch.float32, "w")
+    if idx_rows.dim() != 3:
+        raise ValueError("idx_rows must be [B, cap, di]")
+    _need(idx_rows, (B, idx_rows.shape[1], cfg.dim), cfg.dtype, "idx_rows")
+    _need(sel, (B, S, cfg.topk), torch.int32, "sel")
+    c = cfg.c()
+    _check(lib().dsv4_index_topk_noalloc(
+        ctypes.byref(c), _ptr(qi), _ptr(w), _ptr(idx_rows), idx_rows.shape[1],
+        _host_i64(n_rows, B, "n_rows"), _host_i64(pos0, B, "pos0"), B, S, _ptr(sel),
+        _stream(stream)))
 
 
 def _attn_common_checks(cfg: AttnCfg, rows, sel, n_rows, B, sel_shape):

@@ -205,10 +205,15 @@ int dsv4_compress_step(const dsv4_comp_cfg* cfg, void* state, const void* kv_lan
                                  norm_w, inv_freq, rows, row_cap, stream);
 }
 
-int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
+}  // extern "C"
+
+namespace {
+
+// The checks and the launch of dsv4_index_topk; `ws_what` names the workspace in errors.
+int index_topk_impl(const dsv4_index_cfg* cfg, const void* qi, const float* w,
                     const void* idx_rows, int64_t row_cap, const int64_t* n_rows,
                     const int64_t* pos0, int32_t batch, int64_t s, int32_t* sel, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, void* stream, const char* ws_what) {
     int st = check_index_cfg(cfg);
     if (st) return st;
     if (batch < 0) return fail(DSV4_EINVAL, "batch %d < 0", batch);
@@ -231,7 +236,8 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
     }
     const size_t need_ws = dsv4::index_workspace_bytes(cfg->heads, cfg->dim, cfg->topk, batch, s, n_max);
     if (!ws || ws_bytes < need_ws)
-        return fail(DSV4_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need_ws);
+        return fail(DSV4_EWORKSPACE, "%s of %zu bytes, this call needs %zu", ws_what, ws_bytes,
+                    need_ws);
     if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
         return fail(DSV4_EINVAL, "workspace must be 16-byte aligned");
     dsv4::IndexJob j;
@@ -243,6 +249,60 @@ int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
     j.batch = batch; j.n_rows = n_rows; j.pos0 = pos0; j.sel = sel;
     j.keys = static_cast<uint32_t*>(ws);
     return hip_status(dsv4::launch_index_topk(j, static_cast<hipStream_t>(stream)), "index_topk");
+}
+
+// ------------------------------------------------------------------ allocation-free top-k
+// The scratch of dsv4_index_topk_noalloc: one array per GPU, in the library's device code
+// object, alive until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol; its device address (per device) comes from hipGetSymbolAddress.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DSV4_EUNSUPPORTED, "device %d above %d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(DSV4_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsv4_index_topk(const dsv4_index_cfg* cfg, const void* qi, const float* w,
+                    const void* idx_rows, int64_t row_cap, const int64_t* n_rows,
+                    const int64_t* pos0, int32_t batch, int64_t s, int32_t* sel, void* ws,
+                    size_t ws_bytes, void* stream) {
+    return index_topk_impl(cfg, qi, w, idx_rows, row_cap, n_rows, pos0, batch, s, sel, ws,
+                           ws_bytes, stream, "workspace");
+}
+
+size_t dsv4_index_topk_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+int dsv4_index_topk_noalloc(const dsv4_index_cfg* cfg, const void* qi, const float* w,
+                            const void* idx_rows, int64_t row_cap, const int64_t* n_rows,
+                            const int64_t* pos0, int32_t batch, int64_t s, int32_t* sel,
+                            void* stream) {
+    void* ws = nullptr;
+    int st = scratch_address(&ws);
+    if (st) return st;
+    return index_topk_impl(cfg, qi, w, idx_rows, row_cap, n_rows, pos0, batch, s, sel, ws,
+                           kNoallocScratchBytes, stream, "the library's fixed scratch");
 }
 
 static int attn_common(const dsv4_attn_cfg* cfg, const void* q, const void* kv_new,
