@@ -33,7 +33,6 @@ namespace {
 
 constexpr int kScoreRows = 64;      // rows per workgroup of the scoring kernel
 constexpr int kScoreThreads = 256;
-constexpr int kSelThreads = 256;
 
 template <typename T>
 struct ScoreArgs {
@@ -96,25 +95,11 @@ index_score_kernel(ScoreArgs<T> a, SeqInts pos0, SeqInts n_rows) {
 
 
 // ------------------------------------------------------------------ mfma scoring
-// Queries per wave in prefill scoring: one (226 VGPRs, two waves per SIMD) hides LDS and
-// epilogue latency better than two (more operand reuse, but one wave per SIMD).
-#ifndef DSV4_IDX_QPW
-#define DSV4_IDX_QPW 1
-#endif
-constexpr int kIdxQpw = DSV4_IDX_QPW;
-#ifndef DSV4_IDX_WAVES
-#define DSV4_IDX_WAVES 8
-#endif
-constexpr int kIdxWaves = DSV4_IDX_WAVES;   // waves per prefill workgroup (one query each)
-#ifndef DSV4_IDX_DEC_WGS
-#define DSV4_IDX_DEC_WGS 256
-#endif
-constexpr int64_t kIdxDecodeWgs = DSV4_IDX_DEC_WGS;   // decode scoring workgroups (all queries)
-
-#ifndef DSV4_IDX_STAGES
-#define DSV4_IDX_STAGES 4
-#endif
-constexpr int kIdxStages = DSV4_IDX_STAGES;   // LDS tile buffers of the scoring pipeline
+// Prefill scoring: one query per wave (226 VGPRs, two waves per SIMD), eight waves per
+// workgroup; tiles of the lane staged through a ring of four LDS buffers.  (Two queries per
+// wave, with more operand reuse but one wave per SIMD, measured slower.)
+constexpr int kIdxWaves = 8;
+constexpr int kIdxStages = 4;
 constexpr int IH = 64;                 // indexer heads
 constexpr int ID = 128;                // indexer dims
 constexpr int IRT = 128;               // rows per LDS tile
@@ -134,6 +119,12 @@ struct IdxMfmaArgs {
     float scale;
     int rows_per_block;
     int queries_per_group;     // row-stationary kernel: queries one workgroup scores
+    // fused decode scoring: each workgroup's m best rows, in row order, and the largest key
+    // of the rest ([queries][n_groups][m] keys and rows, [queries][n_groups] cutoffs)
+    uint32_t* cand_key;
+    int32_t* cand_row;
+    uint32_t* cutoff;
+    int n_groups, m;
 };
 
 // Direct global -> LDS copy (16 bytes per lane to lds_base + 16 lane), as inline asm so the
@@ -186,20 +177,18 @@ __device__ __forceinline__ void idx_load_tile(const IdxMfmaArgs& a, int b, int64
     }
 }
 
-// QPW queries per wave (prefill: the workgroup covers 4 * QPW) or, for QPW == 0, one query
-// shared by the whole workgroup (decode: each wave takes one 32-row block of every tile).
-template <int QPW, int WAVES, int NSTAGE>
+// Prefill scoring over a block of rows: wave w scores query 8 * blockIdx.y + w against
+// every 128-row tile of the block, the tiles staged in LDS and shared by the 8 queries.
+template <int WAVES, int NSTAGE>
 __global__ void __launch_bounds__(64 * WAVES)
 index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __shared__ __attribute__((aligned(16))) unsigned char kt[NSTAGE][IRT * IROWB];
-    constexpr bool SHARED_Q = QPW == 0;
-    constexpr int NQ = SHARED_Q ? 1 : QPW;
     const int b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const int64_t pos0 = pos0v.v[b];
-    const int64_t qbase = SHARED_Q ? int64_t(blockIdx.y) : int64_t(blockIdx.y) * WAVES * NQ + w * NQ;
-    int64_t s_last = SHARED_Q ? int64_t(blockIdx.y) : int64_t(blockIdx.y) * WAVES * NQ + WAVES * NQ - 1;
+    const int64_t qs = int64_t(blockIdx.y) * WAVES + w;
+    int64_t s_last = int64_t(blockIdx.y) * WAVES + WAVES - 1;
     if (s_last > a.S - 1) s_last = a.S - 1;
     int64_t nv_max = (pos0 + s_last + 1) / a.r;
     if (nv_max > n_rows.v[b]) nv_max = n_rows.v[b];
@@ -207,27 +196,24 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     if (j_begin >= nv_max) return;
     const int64_t j_end = j_begin + a.rows_per_block < nv_max ? j_begin + a.rows_per_block : nv_max;
 
-    bf16x8 qa[NQ][2][ID / 16];
-    float wsc[NQ][2][16];
-    int64_t nv[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int64_t s = qbase + q;
-        const bool qvalid = s < a.S;
-        nv[q] = 0;
-        if (qvalid) {
-            nv[q] = (pos0 + s + 1) / a.r;
-            if (nv[q] > n_rows.v[b]) nv[q] = n_rows.v[b];
-        }
-        const int64_t sq = qvalid ? s : 0;
+    bf16x8 qa[2][ID / 16];
+    float wsc[2][16];
+    const bool qvalid = qs < a.S;
+    int64_t nv = 0;
+    if (qvalid) {
+        nv = (pos0 + qs + 1) / a.r;
+        if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    }
+    {
+        const int64_t sq = qvalid ? qs : 0;
         const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(sq)) * IH + l32) * ID + 8 * hi;
         const float* wr = a.w + (size_t(b) * a.S + size_t(sq)) * IH;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
-            for (int ks = 0; ks < ID / 16; ++ks) qa[q][m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
+            for (int ks = 0; ks < ID / 16; ++ks) qa[m][ks] = load_bf16x8(qrow + m * 32 * ID + ks * 16);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) wsc[q][m][i] = qvalid ? wr[32 * m + c_row(i, lane)] * a.scale : 0.f;
+            for (int i = 0; i < 16; ++i) wsc[m][i] = qvalid ? wr[32 * m + c_row(i, lane)] * a.scale : 0.f;
         }
     }
 
@@ -250,60 +236,46 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         if (t + NSTAGE - 1 < ntiles)
             idx_load_tile<WAVES>(a, b, j0 + int64_t(NSTAGE - 1) * IRT, j_end, kt[(t + NSTAGE - 1) % NSTAGE]);
         const unsigned char* buf = kt[t % NSTAGE];
-        // 32-row blocks of the tile: prefill waves take all 4 (their own queries), decode waves
-        // one each.  The MFMAs of block u+1 are issued before the epilogue of block u, so the
-        // matrix pipe stays busy while the VALU reduces the previous block.
-        constexpr int NB = SHARED_Q ? 1 : 4;
-        floatx16 c[2][NQ][2];
-        float score[NB][NQ];
+        // the tile's four 32-row blocks; the MFMAs of block u+1 are issued before the epilogue
+        // of block u, so the matrix pipe stays busy while the VALU reduces the previous block
+        floatx16 c[2][2];
+        float score[4];
 #pragma unroll
-        for (int u = 0; u <= NB; ++u) {
-            if (u < NB) {
-                const int nt = SHARED_Q ? w : u;
-                const int row = 32 * nt + l32;
+        for (int u = 0; u <= 4; ++u) {
+            if (u < 4) {
+                const int row = 32 * u + l32;
                 const unsigned char* kr = buf + row * IROWB;
 #pragma unroll
-                for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        c[u & 1][q][0][i] = 0.f;
-                        c[u & 1][q][1][i] = 0.f;
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    c[u & 1][0][i] = 0.f;
+                    c[u & 1][1][i] = 0.f;
+                }
 #pragma unroll
                 for (int ks = 0; ks < ID / 16; ++ks) {
                     const bf16x8 kb = load_bf16x8(kr + swz(row, 2 * ks + hi) * 16);
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) {
-                        c[u & 1][q][0] = mfma32x32x16(qa[q][0][ks], kb, c[u & 1][q][0]);
-                        c[u & 1][q][1] = mfma32x32x16(qa[q][1][ks], kb, c[u & 1][q][1]);
-                    }
+                    c[u & 1][0] = mfma32x32x16(qa[0][ks], kb, c[u & 1][0]);
+                    c[u & 1][1] = mfma32x32x16(qa[1][ks], kb, c[u & 1][1]);
                 }
             }
             if (u > 0) {
                 // weighted relu sum over the 64 heads of block u-1 (relu as an integer max of
                 // the bit pattern: exact, one instruction), kept until the tile's stores
                 const int v = u - 1;
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        s0 = fmaf(wsc[q][0][i], relu_bits(c[v & 1][q][0][i]), s0);
-                        s1 = fmaf(wsc[q][1][i], relu_bits(c[v & 1][q][1][i]), s1);
-                    }
-                    float sc = s0 + s1;
-                    score[v][q] = sc + __shfl_xor(sc, 32, 64);
+                for (int i = 0; i < 16; ++i) {
+                    s0 = fmaf(wsc[0][i], relu_bits(c[v & 1][0][i]), s0);
+                    s1 = fmaf(wsc[1][i], relu_bits(c[v & 1][1][i]), s1);
                 }
+                const float sc = s0 + s1;
+                score[v] = sc + __shfl_xor(sc, 32, 64);
             }
         }
 #pragma unroll
-        for (int v = 0; v < NB; ++v) {
-            const int nt = SHARED_Q ? w : v;
-            const int64_t jj = j0 + 32 * nt + l32;
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if (hi == 0 && jj < nv[q])
-                    a.keys[(size_t(b) * a.S + size_t(qbase + q)) * a.n_stride + size_t(jj)] = score_key(score[v][q]);
+        for (int v = 0; v < 4; ++v) {
+            const int64_t jj = j0 + 32 * v + l32;
+            if (hi == 0 && jj < nv)
+                a.keys[(size_t(b) * a.S + size_t(qs)) * a.n_stride + size_t(jj)] = score_key(score[v]);
         }
     }
 }
@@ -315,10 +287,6 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
 // (64 heads x 128 dims) and head weights come from global memory (L2); the two waves of a
 // SIMD hide each other's loads.
 constexpr int RSB = 512;                      // rows held by one workgroup (128 KB of LDS)
-#ifndef DSV4_IDX_RS
-#define DSV4_IDX_RS 1
-#endif
-constexpr bool kIdxRowStationary = DSV4_IDX_RS != 0;
 constexpr int64_t kIdxRsMinRows = 4096;       // below, too few row blocks to fill the chip
 
 struct IdxQ {
@@ -407,222 +375,12 @@ index_score_rs_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 }
 
-// Decode scoring (each query's rows read once, no sharing between queries): the workgroup
-// stages its query's 64 x 128 fragment in LDS once (16-byte chunks XOR-swizzled by head),
-// then every wave streams its own contiguous run of 32-row blocks straight into registers,
-// with the next block's loads in flight while the current one is scored.  MFMA k slots are
-// ordered so that a lane holds 64 contiguous bytes of its row per 64-dim half: k slot
-// 8 hi + e of MFMA ks = 4 d + j is dim 64 d + 32 hi + 8 j + e, in the query operand alike.
-constexpr int kStreamWaves = 8;
-#ifndef DSV4_IDX_STREAM
-#define DSV4_IDX_STREAM 1
-#endif
-constexpr bool kIdxStream = DSV4_IDX_STREAM != 0;
-
-__device__ __forceinline__ void idx_stream_block(const bf16* rows, int64_t blk, int64_t nv, uint4 (&kb)[8]) {
-    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
-    int64_t j = blk * 32 + l32;
-    j = j < nv ? j : nv - 1;                          // rows past the visible ones: scores not stored
-    const bf16* rp = rows + size_t(j) * ID + 32 * hi;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        kb[c] = *reinterpret_cast<const uint4*>(rp + 8 * c);
-        kb[4 + c] = *reinterpret_cast<const uint4*>(rp + 64 + 8 * c);
-    }
-}
-
-template <int WAVES>
-__global__ void __launch_bounds__(64 * WAVES)
-index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
-    const int b = blockIdx.z;
-    const int64_t s = blockIdx.y;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-    int64_t nv = (int64_t(pos0v.v[b]) + s + 1) / a.r;
-    if (nv > n_rows.v[b]) nv = n_rows.v[b];
-    const int64_t nbt = (nv + 31) / 32;                // 32-row blocks of this query
-    const int bpw = a.rows_per_block / (32 * WAVES);   // blocks per wave
-    if (int64_t(blockIdx.x) * WAVES * bpw >= nbt) return;   // whole workgroup
-    __shared__ __attribute__((aligned(16))) unsigned char qs[IH * IROWB];
-    {
-        const bf16* qg = a.qi + (size_t(b) * a.S + size_t(s)) * IH * ID;
-        for (int i = threadIdx.x; i < IH * 16; i += 64 * WAVES) {
-            const int h = i >> 4, c = i & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(qg + h * ID + c * 8);
-            store16(qs + h * IROWB + ((c ^ (h & 15)) * 16), v);
-        }
-    }
-    __syncthreads();
-    const int64_t blk0 = (int64_t(blockIdx.x) * WAVES + w) * bpw;
-    if (blk0 >= nbt) return;
-    const int nb = int(nbt - blk0 < bpw ? nbt - blk0 : bpw);
-    // query operand in the permuted k order, head weights
-    bf16x8 qa[2][8];
-    float wsc[2][16];
-    {
-        const bf16* qrow = a.qi + ((size_t(b) * a.S + size_t(s)) * IH + l32) * ID + 32 * hi;
-        const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int h = 32 * m + l32, c = 8 * (ks >> 2) + 4 * hi + (ks & 3);
-                const uint4 v = *reinterpret_cast<const uint4*>(qs + h * IROWB + ((c ^ (h & 15)) * 16));
-                __builtin_memcpy(&qa[m][ks], &v, 16);
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 v = *reinterpret_cast<const float4*>(wr + 32 * m + 8 * g + 4 * hi);
-                wsc[m][4 * g + 0] = v.x * a.scale;
-                wsc[m][4 * g + 1] = v.y * a.scale;
-                wsc[m][4 * g + 2] = v.z * a.scale;
-                wsc[m][4 * g + 3] = v.w * a.scale;
-            }
-        }
-    }
-    const bf16* rows = a.rows + size_t(b) * a.row_cap * ID;
-    uint32_t* keys = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
-    auto score = [&](const uint4 (&kb)[8], int64_t blk) {
-        floatx16 c0, c1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            c0[i] = 0.f;
-            c1[i] = 0.f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            bf16x8 kv;
-            __builtin_memcpy(&kv, &kb[ks], 16);
-            c0 = mfma32x32x16(qa[0][ks], kv, c0);
-            c1 = mfma32x32x16(qa[1][ks], kv, c1);
-        }
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0 = fmaf(wsc[0][i], relu_bits(c0[i]), s0);
-            s1 = fmaf(wsc[1][i], relu_bits(c1[i]), s1);
-        }
-        float sc = s0 + s1;
-        sc += __shfl_xor(sc, 32, 64);
-        const int64_t jj = blk * 32 + l32;
-        if (hi == 0 && jj < nv) keys[jj] = score_key(sc);
-    };
-    uint4 kb0[8], kb1[8];
-    idx_stream_block(rows, blk0, nv, kb0);
-    for (int u = 0; u < nb; u += 2) {
-        if (u + 1 < nb) idx_stream_block(rows, blk0 + u + 1, nv, kb1);
-        score(kb0, blk0 + u);
-        if (u + 1 < nb) {
-            if (u + 2 < nb) idx_stream_block(rows, blk0 + u + 2, nv, kb0);
-            score(kb1, blk0 + u + 1);
-        }
-    }
-}
-
 bool use_index_mfma(bool bf16_, int Hi, int di) { return bf16_ && Hi == IH && di == ID; }
 
-struct SelArgs {
-    int k, r;
-    int64_t S;
-    int64_t n_stride;
-    const uint32_t* keys;
-    int32_t* sel;
-    int32_t* cand;             // split selection: [B][S][n_chunks][k] candidate rows
-    uint32_t* cand_key;        // and their keys (0 for a -1 candidate)
-    int chunk, n_chunks;       // rows per chunk, chunks per query
-};
-
-// One workgroup selects for one query.
-__global__ void __launch_bounds__(kSelThreads)
-topk_select_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
-    __shared__ uint32_t hist[256];
-    __shared__ int32_t cnt_gt[kSelThreads], cnt_eq[kSelThreads];
-    __shared__ uint32_t sh_digit;
-    __shared__ int32_t sh_rem;
-    const int b = blockIdx.y;
-    const int64_t s = blockIdx.x;
-    const int64_t p = int64_t(pos0.v[b]) + s;
-    int64_t nv = (p + 1) / a.r;
-    if (nv > n_rows.v[b]) nv = n_rows.v[b];
-    int32_t* out = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
-    const int tid = threadIdx.x;
-    if (nv <= a.k) {                                  // dense regime: every visible row
-        for (int i = tid; i < a.k; i += blockDim.x) out[i] = i < nv ? i : -1;
-        return;
-    }
-    const uint32_t* key = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
-
-    // radix select of the k-th largest key
-    uint32_t prefix = 0, mask = 0;
-    int32_t rem = a.k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
-        __syncthreads();
-        for (int64_t j = tid; j < nv; j += blockDim.x) {
-            const uint32_t kk = key[j];
-            if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int32_t cum = 0;
-            int d = 255;
-            for (; d > 0; --d) {
-                if (cum + int32_t(hist[d]) >= rem) break;
-                cum += int32_t(hist[d]);
-            }
-            sh_digit = uint32_t(d);
-            sh_rem = rem - cum;
-        }
-        __syncthreads();
-        prefix |= sh_digit << shift;
-        mask |= 255u << shift;
-        rem = sh_rem;
-        __syncthreads();
-    }
-    const uint32_t thr = prefix;     // the k-th largest key; take `rem` rows equal to it
-
-    // compaction in row order: each thread owns a contiguous segment of rows
-    const int64_t seg = (nv + blockDim.x - 1) / blockDim.x;
-    const int64_t lo = int64_t(tid) * seg;
-    const int64_t hi = lo + seg < nv ? lo + seg : nv;
-    int32_t ngt = 0, neq = 0;
-    for (int64_t j = lo; j < hi; ++j) {
-        const uint32_t kk = key[j];
-        ngt += kk > thr;
-        neq += kk == thr;
-    }
-    cnt_gt[tid] = ngt;
-    cnt_eq[tid] = neq;
-    __syncthreads();
-    if (tid == 0) {                                   // exclusive scan over the segments
-        int32_t g = 0, e = 0;
-        for (int i = 0; i < int(blockDim.x); ++i) {
-            const int32_t tg = cnt_gt[i], te = cnt_eq[i];
-            cnt_gt[i] = g;
-            cnt_eq[i] = e;
-            g += tg;
-            e += te;
-        }
-    }
-    __syncthreads();
-    int32_t eq_rank = cnt_eq[tid];
-    int32_t o = cnt_gt[tid] + (eq_rank < rem ? eq_rank : rem);
-    for (int64_t j = lo; j < hi; ++j) {
-        const uint32_t kk = key[j];
-        if (kk > thr) {
-            out[o++] = int32_t(j);
-        } else if (kk == thr) {
-            if (eq_rank < rem) out[o++] = int32_t(j);
-            ++eq_rank;
-        }
-    }
-}
-
-
 // ------------------------------------------------------------------ exact top-k select
-// Radix select of the k-th largest key of the query's visible prefix, then compaction in
-// row order (helpers first: block-wide scan and bucket search over a histogram).
-constexpr int64_t kSelRegMaxRows = 1024 * 68;   // largest lane the register select holds
+// The k-th largest key T of a set by radix select, then compaction in row order: every key
+// > T, plus the lowest-placed keys == T until k are taken.  Row-order compaction makes the
+// output ascending without a sort; the lowest-placed ties are the lowest rows.
 
 // Exclusive prefix sum over a workgroup of NT threads; `tmp` holds NT / 64 ints.
 template <int NT>
@@ -670,25 +428,273 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int 
     __syncthreads();
 }
 
-// ------------------------------------------------------------------ select with keys in registers
-// For up to NT * KPT visible rows (NT threads).  Wave w owns the contiguous key range [w C, (w+1) C),
-// C = 64 KPT; within it lane l holds groups of 4 consecutive keys at w C + 256 i + 4 l, read
-// with one 16-byte load each (a wave instruction reads 1 KB contiguous).  The three radix
-// passes (11, 11, 10 bits) histogram the keys straight from registers; the compaction walks
-// each wave's groups in row order, with lane-mask bit counts giving every taken row its slot.
 // Number of set bits of a wave mask in the lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-// Split selection, for few queries over many rows: stage 1 (SEL_CHUNK) selects the k best of
-// each chunk of a.chunk rows into a candidate list, stage 2 (SEL_MERGE) the k best of those
-// candidates.  The order (key descending, then row ascending) is total, so a row among a
-// query's k best is among the k best of its chunk, and the candidate lists, chunk after chunk
-// and ascending within one, are in row order: the lower position wins a tie, and the rows
-// come out ascending.  Stage 1 stores each candidate's key beside its row; a candidate -1 (a
-// chunk with k rows or fewer) has key 0.
+// Keys held in registers by a workgroup of NT threads, KPT per thread: wave w owns the
+// contiguous positions [w C, (w+1) C), C = 64 KPT; within it lane l holds groups of 4
+// consecutive positions at w C + 256 i + 4 l (one 16-byte load each, a wave instruction
+// reading 1 KB contiguous).  Positions past the set hold key 0, below the key of every score
+// (score_key gives 0 only to the NaN with every bit set).  `ngv`: the wave's groups of
+// 4 x 64 positions holding any position of the set (the others are skipped and count as
+// keys 0, which changes no bin at or above the k-th key when at least k keys are above 0).
+struct RegSelect {
+    uint32_t thr;              // the k-th largest key
+    int rem;                   // keys == thr to take, lowest positions first
+};
+
+template <int KPT, int NT>
+__device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, int k,
+                                          uint32_t* hist, int* tmp, int* sh) {
+    constexpr int G = KPT / 4;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+    __syncthreads();
+    // pass 1: bits 31..21
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e) atomicAdd(&hist[key[e] >> 21], 1u);
+        }
+    __syncthreads();
+    find_bucket<NT>(hist, 2048, k, tmp, sh);
+    const uint32_t d1 = uint32_t(sh[0]);
+    int rem = sh[1];
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+    __syncthreads();
+    // pass 2: bits 20..10 of the keys in bucket d1
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e)
+                if ((key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
+        }
+    __syncthreads();
+    find_bucket<NT>(hist, 2048, rem, tmp, sh);
+    const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
+    rem = sh[1];
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+    __syncthreads();
+    // pass 3: bits 9..0 of the keys with prefix (d1, d2)
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        if (i < ngv) {
+#pragma unroll
+            for (int e = 4 * i; e < 4 * i + 4; ++e)
+                if ((key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
+        }
+    __syncthreads();
+    find_bucket<NT>(hist, 1024, rem, tmp, sh);
+    return RegSelect{(pre << 10) | uint32_t(sh[0]), sh[1]};
+}
+
+// Compaction in position order of the keys taken by `sel`.  Lane masks (the compare results
+// themselves) give every count: wave totals first, then each wave walks its groups of 4 x 64
+// positions, where position 4 l + j of a group is key j of lane l, so the positions before it
+// are those of lower lanes and its own lower j.  emit(slot, e, position) for every taken key
+// (e indexes key[]).  Returns, in every lane, the largest key NOT taken (0 if none; only
+// meaningful in the lanes of one wave before a block reduction).
+template <int KPT, int NT, class Emit>
+__device__ uint32_t reg_compact(const uint32_t (&key)[KPT], RegSelect sel, int (*wtot)[NT / 64],
+                                Emit emit) {
+    constexpr int G = KPT / 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wbase = w * 64 * KPT + 4 * lane;
+    const uint32_t thr = sel.thr;
+    const int rem = sel.rem;
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        ngt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
+        neq += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] == thr)));
+    }
+    if (lane == 0) {
+        wtot[0][w] = ngt;
+        wtot[1][w] = neq;
+    }
+    __syncthreads();
+    int o = 0, eqb = 0;                                // keys taken / ties seen before this wave
+    for (int v = 0; v < w; ++v) {
+        eqb += wtot[1][v];
+        o += wtot[0][v];
+    }
+    o += eqb < rem ? eqb : rem;
+    uint32_t rest = 0;                                 // largest key not taken
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        uint64_t em[4], any = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            em[j] = __builtin_amdgcn_ballot_w64(key[4 * i + j] == thr);
+            any |= em[j] | __builtin_amdgcn_ballot_w64(key[4 * i + j] > thr);
+        }
+        if (any == 0) {                                // nothing taken in this group
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rest = key[4 * i + j] > rest ? key[4 * i + j] : rest;
+            continue;
+        }
+        int eq_rank = eqb;                             // ties before this lane's first key
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eq_rank += lanes_below(em[j]);
+        bool take[4];
+        int slot = o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool eq = key[4 * i + j] == thr;
+            take[j] = key[4 * i + j] > thr || (eq && eq_rank < rem);
+            eq_rank += eq;
+            const uint64_t tm = __builtin_amdgcn_ballot_w64(take[j]);
+            slot += lanes_below(tm);
+            o += int(__popcll(tm));
+            eqb += int(__popcll(em[j]));
+            if (!take[j]) rest = key[4 * i + j] > rest ? key[4 * i + j] : rest;
+        }
+        const int j0 = wbase + 256 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (take[j]) emit(slot++, 4 * i + j, j0 + j);
+    }
+    return rest;
+}
+
+// Workgroup-wide max of a u32 over NT threads (`red` holds NT / 64 entries).
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t y = uint32_t(__shfl_xor(int(v), o, 64));
+        v = y > v ? y : v;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) m = red[i] > m ? red[i] : m;
+    return m;
+}
+
+struct SelArgs {
+    int k, r;
+    int64_t S;
+    int64_t n_stride;
+    const uint32_t* keys;
+    int32_t* sel;
+    int32_t* cand;             // split selection: [B][S][n_chunks][k] candidate rows
+    uint32_t* cand_key;        // and their keys (0 for a -1 candidate)
+    int chunk, n_chunks;       // rows per chunk, chunks per query
+    // fused decode selection: the scorer's per-workgroup candidates (see IdxMfmaArgs)
+    const uint32_t* f_key;
+    const int32_t* f_row;
+    const uint32_t* f_cutoff;
+    int f_groups, f_m, f_rows_per_group;
+};
+
+// The k best of nv keys in global memory for one query, by NT threads: four 8-bit radix
+// passes over the keys, then compaction in row order over contiguous per-thread segments.
+// `shm` holds at least 256 + 2 NT + 4 ints.  For any row count.
+template <int NT>
+__device__ void select_keys_mem(const uint32_t* key, int64_t nv, int k, int32_t* out, int* shm) {
+    uint32_t* hist = reinterpret_cast<uint32_t*>(shm);
+    int32_t* cnt_gt = shm + 256;
+    int32_t* cnt_eq = shm + 256 + NT;
+    int32_t* shs = shm + 256 + 2 * NT;
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    int32_t rem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (int64_t j = tid; j < nv; j += NT) {
+            const uint32_t kk = key[j];
+            if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int32_t cum = 0;
+            int d = 255;
+            for (; d > 0; --d) {
+                if (cum + int32_t(hist[d]) >= rem) break;
+                cum += int32_t(hist[d]);
+            }
+            shs[0] = d;
+            shs[1] = rem - cum;
+        }
+        __syncthreads();
+        prefix |= uint32_t(shs[0]) << shift;
+        mask |= 255u << shift;
+        rem = shs[1];
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;     // the k-th largest key; take `rem` rows equal to it
+    const int64_t seg = (nv + NT - 1) / NT;
+    const int64_t lo = int64_t(tid) * seg;
+    const int64_t hi = lo + seg < nv ? lo + seg : nv;
+    int32_t ngt = 0, neq = 0;
+    for (int64_t j = lo; j < hi; ++j) {
+        const uint32_t kk = key[j];
+        ngt += kk > thr;
+        neq += kk == thr;
+    }
+    cnt_gt[tid] = ngt;
+    cnt_eq[tid] = neq;
+    __syncthreads();
+    if (tid == 0) {                                   // exclusive scan over the segments
+        int32_t g = 0, e = 0;
+        for (int i = 0; i < NT; ++i) {
+            const int32_t tg = cnt_gt[i], te = cnt_eq[i];
+            cnt_gt[i] = g;
+            cnt_eq[i] = e;
+            g += tg;
+            e += te;
+        }
+    }
+    __syncthreads();
+    int32_t eq_rank = cnt_eq[tid];
+    int32_t o = cnt_gt[tid] + (eq_rank < rem ? eq_rank : rem);
+    for (int64_t j = lo; j < hi; ++j) {
+        const uint32_t kk = key[j];
+        if (kk > thr) {
+            out[o++] = int32_t(j);
+        } else if (kk == thr) {
+            if (eq_rank < rem) out[o++] = int32_t(j);
+            ++eq_rank;
+        }
+    }
+}
+
+// One workgroup selects for one query, keys in global memory (any row count).
+constexpr int kSelThreads = 256;
+__global__ void __launch_bounds__(kSelThreads)
+topk_select_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
+    __shared__ int shm[256 + 2 * kSelThreads + 4];
+    const int b = blockIdx.y;
+    const int64_t s = blockIdx.x;
+    const int64_t p = int64_t(pos0.v[b]) + s;
+    int64_t nv = (p + 1) / a.r;
+    if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    int32_t* out = a.sel + (size_t(b) * a.S + size_t(s)) * a.k;
+    if (nv <= a.k) {                                  // dense regime: every visible row
+        for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < nv ? i : -1;
+        return;
+    }
+    select_keys_mem<kSelThreads>(a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride, nv, a.k, out, shm);
+}
+
+// ------------------------------------------------------------------ select with keys in registers
+// For up to NT * KPT visible rows.  Split selection, for few queries over many rows: stage 1
+// (SEL_CHUNK) selects the k best of each chunk of a.chunk rows into a candidate list, stage 2
+// (SEL_MERGE) the k best of those candidates.  The order (key descending, then row ascending)
+// is total, so a row among a query's k best is among the k best of its chunk, and the
+// candidate lists, chunk after chunk and ascending within one, are in row order: the lower
+// position wins a tie, and the rows come out ascending.  Stage 1 stores each candidate's key
+// beside its row; a candidate -1 (a chunk with k rows or fewer) has key 0.
 enum SelMode { SEL_DIRECT = 0, SEL_CHUNK = 1, SEL_MERGE = 2 };
+constexpr int64_t kSelRegMaxRows = 1024 * 68;   // largest lane the register select holds
 
 template <int KPT, int NT, int MODE>
 __global__ void __launch_bounds__(NT)
@@ -728,7 +734,6 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
         return;
     }
     if (MODE == SEL_MERGE) n = a.n_chunks * a.k;       // candidate positions
-    // keys (0 past n)
     const int wbase = w * 64 * KPT + 4 * lane;
     uint32_t key[KPT];
     int32_t crow[KPT];                                 // stage 2: the candidates' rows
@@ -751,119 +756,245 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
             key[4 * i + 3] = j + 3 < n ? v.w : 0u;
         }
     }
-    // A row past n holds key 0, below the key of every score (score_key gives 0 only to the
-    // NaN with every bit set).  The passes skip a wave's groups of 4 x 64 rows that lie wholly
-    // past n and count the other zeros as keys of value 0: as at least k valid keys lie above
-    // 0, the k-th largest key is a valid row's, every bin count above it is that of the valid
-    // rows alone, and the compaction takes only keys >= thr > 0.  No per-key validity test is
-    // then needed.
     const int ngv = __builtin_amdgcn_readfirstlane(
-        max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a row below n
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-    __syncthreads();
-    // pass 1: bits 31..21
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-        if (i < ngv) {
-#pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e) atomicAdd(&hist[key[e] >> 21], 1u);
-        }
-    __syncthreads();
-    find_bucket<NT>(hist, 2048, a.k, tmp, sh);
-    const uint32_t d1 = uint32_t(sh[0]);
-    int rem = sh[1];
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-    __syncthreads();
-    // pass 2: bits 20..10 of the keys in bucket d1
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-        if (i < ngv) {
-#pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if ((key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
-        }
-    __syncthreads();
-    find_bucket<NT>(hist, 2048, rem, tmp, sh);
-    const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
-    rem = sh[1];
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-    __syncthreads();
-    // pass 3: bits 9..0 of the keys with prefix (d1, d2)
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-        if (i < ngv) {
-#pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if ((key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
-        }
-    __syncthreads();
-    find_bucket<NT>(hist, 1024, rem, tmp, sh);
-    const uint32_t thr = (pre << 10) | uint32_t(sh[0]);
-    rem = sh[1];                                       // rows with key == thr still to take
+        max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a position below n
+    const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.k, hist, tmp, sh);
+    reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
+        if (MODE == SEL_CHUNK) okey[slot] = key[e];
+        out[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
+    });
+}
 
-    // Compaction in row order.  Lane masks (the compare results themselves) give every count: wave totals
-    // first, then each wave walks its groups of 4 x 64 rows, where row 4 l + j of a group is
-    // key j of lane l, so the rows before it are those of lower lanes and its own lower j.
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        ngt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
-        neq += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] == thr)));
+// Fused decode selection, stage 2: the k best of the scorer's per-workgroup candidates
+// (each group's m best rows in row order, groups in row order, so the list is in row order
+// and a tie goes to the lower row).  The result is exact when every row the scorer did not
+// pass on scores below the k-th candidate key T: each group's cutoff (its largest key not
+// passed on) is checked against T, and a query where some cutoff reaches T selects from its
+// full score keys instead (select_keys_mem), with the same result.
+template <int KPT, int NT>
+__global__ void __launch_bounds__(NT)
+topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
+    constexpr int G = KPT / 4;
+    __shared__ uint32_t hist[2048];
+    __shared__ int tmp[NT / 64];
+    __shared__ int sh[4];
+    __shared__ int wtot[2][NT / 64];
+    __shared__ uint32_t red[NT / 64];
+    const int b = blockIdx.y;
+    const int s = blockIdx.x;
+    const int p = pos0.v[b] + s;
+    int nv = (p + 1) / a.r;
+    if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    const size_t q = size_t(b) * a.S + size_t(s);
+    int32_t* out = a.sel + q * a.k;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (nv <= a.k) {                                   // dense regime: every visible row
+        for (int i = tid; i < a.k; i += NT) out[i] = i < nv ? i : -1;
+        return;
     }
-    if (lane == 0) {
-        wtot[0][w] = ngt;
-        wtot[1][w] = neq;
-    }
-    __syncthreads();
-    int o = 0, eqb = 0;                                // rows taken / ties seen before this wave
-    for (int v = 0; v < w; ++v) {
-        eqb += wtot[1][v];
-        o += wtot[0][v];
-    }
-    o += eqb < rem ? eqb : rem;
+    const int groups = (nv + a.f_rows_per_group - 1) / a.f_rows_per_group;
+    const int n = groups * a.f_m;                      // candidate positions (<= NT * KPT)
+    const uint32_t* ck = a.f_key + q * size_t(a.f_groups) * a.f_m;
+    const int32_t* cr = a.f_row + q * size_t(a.f_groups) * a.f_m;
+    const int wbase = w * 64 * KPT + 4 * lane;
+    uint32_t key[KPT];
+    int32_t crow[KPT];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        uint64_t em[4], any = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            em[j] = __builtin_amdgcn_ballot_w64(key[4 * i + j] == thr);
-            any |= em[j] | __builtin_amdgcn_ballot_w64(key[4 * i + j] > thr);
+        const int j = wbase + 256 * i;
+        uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+        int4 rv = make_int4(-1, -1, -1, -1);
+        if (j < n) {                                   // n is a multiple of 4 (m is)
+            kv = *reinterpret_cast<const uint4*>(ck + j);
+            rv = *reinterpret_cast<const int4*>(cr + j);
         }
-        if (any == 0) continue;                        // nothing taken in this group
-        int eq_rank = eqb;                             // ties before this lane's first key
+        key[4 * i + 0] = kv.x; key[4 * i + 1] = kv.y; key[4 * i + 2] = kv.z; key[4 * i + 3] = kv.w;
+        crow[4 * i + 0] = rv.x; crow[4 * i + 1] = rv.y; crow[4 * i + 2] = rv.z; crow[4 * i + 3] = rv.w;
+    }
+    uint32_t cut = 0;                                  // largest key the scorer did not pass on
+    for (int g = tid; g < groups; g += NT) {
+        const uint32_t c = a.f_cutoff[q * size_t(a.f_groups) + g];
+        cut = c > cut ? c : cut;
+    }
+    cut = block_max_u32<NT>(cut, red);
+    const int ngv = __builtin_amdgcn_readfirstlane(max(0, min(G, (n - w * 64 * KPT + 255) / 256)));
+    const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.k, hist, tmp, sh);
+    if (cut < rs.thr) {
+        reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int) { out[slot] = crow[e]; });
+        return;
+    }
+    // some row not passed on reaches the k-th candidate key: select from every score key
+    __syncthreads();
+    select_keys_mem<NT>(a.keys + q * a.n_stride, nv, a.k, out, reinterpret_cast<int*>(hist));
+}
+
+// ------------------------------------------------------------------ decode scoring
+// Decode scoring (each query's rows read once, no sharing between queries): the workgroup
+// stages its query's 64 x 128 fragment in LDS once (16-byte chunks XOR-swizzled by head),
+// then every wave streams its own contiguous run of 32-row blocks straight into registers,
+// with the next block's loads in flight while the current one is scored.  MFMA k slots are
+// ordered so that a lane holds 64 contiguous bytes of its row per 64-dim half: k slot
+// 8 hi + e of MFMA ks = 4 d + j is dim 64 d + 32 hi + 8 j + e, in the query operand alike.
+//
+// FUSE (the fused indexer): the workgroup's rows (a contiguous run of rows_per_block) keep
+// their keys in LDS as well, and after the scan the workgroup selects its m best (key
+// descending, row ascending) by the same radix select and passes them on in row order, with
+// the largest key it leaves out; the merge kernel above takes the query's k best of those.
+constexpr int kStreamWaves = 8;
+constexpr int kFuseMaxRows = 4096;                    // rows of one workgroup's local select
+constexpr int kFuseKpt = kFuseMaxRows / (64 * kStreamWaves);
+
+__device__ __forceinline__ void idx_stream_block(const bf16* rows, int64_t blk, int64_t nv, uint4 (&kb)[8]) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+    int64_t j = blk * 32 + l32;
+    j = j < nv ? j : nv - 1;                          // rows past the visible ones: scores not stored
+    const bf16* rp = rows + size_t(j) * ID + 32 * hi;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) eq_rank += lanes_below(em[j]);
-        bool take[4];
-        int slot = o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool eq = key[4 * i + j] == thr;
-            take[j] = key[4 * i + j] > thr || (eq && eq_rank < rem);
-            eq_rank += eq;
-            const uint64_t tm = __builtin_amdgcn_ballot_w64(take[j]);
-            slot += lanes_below(tm);
-            o += int(__popcll(tm));
-            eqb += int(__popcll(em[j]));
-        }
-        const int j0 = wbase + 256 * i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (take[j]) {
-                if (MODE == SEL_CHUNK) okey[slot] = key[4 * i + j];
-                out[slot++] = MODE == SEL_MERGE ? crow[4 * i + j] : base + j0 + j;
-            }
+    for (int c = 0; c < 4; ++c) {
+        kb[c] = *reinterpret_cast<const uint4*>(rp + 8 * c);
+        kb[4 + c] = *reinterpret_cast<const uint4*>(rp + 64 + 8 * c);
     }
 }
 
-#ifndef DSV4_TOPK_CHUNK
-#define DSV4_TOPK_CHUNK 8192
-#endif
-constexpr int kSelChunk = DSV4_TOPK_CHUNK;           // rows per chunk of a split selection
+template <int WAVES, bool FUSE>
+__global__ void __launch_bounds__(64 * WAVES)
+index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    constexpr int NT = 64 * WAVES;
+    const int b = blockIdx.z;
+    const int64_t s = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int64_t nv = (int64_t(pos0v.v[b]) + s + 1) / a.r;
+    if (nv > n_rows.v[b]) nv = n_rows.v[b];
+    const int64_t nbt = (nv + 31) / 32;                // 32-row blocks of this query
+    const int bpw = a.rows_per_block / (32 * WAVES);   // blocks per wave
+    if (int64_t(blockIdx.x) * WAVES * bpw >= nbt) return;   // whole workgroup: no rows
+    __shared__ __attribute__((aligned(16))) unsigned char qs[IH * IROWB];
+    {
+        const bf16* qg = a.qi + (size_t(b) * a.S + size_t(s)) * IH * ID;
+        for (int i = threadIdx.x; i < IH * 16; i += NT) {
+            const int h = i >> 4, c = i & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(qg + h * ID + c * 8);
+            store16(qs + h * IROWB + ((c ^ (h & 15)) * 16), v);
+        }
+    }
+    __syncthreads();
+    const int64_t blk0 = (int64_t(blockIdx.x) * WAVES + w) * bpw;
+    const int nb = blk0 >= nbt ? 0 : int(nbt - blk0 < bpw ? nbt - blk0 : bpw);   // this wave's blocks
+    const int64_t row0 = int64_t(blockIdx.x) * a.rows_per_block;                // the workgroup's first row
+    __shared__ __attribute__((aligned(16))) uint32_t kl[FUSE ? kFuseMaxRows : 4];
+    if (nb > 0) {
+        // query operand in the permuted k order, head weights
+        bf16x8 qa[2][8];
+        float wsc[2][16];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int h = 32 * m + l32, c = 8 * (ks >> 2) + 4 * hi + (ks & 3);
+                const uint4 v = *reinterpret_cast<const uint4*>(qs + h * IROWB + ((c ^ (h & 15)) * 16));
+                __builtin_memcpy(&qa[m][ks], &v, 16);
+            }
+            const float* wr = a.w + (size_t(b) * a.S + size_t(s)) * IH;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(wr + 32 * m + 8 * g + 4 * hi);
+                wsc[m][4 * g + 0] = v.x * a.scale;
+                wsc[m][4 * g + 1] = v.y * a.scale;
+                wsc[m][4 * g + 2] = v.z * a.scale;
+                wsc[m][4 * g + 3] = v.w * a.scale;
+            }
+        }
+        const bf16* rows = a.rows + size_t(b) * a.row_cap * ID;
+        uint32_t* keys = a.keys + (size_t(b) * a.S + size_t(s)) * a.n_stride;
+        auto score = [&](const uint4 (&kb)[8], int64_t blk) {
+            floatx16 c0, c1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                c0[i] = 0.f;
+                c1[i] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                bf16x8 kv;
+                __builtin_memcpy(&kv, &kb[ks], 16);
+                c0 = mfma32x32x16(qa[0][ks], kv, c0);
+                c1 = mfma32x32x16(qa[1][ks], kv, c1);
+            }
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0 = fmaf(wsc[0][i], relu_bits(c0[i]), s0);
+                s1 = fmaf(wsc[1][i], relu_bits(c1[i]), s1);
+            }
+            float sc = s0 + s1;
+            sc += __shfl_xor(sc, 32, 64);
+            const int64_t jj = blk * 32 + l32;
+            if (hi == 0 && jj < nv) {
+                const uint32_t kk = score_key(sc);
+                keys[jj] = kk;
+                if (FUSE) kl[jj - row0] = kk;
+            }
+        };
+        uint4 kb0[8], kb1[8];
+        idx_stream_block(rows, blk0, nv, kb0);
+        for (int u = 0; u < nb; u += 2) {
+            if (u + 1 < nb) idx_stream_block(rows, blk0 + u + 1, nv, kb1);
+            score(kb0, blk0 + u);
+            if (u + 1 < nb) {
+                if (u + 2 < nb) idx_stream_block(rows, blk0 + u + 2, nv, kb0);
+                score(kb1, blk0 + u + 1);
+            }
+        }
+    }
+    if constexpr (FUSE) {
+        __shared__ uint32_t hist[2048];
+        __shared__ int tmp[WAVES];
+        __shared__ int sh[4];
+        __shared__ int wtot[2][WAVES];
+        __shared__ uint32_t red[WAVES];
+        __syncthreads();                               // every key of the workgroup in kl
+        int64_t n64 = nv - row0;
+        n64 = n64 < a.rows_per_block ? n64 : a.rows_per_block;
+        const int n = int(n64);                        // > 0: the workgroup has rows
+        const size_t q = size_t(b) * a.S + size_t(s);
+        uint32_t* ck = a.cand_key + (q * a.n_groups + blockIdx.x) * size_t(a.m);
+        int32_t* cr = a.cand_row + (q * a.n_groups + blockIdx.x) * size_t(a.m);
+        if (n <= a.m) {                                // every row passed on
+            for (int i = threadIdx.x; i < a.m; i += NT) {
+                ck[i] = i < n ? kl[i] : 0u;
+                cr[i] = i < n ? int32_t(row0 + i) : -1;
+            }
+            if (threadIdx.x == 0) a.cutoff[q * a.n_groups + blockIdx.x] = 0u;
+            return;
+        }
+        constexpr int KPT = kFuseKpt, G = KPT / 4;
+        const int wbase = w * 64 * KPT + 4 * lane;
+        uint32_t key[KPT];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int j = wbase + 256 * i;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (j < n) v = *reinterpret_cast<const uint4*>(kl + j);
+            key[4 * i + 0] = v.x;
+            key[4 * i + 1] = j + 1 < n ? v.y : 0u;
+            key[4 * i + 2] = j + 2 < n ? v.z : 0u;
+            key[4 * i + 3] = j + 3 < n ? v.w : 0u;
+        }
+        const int ngv = __builtin_amdgcn_readfirstlane(max(0, min(G, (n - w * 64 * KPT + 255) / 256)));
+        const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.m, hist, tmp, sh);
+        uint32_t rest = reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
+            ck[slot] = key[e];
+            cr[slot] = int32_t(row0 + pos);
+        });
+        rest = block_max_u32<NT>(rest, red);
+        if (threadIdx.x == 0) a.cutoff[q * a.n_groups + blockIdx.x] = rest;
+    }
+}
+
+constexpr int kSelChunk = 8192;                       // rows per chunk of a split selection
+constexpr int kMergeThreads = 512;                    // workgroup of the merge stages
 static_assert(kSelChunk % 2048 == 0 && kSelChunk <= 512 * 64, "chunk: 512 threads x 4k keys");
-#ifndef DSV4_TOPK_MERGE_THREADS
-#define DSV4_TOPK_MERGE_THREADS 512
-#endif
-constexpr int kMergeThreads = DSV4_TOPK_MERGE_THREADS;   // workgroup of the merge stage
 
 // Chunks per query of a split selection, 0 for one workgroup per query.  The split pays where
 // a call has too few queries to fill the chip (at most 64) and many rows each (above 16,384),
@@ -874,6 +1005,44 @@ int64_t topk_chunks(int64_t queries, int64_t n_max, int k) {
     return c * k <= kMergeThreads * 64 ? c : 0;
 }
 
+// The fused decode indexer's shape for a call: fewer than 8 queries per sequence (decode),
+// the MFMA scorer, and each scoring workgroup passing on m rows, m the smallest multiple of
+// 32 of at least three times the workgroup's expected share of the k best (k * rows_per_group
+// / n for the sparsest sequence of the call), so that a group's m best hold all of its share
+// but with vanishing probability (the merge checks it).  At most 128 rows per group and 8192
+// candidates per query.
+struct FusedPlan {
+    bool on = false;
+    int bpw = 0, rows_per_group = 0, m = 0;
+    int64_t groups = 0;
+};
+
+FusedPlan fused_plan(bool mfma, int64_t S, int batch, int64_t n_max, int64_t n_min_sparse, int k) {
+    FusedPlan f;
+    if (!mfma || S >= kIdxWaves || n_max <= k || n_min_sparse <= k) return f;
+    const int64_t queries = int64_t(batch < kSeqSlice ? batch : kSeqSlice) * S;
+    const int64_t nbt = (n_max + 31) / 32;
+    int64_t bpw = (nbt * queries + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
+    bpw = bpw < 1 ? 1 : bpw;
+    if (bpw * 32 * kStreamWaves > kFuseMaxRows) return f;
+    f.bpw = int(bpw);
+    f.rows_per_group = f.bpw * 32 * kStreamWaves;
+    // m >= 3 k rows_per_group / n_min_sparse, rounded up to a multiple of 32
+    const int64_t m = ((3 * int64_t(k) * f.rows_per_group + n_min_sparse - 1) / n_min_sparse + 31) / 32 * 32;
+    if (m > 128) return f;
+    f.m = int(m < 32 ? 32 : m);
+    f.groups = (n_max + f.rows_per_group - 1) / f.rows_per_group;
+    if (f.groups * f.m > 8192) return f;
+    f.on = true;
+    return f;
+}
+
+// Candidate area of a fused call: keys and rows [queries][groups][m], cutoffs [queries][groups].
+size_t fused_cand_bytes(int64_t groups, int m, int batch, int64_t S) {
+    const size_t qg = size_t(batch) * size_t(S) * size_t(groups);
+    return qg * size_t(m) * 2 * sizeof(uint32_t) + qg * sizeof(uint32_t);
+}
+
 // Bytes of the score-key part of the workspace (the candidate lists follow, 256-aligned).
 size_t index_keys_bytes(int batch, int64_t S, int64_t n_stride) {
     return (size_t(batch) * size_t(S) * size_t(n_stride) * sizeof(uint32_t) + 255) & ~size_t(255);
@@ -881,9 +1050,22 @@ size_t index_keys_bytes(int batch, int64_t S, int64_t n_stride) {
 
 template <typename T>
 hipError_t run(const IndexJob& j, hipStream_t st) {
-    const int64_t n_chunks = topk_chunks(int64_t(j.batch) * j.S, j.n_max, j.k);
-    int32_t* cand = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(j.keys) +
-                                               index_keys_bytes(j.batch, j.S, j.n_stride));
+    const bool mfma = use_index_mfma(j.bf16, j.Hi, j.di);
+    // rows of the sequences in the sparse regime at their first query
+    int64_t n_min_sparse = int64_t(1) << 62;
+    for (int b = 0; b < j.batch; ++b) {
+        const int64_t nv = std::min<int64_t>((j.pos0[b] + 1) / j.r, j.n_rows[b]);
+        if (nv > j.k) n_min_sparse = std::min(n_min_sparse, nv);
+    }
+    const FusedPlan fp = fused_plan(mfma, j.S, j.batch, j.n_max, n_min_sparse, j.k);
+    const int64_t n_chunks = fp.on ? 0 : topk_chunks(int64_t(j.batch) * j.S, j.n_max, j.k);
+    char* tail = reinterpret_cast<char*>(j.keys) + index_keys_bytes(j.batch, j.S, j.n_stride);
+    int32_t* cand = reinterpret_cast<int32_t*>(tail);
+    // fused candidates: keys, rows, cutoffs
+    uint32_t* f_key = reinterpret_cast<uint32_t*>(tail);
+    const size_t fq = size_t(j.batch) * j.S * size_t(fp.groups);
+    int32_t* f_row = reinterpret_cast<int32_t*>(f_key + fq * fp.m);
+    uint32_t* f_cut = reinterpret_cast<uint32_t*>(f_row + fq * fp.m);
     for (int b0 = 0; b0 < j.batch; b0 += kSeqSlice) {
         const int nb = std::min(kSeqSlice, j.batch - b0);
         SeqInts pos{}, nr{};
@@ -895,8 +1077,8 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             nv_max = std::max(nv_max, nv);
         }
         const size_t qoff = size_t(b0) * j.S;
-        if (nv_max > j.k && use_index_mfma(j.bf16, j.Hi, j.di)) {
-            IdxMfmaArgs a;
+        if (nv_max > j.k && mfma) {
+            IdxMfmaArgs a{};
             a.qi = static_cast<const bf16*>(j.qi) + qoff * IH * ID;
             a.w = j.w + qoff * IH;
             a.rows = static_cast<const bf16*>(j.rows) + size_t(b0) * j.row_cap * ID;
@@ -906,9 +1088,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             a.keys = j.keys + qoff * j.n_stride;
             a.r = j.r;
             a.scale = 1.0f / sqrtf(float(j.di)) / sqrtf(float(j.Hi));
-            constexpr int QG = kIdxWaves * kIdxQpw;        // queries per prefill workgroup
-            const bool perq = j.S >= QG;
-            if (perq && kIdxRowStationary && nv_max >= kIdxRsMinRows) {
+            if (j.S >= kIdxWaves && nv_max >= kIdxRsMinRows) {
                 // row-stationary: RSB-row blocks x query groups, about one workgroup per CU
                 const int64_t rb = (nv_max + RSB - 1) / RSB;
                 int64_t ng = (256 + rb * nb - 1) / (rb * nb);
@@ -921,24 +1101,29 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 ng = (j.S + qpg - 1) / qpg;
                 DSV4_LAUNCH("index_score_rs", index_score_rs_kernel<kIdxWaves>, dim3(unsigned(rb), unsigned(ng), nb),
                             dim3(64 * kIdxWaves), 0, st, a, pos, nr);
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-            } else {
-            const int64_t groups = perq ? (j.S + QG - 1) / QG : j.S;
-            // enough row blocks to give the chip >= ~2048 workgroups in prefill; in decode (one
-            // query per group) fewer, longer blocks, so each streams several tiles through
-            // the copy ring and loads its query once
-            const int64_t want_wgs = perq ? 2048 : kIdxDecodeWgs;
-            int64_t blocks = (want_wgs + groups * nb - 1) / (groups * nb);
-            const int64_t tiles = (nv_max + IRT - 1) / IRT;
-            if (blocks > tiles) blocks = tiles;
-            if (blocks < 1) blocks = 1;
-            a.rows_per_block = int(((tiles + blocks - 1) / blocks) * IRT);
-            const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
-            if (perq)
-                DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<kIdxQpw, kIdxWaves, kIdxStages>),
+            } else if (j.S >= kIdxWaves) {
+                // query-stationary: blocks of rows x groups of 8 queries, ~2048 workgroups
+                const int64_t groups = (j.S + kIdxWaves - 1) / kIdxWaves;
+                int64_t blocks = (2048 + groups * nb - 1) / (groups * nb);
+                const int64_t tiles = (nv_max + IRT - 1) / IRT;
+                if (blocks > tiles) blocks = tiles;
+                if (blocks < 1) blocks = 1;
+                a.rows_per_block = int(((tiles + blocks - 1) / blocks) * IRT);
+                const unsigned gx = unsigned((nv_max + a.rows_per_block - 1) / a.rows_per_block);
+                DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<kIdxWaves, kIdxStages>),
                             dim3(gx, unsigned(groups), nb), dim3(64 * kIdxWaves), 0, st, a, pos, nr);
-            else if (kIdxStream) {
+            } else if (fp.on) {
+                // fused decode scoring: groups of rows_per_group rows, each passing on its m best
+                a.rows_per_block = fp.rows_per_group;
+                a.cand_key = f_key + qoff * fp.groups * fp.m;
+                a.cand_row = f_row + qoff * fp.groups * fp.m;
+                a.cutoff = f_cut + qoff * fp.groups;
+                a.n_groups = int(fp.groups);
+                a.m = fp.m;
+                DSV4_LAUNCH("index_score_fused", (index_score_stream_kernel<kStreamWaves, true>),
+                            dim3(unsigned(fp.groups), unsigned(j.S), nb), dim3(64 * kStreamWaves), 0, st,
+                            a, pos, nr);
+            } else {
                 // decode: blocks per wave so the chip gets about 256 workgroups
                 const int64_t nbt = (nv_max + 31) / 32;
                 int64_t bpw = (nbt * j.S * nb + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
@@ -946,14 +1131,11 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 if (bpw > (int64_t(1) << 20)) bpw = int64_t(1) << 20;   // rows_per_block fits an int
                 a.rows_per_block = int(bpw * 32 * kStreamWaves);
                 const unsigned sx = unsigned((nbt + bpw * kStreamWaves - 1) / (bpw * kStreamWaves));
-                DSV4_LAUNCH("index_score_stream", index_score_stream_kernel<kStreamWaves>,
+                DSV4_LAUNCH("index_score_stream", (index_score_stream_kernel<kStreamWaves, false>),
                             dim3(sx, unsigned(j.S), nb), dim3(64 * kStreamWaves), 0, st, a, pos, nr);
-            } else
-                DSV4_LAUNCH("index_score_mfma", (index_score_mfma_kernel<0, 4, kIdxStages>),
-                            dim3(gx, unsigned(groups), nb), dim3(256), 0, st, a, pos, nr);
+            }
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            }
         } else if (nv_max > j.k) {
             ScoreArgs<T> a;
             a.Hi = j.Hi; a.di = j.di; a.r = j.r;
@@ -972,7 +1154,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        SelArgs sa;
+        SelArgs sa{};
         sa.k = j.k; sa.r = j.r; sa.S = j.S; sa.n_stride = j.n_stride;
         sa.keys = j.keys + qoff * j.n_stride;
         sa.sel = j.sel + qoff * j.k;
@@ -981,14 +1163,31 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
         sa.cand = cand + qoff * size_t(n_chunks) * j.k;
         sa.cand_key = reinterpret_cast<uint32_t*>(cand + size_t(j.batch) * j.S * n_chunks * j.k) +
                       qoff * size_t(n_chunks) * j.k;
-        if (n_chunks > 0) {
+        constexpr int MT = kMergeThreads;
+        if (fp.on) {
+            sa.f_key = f_key + qoff * fp.groups * fp.m;
+            sa.f_row = f_row + qoff * fp.groups * fp.m;
+            sa.f_cutoff = f_cut + qoff * fp.groups;
+            sa.f_groups = int(fp.groups);
+            sa.f_m = fp.m;
+            sa.f_rows_per_group = fp.rows_per_group;
+            const int64_t nc = fp.groups * fp.m;
+            if (nc <= MT * 4)
+                DSV4_LAUNCH("topk_fused_merge", (topk_fused_merge_kernel<4, MT>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+            else if (nc <= MT * 8)
+                DSV4_LAUNCH("topk_fused_merge", (topk_fused_merge_kernel<8, MT>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+            else
+                DSV4_LAUNCH("topk_fused_merge", (topk_fused_merge_kernel<16, MT>),
+                            dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
+        } else if (n_chunks > 0) {
             // stage 1 over (query, chunk), stage 2 over the n_chunks x k candidates
             DSV4_LAUNCH("topk_select_reg", (topk_select_reg_kernel<kSelChunk / 512, 512, SEL_CHUNK>),
                         dim3(unsigned(j.S), nb, unsigned(n_chunks)), dim3(512), 0, st, sa, pos, nr);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const int64_t nc = n_chunks * j.k;
-            constexpr int MT = kMergeThreads;
             if (nc <= MT * 8)
                 DSV4_LAUNCH("topk_merge", (topk_select_reg_kernel<8, MT, SEL_MERGE>),
                             dim3(unsigned(j.S), nb), dim3(MT), 0, st, sa, pos, nr);
@@ -1039,10 +1238,13 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
 int64_t index_key_stride(int64_t n_max) { return ((n_max < 1 ? 1 : n_max) + 3) & ~int64_t(3); }
 
 size_t index_workspace_bytes(int Hi, int di, int k, int batch, int64_t S, int64_t n_max) {
-    (void)Hi; (void)di;
+    // a fused call's groups follow n_max alone; its m grows as the call's sparsest sequence
+    // gets shorter, up to 128: the area is sized for that bound
+    const FusedPlan fp = fused_plan(use_index_mfma(true, Hi, di), S, batch, n_max, n_max, k);
     const int64_t c = topk_chunks(int64_t(batch) * S, n_max, k);
-    return index_keys_bytes(batch, S, index_key_stride(n_max)) +
-           2 * size_t(batch) * size_t(S) * size_t(c) * size_t(k) * sizeof(int32_t);
+    const size_t split = 2 * size_t(batch) * size_t(S) * size_t(c) * size_t(k) * sizeof(int32_t);
+    const size_t fused = fp.on ? fused_cand_bytes(fp.groups, 128, batch, S) : 0;
+    return index_keys_bytes(batch, S, index_key_stride(n_max)) + (split > fused ? split : fused);
 }
 
 hipError_t launch_index_topk(const IndexJob& j, hipStream_t s) {

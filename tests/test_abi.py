@@ -99,10 +99,14 @@ def test_index_validation(L):
     assert "aligned" in L.dsv4_last_error().decode()
     # key rows are padded to a multiple of 4 keys, the key block to 256 bytes
     assert K.dsv4_index_workspace_bytes(cfg, 2, 3, 601) == 2 * 3 * 604 * 4 + 96
-    # few queries over many rows add k candidate rows and keys per 8192-row chunk (split
-    # selection)
-    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 65536) == 4 * 65536 * 4 + 2 * 4 * 8 * 512 * 4
-    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 16384) == 4 * 16384 * 4
+    # few queries (8 per sequence, past the fused decode indexer) over many rows add k
+    # candidate rows and keys per 8192-row chunk (split selection)
+    assert K.dsv4_index_workspace_bytes(cfg, 1, 8, 65536) == 8 * 65536 * 4 + 2 * 8 * 8 * 512 * 4
+    # a decode call the fused indexer takes: 4 queries over 16,384 rows are scored by 64
+    # workgroups of 256 rows each, which pass on up to 128 of their best (key and row) and a
+    # cutoff; that candidate area is larger than the split selection's (none at 16,384 rows)
+    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 16384) == 4 * 16384 * 4 + 4 * 64 * (128 * 8 + 4)
+    assert K.dsv4_index_workspace_bytes(cfg, 4, 1, 65536) == 4 * 65536 * 4 + 4 * 64 * (128 * 8 + 4)
     assert K.dsv4_index_workspace_bytes(cfg, 65, 1, 65536) == 65 * 65536 * 4
     assert _index(L, cfg, sel=None) == EINVAL
     assert _index(L, cfg, s=70000) == EUNSUP

@@ -27,6 +27,8 @@ def _hipcc():
     ("attention.hip", "attn_prefill_kernel"),
     ("attention.hip", "attn_decode_kernel"),
     ("indexer.hip", "index_score_mfma_kernel"),
+    ("indexer.hip", "index_score_rs_kernel"),
+    ("proj.hip", "gproj_tile_kernel"),
 ])
 def test_m0_only_feeds_lds_dma(tmp_path, src, kernel):
     out = tmp_path / "k.s"

@@ -57,8 +57,8 @@ def _check(rows_i, qi, w, positions, sel, exact, spec=SPEC):
 @pytest.mark.parametrize("n_vis", [600, 2048, 2049, 4096, 5000, 8192, 12000,
                                    16384, 16684, 20001, 32768, 33001, 65600, 69632, 69633])
 def test_topk_large_lanes(n_vis, queries):
-    """Few queries (6) over more than 16,384 rows take the split selection (k best per
-    8192-row chunk, then of the candidates; 16,684 leaves a last chunk of k rows or fewer);
+    """Few queries (2 sequences x 3) from 4096 rows on take the fused decode indexer (each
+    scoring workgroup passes on its m best, m from 128 down to 64 here, then one merge);
     many (65 in one sequence) take one workgroup per query.  Up to 16,384 rows the keys per
     thread follow the row count (4, 8, 16 or 32: the counts below reach each and its edge)."""
     B, S = (2, 3) if queries == "few" else (1, 65)
@@ -116,3 +116,44 @@ def test_topk_1024_pro_shape(n_vis, queries):
     n_rows = [min(cap, (positions[b][-1] + 1) // 4) for b in range(B)]
     sel = _run(rows_i, qi, w, positions, n_rows, spec)
     _check(rows_i, qi, w, positions, sel, exact=False, spec=spec)
+
+
+@pytest.mark.parametrize("n_vis,lo,cnt", [(65600, 30000, 700), (20001, 0, 600), (16384, 15584, 800)])
+def test_topk_clustered_rows(n_vis, lo, cnt):
+    """A contiguous run of rows scores far above the rest (those index keys scaled by 4, exact
+    in bf16), so one scoring workgroup of the fused decode indexer holds more of the k best
+    than it passes on: the merge must notice (a workgroup's cutoff reaches the k-th candidate
+    key) and select from every score key instead; the result is the oracle's either way."""
+    B, S = 2, 1
+    cap = n_vis + 8
+    g = 71 + n_vis
+    rows_i = synth.normal((B, cap, SPEC.index_dim), seed=g, stream="rows_i", dtype=torch.bfloat16,
+                          device="cuda")
+    rows_i[:, lo:lo + cnt] *= 4
+    qi = synth.normal((B, S, SPEC.index_heads, SPEC.index_dim), seed=g, stream="qi",
+                      dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, SPEC.index_heads), seed=g, stream="w", device="cuda").abs()
+    positions = [[4 * n_vis - 1 - b] for b in range(B)]
+    n_rows = [min(cap, (positions[b][-1] + 1) // 4) for b in range(B)]
+    sel = _run(rows_i, qi, w, positions, n_rows)
+    _check(rows_i, qi, w, positions, sel, exact=False)
+    inside = ((sel >= lo) & (sel < lo + cnt)).sum(axis=-1)
+    assert (inside > 200).all(), inside                 # the run does hold much of the top-k
+
+
+def test_topk_mixed_dense_and_sparse_decode():
+    """One decode call over sequences at very different lengths: one still dense (fewer
+    visible rows than k), the others sparse at 40,000 and 65,000 rows."""
+    B, S = 3, 1
+    n_vis = [300, 40000, 65000]
+    cap = max(n_vis) + 8
+    rows_i = synth.normal((B, cap, SPEC.index_dim), seed=5, stream="rows_i", dtype=torch.bfloat16,
+                          device="cuda")
+    qi = synth.normal((B, S, SPEC.index_heads, SPEC.index_dim), seed=5, stream="qi",
+                      dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, SPEC.index_heads), seed=5, stream="w", device="cuda")
+    positions = [[4 * n + 2] for n in n_vis]
+    n_rows = [n for n in n_vis]
+    sel = _run(rows_i, qi, w, positions, n_rows)
+    assert list(sel[0, 0, :300]) == list(range(300)) and (sel[0, 0, 300:] == -1).all()
+    _check(rows_i, qi, w, positions, sel, exact=False)
