@@ -1173,6 +1173,9 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": dec["roofline"],
         "decode_mode": dec["mode"],
+        "decode_raw": dec["raw"],
+        "decode_emission": dec["emission"],
+        "decode_bytes_per_step": dec["bytes_per_step"],
         "eager": dec["eager"],
         "kernels": dec["kernels"],
         "prefill": pre,

@@ -18,11 +18,12 @@
 // Two kernels per call:
 //   compress_rows_kernel  one workgroup per emitted row: reads every slot of the row from
 //                         the state (tokens before the call) or the new lanes, pools per
-//                         channel with an online softmax, then norm and RoPE in LDS;
+//                         channel with a softmax, then norm and RoPE in LDS;
 //   compress_state_kernel copies the new tokens of the last nw windows into the state.
 // The second runs after the first on the stream, because a row of this call may read a
-// state slot that the update overwrites.  With one new token per sequence (decode) the two
-// fuse into compress_step_kernel.
+// state slot that the update overwrites.  With one new token per sequence (decode): the
+// frontier store alone, or, when a sequence completes a row, compress_pool_kernel (the store
+// and the pooling, spread over channel blocks) then compress_finish_kernel (norm and RoPE).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,8 +31,9 @@ namespace dsv4 {
 
 namespace {
 
-constexpr int kCompThreads = 256;
-constexpr int kStepThreads = 512;     // decode step: one latent channel per thread at D = 512
+constexpr int kCompThreads = 512;     // an emitting workgroup (prefill row or decode finish)
+constexpr int kMaxDim = 4096;         // largest latent (the configs' dim bound)
+constexpr int kPairs = 1024;          // (channel group, slot group) pairs of a row
 
 template <typename T>
 struct CompArgs {
@@ -48,72 +50,161 @@ struct CompArgs {
     int64_t n_new;
 };
 
-// One slot of the per-channel online softmax.  Branch-free form of the usual update: when
-// the logit does not raise the running max, f = exp(0) = 1 and e = exp(logit - m); when it
-// does, f = exp(m - logit) and e = exp(0) = 1 -- the same values as the branching update.
-__device__ __forceinline__ void pool_slot(float logit, float v, float& m, float& l, float& acc) {
-    const float mn = fmaxf(m, logit);
-    const float f = expf(m - mn);             // 0 when m = -inf
-    const float e = expf(logit - mn);
-    acc = acc * f + e * v;
-    l = l * f + e;
-    m = mn;
+// VEC consecutive storage elements (16 bytes, aligned; VEC = 1: one element anywhere): a raw
+// load, and element e of it as a float.
+template <typename T, int VEC>
+struct RawVec {
+    uint4 u;
+    __device__ __forceinline__ void load(const T* p) { u = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t x = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+            return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+        } else {
+            const uint32_t x = e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+            return __uint_as_float(x);
+        }
+    }
+};
+template <typename T>
+struct RawVec<T, 1> {
+    T v;
+    __device__ __forceinline__ void load(const T* p) { v = *p; }
+    __device__ __forceinline__ float get(int) const { return to_f32(v); }
+};
+
+// Pooling of one row.  The coff*r slots of a channel are split over SG slot groups (slot
+// group g: slots g, g + SG, ...); each (channel group of VEC channels, slot group) keeps a
+// softmax state (max, sum, weighted sum) in base-2 units (logits times log2 e), updated a
+// batch of UNR slots at a time: the batch's own max, its exponentials, then one rescale --
+// about 1.25 exponentials per slot, each a bare exp2.  The groups' states then merge per
+// channel in the fixed order g = 0 .. SG-1.  Prefill rows and decode emissions run this same
+// arithmetic per channel (whichever workgroup computes it), so their rows are bit-identical.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kUnr = 8;
+
+// Channel groups (VEC channels) and slot groups of a row of D channels: about kPairs pairs
+// in all, at most 256 slot groups -- a function of D alone, so every kernel that pools a row
+// splits it the same way.
+__host__ __device__ inline void slot_groups(int D, int vec, int& ncg, int& SG) {
+    ncg = D / vec;
+    SG = kPairs / ncg;
+    SG = SG < 1 ? 1 : (SG > 256 ? 256 : SG);
 }
 
-// Row j of sequence b: pooled per channel with an online softmax over its slots, rounded,
-// RMS-normalised, rounded, RoPE'd on the last rd dims at position j*r, rounded.  Slot s of
-// window w is token w*r + s: tokens before the call (t < lb) sit in state window (w % nw)
-// at position s, later ones in the new lanes at t - lb.  All positions fit in 32 bits.
-template <typename T>
-__device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int lb,
-                                         float* zrow, float* red) {
+template <typename T, int VEC>
+__device__ __forceinline__ void pool_part(const CompArgs<T>& a, int b, int j, int lb, int cg, int g,
+                                          int SG, float (&m)[VEC], float (&l)[VEC], float (&acc)[VEC]) {
     const int D = a.D, W = a.coff * a.D, r = a.r;
     const size_t st = size_t(2) * a.nw * r * W;
     const T* sa0 = a.state + size_t(b) * st;                 // kv lane of this sequence
     const T* sg0 = sa0 + size_t(a.nw) * r * W;               // gate lane
-    float ss = 0.f;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
-        float m = -INFINITY, l = 0.f, acc = 0.f;
-        for (int half = 0; half < a.coff; ++half) {
+    const int nslots = a.coff * r;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        m[e] = -INFINITY;
+        l[e] = 0.f;
+        acc[e] = 0.f;
+    }
+    // slot u = g + SG i is position sl of half `half` (u = half r + sl), advanced without
+    // division; the frontier window of each half is fixed for the row
+    const int wmod1 = j % a.nw;                                  // window j
+    const int wmod0 = j >= 1 ? (j - 1) % a.nw : 0;               // window j - 1 (overlap)
+    const int dh = SG / r, ds = SG - dh * r;
+    int half = g / r, sl = g - (g / r) * r;
+    for (int u0 = g; u0 < nslots; u0 += SG * kUnr) {
+        RawVec<T, VEC> v[kUnr], gt[kUnr], ap[kUnr];
+        bool ok[kUnr];
+#pragma unroll
+        for (int q = 0; q < kUnr; ++q) {
+            const int u = u0 + q * SG;
             // overlap: half 0 <- window j-1, half 1 <- window j; plain: half 0 <- window j
-            const int win = (a.coff == 2 && half == 0) ? j - 1 : j;
-            if (win < 0) continue;
-            const int col = half * D + c;
-            const int t0 = win * r;
-            int n_state = lb - t0;                             // slots taken from the state
-            n_state = n_state < 0 ? 0 : (n_state > r ? r : n_state);
-            const size_t wo = size_t(win % a.nw) * r * W + col;
-            const T* sa = sa0 + wo;
-            const T* sg = sg0 + wo;
-            const T* ap = a.ape + col;
-#pragma unroll 8
-            for (int s = 0; s < n_state; ++s)
-                pool_slot(to_f32(sg[size_t(s) * W]) + to_f32(ap[size_t(s) * W]),
-                          to_f32(sa[size_t(s) * W]), m, l, acc);
-            if (n_state < r) {                                 // first new token: t0 + n_state
-                const size_t first = size_t(b) * a.n_new + size_t(t0 + n_state - lb);
-                const T* la = a.lane_a + first * W + col;
-                const T* lg = a.lane_g + first * W + col;
-#pragma unroll 8
-                for (int s = n_state; s < r; ++s) {
-                    const size_t o = size_t(s - n_state) * W;
-                    pool_slot(to_f32(lg[o]) + to_f32(ap[size_t(s) * W]), to_f32(la[o]), m, l, acc);
+            const bool prev = a.coff == 2 && half == 0;
+            const int win = prev ? j - 1 : j;
+            ok[q] = u < nslots && win >= 0;
+            if (ok[q]) {
+                const int col = half * D + cg * VEC;
+                const int t = win * r + sl;
+                if (t < lb) {
+                    const size_t o = (size_t(prev ? wmod0 : wmod1) * r + size_t(sl)) * W + col;
+                    v[q].load(sa0 + o);
+                    gt[q].load(sg0 + o);
+                } else {
+                    const size_t o = (size_t(b) * a.n_new + size_t(t - lb)) * W + col;
+                    v[q].load(a.lane_a + o);
+                    gt[q].load(a.lane_g + o);
                 }
+                ap[q].load(a.ape + size_t(sl) * W + col);
+            }
+            sl += ds;
+            half += dh;
+            if (sl >= r) {
+                sl -= r;
+                ++half;
             }
         }
-    const float y = round_to<T>(acc / l);
-        zrow[c] = y;
-        ss += y * y;
+        bool any = false;
+#pragma unroll
+        for (int q = 0; q < kUnr; ++q) any |= ok[q];
+        if (!any) continue;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float c[kUnr];
+            float mb = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < kUnr; ++q) {
+                c[q] = (gt[q].get(e) + ap[q].get(e)) * kLog2e;
+                if (ok[q]) mb = fmaxf(mb, c[q]);
+            }
+            float lb_ = 0.f, ab = 0.f;
+#pragma unroll
+            for (int q = 0; q < kUnr; ++q)
+                if (ok[q]) {
+                    const float x = __builtin_amdgcn_exp2f(c[q] - mb);
+                    lb_ += x;
+                    ab = fmaf(x, v[q].get(e), ab);
+                }
+            const float M = fmaxf(m[e], mb);
+            const float f = m[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[e] - M);
+            const float fb = __builtin_amdgcn_exp2f(mb - M);
+            l[e] = fmaf(l[e], f, lb_ * fb);
+            acc[e] = fmaf(acc[e], f, ab * fb);
+            m[e] = M;
+        }
     }
+}
+
+// Merge of the slot groups' states of channel c (part: [3][SG][D]): the pooled value.
+__device__ __forceinline__ float merge_part(const float* part, int SG, int D, int c) {
+    float mx = -INFINITY;
+    for (int i = 0; i < SG; ++i) mx = fmaxf(mx, part[(0 * SG + i) * D + c]);
+    float ls = 0.f, as = 0.f;
+    for (int i = 0; i < SG; ++i) {
+        const float mi = part[(0 * SG + i) * D + c];
+        const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mx);
+        ls = fmaf(part[(1 * SG + i) * D + c], f, ls);
+        as = fmaf(part[(2 * SG + i) * D + c], f, as);
+    }
+    return as / ls;
+}
+
+// The rest of row j once its pooled (rounded) values are in zrow and each thread's sum of
+// squares (channels tid, tid + NT, ...) in ss: RMSNorm * gamma (rounded), RoPE of the last rd
+// dims at position j*r (rounded), stored.
+template <typename T>
+__device__ __forceinline__ void finish_row(const CompArgs<T>& a, int b, int j, float ss, float* zrow,
+                                           float* red) {
+    constexpr int NT = kCompThreads;
+    const int D = a.D, tid = threadIdx.x;
     const float tot = block_sum(ss, red);
     const float den = sqrtf(tot / float(D) + a.eps);
-    for (int c = threadIdx.x; c < D; c += blockDim.x)
+    for (int c = tid; c < D; c += NT)
         zrow[c] = round_to<T>(zrow[c] / den * to_f32(a.gamma[c]));
     __syncthreads();
     const int r0 = D - a.rd;
     const float pos = float(int64_t(j) * a.r);
     T* out = a.rows + (size_t(b) * a.row_cap + size_t(j)) * D;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    for (int c = tid; c < D; c += NT) {
         float v = zrow[c];
         if (c >= r0) {
             const int i = (c - r0) >> 1;
@@ -126,37 +217,118 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
     }
 }
 
-template <typename T>
+// Row j of sequence b by one workgroup (prefill): pooled per channel (pool_part for every
+// (channel group, slot group) pair, merge_part), rounded, then finish_row.  Slot s of window
+// w is token w*r + s: tokens before the call (t < lb) sit in state window (w % nw) at
+// position s, later ones in the new lanes at t - lb.
+template <typename T, int VEC>
+__device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int lb,
+                                         float* zrow, float* part, float* red) {
+    constexpr int NT = kCompThreads;
+    const int D = a.D, tid = threadIdx.x;
+    int ncg, SG;
+    slot_groups(D, VEC, ncg, SG);
+    for (int pr = tid; pr < ncg * SG; pr += NT) {
+        const int cg = pr % ncg, g = pr / ncg;
+        float m[VEC], l[VEC], acc[VEC];
+        pool_part<T, VEC>(a, b, j, lb, cg, g, SG, m, l, acc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int c = cg * VEC + e;
+            part[(0 * SG + g) * D + c] = m[e];
+            part[(1 * SG + g) * D + c] = l[e];
+            part[(2 * SG + g) * D + c] = acc[e];
+        }
+    }
+    __syncthreads();
+    float ss = 0.f;
+    for (int c = tid; c < D; c += NT) {
+        const float y = round_to<T>(merge_part(part, SG, D, c));
+        zrow[c] = y;
+        ss += y * y;
+    }
+    finish_row<T>(a, b, j, ss, zrow, red);
+}
+
+template <typename T, int VEC>
 __global__ void __launch_bounds__(kCompThreads)
 compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
-    extern __shared__ float zrow[];           // [D]
+    __shared__ float zrow[kMaxDim];
+    __shared__ float part[3 * kPairs * VEC];         // [3][SG][D], SG * D <= kPairs * VEC
     __shared__ float red[16];
     const int b = blockIdx.y;
     const int lb = len_before.v[b];
     const int j = lb / a.r + int(blockIdx.x);  // row index
     if (int64_t(j + 1) * a.r > lb + a.n_new) return;
-    emit_row(a, b, j, lb, zrow, red);
+    emit_row<T, VEC>(a, b, j, lb, zrow, part, red);
 }
 
-// One new token per sequence (decode): store it in the frontier and, when it completes a
-// window, emit that row -- one launch.  The row reads the state only at positions of
-// earlier tokens and takes the new token from the lane, so the store cannot race it.
+// A decode step in two launches when some sequence completes a row.  compress_pool_kernel:
+// one workgroup per (block of channel groups, sequence) pools its channels exactly as
+// emit_row does and stores the rounded pooled values in the row's place; the first
+// workgroup of each sequence also stores the token in the frontier (the row reads the state
+// only at earlier tokens and takes this token from the lane, so the store cannot race it).
+// compress_finish_kernel: one workgroup per emitting sequence reads the pooled row back and
+// finishes it (finish_row, the same channel-to-thread mapping as emit_row).
+template <typename T, int VEC>
+__global__ void __launch_bounds__(256)
+compress_pool_kernel(CompArgs<T> a, SeqInts len_before) {
+    extern __shared__ float part[];           // [3][SG][CGW * VEC]
+    const int b = blockIdx.y;
+    const int lb = len_before.v[b];
+    const int W = a.coff * a.D;
+    if (blockIdx.x == 0) {
+        const size_t st = size_t(2) * a.nw * a.r * W;
+        T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
+        T* sg = sa + size_t(a.nw) * a.r * W;
+        for (int c = threadIdx.x; c < W; c += blockDim.x) {
+            sa[c] = a.lane_a[size_t(b) * W + c];
+            sg[c] = a.lane_g[size_t(b) * W + c];
+        }
+    }
+    if ((lb + 1) % a.r != 0) return;
+    const int j = lb / a.r;
+    int ncg, SG;
+    slot_groups(a.D, VEC, ncg, SG);
+    const int CGW = int(blockDim.x) / SG;                 // channel groups per workgroup
+    const int cl = threadIdx.x % CGW, g = threadIdx.x / CGW;
+    const int cg = int(blockIdx.x) * CGW + cl;
+    const int CW = CGW * VEC;                             // channels of this workgroup
+    if (cg < ncg) {
+        float m[VEC], l[VEC], acc[VEC];
+        pool_part<T, VEC>(a, b, j, lb, cg, g, SG, m, l, acc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int c = cl * VEC + e;
+            part[(0 * SG + g) * CW + c] = m[e];
+            part[(1 * SG + g) * CW + c] = l[e];
+            part[(2 * SG + g) * CW + c] = acc[e];
+        }
+    }
+    __syncthreads();
+    T* row = a.rows + (size_t(b) * a.row_cap + size_t(j)) * a.D;
+    const int c0 = int(blockIdx.x) * CW;
+    for (int c = threadIdx.x; c < CW && c0 + c < a.D; c += blockDim.x)
+        row[c0 + c] = from_f32<T>(merge_part(part, SG, CW, c));
+}
+
 template <typename T>
-__global__ void __launch_bounds__(kStepThreads)
-compress_step_kernel(CompArgs<T> a, SeqInts len_before) {
-    extern __shared__ float zrow[];
+__global__ void __launch_bounds__(kCompThreads)
+compress_finish_kernel(CompArgs<T> a, SeqInts len_before) {
+    __shared__ float zrow[kMaxDim];
     __shared__ float red[16];
     const int b = blockIdx.x;
-    const int64_t lb = len_before.v[b];
-    const int W = a.coff * a.D;
-    const size_t st = size_t(2) * a.nw * a.r * W;
-    T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
-    T* sg = sa + size_t(a.nw) * a.r * W;
-    for (int c = threadIdx.x; c < W; c += blockDim.x) {
-        sa[c] = a.lane_a[size_t(b) * W + c];
-        sg[c] = a.lane_g[size_t(b) * W + c];
+    const int lb = len_before.v[b];
+    if ((lb + 1) % a.r != 0) return;
+    const int j = lb / a.r;
+    const T* row = a.rows + (size_t(b) * a.row_cap + size_t(j)) * a.D;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < a.D; c += kCompThreads) {
+        const float y = to_f32(row[c]);
+        zrow[c] = y;
+        ss += y * y;
     }
-    if ((lb + 1) % a.r == 0) emit_row(a, b, int(lb / a.r), int(lb), zrow, red);
+    finish_row<T>(a, b, j, ss, zrow, red);
 }
 
 template <typename T>
@@ -196,6 +368,11 @@ frontier_store_kernel(FrontierJob f, SeqInts pos) {
     }
 }
 
+// 16-byte vectors of the storage type where every lane column is a multiple of them (the
+// lanes and the APE are rows of coff*D elements, so D % VEC == 0 aligns every slot).
+template <typename T> constexpr int kVec = 16 / int(sizeof(T));
+template <typename T> bool vec_ok(int D) { return D % kVec<T> == 0; }
+
 template <typename T>
 hipError_t run(const CompressJob& j, hipStream_t s) {
     const int W = j.coff * j.D;
@@ -216,9 +393,34 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
             a.row_cap = j.row_cap;
             a.n_new = 1;
             for (int i = 0; i < nb; ++i) lb.v[i] = int32_t(j.len_before[b0 + i]);
-            DSV4_LAUNCH("compress_step", compress_step_kernel<T>, dim3(nb), dim3(kStepThreads),
-                               j.D * sizeof(float), s, a, lb);
+            bool emits = false;
+            for (int i = 0; i < nb; ++i) emits |= (j.len_before[b0 + i] + 1) % j.r == 0;
+            if (!emits) {                                   // the frontier store alone
+                FrontierJob f;
+                f.state = a.state; f.lane_a = a.lane_a; f.lane_g = a.lane_g;
+                f.r = j.r; f.nw = j.nw; f.W = W;
+                hipError_t e = launch_frontier_store(f, sizeof(T) == 2, nb, j.len_before + b0, s);
+                if (e != hipSuccess) return e;
+                continue;
+            }
+            // one (channel group, slot group) pair per thread: a wave of 64 / SG channel
+            // groups, or SG threads for one channel group
+            const int vec = vec_ok<T>(j.D) ? kVec<T> : 1;
+            int ncg, SG;
+            slot_groups(j.D, vec, ncg, SG);
+            const int CGW = SG >= 64 ? 1 : 64 / SG;
+            const int nt = CGW * SG;
+            const size_t lds = size_t(3) * nt * vec * sizeof(float);
+            const dim3 grid(unsigned((ncg + CGW - 1) / CGW), nb);
+            if (vec > 1)
+                DSV4_LAUNCH("compress_pool", (compress_pool_kernel<T, kVec<T>>), grid, dim3(nt), lds, s, a, lb);
+            else
+                DSV4_LAUNCH("compress_pool", (compress_pool_kernel<T, 1>), grid, dim3(nt), lds, s, a, lb);
             hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            DSV4_LAUNCH("compress_finish", compress_finish_kernel<T>, dim3(nb), dim3(kCompThreads), 0, s,
+                        a, lb);
+            e = hipGetLastError();
             if (e != hipSuccess) return e;
             continue;
         }
@@ -243,8 +445,12 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
         a.row_cap = j.row_cap;
         a.n_new = j.n_new;
         if (max_rows > 0) {
-            DSV4_LAUNCH("compress_rows", compress_rows_kernel<T>, dim3(unsigned(max_rows), nb),
-                               dim3(kCompThreads), j.D * sizeof(float), s, a, lb);
+            if (vec_ok<T>(j.D))
+                DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, kVec<T>>), dim3(unsigned(max_rows), nb),
+                            dim3(kCompThreads), 0, s, a, lb);
+            else
+                DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, 1>), dim3(unsigned(max_rows), nb),
+                            dim3(kCompThreads), 0, s, a, lb);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
