@@ -207,10 +207,7 @@ constexpr int MD = 512;                   // latent dims
 constexpr int MKT = 64;                   // keys per tile
 // LDS bytes per key row: 1024 + 48 makes both the Q.K^T operand reads (16 rows x 16 B) and
 // the transposed P.V operand reads (4 rows x 32 B per 16-lane group) bank-conflict free.
-#ifndef DSV4_KPITCH_PAD
-#define DSV4_KPITCH_PAD 48
-#endif
-constexpr int KPITCH = MD * 2 + DSV4_KPITCH_PAD;
+constexpr int KPITCH = MD * 2 + 48;
 constexpr int KBUF = MKT * KPITCH;        // one key tile
 constexpr int PPITCH = MKT * 2 + 16;      // LDS bytes per head row of P
 constexpr int OPITCH = MD * 4 + 16;       // LDS bytes per head row of staged fp32 output

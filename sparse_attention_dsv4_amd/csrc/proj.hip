@@ -74,10 +74,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 
 // MFMA k-slot order: in a 64-wide k block, lane (m, hh) of MFMA j holds k = 32 hh + 8 j + e,
 // so the 4 MFMAs of a block take a lane's 64 contiguous bytes of its row (A and B alike).
-#ifndef DSV4_GPROJ_SMALL_WAVES
-#define DSV4_GPROJ_SMALL_WAVES 8
-#endif
-constexpr int kSmallWaves = DSV4_GPROJ_SMALL_WAVES;
+constexpr int kSmallWaves = 8;          // (16 measured: no change)
 constexpr int kSmallMaxT = 32;
 
 // Up to 32 tokens: workgroup (32-row block, group); wave w of the W waves multiplies k in
