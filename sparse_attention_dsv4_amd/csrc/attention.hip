@@ -431,7 +431,8 @@ __device__ __forceinline__ void prefill_load_tile(const TileCtx& c, const int32_
 }
 
 // One key tile of the 8-wave prefill workgroup (see above).  nx: the next tile, whose 8 row
-// copies of this wave go out between this tile's MFMA groups.
+// copies of this wave go out two per subtile of the score product: early, so they have the
+// rest of the tile to land (issued later, the last ones' latency showed at the tile's end).
 __device__ __forceinline__ void prefill_tile(const AttnMfmaArgs& a, const TileCtx& c, const unsigned char* buf,
                                              unsigned char* ptile, float (*xch)[2][MH], const bf16x8 (&qa)[8],
                                              floatx4 (&o)[16], float& m_run, float& l_run, int nkt,
@@ -456,7 +457,10 @@ __device__ __forceinline__ void prefill_tile(const AttnMfmaArgs& a, const TileCt
         sp[u] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) sp[u] = mfma16x16x32(ka[u & 1][ks], qa[ks], sp[u]);
-        if (nx.on) prow_copy(c, nx.src, nx.buf, nx.nkt, u);
+        if (nx.on) {
+            prow_copy(c, nx.src, nx.buf, nx.nkt, 2 * u);
+            prow_copy(c, nx.src, nx.buf, nx.nkt, 2 * u + 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
     // keep key half nt (subtiles 2 nt, 2 nt + 1); the partner wave (other dims) gets the other
@@ -542,7 +546,6 @@ __device__ __forceinline__ void prefill_tile(const AttnMfmaArgs& a, const TileCt
         const int m0 = 8 * (grp & 1);
 #pragma unroll
         for (int m = 0; m < 8; ++m) o[m0 + m] = mfma16x16x32(va[grp & 1][m], pb, o[m0 + m]);
-        if (nx.on) prow_copy(c, nx.src, nx.buf, nx.nkt, 4 + grp);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
