@@ -31,7 +31,7 @@ namespace dsv4 {
 
 namespace {
 
-constexpr int kCompThreads = 512;     // an emitting workgroup (prefill row or decode finish)
+constexpr int kCompThreads = 256;     // an emitting workgroup (prefill row or decode finish)
 constexpr int kMaxDim = 4096;         // largest latent (the configs' dim bound)
 constexpr int kPairs = 1024;          // (channel group, slot group) pairs of a row
 
@@ -83,13 +83,16 @@ struct RawVec<T, 1> {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kUnr = 8;
 
-// Channel groups (VEC channels) and slot groups of a row of D channels: about kPairs pairs
-// in all, at most 256 slot groups -- a function of D alone, so every kernel that pools a row
-// splits it the same way.
-__host__ __device__ inline void slot_groups(int D, int vec, int& ncg, int& SG) {
+// Channel groups (VEC channels) and slot groups of a row of D channels and nslots slots:
+// about kPairs pairs in all, at most 256 slot groups and no more than a batch of kUnr slots
+// per group needs (a ratio-4 row's 8 slots: one group) -- a function of the lane shape
+// alone, so every kernel that pools a row splits it the same way.
+__host__ __device__ inline void slot_groups(int D, int vec, int nslots, int& ncg, int& SG) {
     ncg = D / vec;
     SG = kPairs / ncg;
     SG = SG < 1 ? 1 : (SG > 256 ? 256 : SG);
+    const int need = (nslots + kUnr - 1) / kUnr;
+    SG = SG < need ? SG : (need < 1 ? 1 : need);
 }
 
 template <typename T, int VEC>
@@ -188,29 +191,52 @@ __device__ __forceinline__ float merge_part(const float* part, int SG, int D, in
     return as / ls;
 }
 
+// Per-thread constants of the row epilogue for channels tid + k*NT: gamma and the RoPE
+// frequency, loaded when the workgroup starts so their latency overlaps the pooling.
+constexpr int kChan = kMaxDim / kCompThreads;
+struct RowConst {
+    float gam[kChan], frq[kChan];
+};
+template <typename T>
+__device__ __forceinline__ void load_row_const(const CompArgs<T>& a, RowConst& rc) {
+    const int r0 = a.D - a.rd;
+#pragma unroll
+    for (int k = 0; k < kChan; ++k) {
+        const int c = int(threadIdx.x) + k * kCompThreads;
+        rc.gam[k] = c < a.D ? to_f32(a.gamma[c]) : 0.f;
+        rc.frq[k] = c < a.D && c >= r0 ? a.inv_freq[(c - r0) >> 1] : 0.f;
+    }
+}
+
 // The rest of row j once its pooled (rounded) values are in zrow and each thread's sum of
 // squares (channels tid, tid + NT, ...) in ss: RMSNorm * gamma (rounded), RoPE of the last rd
 // dims at position j*r (rounded), stored.
 template <typename T>
-__device__ __forceinline__ void finish_row(const CompArgs<T>& a, int b, int j, float ss, float* zrow,
-                                           float* red) {
+__device__ __forceinline__ void finish_row(const CompArgs<T>& a, const RowConst& rc, int b, int j, float ss,
+                                           float* zrow, float* red) {
     constexpr int NT = kCompThreads;
     const int D = a.D, tid = threadIdx.x;
     const float tot = block_sum(ss, red);
     const float den = sqrtf(tot / float(D) + a.eps);
-    for (int c = tid; c < D; c += NT)
-        zrow[c] = round_to<T>(zrow[c] / den * to_f32(a.gamma[c]));
+#pragma unroll
+    for (int k = 0; k < kChan; ++k) {
+        const int c = tid + k * NT;
+        if (c < D) zrow[c] = round_to<T>(zrow[c] / den * rc.gam[k]);
+    }
     __syncthreads();
     const int r0 = D - a.rd;
     const float pos = float(int64_t(j) * a.r);
     T* out = a.rows + (size_t(b) * a.row_cap + size_t(j)) * D;
-    for (int c = tid; c < D; c += NT) {
+#pragma unroll
+    for (int k = 0; k < kChan; ++k) {
+        const int c = tid + k * NT;
+        if (c >= D) break;
         float v = zrow[c];
         if (c >= r0) {
             const int i = (c - r0) >> 1;
             const float x0 = zrow[r0 + 2 * i], x1 = zrow[r0 + 2 * i + 1];
             float sn, cs;
-            sincosf(pos * a.inv_freq[i], &sn, &cs);
+            sincosf(pos * rc.frq[k], &sn, &cs);
             v = ((c - r0) & 1) ? (x0 * sn + x1 * cs) : (x0 * cs - x1 * sn);
         }
         out[c] = from_f32<T>(v);
@@ -226,8 +252,10 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
                                          float* zrow, float* part, float* red) {
     constexpr int NT = kCompThreads;
     const int D = a.D, tid = threadIdx.x;
+    RowConst rc;
+    load_row_const(a, rc);
     int ncg, SG;
-    slot_groups(D, VEC, ncg, SG);
+    slot_groups(D, VEC, a.coff * a.r, ncg, SG);
     for (int pr = tid; pr < ncg * SG; pr += NT) {
         const int cg = pr % ncg, g = pr / ncg;
         float m[VEC], l[VEC], acc[VEC];
@@ -247,15 +275,16 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
         zrow[c] = y;
         ss += y * y;
     }
-    finish_row<T>(a, b, j, ss, zrow, red);
+    finish_row<T>(a, rc, b, j, ss, zrow, red);
 }
 
 template <typename T, int VEC>
 __global__ void __launch_bounds__(kCompThreads)
 compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
-    __shared__ float zrow[kMaxDim];
-    __shared__ float part[3 * kPairs * VEC];         // [3][SG][D], SG * D <= kPairs * VEC
+    extern __shared__ float smem[];                  // zrow [D], then part [3][SG][D]
     __shared__ float red[16];
+    float* zrow = smem;
+    float* part = smem + a.D;
     const int b = blockIdx.y;
     const int lb = len_before.v[b];
     const int j = lb / a.r + int(blockIdx.x);  // row index
@@ -289,7 +318,7 @@ compress_pool_kernel(CompArgs<T> a, SeqInts len_before) {
     if ((lb + 1) % a.r != 0) return;
     const int j = lb / a.r;
     int ncg, SG;
-    slot_groups(a.D, VEC, ncg, SG);
+    slot_groups(a.D, VEC, a.coff * a.r, ncg, SG);
     const int CGW = int(blockDim.x) / SG;                 // channel groups per workgroup
     const int cl = threadIdx.x % CGW, g = threadIdx.x / CGW;
     const int cg = int(blockIdx.x) * CGW + cl;
@@ -321,6 +350,8 @@ compress_finish_kernel(CompArgs<T> a, SeqInts len_before) {
     const int lb = len_before.v[b];
     if ((lb + 1) % a.r != 0) return;
     const int j = lb / a.r;
+    RowConst rc;
+    load_row_const(a, rc);
     const T* row = a.rows + (size_t(b) * a.row_cap + size_t(j)) * a.D;
     float ss = 0.f;
     for (int c = threadIdx.x; c < a.D; c += kCompThreads) {
@@ -328,7 +359,7 @@ compress_finish_kernel(CompArgs<T> a, SeqInts len_before) {
         zrow[c] = y;
         ss += y * y;
     }
-    finish_row<T>(a, b, j, ss, zrow, red);
+    finish_row<T>(a, rc, b, j, ss, zrow, red);
 }
 
 template <typename T>
@@ -366,6 +397,24 @@ frontier_store_kernel(FrontierJob f, SeqInts pos) {
         sa[c] = la[c];
         sg[c] = lg[c];
     }
+}
+
+// Dynamic LDS beyond the default 64 KB must be allowed per kernel and device before its
+// launch (once: the limit is raised to the largest size asked for so far on that device).
+template <typename K>
+hipError_t allow_lds(K* kernel, size_t bytes) {
+    constexpr size_t kDefault = 64 * 1024;
+    static size_t allowed[64];
+    if (bytes <= kDefault) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (bytes <= allowed[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(bytes));
+    if (e == hipSuccess) allowed[dev] = bytes;
+    return e;
 }
 
 // 16-byte vectors of the storage type where every lane column is a multiple of them (the
@@ -407,7 +456,7 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
             // groups, or SG threads for one channel group
             const int vec = vec_ok<T>(j.D) ? kVec<T> : 1;
             int ncg, SG;
-            slot_groups(j.D, vec, ncg, SG);
+            slot_groups(j.D, vec, j.coff * j.r, ncg, SG);
             const int CGW = SG >= 64 ? 1 : 64 / SG;
             const int nt = CGW * SG;
             const size_t lds = size_t(3) * nt * vec * sizeof(float);
@@ -445,13 +494,21 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
         a.row_cap = j.row_cap;
         a.n_new = j.n_new;
         if (max_rows > 0) {
-            if (vec_ok<T>(j.D))
+            // LDS: the row, then the slot groups' states (ratio-4 rows: one group, 8 KB at D = 512)
+            const int vec = vec_ok<T>(j.D) ? kVec<T> : 1;
+            int ncg, SG;
+            slot_groups(j.D, vec, j.coff * j.r, ncg, SG);
+            const size_t lds = size_t(j.D) * (1 + 3 * SG) * sizeof(float);
+            hipError_t e = vec > 1 ? allow_lds(compress_rows_kernel<T, kVec<T>>, lds)
+                                   : allow_lds(compress_rows_kernel<T, 1>, lds);
+            if (e != hipSuccess) return e;
+            if (vec > 1)
                 DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, kVec<T>>), dim3(unsigned(max_rows), nb),
-                            dim3(kCompThreads), 0, s, a, lb);
+                            dim3(kCompThreads), lds, s, a, lb);
             else
                 DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, 1>), dim3(unsigned(max_rows), nb),
-                            dim3(kCompThreads), 0, s, a, lb);
-            hipError_t e = hipGetLastError();
+                            dim3(kCompThreads), lds, s, a, lb);
+            e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         if (max_keep > 0) {
