@@ -289,6 +289,22 @@ typedef struct {
 int dsv4_grouped_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w, void* y,
                       int64_t tokens, void* stream);
 
+/* Both lanes of one compressor from the layer's hidden states in one call: a = x w_kv^T and
+ * g = x w_gate^T, fp32 accumulation, each rounded once to the storage dtype.  Pages: mlx-lm
+ * PR #1189, Thump604's fix list (the ratio-4 compressor's wkv and wgate are [1024, 4096]
+ * projections of the hidden state, the lanes 2*D wide); MTPLX PR #216 "What V4 adds" (the
+ * gated pooling takes a kv lane and a gate lane per token).
+ *   cfg   groups = 1, in_dim = hidden size K, out_dim = lane width W (coff * D), dtype
+ *   x [tokens, K]; w_kv, w_gate [W, K]; a, g [tokens, W] (caller-owned device buffers, the
+ *   lanes dsv4_compress_prefill / dsv4_compress_step read)
+ * The two products share one launch where the tiled kernel applies (bf16, more than 32
+ * tokens, K a multiple of 64, W of 128); otherwise they run as two dsv4_grouped_proj-style
+ * launches with the same arithmetic.
+ * Errors: EINVAL (NULL pointer, groups != 1, bad cfg, tokens < 0), EUNSUPPORTED (tokens x W
+ * above 2^39), EHIP. */
+int dsv4_lane_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w_kv, const void* w_gate, void* a,
+                   void* g, int64_t tokens, void* stream);
+
 /* Kernel timing for measurement.  While enabled, every kernel the library launches carries
  * a start/stop HIP event pair attached to its own dispatch (hipExtLaunchKernelGGL), so each
  * record is that kernel's execution time on its launch stream.  dsv4_trace_read() waits for the

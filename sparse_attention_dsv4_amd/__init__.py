@@ -20,7 +20,7 @@ __all__ = [
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
     "dsv4_index_topk", "dsv4_index_topk_noalloc", "dsv4_index_topk_noalloc_scratch_bytes",
     "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
-    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "RopeCfg", "GprojCfg",
+    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "dsv4_lane_proj", "RopeCfg", "GprojCfg",
     "dsv4_trace_enable", "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernels",
     "EXPORTED_SYMBOLS",
 ]
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "dsv4_attn_workspace_bytes", "dsv4_compress_prefill", "dsv4_compress_step",
     "dsv4_index_topk", "dsv4_index_topk_noalloc", "dsv4_index_topk_noalloc_scratch_bytes",
     "dsv4_csa_attn_decode", "dsv4_csa_attn_decode_store",
-    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "dsv4_trace_enable",
+    "dsv4_csa_attn_prefill", "dsv4_rope", "dsv4_grouped_proj", "dsv4_lane_proj", "dsv4_trace_enable",
     "dsv4_trace_reset", "dsv4_trace_read", "dsv4_trace_kernel_name",
 )
 
@@ -194,6 +194,7 @@ def lib():
         L.dsv4_rope.argtypes = [ctypes.POINTER(_RopeCfg), _P, _I64P, ctypes.c_int32, ctypes.c_int64,
                                 _P, _P]
         L.dsv4_grouped_proj.argtypes = [ctypes.POINTER(_GprojCfg), _P, _P, _P, ctypes.c_int64, _P]
+        L.dsv4_lane_proj.argtypes = [ctypes.POINTER(_GprojCfg), _P, _P, _P, _P, _P, ctypes.c_int64, _P]
         L.dsv4_trace_enable.argtypes = [ctypes.c_int32]
         L.dsv4_trace_read.argtypes = [ctypes.c_char_p, _I64P, ctypes.POINTER(ctypes.c_double)]
         _lib = L
@@ -469,3 +470,21 @@ def dsv4_grouped_proj(cfg: GprojCfg, x, w, y, stream=None):
     _need(y, (T, cfg.groups, cfg.out_dim), cfg.dtype, "y")
     c = cfg.c()
     _check(lib().dsv4_grouped_proj(ctypes.byref(c), _ptr(x), _ptr(w), _ptr(y), T, _stream(stream)))
+
+
+def dsv4_lane_proj(cfg: GprojCfg, x, w_kv, w_gate, a, g, stream=None):
+    """a [T, W] = x [T, K] @ w_kv [W, K].T and g [T, W] = x @ w_gate.T (one group; one launch
+    where the tiled kernel applies)."""
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be [T, K]")
+    if cfg.groups != 1:
+        raise ValueError("the lane projection takes one group")
+    T = x.shape[0]
+    _need(x, (T, cfg.in_dim), cfg.dtype, "x")
+    _need(w_kv, (cfg.out_dim, cfg.in_dim), cfg.dtype, "w_kv")
+    _need(w_gate, (cfg.out_dim, cfg.in_dim), cfg.dtype, "w_gate")
+    _need(a, (T, cfg.out_dim), cfg.dtype, "a")
+    _need(g, (T, cfg.out_dim), cfg.dtype, "g")
+    c = cfg.c()
+    _check(lib().dsv4_lane_proj(ctypes.byref(c), _ptr(x), _ptr(w_kv), _ptr(w_gate), _ptr(a), _ptr(g), T,
+                                _stream(stream)))

@@ -454,6 +454,24 @@ int dsv4_grouped_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w, v
     return hip_status(dsv4::launch_grouped_proj(j, static_cast<hipStream_t>(stream)), "grouped_proj");
 }
 
+int dsv4_lane_proj(const dsv4_gproj_cfg* cfg, const void* x, const void* w_kv, const void* w_gate, void* a,
+                   void* g, int64_t tokens, void* stream) {
+    if (!cfg) return fail(DSV4_EINVAL, "cfg is NULL");
+    if (cfg->groups != 1) return fail(DSV4_EINVAL, "groups %d: the lane projection takes one group", cfg->groups);
+    if (cfg->in_dim < 1 || cfg->in_dim > 65536) return fail(DSV4_EINVAL, "in_dim %d outside 1..65536", cfg->in_dim);
+    if (cfg->out_dim < 1 || cfg->out_dim > 65536) return fail(DSV4_EINVAL, "out_dim %d outside 1..65536", cfg->out_dim);
+    if (!dtype_ok(cfg->dtype)) return fail(DSV4_EINVAL, "unknown dtype %d", cfg->dtype);
+    if (tokens < 0) return fail(DSV4_EINVAL, "tokens < 0");
+    if (tokens == 0) return ok();
+    if (!x || !w_kv || !w_gate || !a || !g) return fail(DSV4_EINVAL, "NULL buffer pointer");
+    if (tokens * int64_t(cfg->out_dim) > (int64_t(1) << 39) || tokens > (int64_t(1) << 31))
+        return fail(DSV4_EUNSUPPORTED, "tokens x out_dim too large");
+    dsv4::GprojJob j;
+    j.G = 1; j.K = cfg->in_dim; j.R = cfg->out_dim; j.bf16 = cfg->dtype == DSV4_BF16;
+    j.x = x; j.w = w_kv; j.y = a; j.T = tokens; j.w2 = w_gate; j.y2 = g;
+    return hip_status(dsv4::launch_grouped_proj(j, static_cast<hipStream_t>(stream)), "lane_proj");
+}
+
 int dsv4_trace_enable(int32_t on) {
     g_trace_on.store(on != 0);
     return ok();

@@ -64,6 +64,8 @@ struct GprojArgs {
     const bf16* w;             // [G][R][K]
     bf16* y;                   // [T][G][R]
     int64_t T;
+    const bf16* w2;            // with G = 1: a second weight [R][K] and output [T][R] over the
+    bf16* y2;                  // same x, taken by the workgroups of blockIdx.z = 1 (else null)
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
@@ -164,7 +166,7 @@ __device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ ((row /
 // Copy k block kb of the tile into stage buffer buf: 1 KB copies of kRowsPerOp rows; wave w
 // takes copies w, w + waves, ... (the token rows first, then the weight rows).
 template <class SH>
-__device__ __forceinline__ void tile_load(const GprojArgs& a, int g, int64_t t0, int r0, int kb,
+__device__ __forceinline__ void tile_load(const GprojArgs& a, const bf16* wg, int g, int64_t t0, int r0, int kb,
                                           unsigned char* buf) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -179,7 +181,7 @@ __device__ __forceinline__ void tile_load(const GprojArgs& a, int g, int64_t t0,
             src = a.x + (size_t(t) * a.G + g) * a.K + size_t(kb) * kTileK + 8 * c;
         } else {
             const int r = r0 + row - SH::T;
-            src = a.w + (size_t(g) * a.R + r) * a.K + size_t(kb) * kTileK + 8 * c;
+            src = wg + (size_t(g) * a.R + r) * a.K + size_t(kb) * kTileK + 8 * c;
         }
         dma16(src, buf + op * 1024);
     }
@@ -189,7 +191,11 @@ template <int WT, int WRB>
 __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
     using SH = TileShape<WT, WRB>;
     __shared__ __attribute__((aligned(16))) unsigned char st[kTileStages][SH::stage_bytes];
-    const int g = blockIdx.z;
+    // blockIdx.z: the group, or with a second pair (G = 1) which of the two products
+    const bool second = a.w2 != nullptr && blockIdx.z == 1;
+    const int g = a.w2 != nullptr ? 0 : int(blockIdx.z);
+    const bf16* wsel = second ? a.w2 : a.w;
+    bf16* ysel = second ? a.y2 : a.y;
     const int64_t t0 = int64_t(blockIdx.x) * SH::T;
     const int r0 = int(blockIdx.y) * SH::R;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -203,11 +209,11 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
         for (int v = 0; v < WRB; ++v)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
-    tile_load<SH>(a, g, t0, r0, 0, st[0]);
+    tile_load<SH>(a, wsel, g, t0, r0, 0, st[0]);
     for (int kb = 0; kb < nk; ++kb) {
         wait_vm<0>();                                    // block kb (the only copies in flight)
         lds_barrier();                                   // block kb visible; kb-1 fully read
-        if (kb + 1 < nk) tile_load<SH>(a, g, t0, r0, kb + 1, st[(kb + 1) % kTileStages]);
+        if (kb + 1 < nk) tile_load<SH>(a, wsel, g, t0, r0, kb + 1, st[(kb + 1) % kTileStages]);
         const unsigned char* buf = st[kb % kTileStages];
 #pragma unroll
         for (int j = 0; j < kTileK / 16; ++j) {          // MFMA k steps of this block
@@ -236,7 +242,7 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
         for (int i = 0; i < 16; ++i) {
             const int64_t t = t0 + 64 * wt + 32 * u + c_row(i, lane);
             if (t >= a.T) continue;
-            bf16* yr = a.y + (size_t(t) * a.G + g) * a.R + r0 + 32 * WRB * wr + m;
+            bf16* yr = ysel + (size_t(t) * a.G + g) * a.R + r0 + 32 * WRB * wr + m;
 #pragma unroll
             for (int v = 0; v < WRB; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
         }
@@ -295,9 +301,37 @@ hipError_t launch_rope(const RopeJob& j, hipStream_t s) {
 
 hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
     constexpr int kSmallK = 64 * kSmallWaves;          // k per KBW step of the workgroup
+    if (j.w2 != nullptr) {
+        // two products over one x: one launch of the tiled kernel (twice the workgroups, so
+        // shapes that leave half the chip idle alone fill it), else one call each
+        const bool tiled = j.bf16 && j.G == 1 && j.T > kSmallMaxT && j.K % kTileK == 0 && j.R % 128 == 0;
+        if (!tiled) {
+            GprojJob one = j;
+            one.w2 = nullptr;
+            one.y2 = nullptr;
+            hipError_t e = launch_grouped_proj(one, s);
+            if (e != hipSuccess) return e;
+            one.w = j.w2;
+            one.y = j.y2;
+            return launch_grouped_proj(one, s);
+        }
+        GprojArgs a{1, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
+                    static_cast<bf16*>(j.y), j.T, static_cast<const bf16*>(j.w2), static_cast<bf16*>(j.y2)};
+        using Big = TileShape<4, 4>;
+        using Small = TileShape<2, 2>;
+        const int64_t big_tiles = (j.T + Big::T - 1) / Big::T * (j.R / Big::R) * 2;
+        if (j.R % Big::R == 0 && big_tiles >= 256) {
+            const dim3 grid(unsigned((j.T + Big::T - 1) / Big::T), unsigned(j.R / Big::R), 2);
+            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<4, 4>), grid, dim3(64 * Big::waves), 0, s, a);
+        } else {
+            const dim3 grid(unsigned((j.T + Small::T - 1) / Small::T), unsigned(j.R / Small::R), 2);
+            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<2, 2>), grid, dim3(64 * Small::waves), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     if (j.bf16 && j.T <= kSmallMaxT && j.K % kSmallK == 0 && j.K <= 8 * kSmallK && j.R % 32 == 0) {
         GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
-                    static_cast<bf16*>(j.y), j.T};
+                    static_cast<bf16*>(j.y), j.T, nullptr, nullptr};
         const dim3 grid(unsigned(j.R / 32), unsigned(j.G));
         const dim3 block(64 * kSmallWaves);
         switch (j.K / kSmallK) {
@@ -314,7 +348,7 @@ hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
     }
     if (j.bf16 && j.K % kTileK == 0 && j.R % 128 == 0) {
         GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
-                    static_cast<bf16*>(j.y), j.T};
+                    static_cast<bf16*>(j.y), j.T, nullptr, nullptr};
         using Big = TileShape<4, 4>;
         using Small = TileShape<2, 2>;
         const int64_t big_tiles = (j.T + Big::T - 1) / Big::T * (j.R / Big::R) * j.G;

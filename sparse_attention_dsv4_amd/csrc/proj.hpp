@@ -28,6 +28,10 @@ struct GprojJob {
     const void* w;             // [G][R][K]
     void* y;                   // [T][G][R]
     int64_t T;
+    // optional second (weight, output) pair over the same x (G = 1): y2 = x w2^T, launched
+    // together with the first where the tiled kernel applies
+    const void* w2 = nullptr;
+    void* y2 = nullptr;
 };
 hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s);
 

@@ -23,7 +23,7 @@ import torch
 
 from . import (AttnCfg, CompCfg, GprojCfg, IndexCfg, RopeCfg, dsv4_comp_state_bytes,
                dsv4_compress_prefill, dsv4_compress_step, dsv4_csa_attn_decode,
-               dsv4_csa_attn_decode_store, dsv4_csa_attn_prefill, dsv4_grouped_proj,
+               dsv4_csa_attn_decode_store, dsv4_csa_attn_prefill, dsv4_grouped_proj, dsv4_lane_proj,
                dsv4_index_topk, dsv4_index_workspace_bytes, dsv4_attn_workspace_bytes, dsv4_rope)
 
 
@@ -358,12 +358,12 @@ def compressor_lanes(x: torch.Tensor, w_kv: torch.Tensor, w_gate: torch.Tensor):
     g = x w_gate^T (the ratio-4 layer's wkv and wgate are [1024, 4096]: [MLXLM-1189]
     Thump604's fix list).  x [T, hidden]; w_kv, w_gate [coff*D, hidden]; returns a, g
     [T, coff*D], ready for dsv4_compress_prefill (one sequence's chunk) or, with one token
-    per sequence, dsv4_compress_step.  Two dsv4_grouped_proj calls with one group."""
+    per sequence, dsv4_compress_step.  One dsv4_lane_proj call (both products in one launch
+    from 33 tokens on)."""
     T, Kd = x.shape
     W = w_kv.shape[0]
     cfg = GprojCfg(1, Kd, W, x.dtype)
     a = torch.empty(T, W, dtype=x.dtype, device=x.device)
     g = torch.empty(T, W, dtype=x.dtype, device=x.device)
-    dsv4_grouped_proj(cfg, x.view(T, 1, Kd), w_kv.view(1, W, Kd), a.view(T, 1, W))
-    dsv4_grouped_proj(cfg, x.view(T, 1, Kd), w_gate.view(1, W, Kd), g.view(T, 1, W))
+    dsv4_lane_proj(cfg, x, w_kv, w_gate, a, g)
     return a, g

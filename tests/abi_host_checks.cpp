@@ -61,6 +61,11 @@ int main() {
     EXPECT(dsv4_rope(&rc, fake, neg, 1, 1, reinterpret_cast<float*>(fake), nullptr) == DSV4_EINVAL);
     dsv4_gproj_cfg gc{0, 4096, 1024, DSV4_BF16};
     EXPECT(dsv4_grouped_proj(&gc, fake, fake, fake, 8, nullptr) == DSV4_EINVAL);
+    dsv4_gproj_cfg lc{2, 4096, 1024, DSV4_BF16};                       // lanes take one group
+    EXPECT(dsv4_lane_proj(&lc, fake, fake, fake, fake, fake, 8, nullptr) == DSV4_EINVAL);
+    lc.groups = 1;
+    EXPECT(dsv4_lane_proj(&lc, fake, fake, nullptr, fake, fake, 8, nullptr) == DSV4_EINVAL);
+    EXPECT(dsv4_lane_proj(&lc, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == DSV4_OK);
     // trace bookkeeping
     int64_t n = -1;
     double ms = -1.0;

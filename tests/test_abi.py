@@ -225,6 +225,18 @@ def test_rope_and_projection_validation(L):
     assert proj(g, t=1 << 32) == EUNSUP
     assert proj(g, t=0, x=None) == 0
 
+    def lanes(cfg, x=FAKE, wk=FAKE, wg=FAKE, a=FAKE, gl=FAKE, t=8):
+        c = cfg.c()
+        return L.dsv4_lane_proj(ctypes.byref(c), x, wk, wg, a, gl, t, None)
+    lc = K.GprojCfg(groups=1, in_dim=4096, out_dim=1024)
+    assert lanes(K.GprojCfg(groups=2, in_dim=4096, out_dim=1024)) == EINVAL   # one group only
+    assert lanes(K.GprojCfg(groups=1, in_dim=0, out_dim=1024)) == EINVAL
+    assert lanes(lc, wg=None) == EINVAL
+    assert lanes(lc, a=None) == EINVAL
+    assert lanes(lc, t=-1) == EINVAL
+    assert lanes(lc, t=1 << 32) == EUNSUP
+    assert lanes(lc, t=0, x=None, wk=None, wg=None, a=None, gl=None) == 0
+
 
 def test_trace_calls(L):
     K.dsv4_trace_reset()

@@ -2,7 +2,8 @@
 RoPE of per-head vectors and its inverse (dsv4_rope), the grouped block-diagonal output
 projection (dsv4_grouped_proj) on all three of its kernels (up to 32 tokens: weight
 streaming; more: LDS-tiled MFMA; fp32 or other shapes: one thread per output), and the
-compressor lanes projected from hidden states by the same call with one group.
+compressor lanes projected from hidden states (dsv4_lane_proj: both lanes in one launch of
+the tiled kernel, each equal bit for bit to the one-group projection).
 
 Bars: RoPE as the compressed rows (bf16 within 2 ulp of the pair's norm, fp32 max-rel
 1e-5 per head); projection max-rel per (token, group) row 4e-3 in bf16 (two ulps of the
@@ -128,6 +129,35 @@ def test_output_path_matches_oracle(S):
         ref = oracle.grouped_out_proj(turned, w64).reshape(S, Gr, R)
         mr = G.max_rel_rows(G.f64(y[b]), ref)
         assert mr.max() <= 4e-3, f"sequence {b}: max-rel {mr.max():.3g}"
+
+
+@pytest.mark.parametrize("T", [8, 33, 300, 2048, 2049])
+def test_lane_proj_equals_two_projections(T):
+    """dsv4_lane_proj computes both lanes in one launch from 33 tokens on (up to 32: the
+    streaming kernel, one call per lane); either way each lane equals, bit for bit, the
+    one-group dsv4_grouped_proj of the same weight (same tiles, same arithmetic)."""
+    W, hid = 1024, 4096
+    x = synth.normal((T, hid), seed=61 + T, stream="hidden", dtype=torch.bfloat16, device="cuda")
+    wkv = synth.normal((W, hid), seed=61, stream="wkv", scale=hid ** -0.5, dtype=torch.bfloat16,
+                       device="cuda")
+    wg = synth.normal((W, hid), seed=61, stream="wgate", scale=hid ** -0.5, dtype=torch.bfloat16,
+                      device="cuda")
+    a, g = compressor_lanes(x, wkv, wg)
+    cfg = K.GprojCfg(1, hid, W, torch.bfloat16)
+    ra = torch.empty(T, 1, W, dtype=torch.bfloat16, device="cuda")
+    rg = torch.empty(T, 1, W, dtype=torch.bfloat16, device="cuda")
+    K.dsv4_grouped_proj(cfg, x.view(T, 1, hid), wkv.view(1, W, hid), ra)
+    K.dsv4_grouped_proj(cfg, x.view(T, 1, hid), wg.view(1, W, hid), rg)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), ra.view(T, W).view(torch.int16))
+    assert torch.equal(g.view(torch.int16), rg.view(T, W).view(torch.int16))
+    # and against the oracle on sampled tokens (first, last, a middle one)
+    for t in sorted({0, T // 2, T - 1}):
+        x64 = G.f64(x[t:t + 1])[:, None, :]
+        for got, w, n in ((a, wkv, "a"), (g, wg, "g")):
+            ref = oracle.grouped_out_proj(x64, G.f64(w)[None])
+            mr = G.max_rel_rows(G.f64(got[t:t + 1]), ref)
+            assert mr.max() <= 4e-3, f"token {t} lane {n}: max-rel {mr.max():.3g}"
 
 
 @pytest.mark.parametrize("T", [1, 8, 300], ids=["step", "b8", "chunk300"])
