@@ -807,7 +807,7 @@ def bench_output_path(args, seed=41):
         out[name] = entry
         del o, y
     # the ratio-4 compressor's lanes of a 2048-token chunk from hidden states (wkv, wgate
-    # [1024, 4096]): two one-group projections of 128 x 128 tiles
+    # [1024, 4096]): both one-group projections in one launch (dsv4_lane_proj)
     T, hid, W = args.chunk, 4096, spec.coff * spec.dim
     x = synth.normal((T, hid), seed=seed, stream="hidden", dtype=torch.bfloat16, device="cuda")
     wkv = synth.normal((W, hid), seed=seed, stream="wkv", scale=hid ** -0.5, dtype=torch.bfloat16,
@@ -819,21 +819,22 @@ def bench_output_path(args, seed=41):
     torch.cuda.synchronize()
     K.dsv4_trace_reset()
     K.dsv4_trace_enable(True)
-    for _ in range(10):
+    calls = 10
+    for _ in range(calls):
         compressor_lanes(x, wkv, wg)
     torch.cuda.synchronize()
     K.dsv4_trace_enable(False)
     gname = max((n for n in K.dsv4_trace_kernels() if n.startswith("gproj")),
                 key=lambda n: kernel_time(n)[0])
     n_g, ms_g = kernel_time(gname)
-    us = ms_g / n_g * 1e3
-    fl = 2.0 * T * W * hid
+    us = ms_g / calls * 1e3                        # kernel time per call (both lanes)
+    fl = 2.0 * 2.0 * T * W * hid                   # both products
     ach = fl / (us * 1e-6) / 1e12
     out["lanes_prefill_2048"] = {
-        "tokens": T, "us_per_call": 2 * us,
+        "tokens": T, "us_per_call": us, "launches_per_call": n_g / calls,
         "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": gname,
-                     "flops_per_launch": fl}}
+                     "flops_per_call": fl}}
     return out
 
 
@@ -850,7 +851,7 @@ COPY_CALIB_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_DECODE = os.path.join(PROFILES, "traffic_attn_decode_ctx65536_b8_ratio128.txt")
 TRAFFIC_PREFILL = os.path.join(PROFILES, "traffic_index_score_rs_ctx65536_chunk2048_ratio4.txt")
-TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_stream_decode_ctx262144_b4_stack.txt")
+TRAFFIC_STACK = os.path.join(PROFILES, "traffic_index_score_fused_decode_ctx262144_b4_stack.txt")
 TRAFFIC_DECODE_STEP = os.path.join(PROFILES, "traffic_step_decode_ctx65536_b8_ratio128.txt")
 TRAFFIC_STACK_STEP = os.path.join(PROFILES, "traffic_step_stack_decode_ctx262144_b4.txt")
 

@@ -857,8 +857,8 @@ __device__ __forceinline__ void idx_stream_block(const bf16* rows, int64_t blk, 
 }
 
 template <int WAVES, bool FUSE>
-__global__ void __launch_bounds__(64 * WAVES)
-index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+__device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, const SeqInts& pos0v,
+                                                        const SeqInts& n_rows) {
     constexpr int NT = 64 * WAVES;
     const int b = blockIdx.z;
     const int64_t s = blockIdx.y;
@@ -992,6 +992,21 @@ index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 }
 
+// The plain streamed scorer (score keys to the workspace) and the fused one (each workgroup
+// passes on its best rows): one body, two kernels, so each has a name of its own in traces.
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+index_score_stream_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    index_score_stream_body<WAVES, false>(a, pos0v, n_rows);
+}
+
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+index_score_fused_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    index_score_stream_body<WAVES, true>(a, pos0v, n_rows);
+}
+
+
 constexpr int kSelChunk = 8192;                       // rows per chunk of a split selection
 constexpr int kMergeThreads = 512;                    // workgroup of the merge stages
 static_assert(kSelChunk % 2048 == 0 && kSelChunk <= 512 * 64, "chunk: 512 threads x 4k keys");
@@ -1120,7 +1135,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 a.cutoff = f_cut + qoff * fp.groups;
                 a.n_groups = int(fp.groups);
                 a.m = fp.m;
-                DSV4_LAUNCH("index_score_fused", (index_score_stream_kernel<kStreamWaves, true>),
+                DSV4_LAUNCH("index_score_fused", (index_score_fused_kernel<kStreamWaves>),
                             dim3(unsigned(fp.groups), unsigned(j.S), nb), dim3(64 * kStreamWaves), 0, st,
                             a, pos, nr);
             } else {
@@ -1131,7 +1146,7 @@ hipError_t run(const IndexJob& j, hipStream_t st) {
                 if (bpw > (int64_t(1) << 20)) bpw = int64_t(1) << 20;   // rows_per_block fits an int
                 a.rows_per_block = int(bpw * 32 * kStreamWaves);
                 const unsigned sx = unsigned((nbt + bpw * kStreamWaves - 1) / (bpw * kStreamWaves));
-                DSV4_LAUNCH("index_score_stream", (index_score_stream_kernel<kStreamWaves, false>),
+                DSV4_LAUNCH("index_score_stream", (index_score_stream_kernel<kStreamWaves>),
                             dim3(sx, unsigned(j.S), nb), dim3(64 * kStreamWaves), 0, st, a, pos, nr);
             }
             hipError_t e = hipGetLastError();
