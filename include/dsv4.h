@@ -249,7 +249,7 @@ int dsv4_csa_attn_prefill(const dsv4_attn_cfg* cfg, const void* q, const void* k
 /* The layer's neighbours on either side of the attention.
  * Pages: mlx-lm PR #1189 (OmarB97's note 2 and stepnoy's patch: the rotary dims are the last
  * rd of each head, interleaved pairs turned by position * inv_freq; Thump604's fix list:
- * inverse output rotation of the post-attention rope dims); MTPLX PR #216 opening ("What V4
+ * the attention output's rotary dims turned back); MTPLX PR #216 opening ("What V4
  * adds": grouped output-LoRA, 8 groups of rank 1024) and "Decode path: reference-faithful
  * bf16 activation storage" item 2 (wo_a [8192, 4096]); deepseek-v41-mlx "Why this exists"
  * (the rope inverse on the attention output; wo_a block-diagonal). */

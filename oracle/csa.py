@@ -116,11 +116,13 @@ def compressor_rows(a, g, ape, gamma, inv_freq, *, ratio: int, overlap: bool, ep
                     store: str, work=np.float32, rows=None, token0: int = 0) -> np.ndarray:
     """Compressed rows of one sequence from its kv lane ``a`` and gate lane ``g``.
 
-    [MTPLX-216] "What V4 adds": a second, compressed KV cache built by learned gated pooling,
-    overlapping ratio-4 windows or non-overlapping ratio-128 windows.
+    [MTPLX-216] "What V4 adds": besides the sliding window, each such layer caches rows that
+    each summarise one window of tokens by learned gated pooling; at ratio 4 a window also
+    reaches back over its predecessor, at ratio 128 the windows are disjoint.
     [MLXLM-1189] Thump604's fixes: ratio-4 shapes ape (4, 1024), wkv/wgate (1024, 4096), i.e.
-    the overlapping compressor's lanes are 2*D wide; aidiffuser's indexer path: the overlap
-    transform folds the previous window into each row and pads it with -inf / 0 at the start.
+    the overlapping compressor's lanes are 2*D wide; aidiffuser's indexer path: with overlap
+    a row also pools the window before its own, and the first row's missing predecessor
+    counts as logit -inf, value 0.
     [MTPLX-216] "Decode path": pooling runs in fp32 and the row is cast back to the storage
     dtype before the norm; [MLXLM-1189] OmarB97 note 2: each pooled row is RoPE'd at its
     window-start position j*r before it is cached.
@@ -250,8 +252,8 @@ def csa_attention(q, kv, rows, sel, positions, *, window: int, ratio: int, sinks
                   scale: float, store: str, work=np.float32, kv_offset: int = 0) -> np.ndarray:
     """MQA attention of each query over its sliding window plus its compressed rows.
 
-    [MTPLX-216] "What V4 adds" and its opening: 64 query heads over one 512-dim latent that
-    is both key and value; a 128-token sliding window beside the compressed lane; per-head
+    [MTPLX-216] "What V4 adds" and its opening: 64 heads of queries share a single 512-wide
+    latent per key position, used as key and as value; a 128-token sliding window beside the compressed lane; per-head
     sink logits.  "Decode dispatch reduction" (A): the sink is one extra all-zero-V key
     column, so it enters the softmax denominator only.  [MLXLM-1189] stepnoy's patch: the
     selected compressed rows are attended together with the window keys; visibility and
@@ -309,7 +311,7 @@ def rope_heads(x, positions, inv_freq, *, inverse: bool = False, work=np.float32
 
     [MLXLM-1189] OmarB97's note 2 and stepnoy's patch: the rotary dims are the last ``rd`` of
     each head, turned in interleaved pairs by position * inv_freq (as ``rope_rows``);
-    Thump604's fix list: "inverse output rotation for the post-attention rope dims";
+    Thump604's fix list, the item on turning the attention output's rotary dims back;
     [V41-MLX] "Why this exists": the rope inverse on the attention output.  The inverse turns
     each pair back by the same angle: rotating at -position, since the fp32 angle
     fp32(-p) * inv_freq is exactly the negated fp32(p) * inv_freq.
@@ -327,8 +329,8 @@ def rope_heads(x, positions, inv_freq, *, inverse: bool = False, work=np.float32
 def grouped_out_proj(o, wo_a) -> np.ndarray:
     """Grouped (block-diagonal) output projection of the attention output.
 
-    [MTPLX-216] opening ("What V4 adds"): grouped output-LoRA on the attention output
-    projection, 8 groups of rank 1024; "Decode path: reference-faithful bf16 activation
+    [MTPLX-216] opening ("What V4 adds"): the attention output goes through a low-rank
+    projection split into 8 groups, each of rank 1024; "Decode path: reference-faithful bf16 activation
     storage", item 2: wo_a is [8192, 4096] (8 x 1024 outputs, 4096 inputs per group);
     [V41-MLX] "Why this exists": wo_a is block-diagonal.  READING: group g takes heads
     g*H/G .. (g+1)*H/G - 1 (their H/G * D values, head-major) and produces outputs

@@ -1,9 +1,9 @@
 // Gated-pooling compressor (one lane): rows for completed windows + frontier state update.
 //
-// Pages: MTPLX PR #216 "What V4 adds" (learned gated pooling, overlapping ratio-4 windows,
-// plain ratio-128 windows, compressed lanes maintained incrementally in prefill and decode);
+// Pages: MTPLX PR #216 "What V4 adds" (rows pooled with learned gates over windows of 4
+// that overlap or of 128 that do not; the lanes grow token by token in prefill and decode);
 // mlx-lm PR #1189 Thump604's fix list (ratio-4 lanes are 2*D wide), aidiffuser's indexer
-// path (the overlap transform folds the previous window in; the tail and previous window
+// path (each overlapping row also pools the window before its own; the tail and previous window
 // are carried across calls; absolute positions set the APE origin), stepnoy's index-space
 // fix (tail buffered and replayed, absolute position accumulates), OmarB97 note 2 (rows
 // RoPE'd at birth at j*r); MTPLX PR #216 "Decode path" (pool in fp32, cast to the storage

@@ -238,9 +238,9 @@ class CsaLayer:
 
 class SharedCsaLayer:
     """A layer that owns no compressor (V4.1 cross-layer KV sharing: [V41-MLX] "Why this
-    exists", the cross-layer sharing item: a few layers own the KV compressors and index keys
-    and every other layer consumes the most recent owner's caches; the index-source layers
-    among them score their own queries against the owner's keys).
+    exists", the cross-layer sharing item: only some layers run the compressors and build
+    index keys; each of the others reads what the last such layer before it built, and the
+    index-source layers among them score their own queries against those keys).
 
     ``owner`` is the CsaLayer whose compressed lanes this layer reads; ``spec`` gives this
     layer's own attention shape (heads, window, top-k) and must match the owner's latent

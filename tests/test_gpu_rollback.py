@@ -1,9 +1,9 @@
 """Exact trim for speculative decode on the GPU: decode draft tokens, take some back with
 CsaLayer.trim, decode other tokens.  Every output, selection and compressed row must equal,
 bit for bit, those of a layer that only ever saw the committed tokens, and must match the
-oracle run on the committed token stream (MTPLX PR #216, speculative-decode comment: the
-rewind is exact across a ratio-4 emission, the ratio-128 boundary and the indexer's
-dense-to-sparse threshold).  Needs a gfx950 GPU."""
+oracle run on the committed token stream (MTPLX PR #216, speculative-decode comment, on
+taking draft tokens back without approximation; checked here where a ratio-4 row is
+emitted, where a ratio-128 row completes and where the indexer starts to select).  Needs a gfx950 GPU."""
 import numpy as np
 import pytest
 import torch
