@@ -346,6 +346,24 @@ def bench_decode(args, seed=0):
     return res, (spec, seed)
 
 
+def bench_decode_batch_scan(args, batches=(32, 128)):
+    """The headline decode workload at larger batches (same layer, context and step count),
+    where the launches' fixed latency is spread over more sequences: graph time per step and
+    the whole step's fraction of HBM on its algorithmic bytes."""
+    out = []
+    for B in batches:
+        a = argparse.Namespace(**vars(args))
+        a.decode_batch = B
+        res, _ = bench_decode(a, seed=5)
+        out.append({"batch": B, "tok_s": res["tok_s"], "ms_per_step": res["ms_per_step"],
+                    "whole_step_hbm_frac": res["roofline"]["frac"],
+                    "bytes_per_step": res["bytes_per_step"]["total"],
+                    "kernel_us_per_step": res["roofline"]["kernel_us_per_step"],
+                    "kernels": res["kernels"]})
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_stack(args, seed=23, ratios=(0, 4, 128), topk=512, traffic_profile=None,
                 step_traffic_profile=None):
     """Decode of a layer stack at 262,144 tokens, batch 4.  The default is V4-Flash's head
@@ -1079,6 +1097,8 @@ def main():
     ap.add_argument("--cpu-decode-seqs", type=int, default=8)
     ap.add_argument("--cpu-prefill-queries", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-batch-scan", action="store_true",
+                    help="leave out the decode batch scan (batch 32 and 128 at the headline shape)")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-stack", action="store_true",
                     help="leave out the 262,144-token [0, 4, 128] stack decode sub-line")
@@ -1139,6 +1159,12 @@ def main():
         shared = bench_shared(args)
         log(f"[shared] graph {shared['tok_s']:.0f} tok/s, {shared['ms_per_step']:.4f} ms/step "
             f"({shared['us_per_layer']:.1f} us per layer); index scan {shared['roofline']['achieved']:.0f} GB/s")
+    scan = None
+    if args.only is None and dec is not None and not args.skip_batch_scan:
+        scan = bench_decode_batch_scan(args)
+        log("[decode batch scan] " + "; ".join(
+            f"batch {e['batch']}: {e['tok_s']:.0f} tok/s, {e['ms_per_step'] * 1e3:.1f} us/step, whole step "
+            f"{e['whole_step_hbm_frac'] * 100:.1f}% of HBM" for e in scan))
     if dec is None:                      # prefill-only profiler run
         print(json.dumps({"workload": "prefill", "prefill": pre}), flush=True)
         return
@@ -1180,6 +1206,7 @@ def main():
         "eager": dec["eager"],
         "kernels": dec["kernels"],
         "prefill": pre,
+        "decode_batch_scan": scan,
         "decode_262k_stack": stack,
         "decode_262k_pro_stack": pro,
         "decode_262k_shared_kv": shared,

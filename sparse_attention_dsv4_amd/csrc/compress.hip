@@ -22,8 +22,10 @@
 //   compress_state_kernel copies the new tokens of the last nw windows into the state.
 // The second runs after the first on the stream, because a row of this call may read a
 // state slot that the update overwrites.  With one new token per sequence (decode): the
-// frontier store alone, or, when a sequence completes a row, compress_pool_kernel (the store
-// and the pooling, spread over channel blocks) then compress_finish_kernel (norm and RoPE).
+// frontier store alone, or, when a sequence completes a row, the row kernel with the store
+// folded in (ratio 4: a row's few slots need no more than one workgroup), or for longer rows
+// compress_pool_kernel (the store and the pooling, spread over channel blocks) then
+// compress_finish_kernel (norm and RoPE).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,6 +50,7 @@ struct CompArgs {
     T* rows;
     int64_t row_cap;
     int64_t n_new;
+    int store_new;             // decode (n_new = 1): the row's workgroup also stores the token
 };
 
 // VEC consecutive storage elements (16 bytes, aligned; VEC = 1: one element anywhere): a raw
@@ -287,6 +290,18 @@ compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
     float* part = smem + a.D;
     const int b = blockIdx.y;
     const int lb = len_before.v[b];
+    if (a.store_new && blockIdx.x == 0) {
+        // the token's frontier slot: the row reads the state only at earlier tokens and takes
+        // this one from the lane, so the store cannot race it
+        const int W = a.coff * a.D;
+        const size_t st = size_t(2) * a.nw * a.r * W;
+        T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
+        T* sg = sa + size_t(a.nw) * a.r * W;
+        for (int c = threadIdx.x; c < W; c += blockDim.x) {
+            sa[c] = a.lane_a[size_t(b) * W + c];
+            sg[c] = a.lane_g[size_t(b) * W + c];
+        }
+    }
     const int j = lb / a.r + int(blockIdx.x);  // row index
     if (int64_t(j + 1) * a.r > lb + a.n_new) return;
     emit_row<T, VEC>(a, b, j, lb, zrow, part, red);
@@ -452,11 +467,30 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
                 if (e != hipSuccess) return e;
                 continue;
             }
-            // one (channel group, slot group) pair per thread: a wave of 64 / SG channel
-            // groups, or SG threads for one channel group
             const int vec = vec_ok<T>(j.D) ? kVec<T> : 1;
             int ncg, SG;
             slot_groups(j.D, vec, j.coff * j.r, ncg, SG);
+            a.store_new = 1;
+            if (ncg * SG <= kCompThreads) {
+                // a row of at most one pair per thread (ratio 4): the prefill row kernel, one
+                // workgroup per sequence, which also stores the token -- one launch
+                const size_t lds = size_t(j.D) * (1 + 3 * SG) * sizeof(float);
+                hipError_t e = vec > 1 ? allow_lds(compress_rows_kernel<T, kVec<T>>, lds)
+                                       : allow_lds(compress_rows_kernel<T, 1>, lds);
+                if (e != hipSuccess) return e;
+                if (vec > 1)
+                    DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, kVec<T>>), dim3(1, nb),
+                                dim3(kCompThreads), lds, s, a, lb);
+                else
+                    DSV4_LAUNCH("compress_rows", (compress_rows_kernel<T, 1>), dim3(1, nb),
+                                dim3(kCompThreads), lds, s, a, lb);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                continue;
+            }
+            // longer rows (ratio 128): the pooling spread over channel blocks, one
+            // (channel group, slot group) pair per thread -- a wave of 64 / SG channel groups,
+            // or SG threads for one channel group -- then the norm and RoPE
             const int CGW = SG >= 64 ? 1 : 64 / SG;
             const int nt = CGW * SG;
             const size_t lds = size_t(3) * nt * vec * sizeof(float);
@@ -493,6 +527,7 @@ hipError_t run(const CompressJob& j, hipStream_t s) {
         a.rows = static_cast<T*>(j.rows) + size_t(b0) * j.row_cap * j.D;
         a.row_cap = j.row_cap;
         a.n_new = j.n_new;
+        a.store_new = 0;
         if (max_rows > 0) {
             // LDS: the row, then the slot groups' states (ratio-4 rows: one group, 8 KB at D = 512)
             const int vec = vec_ok<T>(j.D) ? kVec<T> : 1;
