@@ -1039,9 +1039,14 @@ int mfma_splits(int64_t queries, int64_t nk_max, int* keys_per_split) {
 }
 
 // Decode key splits: about kDecodeWgs workgroups over (sequence, head group, split), each
-// split a whole number of 16-key subtiles.
+// split a whole number of 16-key subtiles.  Keys that fit one LDS chunk (a window-only layer,
+// a short context) take one split: the combine launch would cost more than it spreads.
 constexpr int kDecodeWgs = 256;
 int decode_splits(int batch, int64_t nk_max, int* keys_per_split) {
+    if (nk_max <= DKC) {
+        *keys_per_split = DKC;
+        return 1;
+    }
     const int64_t units = (nk_max + 15) / 16;
     int64_t want = (kDecodeWgs + 4 * batch - 1) / (4 * batch);
     if (want > MAX_SPLITS) want = MAX_SPLITS;
