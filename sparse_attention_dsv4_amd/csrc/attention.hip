@@ -279,7 +279,7 @@ __device__ __forceinline__ void lds_barrier() {
 // sources are known before the selection is compacted.  All key and token indices fit in 32
 // bits (the entry points cap positions below 2^31 and keys per query at 2^30).
 struct TileCtx {
-    int b, w, lane, mt, nt, l32, hi;
+    int b, w, lane;
     int nrow, kb;             // attended rows; first key of this workgroup's split (or chunk)
     int nwin, kbs;            // window tokens; selection rank held in codes[0]
     int t0, pos0;             // first window token; first token of this call
@@ -566,10 +566,6 @@ attn_prefill_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int tid = threadIdx.x;
     c.lane = tid & 63;
     c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-    c.mt = c.w >> 1;
-    c.nt = c.w & 1;
-    c.l32 = c.lane & 31;
-    c.hi = c.lane >> 5;
     const int b = c.b, lane = c.lane, l16 = lane & 15, g = lane >> 4;
     const int hq = c.w >> 1, nt = c.w & 1;
     const int head = DHG * hq + l16;
@@ -796,7 +792,6 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     const int tid = threadIdx.x;
     c.lane = tid & 63;
     c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-    c.mt = 0; c.nt = 0; c.l32 = c.lane & 31; c.hi = c.lane >> 5;
     const int b = c.b, w = c.w, lane = c.lane;
     const int l16 = lane & 15, g = lane >> 4;
     const int p = pos0v.v[b];             // one query: pos0 == p
