@@ -8,8 +8,7 @@
 //                        that split K and meet in LDS;
 //   gproj_tile_kernel    the same for more tokens (prefill): MFMA-bound 256 x 256 tiles of
 //                        8 waves (128 x 128 of 4 waves for smaller grids), both operands
-//                        staged in LDS by direct global-to-LDS copies, k blocks of 64
-//                        double-buffered;
+//                        staged in LDS by direct global-to-LDS copies, a ring of k blocks;
 //   gproj_generic_kernel any shape or fp32: one thread per output.
 // Every product accumulates in fp32 (v_mfma_f32_32x32x16_bf16 on the bf16 paths); outputs
 // are rounded once to the storage type.
@@ -125,22 +124,30 @@ __global__ void __launch_bounds__(64 * kSmallWaves) gproj_small_kernel(GprojArgs
 // More tokens: workgroup tile 64 WT tokens x 64 WRB rows of one group, 2 WT waves of
 // 64 x 32 WRB (2 x WRB MFMA blocks; C[token][row]): WT = WRB = 4 (256 x 256, 8 waves) where
 // that gives the chip about a workgroup per CU or more, WT = WRB = 2 (128 x 128, 4 waves)
-// for smaller grids.  k in blocks of 64, double-buffered in LDS.  A stage holds the tile's
-// token rows and weight rows of 128 bytes; the 16-byte chunk c of row r sits at chunk
-// c ^ ((r / 2) % 8), so the 16 rows of one MFMA operand read phase hit 16 different 16-byte
-// bank groups.  Token rows past T load row T - 1 (finite values whose outputs are not stored).
-constexpr int kTileK = 64, kTileStages = 2;
-constexpr int kRowB = kTileK * 2;                        // bytes per staged row
-constexpr int kCpr = kRowB / 16;                         // 16-byte chunks per row
-constexpr int kRowsPerOp = 1024 / kRowB;                 // rows per 1 KB copy
+// for smaller grids.  k in blocks of KD (64 or 128), ST of them resident in LDS as a ring.  A
+// stage holds the tile's token rows and weight rows of 2 KD bytes, the 16-byte chunks of each
+// row XOR-swizzled (see TileShape::swz) so the 16 rows of one MFMA operand read phase hit 16
+// different 16-byte bank groups.  Token rows past T load row T - 1 (finite values whose
+// outputs are not stored).
+constexpr int kTileK = 64;                               // k multiple every tile shape takes
+constexpr int kOperandLead = 1;                          // k steps of operands read ahead
 
-template <int WT, int WRB>
+template <int WT, int WRB, int ST, int KD>
 struct TileShape {
     static constexpr int waves = 2 * WT;
     static constexpr int T = 64 * WT, R = 64 * WRB;
-    static constexpr int stage_bytes = (T + R) * kRowB;
-    static constexpr int ops = (T + R) / kRowsPerOp / waves;   // 1 KB copies per wave per stage
-    static_assert((T + R) % (kRowsPerOp * waves) == 0, "whole copies per wave");
+    static constexpr int stages = ST;                          // k blocks resident in LDS
+    static constexpr int kd = KD;                              // k per block
+    static constexpr int row_bytes = KD * 2;                   // bytes per staged row
+    static constexpr int cpr = row_bytes / 16;                 // 16-byte chunks per row
+    static constexpr int rows_per_op = 1024 / row_bytes;       // rows per 1 KB copy
+    static constexpr int stage_bytes = (T + R) * row_bytes;
+    static constexpr int ops = (T + R) / rows_per_op / waves;  // 1 KB copies per wave per stage
+    static_assert(KD % kTileK == 0 && (KD == 64 || KD == 128), "k block of 64 or 128");
+    static_assert((T + R) % (rows_per_op * waves) == 0, "whole copies per wave");
+    static_assert(ST >= 2 && (ST - 2) * ops < 64, "copies in flight fit the wait counter");
+    // the 16 rows of one MFMA operand read phase land in 16 different 16-byte bank groups
+    __device__ static int swz(int row, int chunk) { return chunk ^ ((row / (16 / cpr)) % cpr); }
 };
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -161,9 +168,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ ((row / (16 / kCpr)) % kCpr); }
-
-// Copy k block kb of the tile into stage buffer buf: 1 KB copies of kRowsPerOp rows; wave w
+// Copy k block kb of the tile into stage buffer buf: 1 KB copies of rows_per_op rows; wave w
 // takes copies w, w + waves, ... (the token rows first, then the weight rows).
 template <class SH>
 __device__ __forceinline__ void tile_load(const GprojArgs& a, const bf16* wg, int g, int64_t t0, int r0, int kb,
@@ -172,25 +177,25 @@ __device__ __forceinline__ void tile_load(const GprojArgs& a, const bf16* wg, in
 #pragma unroll
     for (int i = 0; i < SH::ops; ++i) {
         const int op = w + SH::waves * i;
-        const int row = kRowsPerOp * op + lane / kCpr;   // row of the stage
-        const int c = tswz(row, lane % kCpr);            // logical chunk landing at lane % kCpr
+        const int row = SH::rows_per_op * op + lane / SH::cpr;   // row of the stage
+        const int c = SH::swz(row, lane % SH::cpr);      // logical chunk landing at lane % cpr
         const bf16* src;
         if (row < SH::T) {
             int64_t t = t0 + row;
             t = t < a.T ? t : a.T - 1;
-            src = a.x + (size_t(t) * a.G + g) * a.K + size_t(kb) * kTileK + 8 * c;
+            src = a.x + (size_t(t) * a.G + g) * a.K + size_t(kb) * SH::kd + 8 * c;
         } else {
             const int r = r0 + row - SH::T;
-            src = wg + (size_t(g) * a.R + r) * a.K + size_t(kb) * kTileK + 8 * c;
+            src = wg + (size_t(g) * a.R + r) * a.K + size_t(kb) * SH::kd + 8 * c;
         }
         dma16(src, buf + op * 1024);
     }
 }
 
-template <int WT, int WRB>
+template <int WT, int WRB, int ST, int KD>
 __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
-    using SH = TileShape<WT, WRB>;
-    __shared__ __attribute__((aligned(16))) unsigned char st[kTileStages][SH::stage_bytes];
+    using SH = TileShape<WT, WRB, ST, KD>;
+    __shared__ __attribute__((aligned(16))) unsigned char st[ST][SH::stage_bytes];
     // blockIdx.z: the group, or with a second pair (G = 1) which of the two products
     const bool second = a.w2 != nullptr && blockIdx.z == 1;
     const int g = a.w2 != nullptr ? 0 : int(blockIdx.z);
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 31, hh = lane >> 5;
     const int wt = w % WT, wr = w / WT;                  // wave tile: tokens 64 wt, rows 32 WRB wr
-    const int nk = a.K / kTileK;
+    const int nk = a.K / SH::kd;
     floatx16 acc[2][WRB];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -209,30 +214,45 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
         for (int v = 0; v < WRB; ++v)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
-    tile_load<SH>(a, wsel, g, t0, r0, 0, st[0]);
-    for (int kb = 0; kb < nk; ++kb) {
-        wait_vm<0>();                                    // block kb (the only copies in flight)
-        lds_barrier();                                   // block kb visible; kb-1 fully read
-        if (kb + 1 < nk) tile_load<SH>(a, wsel, g, t0, r0, kb + 1, st[(kb + 1) % kTileStages]);
-        const unsigned char* buf = st[kb % kTileStages];
 #pragma unroll
-        for (int j = 0; j < kTileK / 16; ++j) {          // MFMA k steps of this block
+    for (int s = 0; s < ST - 1; ++s)
+        if (s < nk) tile_load<SH>(a, wsel, g, t0, r0, s, st[s]);
+    for (int kb = 0; kb < nk; ++kb) {
+        // block kb has landed once at most the copies of the ST - 2 blocks behind it are
+        // outstanding (near the end, where fewer follow it, wait for every copy)
+        if (kb + ST - 2 < nk) wait_vm<(ST - 2) * SH::ops>(); else wait_vm<0>();
+        lds_barrier();                                   // block kb visible; kb-1 fully read
+        if (kb + ST - 1 < nk) tile_load<SH>(a, wsel, g, t0, r0, kb + ST - 1, st[(kb + ST - 1) % ST]);
+        const unsigned char* buf = st[kb % ST];
+        constexpr int NJ = SH::kd / 16;                  // MFMA k steps of this block
+        bf16x8 xa[NJ][2], wb[NJ][WRB];
+        auto load_step = [&](int j) {
             const int lc = 2 * j + hh;                   // logical chunk of this lane
-            bf16x8 xa[2], wb[WRB];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = 64 * wt + 32 * u + m;
-                xa[u] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
+                xa[j][u] = load_bf16x8(buf + row * SH::row_bytes + SH::swz(row, lc) * 16);
             }
 #pragma unroll
             for (int v = 0; v < WRB; ++v) {
                 const int row = SH::T + 32 * WRB * wr + 32 * v + m;
-                wb[v] = load_bf16x8(buf + row * kRowB + tswz(row, lc) * 16);
+                wb[j][v] = load_bf16x8(buf + row * SH::row_bytes + SH::swz(row, lc) * 16);
             }
+        };
+        // a k step's operands are read kOperandLead steps ahead of its MFMAs, so their LDS
+        // latency hides behind the MFMAs of the steps before (the scheduling barriers keep the
+        // compiler from moving each read next to its MFMA)
+#pragma unroll
+        for (int j = 0; j < kOperandLead; ++j) load_step(j);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (j + kOperandLead < NJ) load_step(j + kOperandLead);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int v = 0; v < WRB; ++v) acc[u][v] = mfma32x32x16(xa[u], wb[v], acc[u][v]);
+                for (int v = 0; v < WRB; ++v) acc[u][v] = mfma32x32x16(xa[j][u], wb[j][v], acc[u][v]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // C[token][row]: register i of lane l is token c_row(i, l), row l % 32
@@ -299,6 +319,29 @@ hipError_t launch_rope(const RopeJob& j, hipStream_t s) {
     return j.bf16 ? rope_run<bf16>(j, s) : rope_run<float>(j, s);
 }
 
+namespace {
+
+template <int WT, int WRB, int ST, int KD>
+hipError_t launch_tile_shape(const GprojArgs& a, int gz, hipStream_t s) {
+    using SH = TileShape<WT, WRB, ST, KD>;
+    const dim3 grid(unsigned((a.T + SH::T - 1) / SH::T), unsigned(a.R / SH::R), unsigned(gz));
+    DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<WT, WRB, ST, KD>), grid, dim3(64 * SH::waves), 0, s, a);
+    return hipGetLastError();
+}
+
+// The tiled product over gz grid layers (groups, or the two products of a pair): 256 x 256
+// tiles (two k blocks of 64 in LDS, 2 x 64 KB) where that gives about a workgroup per CU or
+// more; else 128 x 128 tiles, one workgroup per CU, with k blocks of 128 (two in LDS) when K
+// allows, else a ring of four blocks of 64 -- both keep 64-96 KB of copies in flight
+hipError_t launch_tiled(const GprojArgs& a, int gz, hipStream_t s) {
+    const int64_t big_tiles = (a.T + 255) / 256 * (a.R / 256) * gz;
+    if (a.R % 256 == 0 && big_tiles >= 256) return launch_tile_shape<4, 4, 2, 64>(a, gz, s);
+    if (a.K % 128 == 0) return launch_tile_shape<2, 2, 2, 128>(a, gz, s);
+    return launch_tile_shape<2, 2, 4, 64>(a, gz, s);
+}
+
+}  // namespace
+
 hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
     constexpr int kSmallK = 64 * kSmallWaves;          // k per KBW step of the workgroup
     if (j.w2 != nullptr) {
@@ -317,17 +360,7 @@ hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
         }
         GprojArgs a{1, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
                     static_cast<bf16*>(j.y), j.T, static_cast<const bf16*>(j.w2), static_cast<bf16*>(j.y2)};
-        using Big = TileShape<4, 4>;
-        using Small = TileShape<2, 2>;
-        const int64_t big_tiles = (j.T + Big::T - 1) / Big::T * (j.R / Big::R) * 2;
-        if (j.R % Big::R == 0 && big_tiles >= 256) {
-            const dim3 grid(unsigned((j.T + Big::T - 1) / Big::T), unsigned(j.R / Big::R), 2);
-            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<4, 4>), grid, dim3(64 * Big::waves), 0, s, a);
-        } else {
-            const dim3 grid(unsigned((j.T + Small::T - 1) / Small::T), unsigned(j.R / Small::R), 2);
-            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<2, 2>), grid, dim3(64 * Small::waves), 0, s, a);
-        }
-        return hipGetLastError();
+        return launch_tiled(a, 2, s);
     }
     if (j.bf16 && j.T <= kSmallMaxT && j.K % kSmallK == 0 && j.K <= 8 * kSmallK && j.R % 32 == 0) {
         GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
@@ -349,17 +382,7 @@ hipError_t launch_grouped_proj(const GprojJob& j, hipStream_t s) {
     if (j.bf16 && j.K % kTileK == 0 && j.R % 128 == 0) {
         GprojArgs a{j.G, j.K, j.R, static_cast<const bf16*>(j.x), static_cast<const bf16*>(j.w),
                     static_cast<bf16*>(j.y), j.T, nullptr, nullptr};
-        using Big = TileShape<4, 4>;
-        using Small = TileShape<2, 2>;
-        const int64_t big_tiles = (j.T + Big::T - 1) / Big::T * (j.R / Big::R) * j.G;
-        if (j.R % Big::R == 0 && big_tiles >= 256) {
-            const dim3 grid(unsigned((j.T + Big::T - 1) / Big::T), unsigned(j.R / Big::R), unsigned(j.G));
-            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<4, 4>), grid, dim3(64 * Big::waves), 0, s, a);
-        } else {
-            const dim3 grid(unsigned((j.T + Small::T - 1) / Small::T), unsigned(j.R / Small::R), unsigned(j.G));
-            DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<2, 2>), grid, dim3(64 * Small::waves), 0, s, a);
-        }
-        return hipGetLastError();
+        return launch_tiled(a, j.G, s);
     }
     const int64_t n = j.T * j.G * j.R;
     const unsigned blocks = unsigned((n + 255) / 256);

@@ -93,10 +93,15 @@ def test_grouped_proj_tiled(T):
 
 
 def test_grouped_proj_other_k():
-    """Smaller K on both MFMA kernels (K = 512 and 1536), and 128-row tiles (R = 384)."""
+    """Smaller K on both MFMA kernels (K = 512 and 1536), and 128-row tiles (R = 384).  The
+    128-row tiles take k blocks of 128 when K allows (K = 128: a single block) and otherwise a
+    ring of four blocks of 64, here with fewer blocks than the ring holds (K = 64, 192) and
+    more (K = 576)."""
     _proj_case(5, 2, 512, 64, torch.bfloat16, seed=7)
     _proj_case(300, 3, 1536, 256, torch.bfloat16, seed=8)
     _proj_case(40, 2, 512, 384, torch.bfloat16, seed=11)
+    for i, kd in enumerate((64, 128, 192, 576)):
+        _proj_case(70, 2, kd, 128, torch.bfloat16, seed=20 + i)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
