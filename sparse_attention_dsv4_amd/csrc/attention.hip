@@ -262,6 +262,7 @@ struct AttnMfmaArgs {
         const bf16* a;                    // [B][W] kv lane, then gate lane
         const bf16* g;
         int r, nw, W;
+        int vec;                          // W / 4 <= 256 and 16-byte aligned: vector copies
     } fr[2];
     int n_fr;
 };
@@ -817,28 +818,42 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
     const int nk = c.nrow + nwin;
     const size_t pbase = (size_t(b) * a.n_splits + split) * MH + DHG * hg;
-    if (split == 0 && hg == 0) {
-        // store the new latent in its ring slot.  Slot p % Wr holds token p - Wr, which this
-        // query does not read (its window is p-W+1 .. p, with p itself taken from kv_new),
-        // so the store cannot race the key loads of the other workgroups.
-        const uint4* src = reinterpret_cast<const uint4*>(c.kv_new);
-        uint4* dst = reinterpret_cast<uint4*>(const_cast<bf16*>(c.ring) + size_t(uint32_t(p) % c.W) * MD);
-        if (tid < MD / 8) dst[tid] = src[tid];
+    // The token's latent goes to its ring slot (workgroup split 0, head group 0) and, at a step
+    // that completes no row, its compressor lanes to their frontier slots (split 0, head groups
+    // 1 .. n_fr): loaded here, stored when the workgroup's attention is done, so these
+    // workgroups wait for no round trip of their own before their key copies.  Slot p % Wr
+    // holds token p - Wr, which this query does not read (its window is p-W+1 .. p, with p
+    // itself taken from kv_new), and nothing here reads the compressor state, so neither store
+    // races a read of this launch.
+    uint4 tok = make_uint4(0, 0, 0, 0);
+    uint4* tok_dst = nullptr;
+    if (split == 0 && hg == 0 && tid < MD / 8) {
+        tok = reinterpret_cast<const uint4*>(c.kv_new)[tid];
+        tok_dst = reinterpret_cast<uint4*>(const_cast<bf16*>(c.ring) + size_t(uint32_t(p) % c.W) * MD) + tid;
     }
     if (split == 0 && hg >= 1 && hg <= a.n_fr) {
-        // the compressor step of this token for lane hg - 1, at a step that completes no row:
-        // its kv and gate lanes go to the token's frontier slot (nothing here reads the state)
         const AttnMfmaArgs::Front f = hg == 1 ? a.fr[0] : a.fr[1];
         bf16* sa = f.state + size_t(b) * (size_t(2) * f.nw * f.r * f.W) + frontier_slot(p, f.r, f.nw, f.W);
         bf16* sg = sa + size_t(f.nw) * f.r * f.W;
         const bf16* la = f.a + size_t(b) * f.W;
         const bf16* lg = f.g + size_t(b) * f.W;
-        for (int c = tid; c < f.W; c += 256) {
-            sa[c] = la[c];
-            sg[c] = lg[c];
+        if (f.vec) {                                  // 16-byte vectors, one per thread
+            const int nv8 = f.W / 8;
+            if (tid < 2 * nv8) {
+                const bool gate = tid >= nv8;
+                const int i = gate ? tid - nv8 : tid;
+                tok = reinterpret_cast<const uint4*>(gate ? lg : la)[i];
+                tok_dst = reinterpret_cast<uint4*>(gate ? sg : sa) + i;
+            }
+        } else {
+            for (int c = tid; c < f.W; c += 256) {
+                sa[c] = la[c];
+                sg[c] = lg[c];
+            }
         }
     }
     if (kb0 >= nk) {
+        if (tok_dst != nullptr) *tok_dst = tok;
         if (tid < DHG) {
             a.part_ml[(pbase + tid) * 2 + 0] = -INFINITY;
             a.part_ml[(pbase + tid) * 2 + 1] = 0.f;
@@ -937,6 +952,8 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             default: decode_chunk_pv<4>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
         }
     }
+
+    if (tok_dst != nullptr) *tok_dst = tok;
 
     // denominator of head 16 hg + l%16: sum over the four lane groups
     l_run += __shfl_xor(l_run, 16, 64);
@@ -1097,6 +1114,9 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
             a.fr[f].r = fj.r;
             a.fr[f].nw = fj.nw;
             a.fr[f].W = fj.W;
+            const uintptr_t al = reinterpret_cast<uintptr_t>(fj.state) | reinterpret_cast<uintptr_t>(fj.lane_a) |
+                                 reinterpret_cast<uintptr_t>(fj.lane_g);
+            a.fr[f].vec = fj.W % 8 == 0 && fj.W / 4 <= 256 && al % 16 == 0;
         }
         float* ws = static_cast<float*>(j.ws);
         a.part_ml = ws;

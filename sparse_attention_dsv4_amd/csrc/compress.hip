@@ -281,6 +281,76 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
     finish_row<T>(a, rc, b, j, ss, zrow, red);
 }
 
+// A token's kv and gate lanes (W values each) copied into its frontier slot by threads
+// i0, i0 + step, ...: four values of each lane per thread are loaded before any is stored,
+// so up to 4 * step values cost one round trip (the stores may alias the loads as far as the
+// compiler knows, so a load placed after a store waits for it).
+template <typename T>
+__device__ __forceinline__ void copy_token_lanes(T* sa, T* sg, const T* la, const T* lg, int W, int i0, int step) {
+    for (int c0 = i0; c0 < W; c0 += 4 * step) {
+        T va[4], vg[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + k * step;
+            if (c < W) {
+                va[k] = la[c];
+                vg[k] = lg[c];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + k * step;
+            if (c < W) {
+                sa[c] = va[k];
+                sg[c] = vg[k];
+            }
+        }
+    }
+}
+
+// A token's two lanes between an early load and a late store into its frontier slot, so the
+// load's round trip overlaps the workgroup's other work: up to 4 values of each lane per
+// thread in registers (wider lanes are copied at once by copy_token_lanes).
+template <typename T>
+struct HeldLanes {
+    T va[4], vg[4];
+    T* sa = nullptr;
+    T* sg = nullptr;
+    int W = 0, i0 = 0, step = 0;
+    bool held = false;
+    __device__ void begin(T* sa_, T* sg_, const T* la, const T* lg, int W_, int i0_, int step_) {
+        sa = sa_;
+        sg = sg_;
+        W = W_;
+        i0 = i0_;
+        step = step_;
+        held = W <= 4 * step;
+        if (!held) {
+            copy_token_lanes(sa, sg, la, lg, W, i0, step);
+            return;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = i0 + k * step;
+            if (c < W) {
+                va[k] = la[c];
+                vg[k] = lg[c];
+            }
+        }
+    }
+    __device__ void finish() const {
+        if (!held) return;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = i0 + k * step;
+            if (c < W) {
+                sa[c] = va[k];
+                sg[c] = vg[k];
+            }
+        }
+    }
+};
+
 template <typename T, int VEC>
 __global__ void __launch_bounds__(kCompThreads)
 compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
@@ -290,28 +360,29 @@ compress_rows_kernel(CompArgs<T> a, SeqInts len_before) {
     float* part = smem + a.D;
     const int b = blockIdx.y;
     const int lb = len_before.v[b];
+    // the token's frontier slot (decode): the row reads the state only at earlier tokens and
+    // takes this one from the lane, so the store cannot race it; stored after the row
+    HeldLanes<T> tok;
     if (a.store_new && blockIdx.x == 0) {
-        // the token's frontier slot: the row reads the state only at earlier tokens and takes
-        // this one from the lane, so the store cannot race it
         const int W = a.coff * a.D;
-        const size_t st = size_t(2) * a.nw * a.r * W;
-        T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
-        T* sg = sa + size_t(a.nw) * a.r * W;
-        for (int c = threadIdx.x; c < W; c += blockDim.x) {
-            sa[c] = a.lane_a[size_t(b) * W + c];
-            sg[c] = a.lane_g[size_t(b) * W + c];
-        }
+        T* sa = a.state + size_t(b) * (size_t(2) * a.nw * a.r * W) + frontier_slot(lb, a.r, a.nw, W);
+        tok.begin(sa, sa + size_t(a.nw) * a.r * W, a.lane_a + size_t(b) * W, a.lane_g + size_t(b) * W, W,
+                  int(threadIdx.x), kCompThreads);
     }
     const int j = lb / a.r + int(blockIdx.x);  // row index
-    if (int64_t(j + 1) * a.r > lb + a.n_new) return;
+    if (int64_t(j + 1) * a.r > lb + a.n_new) {
+        tok.finish();
+        return;
+    }
     emit_row<T, VEC>(a, b, j, lb, zrow, part, red);
+    tok.finish();
 }
 
 // A decode step in two launches when some sequence completes a row.  compress_pool_kernel:
 // one workgroup per (block of channel groups, sequence) pools its channels exactly as
-// emit_row does and stores the rounded pooled values in the row's place; the first
-// workgroup of each sequence also stores the token in the frontier (the row reads the state
-// only at earlier tokens and takes this token from the lane, so the store cannot race it).
+// emit_row does and stores the rounded pooled values in the row's place; the workgroups of a
+// sequence also store the token in the frontier (the row reads the state only at earlier
+// tokens and takes this token from the lane, so the store cannot race it).
 // compress_finish_kernel: one workgroup per emitting sequence reads the pooled row back and
 // finishes it (finish_row, the same channel-to-thread mapping as emit_row).
 template <typename T, int VEC>
@@ -321,16 +392,17 @@ compress_pool_kernel(CompArgs<T> a, SeqInts len_before) {
     const int b = blockIdx.y;
     const int lb = len_before.v[b];
     const int W = a.coff * a.D;
-    if (blockIdx.x == 0) {
-        const size_t st = size_t(2) * a.nw * a.r * W;
-        T* sa = a.state + size_t(b) * st + frontier_slot(lb, a.r, a.nw, W);
-        T* sg = sa + size_t(a.nw) * a.r * W;
-        for (int c = threadIdx.x; c < W; c += blockDim.x) {
-            sa[c] = a.lane_a[size_t(b) * W + c];
-            sg[c] = a.lane_g[size_t(b) * W + c];
-        }
+    // the token's frontier slot, spread over the sequence's workgroups; stored after the pooling
+    HeldLanes<T> tok;
+    {
+        T* sa = a.state + size_t(b) * (size_t(2) * a.nw * a.r * W) + frontier_slot(lb, a.r, a.nw, W);
+        tok.begin(sa, sa + size_t(a.nw) * a.r * W, a.lane_a + size_t(b) * W, a.lane_g + size_t(b) * W, W,
+                  int(blockIdx.x * blockDim.x + threadIdx.x), int(gridDim.x * blockDim.x));
     }
-    if ((lb + 1) % a.r != 0) return;
+    if ((lb + 1) % a.r != 0) {
+        tok.finish();
+        return;
+    }
     const int j = lb / a.r;
     int ncg, SG;
     slot_groups(a.D, VEC, a.coff * a.r, ncg, SG);
@@ -354,6 +426,7 @@ compress_pool_kernel(CompArgs<T> a, SeqInts len_before) {
     const int c0 = int(blockIdx.x) * CW;
     for (int c = threadIdx.x; c < CW && c0 + c < a.D; c += blockDim.x)
         row[c0 + c] = from_f32<T>(merge_part(part, SG, CW, c));
+    tok.finish();
 }
 
 template <typename T>
@@ -391,11 +464,8 @@ compress_state_kernel(CompArgs<T> a, SeqInts len_before) {
     const size_t st = size_t(2) * a.nw * a.r * W;
     const size_t src = (size_t(b) * a.n_new + size_t(t - lb)) * W;
     T* sa = a.state + size_t(b) * st + frontier_slot(t, a.r, a.nw, W);
-    T* sg = sa + size_t(a.nw) * a.r * W;
-    for (int c = threadIdx.x; c < W; c += blockDim.x) {
-        sa[c] = a.lane_a[src + c];
-        sg[c] = a.lane_g[src + c];
-    }
+    copy_token_lanes(sa, sa + size_t(a.nw) * a.r * W, a.lane_a + src, a.lane_g + src, W, int(threadIdx.x),
+                     int(blockDim.x));
 }
 
 // The frontier store of a decode step alone (no row completes): one workgroup per sequence.
@@ -405,13 +475,8 @@ frontier_store_kernel(FrontierJob f, SeqInts pos) {
     const int b = blockIdx.x;
     const size_t st = size_t(2) * f.nw * f.r * f.W;
     T* sa = static_cast<T*>(f.state) + size_t(b) * st + frontier_slot(pos.v[b], f.r, f.nw, f.W);
-    T* sg = sa + size_t(f.nw) * f.r * f.W;
-    const T* la = static_cast<const T*>(f.lane_a) + size_t(b) * f.W;
-    const T* lg = static_cast<const T*>(f.lane_g) + size_t(b) * f.W;
-    for (int c = threadIdx.x; c < f.W; c += blockDim.x) {
-        sa[c] = la[c];
-        sg[c] = lg[c];
-    }
+    copy_token_lanes(sa, sa + size_t(f.nw) * f.r * f.W, static_cast<const T*>(f.lane_a) + size_t(b) * f.W,
+                     static_cast<const T*>(f.lane_g) + size_t(b) * f.W, f.W, int(threadIdx.x), int(blockDim.x));
 }
 
 // Dynamic LDS beyond the default 64 KB must be allowed per kernel and device before its
