@@ -194,20 +194,27 @@ __device__ __forceinline__ float merge_part(const float* part, int SG, int D, in
     return as / ls;
 }
 
-// Per-thread constants of the row epilogue for channels tid + k*NT: gamma and the RoPE
-// frequency, loaded when the workgroup starts so their latency overlaps the pooling.
+// Per-thread constants of the row epilogue for channels tid + k*NT: gamma (raw, converted
+// where it is used) and the RoPE frequency, loaded when the workgroup starts so their
+// latency overlaps the pooling.  The loads sit under a workgroup-uniform guard and read an
+// in-bounds (clamped) element in every lane: a conversion or a per-lane select inside the
+// guard would make each block wait for its load before the next is issued.
 constexpr int kChan = kMaxDim / kCompThreads;
+template <typename T>
 struct RowConst {
-    float gam[kChan], frq[kChan];
+    T gam[kChan];
+    float frq[kChan];
 };
 template <typename T>
-__device__ __forceinline__ void load_row_const(const CompArgs<T>& a, RowConst& rc) {
+__device__ __forceinline__ void load_row_const(const CompArgs<T>& a, RowConst<T>& rc) {
     const int r0 = a.D - a.rd;
 #pragma unroll
     for (int k = 0; k < kChan; ++k) {
-        const int c = int(threadIdx.x) + k * kCompThreads;
-        rc.gam[k] = c < a.D ? to_f32(a.gamma[c]) : 0.f;
-        rc.frq[k] = c < a.D && c >= r0 ? a.inv_freq[(c - r0) >> 1] : 0.f;
+        if (k * kCompThreads >= a.D) break;
+        int c = int(threadIdx.x) + k * kCompThreads;
+        c = c < a.D ? c : a.D - 1;
+        rc.gam[k] = a.gamma[c];
+        rc.frq[k] = a.rd > 0 ? a.inv_freq[c >= r0 ? (c - r0) >> 1 : 0] : 0.f;
     }
 }
 
@@ -215,7 +222,7 @@ __device__ __forceinline__ void load_row_const(const CompArgs<T>& a, RowConst& r
 // squares (channels tid, tid + NT, ...) in ss: RMSNorm * gamma (rounded), RoPE of the last rd
 // dims at position j*r (rounded), stored.
 template <typename T>
-__device__ __forceinline__ void finish_row(const CompArgs<T>& a, const RowConst& rc, int b, int j, float ss,
+__device__ __forceinline__ void finish_row(const CompArgs<T>& a, const RowConst<T>& rc, int b, int j, float ss,
                                            float* zrow, float* red) {
     constexpr int NT = kCompThreads;
     const int D = a.D, tid = threadIdx.x;
@@ -224,7 +231,7 @@ __device__ __forceinline__ void finish_row(const CompArgs<T>& a, const RowConst&
 #pragma unroll
     for (int k = 0; k < kChan; ++k) {
         const int c = tid + k * NT;
-        if (c < D) zrow[c] = round_to<T>(zrow[c] / den * rc.gam[k]);
+        if (c < D) zrow[c] = round_to<T>(zrow[c] / den * to_f32(rc.gam[k]));
     }
     __syncthreads();
     const int r0 = D - a.rd;
@@ -255,7 +262,7 @@ __device__ __forceinline__ void emit_row(const CompArgs<T>& a, int b, int j, int
                                          float* zrow, float* part, float* red) {
     constexpr int NT = kCompThreads;
     const int D = a.D, tid = threadIdx.x;
-    RowConst rc;
+    RowConst<T> rc;
     load_row_const(a, rc);
     int ncg, SG;
     slot_groups(D, VEC, a.coff * a.r, ncg, SG);
@@ -438,7 +445,7 @@ compress_finish_kernel(CompArgs<T> a, SeqInts len_before) {
     const int lb = len_before.v[b];
     if ((lb + 1) % a.r != 0) return;
     const int j = lb / a.r;
-    RowConst rc;
+    RowConst<T> rc;
     load_row_const(a, rc);
     const T* row = a.rows + (size_t(b) * a.row_cap + size_t(j)) * a.D;
     float ss = 0.f;
