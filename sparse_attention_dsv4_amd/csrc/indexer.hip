@@ -422,6 +422,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int 
         if (above < rem && above + h >= rem) {
             sh[0] = t * per + i;
             sh[1] = rem - above;
+            sh[2] = h;
         }
         above += h;
     }
@@ -445,7 +446,11 @@ struct RegSelect {
     int rem;                   // keys == thr to take, lowest positions first
 };
 
-template <int KPT, int NT>
+// EXACT = false: the returned threshold may instead be one below the lowest key of a bucket
+// whose keys are all taken (rem = 0), once a pass finds its bucket's count equal to what is
+// still needed -- the same set of keys, in one or two passes instead of three -- for
+// callers that only compact with it.
+template <int KPT, int NT, bool EXACT = true>
 __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, int k,
                                           uint32_t* hist, int* tmp, int* sh) {
     constexpr int G = KPT / 4;
@@ -463,6 +468,7 @@ __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, i
     find_bucket<NT>(hist, 2048, k, tmp, sh);
     const uint32_t d1 = uint32_t(sh[0]);
     int rem = sh[1];
+    if (!EXACT && sh[2] == rem && d1 > 0) return RegSelect{(d1 << 21) - 1u, 0};
     for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 2: bits 20..10 of the keys in bucket d1
@@ -477,6 +483,7 @@ __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, i
     find_bucket<NT>(hist, 2048, rem, tmp, sh);
     const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
     rem = sh[1];
+    if (!EXACT && sh[2] == rem && pre > 0) return RegSelect{(pre << 10) - 1u, 0};
     for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
     // pass 3: bits 9..0 of the keys with prefix (d1, d2)
@@ -758,7 +765,7 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     }
     const int ngv = __builtin_amdgcn_readfirstlane(
         max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a position below n
-    const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.k, hist, tmp, sh);
+    const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.k, hist, tmp, sh);
     reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
         if (MODE == SEL_CHUNK) okey[slot] = key[e];
         out[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
@@ -982,7 +989,7 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
             key[4 * i + 3] = j + 3 < n ? v.w : 0u;
         }
         const int ngv = __builtin_amdgcn_readfirstlane(max(0, min(G, (n - w * 64 * KPT + 255) / 256)));
-        const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.m, hist, tmp, sh);
+        const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.m, hist, tmp, sh);
         uint32_t rest = reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
             ck[slot] = key[e];
             cr[slot] = int32_t(row0 + pos);
