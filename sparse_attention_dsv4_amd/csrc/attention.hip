@@ -778,8 +778,113 @@ __device__ __forceinline__ void decode_chunk_pv(const float* sx, const unsigned 
     }
 }
 
+// The chunk loop of a split that spans several chunks: two LDS buffers of CK = 64 keys.  At
+// the start of chunk ci (every wave being done with chunk ci - 1, whose buffer chunk ci + 1
+// takes), the selection of chunk ci + 1 is compacted and its copies issued -- wave w copies
+// subtile w -- and then chunk ci is scored while they land: each wave waits only for its own
+// copies of chunk ci (those of chunk ci + 1, issued after them, may stay in flight), the
+// scores meet in LDS, and every wave takes the softmax and its dims of P*V as in the
+// one-chunk path.
+template <int CK>
+__device__ __forceinline__ void decode_db_chunks(const AttnMfmaArgs& a, TileCtx& c, const int32_t (&selv)[SEL_PER_THREAD],
+                                                 int32_t* codes, int* wsum, unsigned char* kbuf,
+                                                 unsigned char* qs, float* sx, int b, int hg, int nv, int nwin,
+                                                 int kb0, int ke, float& m_run, float& l_run, floatx4 (&o)[8]) {
+    const int w = c.w, lane = c.lane, l16 = lane & 15, g = lane >> 4;
+    const int nch = (ke - kb0 + CK - 1) / CK;
+    auto chunk_keys = [&](int ci) { return ke - (kb0 + ci * CK) < CK ? ke - (kb0 + ci * CK) : CK; };
+    // copies of chunk ci into its buffer: lane j < 16 finds the source of row 16 w + j (rows
+    // past the chunk's keys copy its last key: finite values whose scores are masked); an odd
+    // subtile count leaves the second half of the last P*V step, whose rows are zeroed
+    auto issue = [&](int ci) {
+        unsigned char* buf = kbuf + (ci & 1) * CK * KPITCH;
+        const int cb = kb0 + ci * CK, nkt = chunk_keys(ci);
+        const int nsub = (nkt + 15) >> 4, nks = (nkt + 31) >> 5;
+        if (w < nsub) {
+            uint64_t src = 0;
+            const int row = 16 * w + (lane & 15);
+            if (lane < 16) src = reinterpret_cast<uint64_t>(key_src(c, codes, cb + (row < nkt ? row : nkt - 1)));
+            const uint32_t plo = uint32_t(src), phi = uint32_t(src >> 32);
+            unsigned char* dst = buf + 16 * w * KPITCH;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint64_t sp = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(plo), j))) |
+                                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(phi), j))) << 32);
+                dma16(reinterpret_cast<const void*>(sp), uint32_t(lane) * 16, dst + j * KPITCH);
+            }
+        }
+        if (2 * nks > nsub && (nsub & 3) == w) {
+#pragma unroll 4
+            for (int j = 0; j < 16; ++j) store16(buf + (16 * nsub + j) * KPITCH + lane * 16, make_uint4(0, 0, 0, 0));
+        }
+    };
+    {
+        // q rows (4 per wave), then chunk 0 (its selection was compacted with the split's start)
+        const bf16* qg = a.q + (size_t(b) * MH + DHG * hg) * MD;
+#pragma unroll
+        for (int i = 0; i < DHG / 4; ++i)
+            dma16(qg + size_t(w + 4 * i) * MD, uint32_t(lane) * 16, qs + (w + 4 * i) * QPITCH);
+        issue(0);
+    }
+    for (int ci = 0; ci < nch; ++ci) {
+        if (ci > 0) __syncthreads();          // every wave is done with chunk ci - 1 and the scores
+        const bool more = ci + 1 < nch;
+        int own_next = 0;
+        if (more) {
+            const int cb = kb0 + (ci + 1) * CK;
+            c.kb = cb;
+            c.kbs = cb > nwin ? cb - nwin : 0;
+            if (a.sel != nullptr) compact_selection(selv, a.k, nv, c.kbs, CK, codes, wsum);
+            issue(ci + 1);
+            own_next = ((chunk_keys(ci + 1) + 15) >> 4) > w;
+        }
+        const int nkt = chunk_keys(ci);
+        const int nsub = (nkt + 15) >> 4, nks = (nkt + 31) >> 5;
+        const int own = nsub > w;
+        if (ci == 0) {
+            // this wave's q rows precede its copies of chunks 0 and 1
+            const int after = own + own_next;
+            if (after == 2) wait_vm_n<32>(); else if (after == 1) wait_vm_n<16>(); else wait_vm_n<0>();
+            lds_barrier();                    // every wave's q rows have landed
+        }
+        const unsigned char* buf = kbuf + (ci & 1) * CK * KPITCH;
+        if (own) {
+            if (own_next) wait_vm_n<16>(); else wait_vm_n<0>();   // this wave's rows of chunk ci
+            bf16x8 qb[MD / 32];               // Q^T: lane l holds head 16 hg + l%16, dims 32 ks + 8 g
+#pragma unroll
+            for (int ks = 0; ks < MD / 32; ++ks) qb[ks] = load_bf16x8(qs + l16 * QPITCH + ks * 64 + 16 * g);
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            const unsigned char* kr = buf + (16 * w + l16) * KPITCH + 16 * g;
+            bf16x8 ka[MD / 32];
+#pragma unroll
+            for (int ks = 0; ks < MD / 32; ++ks) ka[ks] = load_bf16x8(kr + ks * 64);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < MD / 32; ks += 2) {
+                s0 = mfma16x16x32(ka[ks], qb[ks], s0);
+                s1 = mfma16x16x32(ka[ks + 1], qb[ks + 1], s1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            *reinterpret_cast<float4*>(sx + l16 * SXP + 16 * w + 4 * g) =
+                make_float4((s0[0] + s1[0]) * a.scale_log2, (s0[1] + s1[1]) * a.scale_log2,
+                            (s0[2] + s1[2]) * a.scale_log2, (s0[3] + s1[3]) * a.scale_log2);
+        }
+        lds_barrier();                        // chunk ci's rows, zero rows and scores are in LDS
+        if (nks == 1)
+            decode_chunk_pv<1>(sx, buf, l16, g, w, nkt, ci == 0, m_run, l_run, o);
+        else
+            decode_chunk_pv<2>(sx, buf, l16, g, w, nkt, ci == 0, m_run, l_run, o);
+    }
+}
+
+// CK = DKC: a chunk of up to 128 keys at a time, copied, then scored (splits of one chunk);
+// CK = 64: two buffers of 64 keys, each chunk's copies issued while the chunk before it is
+// scored, for splits that span several chunks (large batches).
+template <int CK>
 __global__ void __launch_bounds__(256)
 attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
+    static_assert(CK == DKC || CK == DKC / 2, "one 128-key chunk or two 64-key buffers");
+    constexpr bool DB = CK < DKC;
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[DKC * KPITCH];
     __shared__ __attribute__((aligned(16))) unsigned char qs[DHG * QPITCH];
     __shared__ __attribute__((aligned(16))) float sx[DHG * SXP];   // scaled scores [head][key]
@@ -787,9 +892,21 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     __shared__ int wsum[8];
 
     TileCtx c;
+    int hg = blockIdx.y;                  // heads 16 hg .. 16 hg + 15
+    int split = blockIdx.x;
     c.b = blockIdx.z;
-    const int hg = blockIdx.y;            // heads 16 hg .. 16 hg + 15
-    const int split = blockIdx.x;
+    if constexpr (DB) {
+        // workgroup i runs on XCD i mod 8: the four head groups of a (split, sequence), which
+        // read the same key rows, are given ids of one residue so they share an XCD's L2
+        const uint32_t ns = gridDim.x, units = ns * gridDim.z;
+        if ((units & 7) == 0) {
+            const uint32_t id = blockIdx.x + ns * (blockIdx.y + gridDim.y * blockIdx.z);
+            const uint32_t j = id >> 3, unit = (id & 7) + 8 * (j >> 2);
+            hg = int(j & 3);
+            split = int(unit % ns);
+            c.b = int(unit / ns);
+        }
+    }
     const int tid = threadIdx.x;
     c.lane = tid & 63;
     c.w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
@@ -813,7 +930,7 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     int32_t selv[SEL_PER_THREAD];
     if (a.sel != nullptr) {
         load_selection(a.sel + size_t(b) * a.k, a.k, selv);
-        c.nrow = compact_selection(selv, a.k, nv, c.kbs, a.keys_per_split < DKC ? a.keys_per_split : DKC,
+        c.nrow = compact_selection(selv, a.k, nv, c.kbs, a.keys_per_split < CK ? a.keys_per_split : CK,
                                    codes, wsum);
     }
     const int nk = c.nrow + nwin;
@@ -869,6 +986,9 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
         for (int i = 0; i < 4; ++i) o[m][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;     // l_run: this lane's keys 8 g + e of every k-step
 
+    if constexpr (DB) {
+        decode_db_chunks<CK>(a, c, selv, codes, wsum, kbuf, qs, sx, b, hg, nv, nwin, kb0, ke, m_run, l_run, o);
+    } else {
     for (int cb = kb0; cb < ke; cb += DKC) {
         const bool first = cb == kb0;
         if (!first) {
@@ -951,6 +1071,7 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             case 3: decode_chunk_pv<3>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
             default: decode_chunk_pv<4>(sx, kbuf, l16, g, w, nkt, first, m_run, l_run, o); break;
         }
+    }
     }
 
     if (tok_dst != nullptr) *tok_dst = tok;
@@ -1123,8 +1244,13 @@ hipError_t run_mfma(const AttnJob& j, hipStream_t st) {
         a.part_o = ws + size_t(nb) * j.S * a.n_splits * MH * 2;
         hipError_t e;
         if (decode) {
-            DSV4_LAUNCH("attn_decode", attn_decode_kernel, dim3(unsigned(a.n_splits), MH / DHG, nb), dim3(256),
-                               0, st, a, pos, nr);
+            // splits longer than one 128-key chunk take the double-buffered 64-key chunks
+            if (a.keys_per_split > DKC)
+                DSV4_LAUNCH("attn_decode", attn_decode_kernel<DKC / 2>, dim3(unsigned(a.n_splits), MH / DHG, nb),
+                            dim3(256), 0, st, a, pos, nr);
+            else
+                DSV4_LAUNCH("attn_decode", attn_decode_kernel<DKC>, dim3(unsigned(a.n_splits), MH / DHG, nb),
+                            dim3(256), 0, st, a, pos, nr);
         } else {
             DSV4_LAUNCH("attn_prefill", attn_prefill_kernel, dim3(unsigned(a.n_splits), unsigned(j.S), nb), dim3(PTHREADS),
                                0, st, a, pos, nr);

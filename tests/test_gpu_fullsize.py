@@ -5,7 +5,8 @@ The layer is driven exactly as bench.py drives it (same seeds, prefix builder, b
 and call sequence), and sampled outputs are checked against the oracle one by one:
   * decode, ratio-128 layer, batch 8, context 65,536 (512 rows + 128-token window per query):
     sampled rows against the oracle compressor; every sequence's output of three decode steps
-    against the oracle attention over the GPU's rows;
+    against the oracle attention over the GPU's rows; the same at batches 32 and 128 (the
+    batch scan), on sampled sequences;
   * prefill, ratio-4 layer with the indexer, the 2048-token chunk 63,488 -> 65,536: sampled
     rows of both lanes, then for sampled queries the top-512 over ~16K visible rows (exact up
     to the 1e-5 band) and the attention output.
@@ -61,9 +62,13 @@ def _check_rows(spec, seed, gpu_rows, b, js, index_lane=False):
                             spec.rope_dim)
 
 
-def test_fullsize_decode_64k_batch8_ratio128():
+@pytest.mark.parametrize("B", [8, 32, 128])
+def test_fullsize_decode_64k_ratio128(B):
+    """The decode benchmark's layer and context at batch 8 (splits of one LDS chunk) and at
+    the batch scan's 32 and 128 (splits of 320 and 640 keys: double-buffered 64-key chunks,
+    the head groups of a split grouped on one XCD); sampled sequences against the oracle."""
     spec = LayerSpec(ratio=128, indexer=False, topk=0)
-    seed, B, L, steps = 0, 8, 65536, 3               # bench_decode's seed, batch and context
+    seed, L, steps = 0, 65536, 3                     # bench_decode's seed and context
     params = SC.layer_params(spec, seed, device="cuda")
     layer = CsaLayer(spec, B, L + steps + 8, params, device="cuda", max_chunk=spec.window)
     bench.build_prefix(layer, spec, seed, L)
@@ -73,14 +78,15 @@ def test_fullsize_decode_64k_batch8_ratio128():
         outs.append(layer.decode({k: v[:, 0].contiguous() for k, v in t.items()}).cpu())
     torch.cuda.synchronize()
     rows = layer.rows.cpu()
-    for b in (0, 5, 7):
+    for b in (0, 5, B - 1):
         _check_rows(spec, seed, rows, b, [0, 1, 255, 510, 511])
     par = _params64(spec, seed)
     worst = 0.0
+    seqs = range(B) if B <= 8 else sorted({0, 1, B // 2, B - 1})
     for i in range(steps):
         p = L + i
         nv = oracle.visible_rows(p, spec.ratio)
-        for b in range(B):
+        for b in seqs:
             tk = _lanes(spec, seed, b, p - spec.window + 1, p + 1, ["q", "kv"])
             ref = oracle.csa_attention(tk["q"][-1:], tk["kv"], G.f64(rows[b, :nv]), None, [p],
                                        window=spec.window, ratio=spec.ratio, sinks=par["sinks"],
@@ -88,7 +94,7 @@ def test_fullsize_decode_64k_batch8_ratio128():
             mr = G.max_rel_rows(G.f64(outs[i][b]), ref[0]).max()
             worst = max(worst, mr)
             assert mr <= 2e-2, f"step {i} sequence {b}: max-rel {mr:.3g}"
-    print(f"  decode outputs: worst per-head max-rel {worst:.3g} over {steps * B} queries x 64 heads")
+    print(f"  decode outputs: worst per-head max-rel {worst:.3g} over {steps * len(seqs)} queries x 64 heads")
 
 
 def test_fullsize_prefill_chunk_64k_ratio4():
