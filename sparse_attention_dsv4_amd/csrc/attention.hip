@@ -16,12 +16,13 @@
 // mfma kernels (bf16, 64 heads, 512 latent), all on v_mfma_f32_16x16x32_bf16 with the key
 // rows copied straight from memory into LDS tiles: prefill runs one workgroup of 8 waves per
 // (query, key split) over 64-key tiles; decode runs one workgroup per (sequence, group of 16
-// heads, key split) holding the whole split in LDS.  The softmax is in base 2 with fp32 max
-// and sum; P is rounded to bf16 before P*V (the pages' reference kernel does the same, MTPLX
-// PR #216 "Decode path").  A query whose key list is split over several workgroups writes
-// partials (fp32 max and sum; the unnormalised output in bf16 for decode, fp32 for prefill)
-// that attn_combine_kernel merges with the sink; a query handled by one workgroup normalises
-// and writes its output.
+// heads, key split) holding a split of up to 128 keys in LDS whole, and longer splits (large
+// batches) in two 64-key buffers, the next filling while one is scored.  The softmax is in
+// base 2 with fp32 max and sum; P is rounded to bf16 before P*V (the pages' reference kernel
+// does the same, MTPLX PR #216 "Decode path").  A query whose key list is split over several
+// workgroups writes partials (fp32 max and sum; the unnormalised output in bf16 for decode,
+// fp32 for prefill) that attn_combine_kernel merges with the sink; a query handled by one
+// workgroup normalises and writes its output.
 //
 // The window ring holds Wr >= W slots (token t in slot t % Wr): the W attended tokens plus
 // those retained for rollback.  The ring update runs after the attention kernel on the
