@@ -41,18 +41,31 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeArgs<T> a, SeqInts pos0) 
     const int hc = item / P, i = item % P;
     const int64_t s = blockIdx.y;
     const int b = blockIdx.z;
+    T* base = a.x + (size_t(b) * a.S + size_t(s)) * a.H * a.D + (a.D - a.rd) + 2 * i;
+    const int h0 = hc * kRopeHeadsPerThread;
+    const int nh = a.H - h0 < kRopeHeadsPerThread ? a.H - h0 : kRopeHeadsPerThread;
+    // every head's pair is loaded before any is stored (in place: a load after a store to the
+    // same array would wait for it, one round trip per head); heads past H load the last one,
+    // unconditionally, so no load sits in a branch that waits for it
+    float x0[kRopeHeadsPerThread], x1[kRopeHeadsPerThread];
+#pragma unroll
+    for (int k = 0; k < kRopeHeadsPerThread; ++k) {
+        const T* px = base + size_t(k < nh ? h0 + k : a.H - 1) * a.D;
+        x0[k] = to_f32(px[0]);
+        x1[k] = to_f32(px[1]);
+    }
     // fp32 angle of the fp32 position, as the compressor's rows
     const float p = float(int64_t(pos0.v[b]) + s);
     float sn, cs;
     sincosf(p * a.inv_freq[i], &sn, &cs);
     if (a.inverse) sn = -sn;
-    T* base = a.x + (size_t(b) * a.S + size_t(s)) * a.H * a.D + (a.D - a.rd) + 2 * i;
-    const int h1 = (hc + 1) * kRopeHeadsPerThread < a.H ? (hc + 1) * kRopeHeadsPerThread : a.H;
-    for (int h = hc * kRopeHeadsPerThread; h < h1; ++h) {
-        T* px = base + size_t(h) * a.D;
-        const float x0 = to_f32(px[0]), x1 = to_f32(px[1]);
-        px[0] = from_f32<T>(x0 * cs - x1 * sn);
-        px[1] = from_f32<T>(x0 * sn + x1 * cs);
+#pragma unroll
+    for (int k = 0; k < kRopeHeadsPerThread; ++k) {
+        if (k < nh) {
+            T* px = base + size_t(h0 + k) * a.D;
+            px[0] = from_f32<T>(x0[k] * cs - x1[k] * sn);
+            px[1] = from_f32<T>(x0[k] * sn + x1[k] * cs);
+        }
     }
 }
 
