@@ -343,12 +343,16 @@ def test_v4_attention_with_ragged_selection():
     assert mr.max() <= 2e-2, mr.max()
 
 
-@pytest.mark.parametrize("spec_name", ["small_bf16", "v4_ratio4"])
+@pytest.mark.parametrize("spec_name", ["small_bf16", "v4_ratio4", "v4_ratio4_long"])
 def test_batch_beyond_one_launch_slice(spec_name):
     """130 sequences: every launcher walks the batch in slices of 128 sequences, so
     sequences 127, 128 and 129 sit on either side of a slice edge (the generic kernels at the
-    small shape, sparse regime; the MFMA kernels at the V4 shape, dense regime)."""
-    spec, chunks, n_dec = (SMALL_BF16, [120, 50], 30) if spec_name == "small_bf16" else (V4_R4, [40], 4)
+    small shape, sparse regime; the MFMA kernels at the V4 shape, dense regime).  The long
+    case's decode steps attend 204 keys: the 128-sequence slice as one split per query (the
+    double-buffered 64-key chunks, head groups grouped by XCD), the 2-sequence slice as
+    13 one-chunk splits."""
+    spec, chunks, n_dec = {"small_bf16": (SMALL_BF16, [120, 50], 30), "v4_ratio4": (V4_R4, [40], 4),
+                           "v4_ratio4_long": (V4_R4, [300], 4)}[spec_name]
     res = G.run_gpu(spec, 21, 130, chunks, n_dec)
     T = sum(chunks) + n_dec
     pos = sorted(set(list(range(0, T, 7)) + list(range(T - 6, T))))
