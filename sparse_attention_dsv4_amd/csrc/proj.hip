@@ -134,21 +134,20 @@ __global__ void __launch_bounds__(64 * kSmallWaves) gproj_small_kernel(GprojArgs
     }
 }
 
-// More tokens: workgroup tile 64 WT tokens x 64 WRB rows of one group, 2 WT waves of
-// 64 x 32 WRB (2 x WRB MFMA blocks; C[token][row]): WT = WRB = 4 (256 x 256, 8 waves) where
-// that gives the chip about a workgroup per CU or more, WT = WRB = 2 (128 x 128, 4 waves)
-// for smaller grids.  k in blocks of KD (64 or 128), ST of them resident in LDS as a ring.  A
-// stage holds the tile's token rows and weight rows of 2 KD bytes, the 16-byte chunks of each
-// row XOR-swizzled (see TileShape::swz) so the 16 rows of one MFMA operand read phase hit 16
-// different 16-byte bank groups.  Token rows past T load row T - 1 (finite values whose
-// outputs are not stored).
+// More tokens: workgroup tile of 32 TM WT tokens x 32 RN WR rows of one group, WT x WR waves,
+// each a block of 32 TM tokens x 32 RN rows (TM x RN MFMA blocks; C[token][row]).  k in
+// blocks of KD (64 or 128), ST of them resident in LDS as a ring.  A stage holds the tile's
+// token rows and weight rows of 2 KD bytes, the 16-byte chunks of each row XOR-swizzled (see
+// TileShape::swz) so the 16 rows of one MFMA operand read phase hit 16 different 16-byte
+// bank groups.  Token rows past T load row T - 1 (finite values whose outputs are not
+// stored).
 constexpr int kTileK = 64;                               // k multiple every tile shape takes
 constexpr int kOperandLead = 1;                          // k steps of operands read ahead
 
-template <int WT, int WRB, int ST, int KD>
+template <int WT, int WR, int TM, int RN, int ST, int KD>
 struct TileShape {
-    static constexpr int waves = 2 * WT;
-    static constexpr int T = 64 * WT, R = 64 * WRB;
+    static constexpr int waves = WT * WR;
+    static constexpr int T = 32 * TM * WT, R = 32 * RN * WR;
     static constexpr int stages = ST;                          // k blocks resident in LDS
     static constexpr int kd = KD;                              // k per block
     static constexpr int row_bytes = KD * 2;                   // bytes per staged row
@@ -205,9 +204,9 @@ __device__ __forceinline__ void tile_load(const GprojArgs& a, const bf16* wg, in
     }
 }
 
-template <int WT, int WRB, int ST, int KD>
-__global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
-    using SH = TileShape<WT, WRB, ST, KD>;
+template <int WT, int WR, int TM, int RN, int ST, int KD>
+__global__ void __launch_bounds__(64 * WT * WR) gproj_tile_kernel(GprojArgs a) {
+    using SH = TileShape<WT, WR, TM, RN, ST, KD>;
     __shared__ __attribute__((aligned(16))) unsigned char st[ST][SH::stage_bytes];
     // blockIdx.z: the group, or with a second pair (G = 1) which of the two products
     const bool second = a.w2 != nullptr && blockIdx.z == 1;
@@ -218,13 +217,13 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
     const int r0 = int(blockIdx.y) * SH::R;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = lane & 31, hh = lane >> 5;
-    const int wt = w % WT, wr = w / WT;                  // wave tile: tokens 64 wt, rows 32 WRB wr
+    const int wt = w % WT, wr = w / WT;                  // wave tile: tokens 32 TM wt, rows 32 RN wr
     const int nk = a.K / SH::kd;
-    floatx16 acc[2][WRB];
+    floatx16 acc[TM][RN];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < TM; ++u)
 #pragma unroll
-        for (int v = 0; v < WRB; ++v)
+        for (int v = 0; v < RN; ++v)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[u][v][i] = 0.f;
 #pragma unroll
@@ -238,17 +237,17 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
         if (kb + ST - 1 < nk) tile_load<SH>(a, wsel, g, t0, r0, kb + ST - 1, st[(kb + ST - 1) % ST]);
         const unsigned char* buf = st[kb % ST];
         constexpr int NJ = SH::kd / 16;                  // MFMA k steps of this block
-        bf16x8 xa[NJ][2], wb[NJ][WRB];
+        bf16x8 xa[NJ][TM], wb[NJ][RN];
         auto load_step = [&](int j) {
             const int lc = 2 * j + hh;                   // logical chunk of this lane
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int row = 64 * wt + 32 * u + m;
+            for (int u = 0; u < TM; ++u) {
+                const int row = 32 * TM * wt + 32 * u + m;
                 xa[j][u] = load_bf16x8(buf + row * SH::row_bytes + SH::swz(row, lc) * 16);
             }
 #pragma unroll
-            for (int v = 0; v < WRB; ++v) {
-                const int row = SH::T + 32 * WRB * wr + 32 * v + m;
+            for (int v = 0; v < RN; ++v) {
+                const int row = SH::T + 32 * RN * wr + 32 * v + m;
                 wb[j][v] = load_bf16x8(buf + row * SH::row_bytes + SH::swz(row, lc) * 16);
             }
         };
@@ -262,22 +261,22 @@ __global__ void __launch_bounds__(128 * WT) gproj_tile_kernel(GprojArgs a) {
             if (j + kOperandLead < NJ) load_step(j + kOperandLead);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < TM; ++u)
 #pragma unroll
-                for (int v = 0; v < WRB; ++v) acc[u][v] = mfma32x32x16(xa[j][u], wb[j][v], acc[u][v]);
+                for (int v = 0; v < RN; ++v) acc[u][v] = mfma32x32x16(xa[j][u], wb[j][v], acc[u][v]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     // C[token][row]: register i of lane l is token c_row(i, l), row l % 32
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < TM; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int64_t t = t0 + 64 * wt + 32 * u + c_row(i, lane);
+            const int64_t t = t0 + 32 * TM * wt + 32 * u + c_row(i, lane);
             if (t >= a.T) continue;
-            bf16* yr = ysel + (size_t(t) * a.G + g) * a.R + r0 + 32 * WRB * wr + m;
+            bf16* yr = ysel + (size_t(t) * a.G + g) * a.R + r0 + 32 * RN * wr + m;
 #pragma unroll
-            for (int v = 0; v < WRB; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
+            for (int v = 0; v < RN; ++v) yr[32 * v] = from_f32<bf16>(acc[u][v][i]);
         }
 }
 
@@ -334,23 +333,27 @@ hipError_t launch_rope(const RopeJob& j, hipStream_t s) {
 
 namespace {
 
-template <int WT, int WRB, int ST, int KD>
+// 256 x 256 tiles: 8 waves of 64 tokens x 128 rows
+constexpr int kBigWT = 4, kBigWR = 2, kBigTM = 2, kBigRN = 4;
+
+template <int WT, int WR, int TM, int RN, int ST, int KD>
 hipError_t launch_tile_shape(const GprojArgs& a, int gz, hipStream_t s) {
-    using SH = TileShape<WT, WRB, ST, KD>;
+    using SH = TileShape<WT, WR, TM, RN, ST, KD>;
     const dim3 grid(unsigned((a.T + SH::T - 1) / SH::T), unsigned(a.R / SH::R), unsigned(gz));
-    DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<WT, WRB, ST, KD>), grid, dim3(64 * SH::waves), 0, s, a);
+    DSV4_LAUNCH("gproj_tile", (gproj_tile_kernel<WT, WR, TM, RN, ST, KD>), grid, dim3(64 * SH::waves), 0, s, a);
     return hipGetLastError();
 }
 
 // The tiled product over gz grid layers (groups, or the two products of a pair): 256 x 256
 // tiles (two k blocks of 64 in LDS, 2 x 64 KB) where that gives about a workgroup per CU or
-// more; else 128 x 128 tiles, one workgroup per CU, with k blocks of 128 (two in LDS) when K
-// allows, else a ring of four blocks of 64 -- both keep 64-96 KB of copies in flight
+// more; else 128 x 128 tiles of 4 waves (64 x 64 each), one workgroup per CU, with k blocks
+// of 128 (two in LDS) when K allows, else a ring of four blocks of 64 -- both keep 64-96 KB
+// of copies in flight
 hipError_t launch_tiled(const GprojArgs& a, int gz, hipStream_t s) {
     const int64_t big_tiles = (a.T + 255) / 256 * (a.R / 256) * gz;
-    if (a.R % 256 == 0 && big_tiles >= 256) return launch_tile_shape<4, 4, 2, 64>(a, gz, s);
-    if (a.K % 128 == 0) return launch_tile_shape<2, 2, 2, 128>(a, gz, s);
-    return launch_tile_shape<2, 2, 4, 64>(a, gz, s);
+    if (a.R % 256 == 0 && big_tiles >= 256) return launch_tile_shape<kBigWT, kBigWR, kBigTM, kBigRN, 2, 64>(a, gz, s);
+    if (a.K % 128 == 0) return launch_tile_shape<2, 2, 2, 2, 2, 128>(a, gz, s);
+    return launch_tile_shape<2, 2, 2, 2, 4, 64>(a, gz, s);
 }
 
 }  // namespace
