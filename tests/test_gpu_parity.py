@@ -343,6 +343,47 @@ def test_v4_attention_with_ragged_selection():
     assert mr.max() <= 2e-2, mr.max()
 
 
+@pytest.mark.parametrize("B", [8, 64])
+def test_v4_decode_with_ragged_selection(B):
+    """Decode over caller-made selections with -1 entries in the middle, rows not yet visible
+    and negative codes: 200 attended rows + the 128-token window per query.  At batch 64 a
+    query's ~330 keys are one split, several 64-key chunks each compacted from the selection
+    (the double-buffered path); at batch 8, one-chunk splits."""
+    import sparse_attention_dsv4_amd as K
+    import synth.csa as SC
+    from sparse_attention_dsv4_amd.layer import CsaLayer
+    spec = V4_R4
+    seed, T = 16, 1200
+    params = SC.layer_params(spec, seed, device="cuda")
+    layer = CsaLayer(spec, B, T + 8, params, device="cuda")
+    layer.prefill(SC.batch_token_inputs(spec, seed, [0] * B, T, device="cuda"))
+    p = T
+    nv = oracle.visible_rows(p, 4)
+    tok = SC.batch_token_inputs(spec, seed, [p] * B, 1, device="cuda", fields=["q", "kv"])
+    rng = np.random.default_rng(1)
+    sel = np.full((B, spec.topk), -1, dtype=np.int32)
+    for b in range(B):
+        row = np.full(spec.topk, -1, dtype=np.int32)
+        slots = np.sort(rng.choice(spec.topk, size=260, replace=False))
+        row[slots[:200]] = np.sort(rng.choice(nv, size=200, replace=False))
+        row[slots[200:230]] = nv + rng.integers(0, 50, size=30)         # not yet visible
+        row[slots[230:]] = -7
+        sel[b] = row
+    out = torch.empty(B, spec.heads, spec.dim, dtype=spec.dtype, device="cuda")
+    K.dsv4_csa_attn_decode(spec.attn_cfg(), tok["q"][:, 0].contiguous(), tok["kv"][:, 0].contiguous(),
+                           layer.ring, layer.rows, torch.from_numpy(sel).cuda(), [nv] * B, [p] * B,
+                           params["sinks"], out, layer.ws_attn)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    for b in (range(B) if B <= 8 else (0, 1, B // 2, B - 1)):
+        tk, par = G.oracle_inputs(spec, seed, b, p + 1)
+        r = sel[b][(sel[b] >= 0) & (sel[b] < nv)]
+        ref_sel = np.concatenate([r, np.full(spec.topk - len(r), -1)])[None]
+        ref = G.oracle_attention(spec, tk, par, G.f64(layer.rows[b, :nv]), ref_sel, [p])
+        mr = G.max_rel_rows(G.f64(out[b])[None], ref)
+        assert mr.max() <= 2e-2, f"sequence {b}: max-rel {mr.max():.3g}"
+
+
 @pytest.mark.parametrize("spec_name", ["small_bf16", "v4_ratio4", "v4_ratio4_long"])
 def test_batch_beyond_one_launch_slice(spec_name):
     """130 sequences: every launcher walks the batch in slices of 128 sequences, so
