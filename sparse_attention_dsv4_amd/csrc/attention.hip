@@ -1095,10 +1095,18 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
             a.part_ml[(pbase + l16) * 2 + 0] = m_run;
             a.part_ml[(pbase + l16) * 2 + 1] = l_tot;
         }
-        // bf16 partial output (the kernel's run time is dominated by writing these back)
+        // bf16 partial output, written through to memory (relaxed system-scope stores carry
+        // the coherence bits), so the write-back at the kernel's end finds fewer dirty lines
+        // in the L2 (launch 9.07 -> 8.88 us at 64K, batch 8); only the combine launch after
+        // this one reads them
         bf16* po = reinterpret_cast<bf16*>(a.part_o) + (pbase + l16) * MD + 128 * w + 4 * g;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) *reinterpret_cast<uint2*>(po + 16 * m) = pack4_bf16(o[m][0], o[m][1], o[m][2], o[m][3]);
+        for (int m = 0; m < 8; ++m) {
+            const uint2 v = pack4_bf16(o[m][0], o[m][1], o[m][2], o[m][3]);
+            __hip_atomic_store(reinterpret_cast<unsigned long long*>(po + 16 * m),
+                               (static_cast<unsigned long long>(v.y) << 32) | v.x, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 }
 
