@@ -275,10 +275,10 @@ def test_pro_stack_262k_batch4(ratio):
 @pytest.mark.parametrize("case", ["dense_ratio4_b8", "selected_b16"])
 def test_decode_splits_longer_than_one_lds_chunk(case):
     """Decode splits that hold more keys than one LDS chunk (128 keys), so the attention
-    workgroup runs several chunks with the running max carried between them: a dense ratio-4
-    lane at batch 8 (1500 rows + window: 208-key splits, chunks 128 + 80), and the indexer's
-    top-512 at batch 16 (640 keys: 160-key splits, the selection compacted again for the
-    second chunk)."""
+    workgroup runs several 64-key chunks (two buffers) with the running max carried between
+    them: a dense ratio-4 lane at batch 8 (1500 rows + window: 240-key splits, four chunks),
+    and the indexer's top-512 at batch 16 (640 keys: 160-key splits, three chunks, the
+    selection compacted again for each)."""
     if case == "dense_ratio4_b8":
         spec = LayerSpec(ratio=4, indexer=False, topk=0)
         seed, B, L, steps = 31, 8, 6000, 2
