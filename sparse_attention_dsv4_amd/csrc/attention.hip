@@ -896,9 +896,11 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     int hg = blockIdx.y;                  // heads 16 hg .. 16 hg + 15
     int split = blockIdx.x;
     c.b = blockIdx.z;
-    if constexpr (DB) {
+    {
         // workgroup i runs on XCD i mod 8: the four head groups of a (split, sequence), which
-        // read the same key rows, are given ids of one residue so they share an XCD's L2
+        // read the same key rows, are given ids of one residue so they share an XCD's L2 (in
+        // the plain order they share one only when the split count is a multiple of 8: at 7
+        // splits each row was fetched four times over the fabric)
         const uint32_t ns = gridDim.x, units = ns * gridDim.z;
         if ((units & 7) == 0) {
             const uint32_t id = blockIdx.x + ns * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -1183,8 +1185,8 @@ int mfma_splits(int64_t queries, int64_t nk_max, int* keys_per_split) {
 // Decode key splits: about kDecodeWgs workgroups over (sequence, head group, split), each
 // split a whole number of 16-key subtiles.  Keys that fit one LDS chunk (a window-only layer,
 // a short context) take one split: the combine launch would cost more than it spreads.  224
-// rather than one per CU: at batch 8 (640 keys) 7 splits of 96 keys finish sooner than 8 of 80
-// (8.7 against 8.9 us per launch), fewer partials being written and merged.
+// rather than one per CU: at batch 8 (640 keys) 7 splits of 96 keys finish a little sooner
+// than 8 of 80 (8.8 against 8.9 us per launch), fewer partials being written and merged.
 constexpr int kDecodeWgs = 224;
 int decode_splits(int batch, int64_t nk_max, int* keys_per_split) {
     if (nk_max <= DKC) {
