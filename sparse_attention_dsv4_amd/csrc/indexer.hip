@@ -382,41 +382,52 @@ bool use_index_mfma(bool bf16_, int Hi, int di) { return bf16_ && Hi == IH && di
 // > T, plus the lowest-placed keys == T until k are taken.  Row-order compaction makes the
 // output ascending without a sort; the lowest-placed ties are the lowest rows.
 
-// Exclusive prefix sum over a workgroup of NT threads; `tmp` holds NT / 64 ints.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    __syncthreads();
-    if (lane == 63) tmp[w] = x;
-    __syncthreads();
-    int add = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-        tot += tmp[i];
-        add += i < w ? tmp[i] : 0;
-    }
-    *total = tot;
-    return x - v + add;
+// Inclusive prefix sum over the lanes of a wave in DPP steps: shifts by 1, 2, 4 and 8 lanes
+// within each row of 16 lanes, then the last lane of row 0 (2) added to row 1 (3), and the
+// last lane of row 1 to rows 2 and 3.  Lanes a step does not reach add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Largest (MAX) or smallest u32 over the lanes of a wave: within each row of 16 lanes by
+// DPP, then the four rows' values read back by the scalar unit.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t v) {
+    auto pick = [](uint32_t x, uint32_t y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+    v = pick(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xb1, 0xf, 0xf, false)));    // quad_perm [1,0,3,2]
+    v = pick(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4e, 0xf, 0xf, false)));    // quad_perm [2,3,0,1]
+    v = pick(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x124, 0xf, 0xf, false)));   // row_ror:4
+    v = pick(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x128, 0xf, 0xf, false)));   // row_ror:8
+    const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 0));
+    const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+    const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 32));
+    const uint32_t r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+    return pick(pick(r0, r1), pick(r2, r3));
 }
 
 // Given a histogram of `bins` bins and the count `rem` still needed from the keys it covers,
-// find the bin holding the rem-th largest key.  Writes the bin and the count still needed
-// inside it to sh[0], sh[1].  NT threads, bins a multiple of NT.
+// find the bin holding the rem-th largest key.  Writes the bin, the count still needed inside
+// it and the bin's count to sh[0..2].  NT threads, bins a multiple of NT; `tmp` holds NT / 64
+// ints.  Thread t sums bins [t per, (t + 1) per); the counts above it are the later waves'
+// totals plus the lanes above it in its own wave (a DPP scan): two barriers.
 template <int NT>
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, int bins, int rem, int* tmp, int* sh) {
     const int per = bins / NT;                        // 1 to 4 bins per thread
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int part = 0;
     for (int i = 0; i < per; ++i) part += int(hist[t * per + i]);
-    int total;
-    const int excl = block_excl_scan<NT>(part, tmp, &total);
-    int above = total - excl - part;                  // keys in bins above this thread's bins
+    const int x = wave_incl_scan(part);
+    if (lane == 63) tmp[w] = x;
+    __syncthreads();
+    int above = __builtin_amdgcn_readlane(x, 63) - x;  // this wave's bins above this thread's
+#pragma unroll
+    for (int v = 0; v < NT / 64; ++v) above += v > w ? tmp[v] : 0;
     for (int i = per - 1; i >= 0; --i) {
         const int h = int(hist[t * per + i]);
         if (above < rem && above + h >= rem) {
@@ -446,57 +457,101 @@ struct RegSelect {
     int rem;                   // keys == thr to take, lowest positions first
 };
 
+// Words of LDS the threshold search uses: the three passes' histograms (2048, 2048 and
+// 1024 bins), all cleared at the start, and a spare word per lane.
+constexpr int kHistBins = 2048 + 2048 + 1024;
+constexpr int kHistWords = kHistBins + 64;
+
+// The k-th largest key by radix select over digits fitted to the keys that can matter.
+// When k <= NT, the smallest of the threads' largest keys, q, is at or below the k-th
+// largest key (the NT threads' largest keys are NT keys >= q), so keys below q are left out
+// and the digits are those of key - q over the range [q, max]: pass 1 bins the keys >= q by
+// (key - q) >> s1 (s1 fitting max - q to 11 bits), pass 2 bins the keys of the chosen bin by
+// the next 11 bits, pass 3 by the rest (at most 10).  Near the threshold the bins are narrow,
+// so one pass often suffices.  `tmp` holds 2 NT / 64 ints, `hist` kHistWords (16-byte
+// aligned).
 // EXACT = false: the returned threshold may instead be one below the lowest key of a bucket
 // whose keys are all taken (rem = 0), once a pass finds its bucket's count equal to what is
-// still needed -- the same set of keys, in one or two passes instead of three -- for
-// callers that only compact with it.
+// still needed -- the same set of keys in fewer passes -- for callers that only compact
+// with it.
 template <int KPT, int NT, bool EXACT = true>
 __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, int k,
                                           uint32_t* hist, int* tmp, int* sh) {
-    constexpr int G = KPT / 4;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+    constexpr int G = KPT / 4, NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kHistBins / 4; i += NT)
+        reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) m = key[e] > m ? key[e] : m;
+    const uint32_t wmax = wave_extreme_u32<true>(m), wmin = wave_extreme_u32<false>(m);
+    if (lane == 0) {
+        tmp[w] = int(wmax);
+        tmp[NW + w] = int(wmin);
+    }
     __syncthreads();
-    // pass 1: bits 31..21
+    uint32_t kmax = 0, q = 0xffffffffu;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const uint32_t x = uint32_t(tmp[v]), y = uint32_t(tmp[NW + v]);
+        kmax = x > kmax ? x : kmax;
+        q = y < q ? y : q;
+    }
+    if (k > NT) q = 0;
+    q = uint32_t(__builtin_amdgcn_readfirstlane(int(q)));
+    kmax = uint32_t(__builtin_amdgcn_readfirstlane(int(kmax)));
+    const uint32_t range = kmax - q;
+    const int bits = range ? 32 - __builtin_clz(range) : 0;
+    const int s1 = bits > 11 ? bits - 11 : 0, s2 = s1 > 11 ? s1 - 11 : 0;
+    uint32_t* h1 = hist;
+    uint32_t* h2 = hist + 2048;
+    uint32_t* h3 = hist + 4096;
+    // pass 1: (key - q) >> s1 of every key >= q; a key below q counts into its lane's spare
+    // word instead (no branch, and no two lanes of an instruction on one word)
+    const uint32_t spare = uint32_t(kHistBins + lane);
 #pragma unroll
     for (int i = 0; i < G; ++i)
         if (i < ngv) {
 #pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e) atomicAdd(&hist[key[e] >> 21], 1u);
+            for (int e = 4 * i; e < 4 * i + 4; ++e)
+                atomicAdd(&hist[key[e] >= q ? (key[e] - q) >> s1 : spare], 1u);
         }
     __syncthreads();
-    find_bucket<NT>(hist, 2048, k, tmp, sh);
-    const uint32_t d1 = uint32_t(sh[0]);
+    find_bucket<NT>(h1, 2048, k, tmp, sh);
+    const uint32_t b1 = uint32_t(sh[0]);
     int rem = sh[1];
-    if (!EXACT && sh[2] == rem && d1 > 0) return RegSelect{(d1 << 21) - 1u, 0};
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-    __syncthreads();
-    // pass 2: bits 20..10 of the keys in bucket d1
+    const uint32_t lo1 = q + (b1 << s1);               // lowest key of bin b1
+    if (!EXACT && sh[2] == rem && lo1 > 0) return RegSelect{lo1 - 1u, 0};
+    if (s1 == 0) return RegSelect{lo1, rem};          // a bin per key value
+    // pass 2: ((key - q) >> s2) mod 2048 of the keys in bin b1 (2^(s1 - s2) <= 2048 values,
+    // aligned, so the order holds)
 #pragma unroll
     for (int i = 0; i < G; ++i)
         if (i < ngv) {
 #pragma unroll
             for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if ((key[e] >> 21) == d1) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
+                if (key[e] >= q && ((key[e] - q) >> s1) == b1) atomicAdd(&h2[((key[e] - q) >> s2) & 2047u], 1u);
         }
     __syncthreads();
-    find_bucket<NT>(hist, 2048, rem, tmp, sh);
-    const uint32_t pre = (d1 << 11) | uint32_t(sh[0]);
+    find_bucket<NT>(h2, 2048, rem, tmp, sh);
+    const uint32_t p2 = ((b1 << (s1 - s2)) & ~2047u) | uint32_t(sh[0]);   // (key - q) >> s2
     rem = sh[1];
-    if (!EXACT && sh[2] == rem && pre > 0) return RegSelect{(pre << 10) - 1u, 0};
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-    __syncthreads();
-    // pass 3: bits 9..0 of the keys with prefix (d1, d2)
+    const uint32_t lo2 = q + (p2 << s2);
+    if (!EXACT && sh[2] == rem && lo2 > 0) return RegSelect{lo2 - 1u, 0};
+    if (s2 == 0) return RegSelect{lo2, rem};
+    // pass 3: the low s2 (<= 10) bits of key - q for the keys with (key - q) >> s2 == p2
 #pragma unroll
     for (int i = 0; i < G; ++i)
         if (i < ngv) {
 #pragma unroll
             for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if ((key[e] >> 10) == pre) atomicAdd(&hist[key[e] & 1023u], 1u);
+                if (key[e] >= q && ((key[e] - q) >> s2) == p2) atomicAdd(&h3[(key[e] - q) & ((1u << s2) - 1u)], 1u);
         }
     __syncthreads();
-    find_bucket<NT>(hist, 1024, rem, tmp, sh);
-    return RegSelect{(pre << 10) | uint32_t(sh[0]), sh[1]};
+    find_bucket<NT>(h3, 1024, rem, tmp, sh);
+    const uint32_t t = lo2 + uint32_t(sh[0]);
+    if (!EXACT && sh[2] == sh[1] && t > 0) return RegSelect{t - 1u, 0};   // every tie taken
+    return RegSelect{t, sh[1]};
 }
 
 // Compaction in position order of the keys taken by `sel`.  Lane masks (the compare results
@@ -566,6 +621,43 @@ __device__ uint32_t reg_compact(const uint32_t (&key)[KPT], RegSelect sel, int (
             if (take[j]) emit(slot++, 4 * i + j, j0 + j);
     }
     return rest;
+}
+
+// Compaction in position order when the keys taken are exactly those above `thr` (no tie
+// split at the threshold, rem == 0): one compare per key, its ballot giving both the wave's
+// count and, through a chain of mbcnt over a group's four masks, a lane's first slot.
+// emit(slot, e, position) for every taken key; the slots are 0 .. taken - 1 over the
+// workgroup.  `wtot` holds NT / 64 ints.
+template <int KPT, int NT, class Emit>
+__device__ void reg_compact_gt(const uint32_t (&key)[KPT], uint32_t thr, int* wtot, Emit emit) {
+    constexpr int G = KPT / 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) cnt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
+    if (lane == 0) wtot[w] = cnt;
+    __syncthreads();
+    int o = 0;                                         // keys taken by the waves before
+#pragma unroll
+    for (int v = 0; v < NT / 64; ++v) o += v < w ? wtot[v] : 0;
+    o = __builtin_amdgcn_readfirstlane(o);
+    const int wbase = w * 64 * KPT + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        uint64_t m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = __builtin_amdgcn_ballot_w64(key[4 * i + j] > thr);
+        if ((m[0] | m[1] | m[2] | m[3]) == 0) continue;
+        uint32_t slot = uint32_t(o);                   // + taken keys of the lower lanes
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            slot = __builtin_amdgcn_mbcnt_hi(uint32_t(m[j] >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m[j]), slot));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (key[4 * i + j] > thr) emit(int(slot++), 4 * i + j, wbase + 256 * i + j);
+            o += int(__popcll(m[j]));
+        }
+    }
 }
 
 // Workgroup-wide max of a u32 over NT threads (`red` holds NT / 64 entries).
@@ -707,8 +799,8 @@ template <int KPT, int NT, int MODE>
 __global__ void __launch_bounds__(NT)
 topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     constexpr int G = KPT / 4;                         // groups of 4 keys per lane
-    __shared__ uint32_t hist[2048];
-    __shared__ int tmp[NT / 64];
+    __shared__ __align__(16) uint32_t hist[kHistWords];
+    __shared__ int tmp[2 * NT / 64];
     __shared__ int sh[4];
     __shared__ int wtot[2][NT / 64];
     const int b = blockIdx.y;
@@ -766,6 +858,21 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     const int ngv = __builtin_amdgcn_readfirstlane(
         max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a position below n
     const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.k, hist, tmp, sh);
+    if (rs.rem == 0 && a.k <= (MODE == SEL_CHUNK ? kHistWords / 2 : kHistWords)) {
+        // exactly k keys lie above the threshold: their values are staged in slot order in
+        // the histogram's memory (free once the threshold is known), then stored coalesced
+        int32_t* st = reinterpret_cast<int32_t*>(hist);
+        reg_compact_gt<KPT, NT>(key, rs.thr, wtot[0], [&](int slot, int e, int pos) {
+            st[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
+            if (MODE == SEL_CHUNK) st[a.k + slot] = int32_t(key[e]);
+        });
+        __syncthreads();
+        for (int i = tid; i < a.k; i += NT) {
+            out[i] = st[i];
+            if (MODE == SEL_CHUNK) okey[i] = uint32_t(st[a.k + i]);
+        }
+        return;
+    }
     reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
         if (MODE == SEL_CHUNK) okey[slot] = key[e];
         out[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
@@ -782,8 +889,8 @@ template <int KPT, int NT>
 __global__ void __launch_bounds__(NT)
 topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     constexpr int G = KPT / 4;
-    __shared__ uint32_t hist[2048];
-    __shared__ int tmp[NT / 64];
+    __shared__ __align__(16) uint32_t hist[kHistWords];
+    __shared__ int tmp[2 * NT / 64];
     __shared__ int sh[4];
     __shared__ int wtot[2][NT / 64];
     __shared__ uint32_t red[NT / 64];
@@ -955,8 +1062,8 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
         }
     }
     if constexpr (FUSE) {
-        __shared__ uint32_t hist[2048];
-        __shared__ int tmp[WAVES];
+        __shared__ __align__(16) uint32_t hist[kHistWords];
+        __shared__ int tmp[2 * WAVES];
         __shared__ int sh[4];
         __shared__ int wtot[2][WAVES];
         __shared__ uint32_t red[WAVES];
