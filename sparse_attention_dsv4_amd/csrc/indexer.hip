@@ -882,9 +882,11 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
 // Fused decode selection, stage 2: the k best of the scorer's per-workgroup candidates
 // (each group's m best rows in row order, groups in row order, so the list is in row order
 // and a tie goes to the lower row).  The result is exact when every row the scorer did not
-// pass on scores below the k-th candidate key T: each group's cutoff (its largest key not
-// passed on) is checked against T, and a query where some cutoff reaches T selects from its
-// full score keys instead (select_keys_mem), with the same result.
+// pass on ranks below every candidate taken: each group's cutoff (its largest key not passed
+// on) must be at or below the threshold when the k taken are exactly the candidates above
+// it, and below the k-th candidate key when a tie is split there; a query where some cutoff
+// fails that selects from its full score keys instead (select_keys_mem), with the same
+// result.
 template <int KPT, int NT>
 __global__ void __launch_bounds__(NT)
 topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
@@ -932,8 +934,16 @@ topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     }
     cut = block_max_u32<NT>(cut, red);
     const int ngv = __builtin_amdgcn_readfirstlane(max(0, min(G, (n - w * 64 * KPT + 255) / 256)));
-    const RegSelect rs = reg_select_threshold<KPT, NT>(key, ngv, a.k, hist, tmp, sh);
-    if (cut < rs.thr) {
+    const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.k, hist, tmp, sh);
+    if (rs.rem == 0 && cut <= rs.thr && a.k <= kHistWords) {
+        // the k candidates above rs.thr are taken, every row not passed on is at or below it
+        int32_t* st = reinterpret_cast<int32_t*>(hist);
+        reg_compact_gt<KPT, NT>(key, rs.thr, wtot[0], [&](int slot, int e, int) { st[slot] = crow[e]; });
+        __syncthreads();
+        for (int i = tid; i < a.k; i += NT) out[i] = st[i];
+        return;
+    }
+    if (rs.rem > 0 && cut < rs.thr) {                  // a tie split at the k-th key rs.thr
         reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int) { out[slot] = crow[e]; });
         return;
     }
@@ -1097,10 +1107,20 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
         }
         const int ngv = __builtin_amdgcn_readfirstlane(max(0, min(G, (n - w * 64 * KPT + 255) / 256)));
         const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.m, hist, tmp, sh);
-        uint32_t rest = reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
-            ck[slot] = key[e];
-            cr[slot] = int32_t(row0 + pos);
-        });
+        uint32_t rest = 0;                             // largest key not passed on
+        if (rs.rem == 0) {
+            reg_compact_gt<KPT, NT>(key, rs.thr, wtot[0], [&](int slot, int e, int pos) {
+                ck[slot] = key[e];
+                cr[slot] = int32_t(row0 + pos);
+            });
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) rest = key[e] <= rs.thr && key[e] > rest ? key[e] : rest;
+        } else {
+            rest = reg_compact<KPT, NT>(key, rs, wtot, [&](int slot, int e, int pos) {
+                ck[slot] = key[e];
+                cr[slot] = int32_t(row0 + pos);
+            });
+        }
         rest = block_max_u32<NT>(rest, red);
         if (threadIdx.x == 0) a.cutoff[q * a.n_groups + blockIdx.x] = rest;
     }
