@@ -157,3 +157,35 @@ def test_topk_mixed_dense_and_sparse_decode():
     sel = _run(rows_i, qi, w, positions, n_rows)
     assert list(sel[0, 0, :300]) == list(range(300)) and (sel[0, 0, 300:] == -1).all()
     _check(rows_i, qi, w, positions, sel, exact=False)
+
+
+@pytest.mark.parametrize("queries", ["few", "many"])
+@pytest.mark.parametrize("n_vis", [2048, 16384, 30000, 70001])
+@pytest.mark.parametrize("mode", ["equal", "quantised"])
+def test_topk_degenerate_scores(mode, n_vis, queries):
+    """Scores both sides compute exactly, with the k-th inside a block of equal scores.
+    'equal': a zero query, every score 0, so the k lowest rows are the selection.
+    'quantised': one head whose query is the unit vector on dim 0 (weight 1, the other
+    heads' weights 0), so a row's score is its first element, one of 128 bf16 values in
+    [1, 2) (a multiple of 2^-7, repeating with row index): each value is shared by many
+    rows, the selection's digit passes narrow down to one value and split its tie.  Row
+    counts and query counts reach each selection kernel (registers, fused, in memory)."""
+    B, S = (2, 3) if queries == "few" else (1, 65)
+    cap = n_vis + 8
+    g = 91 + n_vis
+    rows_i = synth.normal((B, cap, SPEC.index_dim), seed=g, stream="rows_i", dtype=torch.bfloat16,
+                          device="cuda")
+    qi = torch.zeros((B, S, SPEC.index_heads, SPEC.index_dim), dtype=torch.bfloat16, device="cuda")
+    w = synth.normal((B, S, SPEC.index_heads), seed=g, stream="w", device="cuda")
+    if mode == "quantised":
+        j = torch.arange(cap, device="cuda")
+        rows_i[:, :, 0] = (1.0 + ((j * 37) % 128).float() / 128.0).to(torch.bfloat16)
+        qi[:, :, 0, 0] = 1.0
+        w.zero_()
+        w[:, :, 0] = 1.0
+    positions = [[4 * n_vis - S - b + i for i in range(S)] for b in range(B)]
+    n_rows = [min(cap, (positions[b][-1] + 1) // 4) for b in range(B)]
+    sel = _run(rows_i, qi, w, positions, n_rows)
+    _check(rows_i, qi, w, positions, sel, exact=True)
+    if mode == "equal":
+        assert (sel == np.arange(SPEC.topk, dtype=np.int32)).all()
