@@ -528,9 +528,13 @@ __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, i
 #pragma unroll
     for (int i = 0; i < G; ++i)
         if (i < ngv) {
+            bool in[4];
 #pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if (key[e] >= q && ((key[e] - q) >> s1) == b1) atomicAdd(&h2[((key[e] - q) >> s2) & 2047u], 1u);
+            for (int j = 0; j < 4; ++j) in[j] = key[4 * i + j] >= q && ((key[4 * i + j] - q) >> s1) == b1;
+            if (__builtin_amdgcn_ballot_w64(in[0] || in[1] || in[2] || in[3]) == 0) continue;   // usual
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (in[j]) atomicAdd(&h2[((key[4 * i + j] - q) >> s2) & 2047u], 1u);
         }
     __syncthreads();
     find_bucket<NT>(h2, 2048, rem, tmp, sh);
@@ -543,9 +547,13 @@ __device__ RegSelect reg_select_threshold(const uint32_t (&key)[KPT], int ngv, i
 #pragma unroll
     for (int i = 0; i < G; ++i)
         if (i < ngv) {
+            bool in[4];
 #pragma unroll
-            for (int e = 4 * i; e < 4 * i + 4; ++e)
-                if (key[e] >= q && ((key[e] - q) >> s2) == p2) atomicAdd(&h3[(key[e] - q) & ((1u << s2) - 1u)], 1u);
+            for (int j = 0; j < 4; ++j) in[j] = key[4 * i + j] >= q && ((key[4 * i + j] - q) >> s2) == p2;
+            if (__builtin_amdgcn_ballot_w64(in[0] || in[1] || in[2] || in[3]) == 0) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (in[j]) atomicAdd(&h3[(key[4 * i + j] - q) & ((1u << s2) - 1u)], 1u);
         }
     __syncthreads();
     find_bucket<NT>(h3, 1024, rem, tmp, sh);
@@ -565,7 +573,8 @@ __device__ uint32_t reg_compact(const uint32_t (&key)[KPT], RegSelect sel, int (
                                 Emit emit) {
     constexpr int G = KPT / 4;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wbase = w * 64 * KPT + 4 * lane;
+    // lane index from mbcnt: positions computed afresh (see reg_compact_gt)
+    const int wbase = w * 64 * KPT + 4 * int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
     const uint32_t thr = sel.thr;
     const int rem = sel.rem;
     int ngt = 0, neq = 0;
@@ -626,22 +635,30 @@ __device__ uint32_t reg_compact(const uint32_t (&key)[KPT], RegSelect sel, int (
 // Compaction in position order when the keys taken are exactly those above `thr` (no tie
 // split at the threshold, rem == 0): one compare per key, its ballot giving both the wave's
 // count and, through a chain of mbcnt over a group's four masks, a lane's first slot.
-// emit(slot, e, position) for every taken key; the slots are 0 .. taken - 1 over the
-// workgroup.  `wtot` holds NT / 64 ints.
-template <int KPT, int NT, class Emit>
-__device__ void reg_compact_gt(const uint32_t (&key)[KPT], uint32_t thr, int* wtot, Emit emit) {
+// emit(slot, e, position) for every taken key.  WAVE_SLOTS: the slots are the wave's own,
+// 0 .. taken by the wave - 1 (no count pass, no barrier; the caller places the waves' runs);
+// else 0 .. taken - 1 over the workgroup, after a count pass (`wtot`: NT / 64 ints).
+// Returns the wave's count of keys taken.
+template <int KPT, int NT, bool WAVE_SLOTS = false, class Emit>
+__device__ int reg_compact_gt(const uint32_t (&key)[KPT], uint32_t thr, int* wtot, Emit emit) {
     constexpr int G = KPT / 4;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) cnt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
-    if (lane == 0) wtot[w] = cnt;
-    __syncthreads();
     int o = 0;                                         // keys taken by the waves before
+    if (!WAVE_SLOTS) {
+        int cnt = 0;
 #pragma unroll
-    for (int v = 0; v < NT / 64; ++v) o += v < w ? wtot[v] : 0;
-    o = __builtin_amdgcn_readfirstlane(o);
-    const int wbase = w * 64 * KPT + 4 * lane;
+        for (int e = 0; e < KPT; ++e) cnt += int(__popcll(__builtin_amdgcn_ballot_w64(key[e] > thr)));
+        if (lane == 0) wtot[w] = cnt;
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < NT / 64; ++v) o += v < w ? wtot[v] : 0;
+        o = __builtin_amdgcn_readfirstlane(o);
+    }
+    const int o0 = o;
+    // the lane index from mbcnt rather than threadIdx: positions computed afresh here, not
+    // kept in registers from the callers' loads, which compute the same expressions (32 more
+    // registers live through the whole select)
+    const int wbase = w * 64 * KPT + 4 * int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         uint64_t m[4];
@@ -658,6 +675,7 @@ __device__ void reg_compact_gt(const uint32_t (&key)[KPT], uint32_t thr, int* wt
             o += int(__popcll(m[j]));
         }
     }
+    return o - o0;
 }
 
 // Workgroup-wide max of a u32 over NT threads (`red` holds NT / 64 entries).
@@ -858,9 +876,38 @@ topk_select_reg_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
     const int ngv = __builtin_amdgcn_readfirstlane(
         max(0, min(G, (n - w * 64 * KPT + 255) / 256)));   // groups holding a position below n
     const RegSelect rs = reg_select_threshold<KPT, NT, false>(key, ngv, a.k, hist, tmp, sh);
-    if (rs.rem == 0 && a.k <= (MODE == SEL_CHUNK ? kHistWords / 2 : kHistWords)) {
-        // exactly k keys lie above the threshold: their values are staged in slot order in
-        // the histogram's memory (free once the threshold is known), then stored coalesced
+    constexpr int NW = NT / 64;
+    const int seg = a.k < 64 * KPT ? a.k : 64 * KPT;  // most keys one wave can take
+    if (rs.rem == 0 && NW * seg * (MODE == SEL_CHUNK ? 2 : 1) <= kHistWords) {
+        // exactly k keys lie above the threshold: each wave stages the values of those it
+        // holds in its own run of the histogram's memory (free once the threshold is known),
+        // in position order; then the workgroup stores the runs one after another, coalesced
+        int32_t* st = reinterpret_cast<int32_t*>(hist);
+        int32_t* sw = st + w * seg;
+        const int cnt = reg_compact_gt<KPT, NT, true>(key, rs.thr, nullptr, [&](int slot, int e, int pos) {
+            sw[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
+            if (MODE == SEL_CHUNK) sw[NW * seg + slot] = int32_t(key[e]);
+        });
+        if (lane == 0) wtot[0][w] = cnt;
+        __syncthreads();
+        int wc[NW];
+#pragma unroll
+        for (int v = 0; v < NW; ++v) wc[v] = wtot[0][v];
+        for (int i = tid; i < a.k; i += NT) {
+            int src = i, run = 0;                      // run v holds slots [sum wc[< v], + wc[v])
+#pragma unroll
+            for (int v = 0; v < NW - 1; ++v)
+                if (run == v && src >= wc[v]) {
+                    src -= wc[v];
+                    run = v + 1;
+                }
+            out[i] = st[run * seg + src];
+            if (MODE == SEL_CHUNK) okey[i] = uint32_t(st[NW * seg + run * seg + src]);
+        }
+        return;
+    }
+    if (rs.rem == 0 && a.k * (MODE == SEL_CHUNK ? 2 : 1) <= kHistWords) {
+        // the same with workgroup slots (a count pass first) when the waves' runs do not fit
         int32_t* st = reinterpret_cast<int32_t*>(hist);
         reg_compact_gt<KPT, NT>(key, rs.thr, wtot[0], [&](int slot, int e, int pos) {
             st[slot] = MODE == SEL_MERGE ? crow[e] : base + pos;
