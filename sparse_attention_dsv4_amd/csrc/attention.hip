@@ -493,8 +493,7 @@ __device__ __forceinline__ void prefill_tile(const AttnMfmaArgs& a, const TileCt
             }
         }
     }
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));       // this key half, this head
+    lmax = max_xor32(max_xor16(lmax));                  // this key half, this head
     if (g == 0) xch[0][nt][head] = lmax;
     lds_barrier();
     const float tmax = fmaxf(lmax, xch[0][nt ^ 1][head]);
@@ -638,8 +637,7 @@ attn_prefill_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     }
 
     // denominator of this lane's head: its lane group's keys, then both key halves
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = sum_xor32(sum_xor16(l_run));
     if (g == 0) xch[1][nt][head] = l_run;
     __syncthreads();
     const float l_tot = xch[1][0][head] + xch[1][1][head];
@@ -727,8 +725,7 @@ __device__ __forceinline__ void decode_chunk_pv(const float* sx, const unsigned 
             cmax = fmaxf(cmax, sv[ks][e]);
         }
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    cmax = max_xor32(max_xor16(cmax));
     if (first) {
         m_run = cmax;                         // o and l_run are still zero
     } else if (cmax > m_run + kLazy) {
@@ -1080,8 +1077,7 @@ attn_decode_kernel(AttnMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
     if (tok_dst != nullptr) *tok_dst = tok;
 
     // denominator of head 16 hg + l%16: sum over the four lane groups
-    l_run += __shfl_xor(l_run, 16, 64);
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = sum_xor32(sum_xor16(l_run));
     const int head = DHG * hg + l16;
     if (a.n_splits == 1) {
         const float z = a.sinks[head] * kLog2e;
@@ -1128,9 +1124,11 @@ __device__ __forceinline__ void load8_f32(const bf16* p, float (&v)[8]) {
 }
 
 // Merge the split partials of one query with the sink: weights 2^(m_i - M) / den.  One wave
-// per (query, head): lane l holds split l's (max, sum) and latent dims 8l .. 8l + 7.  The
-// partial-output loads of the first 8 splits go out before the weights are formed, the
-// weights reach every lane by readlane, and nothing passes through LDS.
+// per (query, head): lane l holds split l's (max, sum) (at most 32 splits) and latent dims
+// 8l .. 8l + 7.  The (max, sum) loads go out just before the first 8 splits' partial-output
+// loads, one round trip; M and the denominator are VALU reductions over the lanes (no LDS), each
+// lane forms its split's weight, and the weights reach every lane by readlane.  An empty split
+// (max -inf, sum 0) wrote no output: its stale values are skipped.
 template <typename P>
 __global__ void __launch_bounds__(64)
 attn_combine_kernel(AttnMfmaArgs a) {
@@ -1140,29 +1138,33 @@ attn_combine_kernel(AttnMfmaArgs a) {
     const int lane = threadIdx.x;
     const int n = a.n_splits;
     const size_t base = (size_t(b) * a.S + size_t(s)) * n;
-    const bool on = lane < n;
-    const float m = on ? a.part_ml[((base + lane) * MH + h) * 2] : -INFINITY;
-    const float l = on ? a.part_ml[((base + lane) * MH + h) * 2 + 1] : 0.f;
     const P* po = reinterpret_cast<const P*>(a.part_o) + (base * MH + h) * MD + 8 * lane;
-    float wl = 0.f;                           // weight of split `lane`
+    // (max, sum) first, the weights need it first; every load before any wait (no branch, and
+    // the fence keeps the compiler from sinking the partial loads below the reductions)
+    float2 t = *reinterpret_cast<const float2*>(a.part_ml + ((base + (lane < n ? lane : n - 1)) * MH + h) * 2);
+    const float sink = a.sinks[h];
+    float v[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load8_f32(po + size_t(i < n ? i : n - 1) * MH * MD, v[i]);
+    asm volatile("" ::: "memory");
+    if (lane >= n) t = make_float2(-INFINITY, 0.f);
+    const float z = sink * kLog2e;
+    const float M = fmaxf(wave_max_valu(t.x), z);
+    const float e = t.x == -INFINITY ? 0.f : exp2f(t.x - M);
+    const float den = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_sum_valu(t.y * e)))) +
+                      exp2f(z - M);
+    const float wl = e / den;                          // weight of split `lane`
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int g0 = 0; g0 < n; g0 += 8) {
-        float v[8][8];
+        if (g0 > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) load8_f32(po + size_t(g0 + i < n ? g0 + i : n - 1) * MH * MD, v[i]);
-        if (g0 == 0) {
-            const float z = a.sinks[h] * kLog2e;
-            const float M = wave_max(fmaxf(m, z));
-            const float e = m == -INFINITY ? 0.f : exp2f(m - M);
-            const float den = wave_sum(l * e) + exp2f(z - M);
-            wl = e / den;
+            for (int i = 0; i < 8; ++i) load8_f32(po + size_t(g0 + i < n ? g0 + i : n - 1) * MH * MD, v[i]);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            // an empty split (weight 0) wrote no output: its stale values are skipped
             const float wv = g0 + i < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), g0 + i)) : 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += wv != 0.f ? wv * v[i][e] : 0.f;
+            for (int c = 0; c < 8; ++c) acc[c] += wv != 0.f ? wv * v[i][c] : 0.f;
         }
     }
     bf16* ob = a.out + ((size_t(b) * a.S + size_t(s)) * MH + h) * MD + 8 * lane;

@@ -268,7 +268,7 @@ index_score_mfma_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
                     s1 = fmaf(wsc[1][i], relu_bits(c[v & 1][1][i]), s1);
                 }
                 const float sc = s0 + s1;
-                score[v] = sc + __shfl_xor(sc, 32, 64);
+                score[v] = sum_xor32(sc);
             }
         }
 #pragma unroll
@@ -367,7 +367,7 @@ index_score_rs_kernel(IdxMfmaArgs a, SeqInts pos0v, SeqInts n_rows) {
                     s1 = fmaf(cur.wsc[1][i], relu_bits(c[v & 1][1][i]), s1);
                 }
                 float sc = s0 + s1;
-                sc += __shfl_xor(sc, 32, 64);
+                sc = sum_xor32(sc);
                 const int64_t jj = j_begin + 32 * v + l32;
                 if (hi == 0 && jj < nvq) keys[jj] = score_key(sc);
             }
@@ -681,11 +681,7 @@ __device__ int reg_compact_gt(const uint32_t (&key)[KPT], uint32_t thr, int* wto
 // Workgroup-wide max of a u32 over NT threads (`red` holds NT / 64 entries).
 template <int NT>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = uint32_t(__shfl_xor(int(v), o, 64));
-        v = y > v ? y : v;
-    }
+    v = wave_extreme_u32<true>(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -1099,7 +1095,7 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
                 s1 = fmaf(wsc[1][i], relu_bits(c1[i]), s1);
             }
             float sc = s0 + s1;
-            sc += __shfl_xor(sc, 32, 64);
+            sc = sum_xor32(sc);
             const int64_t jj = blk * 32 + l32;
             if (hi == 0 && jj < nv) {
                 const uint32_t kk = score_key(sc);
