@@ -691,6 +691,28 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
     return m;
 }
 
+// The decode scorer's waves per workgroup and the fused indexer's row groups (below).
+constexpr int kStreamWaves = 8;
+constexpr int kFuseMaxRows = 4096;                    // rows of one workgroup's local select
+constexpr int kFuseKpt = kFuseMaxRows / (64 * kStreamWaves);
+
+// Row groups of the fused scorer for a query of nbt 32-row blocks at bpw blocks per wave:
+// whole groups of WAVES bpw blocks, and a remainder of at most one block per wave goes to the
+// last group (its first waves take one block more: one longer wave instead of every wave's
+// count rounded up, which left a fifth of the chip idle at 65,538 rows); a larger remainder
+// makes a group of its own.  *extra: the blocks the last group takes beyond WAVES bpw.
+// (Only while the longer group still fits the local select's kFuseMaxRows.)
+__host__ __device__ inline int64_t fused_groups(int64_t nbt, int bpw, int waves, int* extra) {
+    const int64_t per = int64_t(waves) * bpw;
+    const int64_t g = nbt / per, r = nbt - g * per;
+    if (g > 0 && r <= waves && (bpw + 1) * 32 * waves <= kFuseMaxRows) {
+        *extra = int(r);
+        return g;
+    }
+    *extra = 0;
+    return g + (r > 0 ? 1 : 0);
+}
+
 struct SelArgs {
     int k, r;
     int64_t S;
@@ -951,7 +973,9 @@ topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
         for (int i = tid; i < a.k; i += NT) out[i] = i < nv ? i : -1;
         return;
     }
-    const int groups = (nv + a.f_rows_per_group - 1) / a.f_rows_per_group;
+    int extra_blocks;
+    const int groups = int(fused_groups((nv + 31) / 32, a.f_rows_per_group / (32 * kStreamWaves), kStreamWaves,
+                                        &extra_blocks));
     const int n = groups * a.f_m;                      // candidate positions (<= NT * KPT)
     const uint32_t* ck = a.f_key + q * size_t(a.f_groups) * a.f_m;
     const int32_t* cr = a.f_row + q * size_t(a.f_groups) * a.f_m;
@@ -1007,9 +1031,6 @@ topk_fused_merge_kernel(SelArgs a, SeqInts pos0, SeqInts n_rows) {
 // their keys in LDS as well, and after the scan the workgroup selects its m best (key
 // descending, row ascending) by the same radix select and passes them on in row order, with
 // the largest key it leaves out; the merge kernel above takes the query's k best of those.
-constexpr int kStreamWaves = 8;
-constexpr int kFuseMaxRows = 4096;                    // rows of one workgroup's local select
-constexpr int kFuseKpt = kFuseMaxRows / (64 * kStreamWaves);
 
 __device__ __forceinline__ void idx_stream_block(const bf16* rows, int64_t blk, int64_t nv, uint4 (&kb)[8]) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
@@ -1035,7 +1056,11 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
     if (nv > n_rows.v[b]) nv = n_rows.v[b];
     const int64_t nbt = (nv + 31) / 32;                // 32-row blocks of this query
     const int bpw = a.rows_per_block / (32 * WAVES);   // blocks per wave
-    if (int64_t(blockIdx.x) * WAVES * bpw >= nbt) return;   // whole workgroup: no rows
+    int extra = 0;                                     // the fused last group's added blocks
+    const int64_t ngroups = FUSE ? fused_groups(nbt, bpw, WAVES, &extra)
+                                 : (nbt + int64_t(WAVES) * bpw - 1) / (int64_t(WAVES) * bpw);
+    if (int64_t(blockIdx.x) >= ngroups) return;        // whole workgroup: no rows
+    const int ex = int64_t(blockIdx.x) == ngroups - 1 ? extra : 0;
     __shared__ __attribute__((aligned(16))) unsigned char qs[IH * IROWB];
     {
         const bf16* qg = a.qi + (size_t(b) * a.S + size_t(s)) * IH * ID;
@@ -1046,8 +1071,9 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
         }
     }
     __syncthreads();
-    const int64_t blk0 = (int64_t(blockIdx.x) * WAVES + w) * bpw;
-    const int nb = blk0 >= nbt ? 0 : int(nbt - blk0 < bpw ? nbt - blk0 : bpw);   // this wave's blocks
+    const int64_t blk0 = int64_t(blockIdx.x) * WAVES * bpw + int64_t(w) * bpw + (w < ex ? w : ex);
+    const int wb = bpw + (w < ex ? 1 : 0);
+    const int nb = blk0 >= nbt ? 0 : int(nbt - blk0 < wb ? nbt - blk0 : wb);     // this wave's blocks
     const int64_t row0 = int64_t(blockIdx.x) * a.rows_per_block;                // the workgroup's first row
     __shared__ __attribute__((aligned(16))) uint32_t kl[FUSE ? kFuseMaxRows : 4];
     if (nb > 0) {
@@ -1122,7 +1148,8 @@ __device__ __forceinline__ void index_score_stream_body(const IdxMfmaArgs& a, co
         __shared__ uint32_t red[WAVES];
         __syncthreads();                               // every key of the workgroup in kl
         int64_t n64 = nv - row0;
-        n64 = n64 < a.rows_per_block ? n64 : a.rows_per_block;
+        const int64_t cap = a.rows_per_block + 32 * int64_t(ex);
+        n64 = n64 < cap ? n64 : cap;
         const int n = int(n64);                        // > 0: the workgroup has rows
         const size_t q = size_t(b) * a.S + size_t(s);
         uint32_t* ck = a.cand_key + (q * a.n_groups + blockIdx.x) * size_t(a.m);
@@ -1214,8 +1241,14 @@ FusedPlan fused_plan(bool mfma, int64_t S, int batch, int64_t n_max, int64_t n_m
     if (!mfma || S >= kIdxWaves || n_max <= k || n_min_sparse <= k) return f;
     const int64_t queries = int64_t(batch < kSeqSlice ? batch : kSeqSlice) * S;
     const int64_t nbt = (n_max + 31) / 32;
-    int64_t bpw = (nbt * queries + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
+    // blocks per wave: the fewest whose row groups still give at most one workgroup per CU over
+    // the call's queries, else an even share rounded up
+    int64_t bpw = nbt * queries / (256 * kStreamWaves);
     bpw = bpw < 1 ? 1 : bpw;
+    int extra;
+    if (bpw * 32 * kStreamWaves > kFuseMaxRows ||
+        fused_groups(nbt, int(bpw), kStreamWaves, &extra) * queries > 256)
+        bpw = (nbt * queries + 256 * kStreamWaves - 1) / (256 * kStreamWaves);
     if (bpw * 32 * kStreamWaves > kFuseMaxRows) return f;
     f.bpw = int(bpw);
     f.rows_per_group = f.bpw * 32 * kStreamWaves;
@@ -1223,7 +1256,7 @@ FusedPlan fused_plan(bool mfma, int64_t S, int batch, int64_t n_max, int64_t n_m
     const int64_t m = ((3 * int64_t(k) * f.rows_per_group + n_min_sparse - 1) / n_min_sparse + 31) / 32 * 32;
     if (m > 128) return f;
     f.m = int(m < 32 ? 32 : m);
-    f.groups = (n_max + f.rows_per_group - 1) / f.rows_per_group;
+    f.groups = fused_groups(nbt, f.bpw, kStreamWaves, &extra);
     if (f.groups * f.m > 8192) return f;
     f.on = true;
     return f;
