@@ -128,20 +128,18 @@ __device__ __forceinline__ void pool_part(const CompArgs<T>& a, int b, int j, in
             const bool prev = a.coff == 2 && half == 0;
             const int win = prev ? j - 1 : j;
             ok[q] = u < nslots && win >= 0;
-            if (ok[q]) {
-                const int col = half * D + cg * VEC;
-                const int t = win * r + sl;
-                if (t < lb) {
-                    const size_t o = (size_t(prev ? wmod0 : wmod1) * r + size_t(sl)) * W + col;
-                    v[q].load(sa0 + o);
-                    gt[q].load(sg0 + o);
-                } else {
-                    const size_t o = (size_t(b) * a.n_new + size_t(t - lb)) * W + col;
-                    v[q].load(a.lane_a + o);
-                    gt[q].load(a.lane_g + o);
-                }
-                ap[q].load(a.ape + size_t(sl) * W + col);
-            }
+            // every slot's loads go out unconditionally, their sources chosen by selects (loads
+            // under per-lane branches were each waited for before the next slot's went out); a
+            // slot that does not exist reads in bounds (channel group cg of the state's first
+            // slot and of the first APE row) and is masked below
+            const int col = ok[q] ? half * D + cg * VEC : cg * VEC;
+            const int t = win * r + sl;
+            const bool in_state = !ok[q] || t < lb;
+            const size_t os = ok[q] ? (size_t(prev ? wmod0 : wmod1) * r + size_t(sl)) * W + col : size_t(col);
+            const size_t ol = (size_t(b) * a.n_new + size_t(in_state ? 0 : t - lb)) * W + col;
+            v[q].load(in_state ? sa0 + os : a.lane_a + ol);
+            gt[q].load(in_state ? sg0 + os : a.lane_g + ol);
+            ap[q].load(a.ape + size_t(ok[q] ? sl : 0) * W + col);
             sl += ds;
             half += dh;
             if (sl >= r) {
