@@ -115,8 +115,8 @@ __global__ void __launch_bounds__(64 * kSmallWaves) gproj_small_kernel(GprojArgs
     for (int kb = 0; kb < KBW; ++kb) {
         uint4 xv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            xv[c] = tv ? *reinterpret_cast<const uint4*>(xrow + kb * 64 + 8 * c) : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < 4; ++c)   // lanes past T read token 0 (their columns are not stored)
+            xv[c] = *reinterpret_cast<const uint4*>(xrow + kb * 64 + 8 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = mfma32x32x16(as_bf16x8(wv[kb][j]), as_bf16x8(xv[j]), acc);
     }
